@@ -1,0 +1,615 @@
+/*
+ * fp4q_oracle.c -- CPU oracle for block-scaled FP4 quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call this file:
+ * only tests/, the smoke check and the benchmark's CPU-baseline leg load it.
+ * It shares no code, header, table or constant generator with the HIP library.
+ *
+ * Plain, slow, single-threaded C99.  Every floating-point operation is an IEEE
+ * binary32 operation rounded to nearest-even unless stated otherwise; build with
+ * -O1 -ffp-contract=off and never with -ffast-math, so that fl(a*b) and fl(a+b)
+ * stay separate roundings.  fmaf() is used only where the reading adopted below
+ * asks for one fused rounding.
+ *
+ * Sources (cited by page and section, nothing else):
+ *  [NV]  qiita.com/nishiha/items/b98c2b931d588c4c81d5 -- notes on NVIDIA's NVFP4
+ *        pretraining recipe; sections "NVFP4データの変換" (E2M1), "2D scaling",
+ *        "ランダムアダマール変換" (RHT), "確率的丸め" (SR), "NVFP4の表現できる最大値",
+ *        "scaleの導出" (two-level scale).
+ *  [GL]  ultralytics.com/ja/glossary/fp4 -- glossary "FP4"; section "FP4の仕組み"
+ *        (MXFP4 / NVFP4 definitions and the block-size MAE snippet).
+ *  [IF]  gist.science/ja/paper/2603.28765 -- explainer of "Adaptive Block-Scaled
+ *        Data Types"; section "2. 提案手法：IF4" (IF4, the sign-bit flag, the 6/7
+ *        rule) and section "3. 主要な貢献" (Table 1).
+ *  [F6]  blog.ast.moe/blog/2026-09-24 -- "FP6から考えるLLM量子化"; section
+ *        "FP6で隣り合う値の間隔を見てみる" (E8M0 conversion with round-to-nearest-even).
+ *  [PX]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+ *        SC'11 -- the Philox4x32-10 counter-based generator (not on the pages; the
+ *        method asks for a Philox stream keyed on (seed, element index)).
+ *
+ * Readings taken where the pages are silent are listed in the repository's design
+ * notes; each function states the one it uses.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <float.h>
+
+#include "fp4q_oracle.h"
+
+/* ------------------------------------------------------------------------- */
+/* Philox4x32-10 [PX]                                                         */
+/* ------------------------------------------------------------------------- */
+
+/* Ten rounds of the Philox-4x32 bijection.  One round multiplies counter words 0
+ * and 2 by the two round constants (full 64-bit products), then permutes and
+ * whitens with the round key: new = (hi(M1*c2)^c1^k0, lo(M1*c2), hi(M0*c0)^c3^k1,
+ * lo(M0*c0)).  The key is advanced by the two Weyl constants between rounds. */
+void ora_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        uint64_t p0 = (uint64_t)M0 * (uint64_t)c0;
+        uint64_t p1 = (uint64_t)M1 * (uint64_t)c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The 16-bit uniform used by stochastic rounding for element `idx` (row-major index
+ * in the logical quantized matrix) of stream `stream` (0: row-wise, 2D and MXFP4
+ * outputs; 1: the column-wise output, i.e. the matrix X^T).  One Philox call serves
+ * eight consecutive elements: counter {lo32(idx/8), hi32(idx/8), stream, 0}, key
+ * {lo32(seed), hi32(seed)}; element idx takes 16-bit half (idx & 1) of word
+ * (idx / 2) & 3, low half first. */
+uint32_t ora_sr_bits16(uint64_t seed, uint32_t stream, uint64_t idx)
+{
+    uint64_t group = idx >> 3;
+    uint32_t ctr[4] = {(uint32_t)group, (uint32_t)(group >> 32), stream, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    ora_philox4x32_10(ctr, key, out);
+    uint32_t word = out[(idx >> 1) & 3];
+    return (idx & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+/* The RHT's random diagonal S: 128 signs from one Philox call with counter
+ * {0,0,0,1} (the last word keeps this stream apart from the SR stream) and key
+ * {lo32(seed), hi32(seed)}.  Bit t (word t/32, bit t%32) set means s_t = -1. */
+void ora_rht_signs(uint64_t seed, uint32_t signs[4])
+{
+    uint32_t ctr[4] = {0u, 0u, 0u, 1u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    ora_philox4x32_10(ctr, key, signs);
+}
+
+/* ------------------------------------------------------------------------- */
+/* E2M1 element format [NV "NVFP4データの変換"], [GL "FP4の仕組み"]               */
+/* ------------------------------------------------------------------------- */
+
+/* Magnitudes of the eight non-negative E2M1 codes: e=0 gives 0.5*m, e>0 gives
+ * (1 + 0.5*m) * 2^(e-1), for the 3-bit magnitude code (e1 e0 m). */
+static const float E2M1_MAG[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* Nibble layout s e1 e0 m: bit 3 is the sign. */
+float ora_e2m1_decode(uint8_t nibble)
+{
+    float m = E2M1_MAG[nibble & 7];
+    return (nibble & 8) ? -m : m;
+}
+
+/* Round-to-nearest onto the E2M1 grid.  Reading: ties go to the even code (the
+ * IEEE default; the code's last bit is the mantissa bit), magnitudes beyond 6
+ * saturate to 6 (E2M1 has no infinity), and the sign bit is copied from v so -0
+ * and small negatives give 0x8. */
+uint8_t ora_e2m1_rtn(float v)
+{
+    double a = fabs((double)v);
+    if (a >= 6.0) return (uint8_t)(7 | (signbit(v) ? 8 : 0));   /* at or beyond the maximum */
+    int best = 0;
+    double best_d = a;                     /* distance to magnitude 0 */
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - (double)E2M1_MAG[c]);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 8 : 0));
+}
+
+/* Stochastic rounding onto the E2M1 grid [NV "確率的丸め"]: the page's
+ * Round(x + U(-1/2, 1/2)) on a unit grid is floor(x + u) with u ~ U[0, 1).  On the
+ * E2M1 grid this is done on the local interval [lo, hi] that holds a = |v|:
+ * with frac = (a - lo) / (hi - lo) the value rounds up iff frac + u >= 1, where
+ * u = r16 / 2^16 comes from the Philox stream.  |v| >= 6 gives 6.  Sign copied. */
+uint8_t ora_e2m1_sr(float v, uint32_t r16)
+{
+    double a = fabs((double)v);
+    int c;
+    if (a >= 6.0) {
+        c = 7;
+    } else {
+        int lo = 0;
+        for (int k = 0; k < 7; ++k)
+            if ((double)E2M1_MAG[k] <= a) lo = k;
+        double step = (double)E2M1_MAG[lo + 1] - (double)E2M1_MAG[lo];
+        double frac = (a - (double)E2M1_MAG[lo]) / step;      /* exact in binary64 */
+        double u = (double)(r16 & 0xFFFFu) / 65536.0;
+        c = (frac >= 1.0 - u) ? lo + 1 : lo;                   /* frac + u >= 1, exactly */
+    }
+    return (uint8_t)(c | (signbit(v) ? 8 : 0));
+}
+
+/* ------------------------------------------------------------------------- */
+/* E4M3 (fn) block scale [NV "NVFP4の表現できる最大値", "scaleの導出"]            */
+/* ------------------------------------------------------------------------- */
+
+/* Value of a non-negative E4M3 code: exponent bias 7, subnormal step 2^-9. */
+float ora_e4m3_decode(uint8_t code)
+{
+    int e = (code >> 3) & 15, m = code & 7;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (float)((code & 0x80) ? -v : v);
+}
+
+/* Nearest non-negative E4M3 value to y >= 0 by exhaustive search over the 127
+ * finite codes 0x00..0x7E; ties go to the even code.  y >= 448 (the format's
+ * maximum) saturates to 0x7E; 0x7F (NaN) is never produced. */
+uint8_t ora_e4m3_encode(float y)
+{
+    if (!(y > 0.0f)) return 0;
+    if (y >= 448.0f) return 0x7E;
+    int best = 0;
+    double best_d = (double)y;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs((double)y - (double)ora_e4m3_decode((uint8_t)c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* ------------------------------------------------------------------------- */
+/* E8M0 power-of-two scale [GL "FP4の仕組み"], [F6]                              */
+/* ------------------------------------------------------------------------- */
+
+float ora_e8m0_decode(uint8_t code)
+{
+    return (float)ldexp(1.0, (int)code - 127);
+}
+
+/* Round y > 0 to the nearest power of two in value (round-to-nearest-even on the
+ * significand: below 1.5 rounds down, above 1.5 up, exactly 1.5 goes to the even
+ * code), then clamp the code to 0..254 (2^-127 .. 2^127).  y = 0 gives code 0. */
+uint8_t ora_e8m0_encode(float y)
+{
+    if (!(y > 0.0f)) return 0;
+    int e;
+    double m = frexp((double)y, &e);       /* y = m * 2^e, m in [0.5, 1) */
+    double sig = 2.0 * m;                  /* y = sig * 2^(e-1), sig in [1, 2) */
+    int k = e - 1;
+    if (sig > 1.5) {
+        k += 1;
+    } else if (sig == 1.5) {
+        if (((k + 127) & 1) != 0) k += 1;  /* tie: even code of {k+127, k+128} */
+    }
+    int code = k + 127;
+    if (code < 0) code = 0;
+    if (code > 254) code = 254;
+    return (uint8_t)code;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Tensor scale [NV "scaleの導出"]                                              */
+/* ------------------------------------------------------------------------- */
+
+static float load_elem(const void* x, int dtype, int64_t i)
+{
+    if (dtype == ORA_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t*)x)[i] << 16;
+        float f;
+        memcpy(&f, &bits, 4);
+        return f;
+    }
+    return ((const float*)x)[i];
+}
+
+float ora_amax(const void* x, int dtype, int64_t n)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(load_elem(x, dtype, i));
+        if (a > m) m = a;
+    }
+    return m;
+}
+
+/* Global (encode) scale = 6 * 448 / amax, so that the tensor's largest magnitude
+ * lands on the largest NVFP4 value 2688.  Reading for the cases the page leaves
+ * open: amax = 0 gives 1, and a quotient that overflows binary32 is clamped to
+ * FLT_MAX. */
+float ora_tensor_scale(float amax)
+{
+    if (!(amax > 0.0f)) return 1.0f;
+    float gs = 2688.0f / amax;
+    if (gs > FLT_MAX) gs = FLT_MAX;
+    return gs;
+}
+
+/* ------------------------------------------------------------------------- */
+/* NVFP4 with 1x16 and 16x16 blocks                                            */
+/* [NV "scaleの導出", "2D scaling"], [GL "FP4の仕組み"]                           */
+/* ------------------------------------------------------------------------- */
+
+/* Block scale from the block's largest magnitude: s = E4M3(fl(fl(bamax*gs)/6)).
+ * The page takes the block amax of x2 = x*gs and divides it by 6; rounding is
+ * monotone, so amax(fl(x*gs)) = fl(amax(x)*gs). */
+static uint8_t nvfp4_block_scale(float bamax, float gs)
+{
+    float y = (bamax * gs) / 6.0f;
+    return ora_e4m3_encode(y);
+}
+
+/* One element: v = fl(fl(x*gs)/s) (the page's x2 = x*gs, then x2 / scale), then
+ * E2M1.  A block whose scale rounded to zero quantizes every element to a signed
+ * zero. */
+static uint8_t nvfp4_elem(float x, float gs, float s, int rnd, uint32_t r16)
+{
+    if (s == 0.0f) return (uint8_t)(signbit(x) ? 8 : 0);
+    float t = x * gs;
+    float v = t / s;
+    return rnd == ORA_SR ? ora_e2m1_sr(v, r16) : ora_e2m1_rtn(v);
+}
+
+static void put_nibble(uint8_t* codes, int64_t byte_row_stride, int64_t r, int64_t c, uint8_t nib)
+{
+    uint8_t* p = codes + r * byte_row_stride + c / 2;
+    if (c & 1) *p = (uint8_t)((*p & 0x0F) | (nib << 4));
+    else       *p = (uint8_t)((*p & 0xF0) | (nib & 0x0F));
+}
+
+/* NVFP4 1x16 on the logical matrix L[lr][lc] = x[lr*sr + lc*sc] (row-wise: sr=cols,
+ * sc=1; column-wise: the logical matrix is X^T, sr=1, sc=cols).  Blocks are 16
+ * consecutive elements of a logical row.  Outputs: codes[lr][lc/2] (element 2k in
+ * the low nibble of byte k, 2k+1 in the high nibble) and scales[lr][lc/16].
+ * `row0` is the logical index of the first row handed in (0 for a whole matrix);
+ * it only shifts the SR stream index, which is (row0 + r) * lcols + c. */
+void ora_quantize_nvfp4_strided(const void* x, int dtype, int64_t lrows, int64_t lcols,
+                                int64_t sr, int64_t sc, float gs, int rnd, uint64_t seed,
+                                uint32_t stream, int64_t row0, uint8_t* codes, uint8_t* scales)
+{
+    for (int64_t r = 0; r < lrows; ++r) {
+        for (int64_t b = 0; b < lcols / 16; ++b) {
+            float bamax = 0.0f;
+            for (int64_t k = 0; k < 16; ++k) {
+                float a = fabsf(load_elem(x, dtype, r * sr + (b * 16 + k) * sc));
+                if (a > bamax) bamax = a;
+            }
+            uint8_t sc8 = nvfp4_block_scale(bamax, gs);
+            float s = ora_e4m3_decode(sc8);
+            scales[r * (lcols / 16) + b] = sc8;
+            for (int64_t k = 0; k < 16; ++k) {
+                int64_t c = b * 16 + k;
+                float xv = load_elem(x, dtype, r * sr + c * sc);
+                uint32_t r16 = rnd == ORA_SR ? ora_sr_bits16(seed, stream, (uint64_t)((row0 + r) * lcols + c)) : 0u;
+                put_nibble(codes, lcols / 2, r, c, nvfp4_elem(xv, gs, s, rnd, r16));
+            }
+        }
+    }
+}
+
+void ora_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, int colwise,
+                        float gs, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales)
+{
+    if (colwise)
+        ora_quantize_nvfp4_strided(x, dtype, cols, rows, 1, cols, gs, rnd, seed, 1u, 0, codes, scales);
+    else
+        ora_quantize_nvfp4_strided(x, dtype, rows, cols, cols, 1, gs, rnd, seed, 0u, 0, codes, scales);
+}
+
+/* NVFP4 with 16x16 blocks for weights [NV "2D scaling"]: one E4M3 scale per 16x16
+ * tile (scales[rows/16][cols/16]), so quantizing W^T gives the transpose of the
+ * codes and scales of W.  Round-to-nearest only. */
+void ora_quantize_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, float gs,
+                           uint8_t* codes, uint8_t* scales)
+{
+    for (int64_t br = 0; br < rows / 16; ++br) {
+        for (int64_t bc = 0; bc < cols / 16; ++bc) {
+            float bamax = 0.0f;
+            for (int64_t i = 0; i < 16; ++i)
+                for (int64_t j = 0; j < 16; ++j) {
+                    float a = fabsf(load_elem(x, dtype, (br * 16 + i) * cols + bc * 16 + j));
+                    if (a > bamax) bamax = a;
+                }
+            uint8_t sc8 = nvfp4_block_scale(bamax, gs);
+            float s = ora_e4m3_decode(sc8);
+            scales[br * (cols / 16) + bc] = sc8;
+            for (int64_t i = 0; i < 16; ++i)
+                for (int64_t j = 0; j < 16; ++j) {
+                    int64_t r = br * 16 + i, c = bc * 16 + j;
+                    float xv = load_elem(x, dtype, r * cols + c);
+                    put_nibble(codes, cols / 2, r, c, nvfp4_elem(xv, gs, s, ORA_RTN, 0u));
+                }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* MXFP4: 32 elements + one E8M0 scale [GL "FP4の仕組み"], [F6]                  */
+/* ------------------------------------------------------------------------- */
+
+/* Reading: the block scale is amax/6 (the block's largest magnitude maps to about
+ * 6) rounded to a power of two with round-to-nearest-even; elements are divided by
+ * that power of two (one rounding, exact unless the result is subnormal) and
+ * rounded onto E2M1 (RTN, or SR with stream 0).  No tensor scale. */
+void ora_quantize_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, int rnd,
+                        uint64_t seed, uint8_t* codes, uint8_t* scales)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            float bamax = 0.0f;
+            for (int64_t k = 0; k < 32; ++k) {
+                float a = fabsf(load_elem(x, dtype, r * cols + b * 32 + k));
+                if (a > bamax) bamax = a;
+            }
+            uint8_t e8 = ora_e8m0_encode(bamax / 6.0f);
+            scales[r * (cols / 32) + b] = e8;
+            int k_exp = (int)e8 - 127;
+            for (int64_t k = 0; k < 32; ++k) {
+                int64_t c = b * 32 + k;
+                float v = ldexpf(load_elem(x, dtype, r * cols + c), -k_exp);
+                uint8_t nib;
+                if (rnd == ORA_SR)
+                    nib = ora_e2m1_sr(v, ora_sr_bits16(seed, 0u, (uint64_t)(r * cols + c)));
+                else
+                    nib = ora_e2m1_rtn(v);
+                put_nibble(codes, cols / 2, r, c, nib);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* IF4: per-block FP4 or INT4 [IF "2. 提案手法：IF4"]                           */
+/* ------------------------------------------------------------------------- */
+
+/* Each 16-element row block is quantized twice with the NVFP4 scale s:
+ *  - FP4: r_i = E2M1_RTN(v_i);
+ *  - INT4 with the 6/7 rule: q_i = clamp(rint(fl(v_i * fl(7/6))), -7, 7), restored
+ *    as r_i = fl(q_i * fl(6/7)), so both candidates span 0..6;
+ * and the candidate with the lower squared error sum_i (v_i - r_i)^2 is kept.
+ * Readings: the error is taken in the scaled domain (a common factor per block),
+ * summed for i = 0..15 in order, each term added with one fused multiply-add
+ * e = fma(d, d, e) after d = fl(v_i - r_i); INT4 wins only if strictly lower.
+ * The choice is flagged in the scale byte's sign bit (set = INT4); INT4 codes are
+ * two's-complement nibbles.  A zero-scale block is FP4 with signed zeros. */
+void ora_quantize_if4(const void* x, int dtype, int64_t rows, int64_t cols, float gs,
+                      uint8_t* codes, uint8_t* scales)
+{
+    const float c76 = 7.0f / 6.0f;
+    const float c67 = 6.0f / 7.0f;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < cols / 16; ++b) {
+            float xv[16], v[16];
+            float bamax = 0.0f;
+            for (int k = 0; k < 16; ++k) {
+                xv[k] = load_elem(x, dtype, r * cols + b * 16 + k);
+                float a = fabsf(xv[k]);
+                if (a > bamax) bamax = a;
+            }
+            uint8_t sc8 = nvfp4_block_scale(bamax, gs);
+            float s = ora_e4m3_decode(sc8);
+            uint8_t fp_nib[16], int_nib[16];
+            float e_fp = 0.0f, e_int = 0.0f;
+            for (int k = 0; k < 16; ++k) {
+                if (s == 0.0f) {
+                    fp_nib[k] = (uint8_t)(signbit(xv[k]) ? 8 : 0);
+                    int_nib[k] = 0;
+                    continue;
+                }
+                float t = xv[k] * gs;
+                v[k] = t / s;
+                fp_nib[k] = ora_e2m1_rtn(v[k]);
+                float rf = ora_e2m1_decode(fp_nib[k]);
+                float w = v[k] * c76;
+                float q = rintf(w);
+                if (q > 7.0f) q = 7.0f;
+                if (q < -7.0f) q = -7.0f;
+                float ri = q * c67;
+                int_nib[k] = (uint8_t)(((int)q) & 0xF);
+                float dfp = v[k] - rf;
+                float dint = v[k] - ri;
+                e_fp = fmaf(dfp, dfp, e_fp);
+                e_int = fmaf(dint, dint, e_int);
+            }
+            int use_int = (s != 0.0f) && (e_int < e_fp);
+            scales[r * (cols / 16) + b] = (uint8_t)(sc8 | (use_int ? 0x80 : 0));
+            for (int k = 0; k < 16; ++k)
+                put_nibble(codes, cols / 2, r, b * 16 + k, use_int ? int_nib[k] : fp_nib[k]);
+        }
+    }
+}
+
+/* INT4 restore of one two's-complement nibble under the 6/7 rule. */
+float ora_int4_decode(uint8_t nibble)
+{
+    int q = (nibble & 8) ? (int)(nibble & 0xF) - 16 : (int)(nibble & 0xF);
+    return (float)q * (6.0f / 7.0f);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dequantization                                                              */
+/* ------------------------------------------------------------------------- */
+
+static uint8_t get_nibble(const uint8_t* codes, int64_t cols, int64_t r, int64_t c)
+{
+    uint8_t byte = codes[r * (cols / 2) + c / 2];
+    return (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+}
+
+/* x_hat = fl(fl(r*s)/gs): the element value times its block scale, divided by the
+ * tensor's encode scale.  fmt: 0 NVFP4 1x16, 1 NVFP4 16x16, 3 IF4 (flag in scale
+ * bit 7 selects the INT4 restore).  MXFP4 (fmt 2): x_hat = r * 2^(code-127). */
+void ora_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, float gs,
+                    int64_t rows, int64_t cols, float* y)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t nib = get_nibble(codes, cols, r, c);
+            float out;
+            if (fmt == 2) {
+                uint8_t e8 = scales[r * (cols / 32) + c / 32];
+                out = ldexpf(ora_e2m1_decode(nib), (int)e8 - 127);
+            } else {
+                uint8_t sc8 = (fmt == 1) ? scales[(r / 16) * (cols / 16) + c / 16]
+                                         : scales[r * (cols / 16) + c / 16];
+                float s = ora_e4m3_decode((uint8_t)(sc8 & 0x7F));
+                float rv = (fmt == 3 && (sc8 & 0x80)) ? ora_int4_decode(nib) : ora_e2m1_decode(nib);
+                float p = rv * s;
+                out = p / gs;
+            }
+            y[r * cols + c] = out;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Random Hadamard transform [NV "ランダムアダマール変換"]                         */
+/* ------------------------------------------------------------------------- */
+
+/* Sylvester Hadamard entry: H[i][t] = (-1)^popcount(i & t), 128 x 128, H H^T = 128 I. */
+int ora_hadamard_entry(int i, int t)
+{
+    int p = 0;
+    for (int b = i & t; b; b >>= 1) p ^= (b & 1);
+    return p ? -1 : 1;
+}
+
+static int sign_of(const uint32_t signs[4], int t)
+{
+    return ((signs[t >> 5] >> (t & 31)) & 1u) ? -1 : 1;
+}
+
+/* Along the token (row) dimension, per chunk of 128 rows, with R = S*H/sqrt(128):
+ *   forward  B = R^T A:  B[128c+i][j] = (1/sqrt(128)) * sum_t H[i][t] s_t A[128c+t][j]
+ *   inverse  A = R B:    A[128c+t][j] = (1/sqrt(128)) * s_t * sum_i H[t][i] B[128c+i][j]
+ * Products and sums in binary64 (t or i ascending), one rounding to binary32 at the
+ * end.  R R^T = I, so the inverse undoes the forward transform. */
+void ora_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
+             int inverse, float* y)
+{
+    const double kappa = 1.0 / sqrt(128.0);
+    for (int64_t c0 = 0; c0 < rows; c0 += 128) {
+        for (int i = 0; i < 128; ++i) {
+            for (int64_t j = 0; j < cols; ++j) {
+                double acc = 0.0;
+                for (int t = 0; t < 128; ++t) {
+                    double a = (double)load_elem(x, dtype, (c0 + t) * cols + j);
+                    double h = (double)ora_hadamard_entry(i, t);
+                    if (!inverse) h *= (double)sign_of(signs, t);
+                    acc += h * a;
+                }
+                if (inverse) acc *= (double)sign_of(signs, i);
+                y[(c0 + i) * cols + j] = (float)(acc * kappa);
+            }
+        }
+    }
+}
+
+/* The RHT of one column j only, rows [0, rows): y[i] for the chosen column, so
+ * that sampled checks at full size need not transform the whole matrix. */
+void ora_rht_column(const void* x, int dtype, int64_t rows, int64_t cols, int64_t j,
+                    const uint32_t signs[4], float* y)
+{
+    const double kappa = 1.0 / sqrt(128.0);
+    for (int64_t c0 = 0; c0 < rows; c0 += 128) {
+        for (int i = 0; i < 128; ++i) {
+            double acc = 0.0;
+            for (int t = 0; t < 128; ++t) {
+                double a = (double)load_elem(x, dtype, (c0 + t) * cols + j);
+                acc += (double)ora_hadamard_entry(i, t) * (double)sign_of(signs, t) * a;
+            }
+            y[c0 + i] = (float)(acc * kappa);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* The glossary's block-size comparison [GL "FP4の仕組み"]                       */
+/* ------------------------------------------------------------------------- */
+
+/* Plain per-block scaling as the glossary describes it: scale = amax/6 kept as a
+ * binary32 value (no E4M3/E8M0 rounding), each |x|/scale goes to the nearest E2M1
+ * magnitude (ties to the smaller magnitude), and x_hat = sign(x) * g * scale.
+ * A zero block reconstructs to zero.  n must be a multiple of `block`. */
+void ora_plain_block_roundtrip(const float* x, int64_t n, int64_t block, float* y)
+{
+    for (int64_t b0 = 0; b0 < n; b0 += block) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < block; ++k)
+            if (fabsf(x[b0 + k]) > amax) amax = fabsf(x[b0 + k]);
+        float scale = amax / 6.0f;
+        for (int64_t k = 0; k < block; ++k) {
+            float xv = x[b0 + k];
+            if (scale == 0.0f) {
+                y[b0 + k] = 0.0f;
+                continue;
+            }
+            float q = fabsf(xv) / scale;
+            int best = 0;
+            float best_d = fabsf(q - E2M1_MAG[0]);
+            for (int c = 1; c < 8; ++c) {
+                float d = fabsf(q - E2M1_MAG[c]);
+                if (d < best_d) {
+                    best = c;
+                    best_d = d;
+                }
+            }
+            float sgn = xv > 0.0f ? 1.0f : (xv < 0.0f ? -1.0f : 0.0f);
+            y[b0 + k] = E2M1_MAG[best] * sgn * scale;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Array forms of the element codecs (plain loops, for the tests' sweeps)      */
+/* ------------------------------------------------------------------------- */
+
+void ora_e2m1_rtn_array(const float* v, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_e2m1_rtn(v[i]);
+}
+
+void ora_e2m1_sr_array(const float* v, const uint32_t* r16, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_e2m1_sr(v[i], r16[i]);
+}
+
+void ora_e4m3_encode_array(const float* y, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_e4m3_encode(y[i]);
+}
+
+void ora_e8m0_encode_array(const float* y, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_e8m0_encode(y[i]);
+}
+
+void ora_sr_bits16_array(uint64_t seed, uint32_t stream, const uint64_t* idx, int64_t n, uint32_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_sr_bits16(seed, stream, idx[i]);
+}

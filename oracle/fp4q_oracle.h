@@ -1,0 +1,61 @@
+/*
+ * fp4q_oracle.h -- declarations of the CPU oracle (test infrastructure only).
+ * See fp4q_oracle.c for the definitions and the passages each one follows.
+ * This header is private to oracle/: the HIP library never includes it.
+ */
+#ifndef FP4Q_ORACLE_H
+#define FP4Q_ORACLE_H
+
+#include <stdint.h>
+
+#define ORA_F32 0
+#define ORA_BF16 1
+#define ORA_RTN 0
+#define ORA_SR 1
+
+void ora_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+uint32_t ora_sr_bits16(uint64_t seed, uint32_t stream, uint64_t idx);
+void ora_rht_signs(uint64_t seed, uint32_t signs[4]);
+
+float ora_e2m1_decode(uint8_t nibble);
+uint8_t ora_e2m1_rtn(float v);
+uint8_t ora_e2m1_sr(float v, uint32_t r16);
+float ora_e4m3_decode(uint8_t code);
+uint8_t ora_e4m3_encode(float y);
+float ora_e8m0_decode(uint8_t code);
+uint8_t ora_e8m0_encode(float y);
+float ora_int4_decode(uint8_t nibble);
+
+float ora_amax(const void* x, int dtype, int64_t n);
+float ora_tensor_scale(float amax);
+
+void ora_quantize_nvfp4_strided(const void* x, int dtype, int64_t lrows, int64_t lcols,
+                                int64_t sr, int64_t sc, float gs, int rnd, uint64_t seed,
+                                uint32_t stream, int64_t row0, uint8_t* codes, uint8_t* scales);
+void ora_quantize_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, int colwise,
+                        float gs, int rnd, uint64_t seed, uint8_t* codes, uint8_t* scales);
+void ora_quantize_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, float gs,
+                           uint8_t* codes, uint8_t* scales);
+void ora_quantize_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, int rnd,
+                        uint64_t seed, uint8_t* codes, uint8_t* scales);
+void ora_quantize_if4(const void* x, int dtype, int64_t rows, int64_t cols, float gs,
+                      uint8_t* codes, uint8_t* scales);
+void ora_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, float gs,
+                    int64_t rows, int64_t cols, float* y);
+
+int ora_hadamard_entry(int i, int t);
+void ora_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
+             int inverse, float* y);
+void ora_rht_column(const void* x, int dtype, int64_t rows, int64_t cols, int64_t j,
+                    const uint32_t signs[4], float* y);
+
+void ora_plain_block_roundtrip(const float* x, int64_t n, int64_t block, float* y);
+
+
+
+void ora_e2m1_rtn_array(const float* v, int64_t n, uint8_t* out);
+void ora_e2m1_sr_array(const float* v, const uint32_t* r16, int64_t n, uint8_t* out);
+void ora_e4m3_encode_array(const float* y, int64_t n, uint8_t* out);
+void ora_e8m0_encode_array(const float* y, int64_t n, uint8_t* out);
+void ora_sr_bits16_array(uint64_t seed, uint32_t stream, const uint64_t* idx, int64_t n, uint32_t* out);
+#endif
