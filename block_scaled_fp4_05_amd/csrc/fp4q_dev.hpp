@@ -1,0 +1,215 @@
+// fp4q_dev.hpp -- device-side building blocks of libfp4q (gfx950 / CDNA4).
+//
+// Element codec: E2M1 values (+-0, 0.5, 1, 1.5, 2, 3, 4, 6) as on
+// qiita.com/nishiha/items/b98c2b931d588c4c81d5, section "NVFP4データの変換".  Block
+// scales: E4M3 (max 448, section "NVFP4の表現できる最大値") and E8M0 (power of two,
+// ultralytics.com/ja/glossary/fp4, section "FP4の仕組み").
+//
+// Arithmetic discipline: every quantity that decides a code is computed with the
+// same IEEE binary32 roundings as the reference definition (no contraction; this
+// file is compiled with -ffp-contract=off and uses fmaf only where stated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16 / f32 loads
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight consecutive elements starting at element index `i` (16-byte aligned).
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ p, int64_t i, float out[8]) {
+  uint4 w = *reinterpret_cast<const uint4*>(p + i);
+  out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+  out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+  out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
+  out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+}
+
+__device__ __forceinline__ void load8(const float* __restrict__ p, int64_t i, float out[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p + i);
+  float4 b = *reinterpret_cast<const float4*>(p + i + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// Division by a block scale, correctly rounded.
+//
+// The quotient fl(t / s) is formed from rs = fl(1/s) with one Newton-style
+// correction: q0 = fl(t*rs), the residual t - q0*s is exact in one FMA, and
+// q = fl(q0 + res*rs).  For every divisor with at most 4 significant bits (all
+// E4M3 values, and 6) this equals the correctly rounded quotient whenever
+// |t| >= 2^-90; the repository's host tests check all 2^23 dividend significands
+// against the divisors' 8 significands.  The residual is negated twice so that
+// t = -0 yields -0.  Below 2^-90 the result is within a few ulps, which leaves every
+// code unchanged (|t/s| < 2^-80 is far below the first rounding threshold).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float div_rs(float t, float s, float rs) {
+  float q0 = t * rs;
+  float res = -__builtin_fmaf(q0, s, -t);
+  return __builtin_fmaf(res, rs, q0);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 block scale (e4m3fn, saturating at 448).
+// The hardware conversion rounds to nearest-even but does not saturate, so the
+// input is clamped to 448 first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  y = __builtin_fminf(y, 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0u, false) & 0xFFu;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t code) {
+  // exponent bias 7, subnormal step 2^-9: rebuild the binary32 bit pattern
+  uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  if (e == 0) return (float)m * 0x1p-9f;
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// NVFP4 / IF4 block scale from the block max of |x*gs| (= fl(bamax*gs)):
+// s = E4M3(fl(p / 6)).  Division by 6 uses the same corrected reciprocal.
+__device__ __forceinline__ uint32_t nvfp4_scale_code(float p) {
+  const float six = 6.0f, r6 = 1.0f / 6.0f;   // fl(1/6), folded at compile time
+  return e4m3_encode(div_rs(p, six, r6));
+}
+
+// ---------------------------------------------------------------------------
+// E8M0 scale with round-to-nearest-even on the significand (MXFP4).
+// y = fl(bamax/6).  Normal y: (bits + 0x3FFFFF + exponent_lsb) >> 23 rounds the
+// significand to 0 bits, ties (significand exactly 1.5) to the even exponent code.
+// Subnormal y (< 2^-126): nearest of {2^-127, 2^-126} with the same tie rule.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e8m0_encode(float y) {
+  uint32_t b = __float_as_uint(y);
+  uint32_t code;
+  if (b >= 0x00800000u) {
+    code = (b + 0x3FFFFFu + ((b >> 23) & 1u)) >> 23;
+  } else {
+    code = b > 0x00600000u ? 1u : 0u;
+  }
+  return code > 254u ? 254u : code;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 conversion on the gfx950 scaled converts.
+// RTN: v_cvt_scalef32_pk_fp4_f32 rounds x / 2^exponent(scale) to nearest, ties to
+// the even code, saturating at 6, sign copied; src0 lands in the low nibble.  With
+// scale 1.0 it converts v itself.  `sel` picks the destination byte (others kept).
+// ---------------------------------------------------------------------------
+#define FP4Q_CVT_RTN(old, a, b, scale, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), (scale), (sel))
+
+// SR: the first element of v_cvt_scalef32_sr_pk_fp4_f32 rounds up iff
+// frac + r/2^32 >= 1 on its E2M1 interval, where r is the 32-bit random operand.
+// A 16-bit draw placed in the top half (low half zero) therefore gives exactly
+// "up iff frac + r16/2^16 >= 1".  The second element of a pair would consume r << 1,
+// so each element is converted alone with a second source of +0 (code 0).  Only
+// byte 0 of the result is defined: the builtin does not carry the old destination
+// value through, so the other bytes are whatever the register held.
+#define FP4Q_CVT_SR1(a, r32, scale) \
+  __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{(a), 0.0f}, (r32), (scale), 0)
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): multipliers 0xD2511F53 / 0xCD9E8D57,
+// Weyl key increments 0x9E3779B9 / 0xBB67AE85, ten rounds.
+// ---------------------------------------------------------------------------
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                       uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// Draws for the eight elements idx8*8 .. idx8*8+7 of SR stream `stream`:
+// element e uses the 16-bit half (e & 1) of word e >> 1, returned already placed in
+// the top 16 bits of a 32-bit word as the SR convert expects.
+__device__ __forceinline__ void sr_draws8(uint64_t idx8, uint32_t stream, uint32_t k0, uint32_t k1,
+                                          uint32_t r32[8]) {
+  U4 w = philox10((uint32_t)idx8, (uint32_t)(idx8 >> 32), stream, 0u, k0, k1);
+  r32[0] = w.x << 16; r32[1] = w.x & 0xFFFF0000u;
+  r32[2] = w.y << 16; r32[3] = w.y & 0xFFFF0000u;
+  r32[4] = w.z << 16; r32[5] = w.z & 0xFFFF0000u;
+  r32[6] = w.w << 16; r32[7] = w.w & 0xFFFF0000u;
+}
+
+// ---------------------------------------------------------------------------
+// Encoders for 8 scaled values -> one 32-bit word of 8 nibbles (element k in
+// bits 4k..4k+3).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack8_rtn(const float v[8], float scale) {
+  uint32_t w = 0;
+  w = FP4Q_CVT_RTN(w, v[0], v[1], scale, 0);
+  w = FP4Q_CVT_RTN(w, v[2], v[3], scale, 1);
+  w = FP4Q_CVT_RTN(w, v[4], v[5], scale, 2);
+  w = FP4Q_CVT_RTN(w, v[6], v[7], scale, 3);
+  return w;
+}
+
+__device__ __forceinline__ uint32_t pack8_sr(const float v[8], const uint32_t r32[8], float scale) {
+  uint32_t t[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = FP4Q_CVT_SR1(v[2 * k], r32[2 * k], scale);
+    const uint32_t hi = FP4Q_CVT_SR1(v[2 * k + 1], r32[2 * k + 1], scale);
+    t[k] = (hi << 4) | lo;                      // byte 0 = code(2k) | code(2k+1) << 4
+  }
+  const uint32_t u = __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0400u);   // [t0.b0, t1.b0, 0, 0]
+  const uint32_t w = __builtin_amdgcn_perm(t[3], t[2], 0x04000C0Cu);   // [0, 0, t2.b0, t3.b0]
+  return u | w;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64).
+// ---------------------------------------------------------------------------
+template <int XOR>
+__device__ __forceinline__ float lane_xor_max(float v) {
+  // quad_perm DPP for xor 1 / xor 2 within groups of four lanes
+  int iv = __float_as_int(v);
+  int other;
+  if constexpr (XOR == 1)
+    other = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+  else
+    other = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  return __builtin_fmaxf(v, __int_as_float(other));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Tensor encode scale gs = 2688 / amax (amax = 0 -> 1; overflow -> FLT_MAX),
+// [qiita.com/nishiha/items/b98c2b931d588c4c81d5, "scaleの導出"].
+__device__ __forceinline__ float tensor_scale_from_amax(float amax) {
+  if (!(amax > 0.0f)) return 1.0f;
+  float gs = __fdiv_rn(2688.0f, amax);
+  return __builtin_fminf(gs, 3.40282347e38f);
+}
+
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
+  // non-negative floats order like their bit patterns
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace fp4q

@@ -1,0 +1,37 @@
+// fp4q_internal.hpp -- launchers shared between the C-ABI layer and the kernel files.
+// Every launcher enqueues on `st` and assumes its arguments were validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t st);
+
+void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
+                  const float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
+                  uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, hipStream_t st);
+
+void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax,
+                     float* tensor_scale, uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st);
+
+void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
+                  uint8_t* scales, uint64_t seed, hipStream_t st);
+
+void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax,
+                float* tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t st);
+
+void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                    int64_t rows, int64_t cols, int out_dtype, void* y, hipStream_t st);
+
+// Random Hadamard transform along rows (chunks of 128) -- fp4q_rht.hip.
+void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
+                int inverse, float* y, hipStream_t st);
+void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4],
+                     float* amax, hipStream_t st);
+void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4],
+                          bool sr, uint64_t seed, const float* amax, float* tensor_scale,
+                          uint8_t* col_codes, uint8_t* col_scales, hipStream_t st);
+
+}  // namespace fp4q

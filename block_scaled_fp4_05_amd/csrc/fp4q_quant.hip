@@ -1,0 +1,545 @@
+// fp4q_quant.hip -- quantize / dequantize kernels of libfp4q (no RHT).
+//
+// Operations (pages cited by address and section):
+//  * NVFP4 1x16, row-wise and the transposed column-wise layout:
+//    qiita.com/nishiha/items/b98c2b931d588c4c81d5, "Blockwise", "誤差逆伝播と転置",
+//    "scaleの導出"; stochastic rounding: same page, "確率的丸め".
+//  * NVFP4 16x16 (weights): same page, "2D scaling".
+//  * MXFP4 32 + E8M0: ultralytics.com/ja/glossary/fp4, "FP4の仕組み"; RNE of the
+//    E8M0 conversion: blog.ast.moe/blog/2026-09-24, "FP6で隣り合う値の間隔を見てみる".
+//  * IF4: gist.science/ja/paper/2603.28765, "2. 提案手法：IF4".
+//
+// Every kernel is memory-streaming: 16-byte loads, per-block reductions in
+// registers or across neighbouring lanes (DPP), and packed nibble stores.
+#include "fp4q_dev.hpp"
+#include "fp4q_internal.hpp"
+
+namespace fp4q {
+
+// ===========================================================================
+// Tensor amax
+// ===========================================================================
+
+__global__ void k_zero1(float* p) { *p = 0.0f; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t n8, float* __restrict__ amax) {
+  // n8 = number of 8-element groups; 4 groups in flight per thread per trip
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; g + 3 * stride < n8; g += 4 * stride) {
+    float a[8], b[8], c[8], d[8];
+    load8(x, g * 8, a);
+    load8(x, (g + stride) * 8, b);
+    load8(x, (g + 2 * stride) * 8, c);
+    load8(x, (g + 3 * stride) * 8, d);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])),
+                                             __builtin_fmaxf(__builtin_fabsf(c[k]), __builtin_fabsf(d[k]))));
+  }
+  for (; g < n8; g += stride) {
+    float a[8];
+    load8(x, g * 8, a);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(a[k]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+}
+
+// amax over a tail of fewer than 8 elements (only for fp4q_amax on odd sizes)
+template <typename T>
+__global__ void k_amax_tail(const T* __restrict__ x, int64_t start, int64_t n, float* __restrict__ amax) {
+  int64_t i = start + threadIdx.x;
+  float m = 0.0f;
+  if (i < n) {
+    if constexpr (sizeof(T) == 2) m = __builtin_fabsf(__uint_as_float((uint32_t)x[i] << 16));
+    else m = __builtin_fabsf(x[i]);
+  }
+  m = wave_max(m);
+  if (threadIdx.x == 0) atomic_max_nonneg(amax, m);
+}
+
+static int amax_grid(int64_t n8) {
+  int64_t blocks = (n8 + 255) / 256;
+  return (int)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048);
+}
+
+template <typename T>
+static void launch_amax_t(const void* x, int64_t n, float* amax, hipStream_t st) {
+  const T* xp = static_cast<const T*>(x);
+  k_zero1<<<1, 1, 0, st>>>(amax);
+  int64_t n8 = n / 8;
+  if (n8 > 0) k_amax<T><<<amax_grid(n8), 256, 0, st>>>(xp, n8, amax);
+  if (n8 * 8 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n8 * 8, n, amax);
+}
+
+void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t st) {
+  if (dtype == 1) launch_amax_t<uint16_t>(x, n, amax, st);
+  else launch_amax_t<float>(x, n, amax, st);
+}
+
+// ===========================================================================
+// NVFP4 1x16, row-wise and/or column-wise, one pass over x.
+//
+// Workgroup tile: 128 rows x 128 cols (4 waves of 32 rows).  Lane layout inside a
+// wave: quads of four lanes own a 16x16 sub-tile; lane bit 0 picks the upper or
+// lower 8 rows, lane bit 1 the left or right 8 columns, so every lane holds an 8x8
+// micro-tile.  A row block (16 columns) is the lane pair (lane ^ 2) and a column
+// block (16 rows) the pair (lane ^ 1): both block maxima are one DPP max away.
+// The product t = x*gs is formed once and serves both layouts.
+// ===========================================================================
+
+template <typename T, bool ROW, bool COL, bool SR>
+__global__ __launch_bounds__(256) void k_nvfp4_tile(
+    const T* __restrict__ x, int64_t rows, int64_t cols, int tiles_c, int tiles_total,
+    const float* __restrict__ amax, float* __restrict__ tensor_scale,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
+    uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales,
+    uint32_t k0, uint32_t k1) {
+  const float gs = tensor_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+
+  // XCD-aware order: consecutive block ids go round-robin over the 8 XCDs, so
+  // give each XCD a contiguous run of tiles (neighbouring outputs share its L2).
+  int b = blockIdx.x;
+  int tile = b;
+  if ((tiles_total & 7) == 0) tile = (b & 7) * (tiles_total >> 3) + (b >> 3);
+  const int tr = tile / tiles_c, tc = tile - tr * tiles_c;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 2, h = (lane >> 1) & 1, vv = lane & 1;
+  const int64_t row0 = (int64_t)tr * 128 + wave * 32 + (q >> 3) * 16 + vv * 8;
+  const int64_t col0 = (int64_t)tc * 128 + (q & 7) * 16 + h * 8;
+  const bool col_ok = col0 < cols;
+
+  float t[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (col_ok && row0 + i < rows) {
+      load8(x, (row0 + i) * cols + col0, t[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[i][j] = t[i][j] * gs;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[i][j] = 0.0f;
+    }
+  }
+
+  if constexpr (ROW) {
+    const int64_t half_cols = cols >> 1, nb = cols >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
+      m = lane_xor_max<2>(m);
+      const uint32_t sc = nvfp4_scale_code(m);
+      const float s = e4m3_decode(sc);
+      const float s_eff = s == 0.0f ? 1.0f : s;
+      const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = div_rs(t[i][j], s_eff, rs);
+      const int64_t r = row0 + i;
+      uint32_t w;
+      if constexpr (SR) {
+        uint32_t rr[8];
+        sr_draws8((uint64_t)(r * cols + col0) >> 3, 0u, k0, k1, rr);
+        w = pack8_sr(v, rr, 1.0f);
+      } else {
+        w = pack8_rtn(v, 1.0f);
+      }
+      if (col_ok && r < rows) {
+        *reinterpret_cast<uint32_t*>(rcodes + r * half_cols + (col0 >> 1)) = w;
+        if (h == 0) rscales[r * nb + (col0 >> 4)] = (uint8_t)sc;
+      }
+    }
+  }
+
+  if constexpr (COL) {
+    const int64_t half_rows = rows >> 1, nb = rows >> 4;
+    const bool ok = col_ok && row0 < rows;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
+      m = lane_xor_max<1>(m);
+      const uint32_t sc = nvfp4_scale_code(m);
+      const float s = e4m3_decode(sc);
+      const float s_eff = s == 0.0f ? 1.0f : s;
+      const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = div_rs(t[i][j], s_eff, rs);
+      const int64_t c = col0 + j;
+      uint32_t w;
+      if constexpr (SR) {
+        uint32_t rr[8];
+        sr_draws8((uint64_t)(c * rows + row0) >> 3, 1u, k0, k1, rr);
+        w = pack8_sr(v, rr, 1.0f);
+      } else {
+        w = pack8_rtn(v, 1.0f);
+      }
+      if (ok) {
+        *reinterpret_cast<uint32_t*>(ccodes + c * half_rows + (row0 >> 1)) = w;
+        if (vv == 0) cscales[c * nb + (row0 >> 4)] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
+template <typename T, bool ROW, bool COL, bool SR>
+static void launch_nvfp4_t(const void* x, int64_t rows, int64_t cols, const float* amax,
+                           float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs,
+                           uint32_t k0, uint32_t k1, hipStream_t st) {
+  const int tiles_r = (int)((rows + 127) / 128), tiles_c = (int)((cols + 127) / 128);
+  const int total = tiles_r * tiles_c;
+  k_nvfp4_tile<T, ROW, COL, SR><<<total, 256, 0, st>>>(static_cast<const T*>(x), rows, cols, tiles_c,
+                                                       total, amax, tensor_scale, rc, rs, cc, cs, k0, k1);
+}
+
+template <typename T>
+static void launch_nvfp4_dt(const void* x, int64_t rows, int64_t cols, unsigned layouts, bool sr,
+                            const float* amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                            uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+  const bool row = layouts & 1u, col = layouts & 2u;
+#define FP4Q_NV(R, C, S) launch_nvfp4_t<T, R, C, S>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)
+  if (row && col) { if (sr) FP4Q_NV(true, true, true); else FP4Q_NV(true, true, false); }
+  else if (row)   { if (sr) FP4Q_NV(true, false, true); else FP4Q_NV(true, false, false); }
+  else            { if (sr) FP4Q_NV(false, true, true); else FP4Q_NV(false, true, false); }
+#undef FP4Q_NV
+}
+
+void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
+                  const float* amax, float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                  uint8_t* cs, uint64_t seed, hipStream_t st) {
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  if (dtype == 1)
+    launch_nvfp4_dt<uint16_t>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+  else
+    launch_nvfp4_dt<float>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+}
+
+// ===========================================================================
+// MXFP4: flat 1-D kernel, each lane owns half of a 32-element block (16 elements);
+// the pair (lane ^ 1) shares the block maximum.
+// ===========================================================================
+
+template <typename T, bool SR>
+__global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t n16,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                               uint32_t k0, uint32_t k1) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-element group
+  const bool ok = g < n16;
+  float a[8], b[8];
+  if (ok) {
+    load8(x, g * 16, a);
+    load8(x, g * 16 + 8, b);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = b[k] = 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])));
+  m = lane_xor_max<1>(m);
+  const uint32_t code = e8m0_encode(__fdiv_rn(m, 6.0f));   // exact also for subnormal quotients
+  // the converts use only the scale's exponent field: pass 2^(code-127) as its bits
+  const float scale = __uint_as_float(code << 23);
+  uint32_t w0, w1;
+  if constexpr (SR) {
+    uint32_t ra[8], rb[8];
+    sr_draws8((uint64_t)(g * 2), 0u, k0, k1, ra);
+    sr_draws8((uint64_t)(g * 2 + 1), 0u, k0, k1, rb);
+    w0 = pack8_sr(a, ra, scale);
+    w1 = pack8_sr(b, rb, scale);
+  } else {
+    w0 = pack8_rtn(a, scale);
+    w1 = pack8_rtn(b, scale);
+  }
+  if (ok) {
+    *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(w0, w1);
+    if ((threadIdx.x & 1) == 0) scales[g >> 1] = (uint8_t)code;
+  }
+}
+
+void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
+                  uint8_t* scales, uint64_t seed, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  const int grid = (int)((n16 + 255) / 256);
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  if (dtype == 1) {
+    if (sr) k_mxfp4<uint16_t, true><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, codes, scales, k0, k1);
+    else k_mxfp4<uint16_t, false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, codes, scales, k0, k1);
+  } else {
+    if (sr) k_mxfp4<float, true><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, codes, scales, k0, k1);
+    else k_mxfp4<float, false><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, codes, scales, k0, k1);
+  }
+}
+
+// ===========================================================================
+// IF4: flat kernel, one lane per 16-element row block.
+// ===========================================================================
+
+// Eight E2M1 nibbles -> values times 2^exponent(scale) (exact).
+__device__ __forceinline__ void decode8_fp4(uint32_t w, float scale, float r[8]) {
+  f32x2 d;
+  d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0); r[0] = d[0]; r[1] = d[1];
+  d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1); r[2] = d[0]; r[3] = d[1];
+  d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2); r[4] = d[0]; r[5] = d[1];
+  d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3); r[6] = d[0]; r[7] = d[1];
+}
+
+// INT4 candidate for 8 scaled values under the 6/7 rule: q = clamp(rint(v*fl(7/6)), -7, 7)
+// via the 1.5*2^23 rounding constant (its low nibble is q in two's complement), restored
+// as fl(q*fl(6/7)); accumulates both squared-error sums in element order.
+__device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[8], float& e_fp, float& e_int) {
+  const float c76 = 7.0f / 6.0f, c67 = 6.0f / 7.0f, magic = 12582912.0f;
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float wv = v[k] * c76;
+    wv = __builtin_amdgcn_fmed3f(wv, -7.0f, 7.0f);
+    const float y = wv + magic;
+    const float qf = y - magic;
+    const float ri = qf * c67;
+    w |= (__float_as_uint(y) & 0xFu) << (4 * k);
+    const float dfp = v[k] - rf[k];
+    const float dint = v[k] - ri;
+    e_fp = __builtin_fmaf(dfp, dfp, e_fp);
+    e_int = __builtin_fmaf(dint, dint, e_int);
+  }
+  return w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n16, const float* __restrict__ amax,
+                                             float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  const float gs = tensor_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n16) return;
+  float a[8], b[8];
+  load8(x, g * 16, a);
+  load8(x, g * 16 + 8, b);
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = a[k] * gs;
+    b[k] = b[k] * gs;
+    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])));
+  }
+  const uint32_t sc = nvfp4_scale_code(m);
+  const float s = e4m3_decode(sc);
+  const float s_eff = s == 0.0f ? 1.0f : s;
+  const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = div_rs(a[k], s_eff, rs);
+    b[k] = div_rs(b[k], s_eff, rs);
+  }
+  const uint32_t fa = pack8_rtn(a, 1.0f), fb = pack8_rtn(b, 1.0f);
+  float ra[8], rb[8];
+  decode8_fp4(fa, 1.0f, ra);
+  decode8_fp4(fb, 1.0f, rb);
+  float e_fp = 0.0f, e_int = 0.0f;
+  const uint32_t ia = if4_block8(a, ra, e_fp, e_int);
+  const uint32_t ib = if4_block8(b, rb, e_fp, e_int);
+  const bool use_int = e_int < e_fp;
+  *reinterpret_cast<uint2*>(codes + g * 8) = use_int ? make_uint2(ia, ib) : make_uint2(fa, fb);
+  scales[g] = (uint8_t)(sc | (use_int ? 0x80u : 0u));
+}
+
+void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax, float* tensor_scale,
+                uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  const int grid = (int)((n16 + 255) / 256);
+  if (dtype == 1)
+    k_if4<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, amax, tensor_scale, codes, scales);
+  else
+    k_if4<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, amax, tensor_scale, codes, scales);
+}
+
+// ===========================================================================
+// NVFP4 16x16 (2D).  Sixteen lanes own one 16x16 tile, one tile row each; a wave
+// holds four horizontally adjacent tiles.  The tile maximum is a 16-lane DPP
+// reduction.  The optional transposed codes go through LDS.
+// ===========================================================================
+
+__device__ __forceinline__ float max16_lanes(float v) {
+  v = lane_xor_max<1>(v);
+  v = lane_xor_max<2>(v);
+  // rotate within rows of 16 lanes by 4 and 8
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
+
+template <typename T, bool TRANS>
+__global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                  const float* __restrict__ amax, float* __restrict__ tensor_scale,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  uint8_t* __restrict__ codes_t) {
+  __shared__ uint32_t lds[16][16][2];   // [tile in block][row][8 bytes]
+  const float gs = tensor_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  const int64_t tiles_c = cols >> 4, tiles = (rows >> 4) * tiles_c;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tin = lane >> 4, i = lane & 15;                 // tile within wave, row within tile
+  const int64_t tile = ((int64_t)blockIdx.x * 4 + wave) * 4 + tin;
+  const bool ok = tile < tiles;
+  const int64_t br = ok ? tile / tiles_c : 0, bc = ok ? tile - br * tiles_c : 0;
+  const int64_t r = br * 16 + i, c0 = bc * 16;
+  float a[8], b[8];
+  if (ok) {
+    load8(x, r * cols + c0, a);
+    load8(x, r * cols + c0 + 8, b);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = b[k] = 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = a[k] * gs;
+    b[k] = b[k] * gs;
+    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])));
+  }
+  m = max16_lanes(m);
+  const uint32_t sc = nvfp4_scale_code(m);
+  const float s = e4m3_decode(sc);
+  const float s_eff = s == 0.0f ? 1.0f : s;
+  const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = div_rs(a[k], s_eff, rs);
+    b[k] = div_rs(b[k], s_eff, rs);
+  }
+  const uint32_t w0 = pack8_rtn(a, 1.0f), w1 = pack8_rtn(b, 1.0f);
+  if (ok) {
+    *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c0 >> 1)) = make_uint2(w0, w1);
+    if (i == 0) scales[br * tiles_c + bc] = (uint8_t)sc;
+  }
+  if constexpr (TRANS) {
+    const int tb = wave * 4 + tin;
+    lds[tb][i][0] = w0;
+    lds[tb][i][1] = w1;
+    __syncthreads();
+    // lane i now gathers column i of its tile: nibble i of every row
+    uint32_t o0 = 0, o1 = 0;
+    const int word = i >> 3, sh = (i & 7) * 4;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      o0 |= ((lds[tb][rr][word] >> sh) & 0xFu) << (4 * rr);
+      o1 |= ((lds[tb][rr + 8][word] >> sh) & 0xFu) << (4 * rr);
+    }
+    if (ok) *reinterpret_cast<uint2*>(codes_t + (c0 + i) * (rows >> 1) + (br * 16 >> 1)) = make_uint2(o0, o1);
+  }
+}
+
+void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax, float* tensor_scale,
+                     uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st) {
+  const int64_t tiles = (rows >> 4) * (cols >> 4);
+  const int grid = (int)((tiles + 15) / 16);
+#define FP4Q_2D(T, TR) k_nvfp4_2d<T, TR><<<grid, 256, 0, st>>>(static_cast<const T*>(x), rows, cols, amax, \
+                                                              tensor_scale, codes, scales, codes_t)
+  if (dtype == 1) { if (codes_t) FP4Q_2D(uint16_t, true); else FP4Q_2D(uint16_t, false); }
+  else            { if (codes_t) FP4Q_2D(float, true); else FP4Q_2D(float, false); }
+#undef FP4Q_2D
+}
+
+// ===========================================================================
+// Dequantize: x_hat = fl(fl(r*s)/gs) (NVFP4, 2D, IF4) or r*2^(code-127) (MXFP4).
+// One lane per 16 output elements.
+// ===========================================================================
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+template <int FMT, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                 const float* __restrict__ tensor_scale, int64_t rows, int64_t cols,
+                                                 void* __restrict__ y) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-element group
+  const int64_t n16 = rows * cols / 16;
+  if (g >= n16) return;
+  const uint2 w = *reinterpret_cast<const uint2*>(codes + g * 8);
+  float out[16];
+  if constexpr (FMT == 2) {
+    const uint32_t code = scales[g >> 1];
+    const float scale = __uint_as_float(code << 23);
+    decode8_fp4(w.x, scale, out);
+    decode8_fp4(w.y, scale, out + 8);
+  } else {
+    const float gs = *tensor_scale;
+    uint32_t sc;
+    if constexpr (FMT == 1) {
+      const int64_t e = g * 16, r = e / cols, c = e - r * cols;
+      sc = scales[(r >> 4) * (cols >> 4) + (c >> 4)];
+    } else {
+      sc = scales[g];
+    }
+    const float s = e4m3_decode(sc & 0x7Fu);
+    float rv[16];
+    if (FMT == 3 && (sc & 0x80u)) {
+      const float c67 = 6.0f / 7.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t word = k < 8 ? w.x : w.y;
+        const int nib = (int)((word >> (4 * (k & 7))) & 0xFu);
+        const int qv = (nib ^ 8) - 8;
+        rv[k] = (float)qv * c67;
+      }
+    } else {
+      decode8_fp4(w.x, 1.0f, rv);
+      decode8_fp4(w.y, 1.0f, rv + 8);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) out[k] = __fdiv_rn(rv[k] * s, gs);
+  }
+  if constexpr (BF16OUT) {
+    uint4 o0, o1;
+    o0.x = f32_to_bf16_rne(out[0]) | (f32_to_bf16_rne(out[1]) << 16);
+    o0.y = f32_to_bf16_rne(out[2]) | (f32_to_bf16_rne(out[3]) << 16);
+    o0.z = f32_to_bf16_rne(out[4]) | (f32_to_bf16_rne(out[5]) << 16);
+    o0.w = f32_to_bf16_rne(out[6]) | (f32_to_bf16_rne(out[7]) << 16);
+    o1.x = f32_to_bf16_rne(out[8]) | (f32_to_bf16_rne(out[9]) << 16);
+    o1.y = f32_to_bf16_rne(out[10]) | (f32_to_bf16_rne(out[11]) << 16);
+    o1.z = f32_to_bf16_rne(out[12]) | (f32_to_bf16_rne(out[13]) << 16);
+    o1.w = f32_to_bf16_rne(out[14]) | (f32_to_bf16_rne(out[15]) << 16);
+    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
+    p[0] = o0;
+    p[1] = o1;
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + g * 16);
+    p[0] = make_float4(out[0], out[1], out[2], out[3]);
+    p[1] = make_float4(out[4], out[5], out[6], out[7]);
+    p[2] = make_float4(out[8], out[9], out[10], out[11]);
+    p[3] = make_float4(out[12], out[13], out[14], out[15]);
+  }
+}
+
+void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
+                    int64_t cols, int out_dtype, void* y, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  const int grid = (int)((n16 + 255) / 256);
+#define FP4Q_DQ(F) \
+  if (out_dtype == 1) k_dequant<F, true><<<grid, 256, 0, st>>>(codes, scales, tensor_scale, rows, cols, y); \
+  else k_dequant<F, false><<<grid, 256, 0, st>>>(codes, scales, tensor_scale, rows, cols, y)
+  switch (fmt) {
+    case 0: FP4Q_DQ(0); break;
+    case 1: FP4Q_DQ(1); break;
+    case 2: FP4Q_DQ(2); break;
+    default: FP4Q_DQ(3); break;
+  }
+#undef FP4Q_DQ
+}
+
+}  // namespace fp4q

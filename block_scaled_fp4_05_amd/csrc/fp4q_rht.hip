@@ -1,0 +1,337 @@
+// fp4q_rht.hip -- 128x128 random Hadamard transform along the token (row) dimension,
+// qiita.com/nishiha/items/b98c2b931d588c4c81d5, section "ランダムアダマール変換": the
+// Wgrad operands are multiplied by H (H H^T = I after 1/sqrt(128) scaling) whose
+// rows are randomised by a +-1 diagonal S.  Per chunk of 128 rows:
+//   B = R^T A,  R = S H / sqrt(128),  B[i][j] = sum_t H[i][t] s_t A[t][j] / sqrt(128).
+//
+// bf16 inputs run the contraction on MFMA (v_mfma_f32_32x32x16_bf16): the +-1
+// matrix K[i][t] = H[i][t] s_t is exact in bf16 and the sum is accumulated in fp32.
+// One wave owns a tile of 128 tokens x 64 columns; lane l loads a 2-column x 8-token
+// micro-tile with 4-byte loads (lanes 0..31 read 128 contiguous bytes of a token
+// row) and transposes it in registers (v_perm) into the B operand, so no LDS is
+// needed.  Sylvester H factors as H_128[32a+u][32b+w] = H_4[a][b] H_32[u][w]: the A
+// operand of a K-step only depends on the H_32 part (folded with the signs, kept in
+// registers for the wave's lifetime), and the H_4 sign is applied by negating the B
+// operand for the output row-blocks that need it.
+//
+// The same contraction routine feeds the standalone transform, the amax pass and
+// the fused column-wise NVFP4 pass, so all three see bitwise identical values
+// B = fl(acc * fl(1/sqrt(128))).
+#include "fp4q_dev.hpp"
+#include "fp4q_internal.hpp"
+
+namespace fp4q {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kRhtScale = 0.08838834764831845f;   // fl(1/sqrt(128))
+
+struct RhtSigns { uint32_t w[4]; };
+
+__device__ __forceinline__ uint32_t parity(uint32_t v) { return __builtin_popcount(v) & 1u; }
+
+// A-operand fragments: lane (il = lane & 31, hk = lane >> 5), K-step kk holds
+// K[32a + il][16kk + 8hk + e] without the H_4 factor, e = 0..7.
+__device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_signs, u32x4 frag[8]) {
+  const uint32_t lane = threadIdx.x & 63, il = lane & 31, hk = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t half[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint32_t t = 16u * kk + 8u * hk + 2u * q + b;      // token within the chunk
+        uint32_t neg = parity(il & (t & 31u));
+        if (with_signs) neg ^= (sg.w[t >> 5] >> (t & 31u)) & 1u;
+        half[b] = 0x3F80u | (neg << 15);                          // bf16 +-1
+      }
+      d[q] = half[0] | (half[1] << 16);
+    }
+    frag[kk] = u32x4{d[0], d[1], d[2], d[3]};
+  }
+}
+
+// Contract one tile: tokens tok0..tok0+127, columns colp and colp+1 for this lane
+// (colp = col_base + 2*(lane & 31)).  acc[p][a] is the 32x32 MFMA output block a
+// (output tokens 32a..32a+31) for column parity p.
+__device__ __forceinline__ void rht_contract(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0,
+                                             int64_t colp, bool valid, const u32x4 frag[8], f32x16 acc[2][4]) {
+  const uint32_t hk = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc[p][a] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    uint32_t rowv[8];
+    const int64_t tb = tok0 + 16 * kk + 8 * hk;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      rowv[r] = valid ? *reinterpret_cast<const uint32_t*>(x + (tb + r) * cols + colp) : 0u;
+    u32x4 b0, b1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      b0[q] = __builtin_amdgcn_perm(rowv[2 * q + 1], rowv[2 * q], 0x05040100u);
+      b1[q] = __builtin_amdgcn_perm(rowv[2 * q + 1], rowv[2 * q], 0x07060302u);
+    }
+    const u32x4 nb0 = b0 ^ 0x80008000u, nb1 = b1 ^ 0x80008000u;
+    const bf16x8 fa = __builtin_bit_cast(bf16x8, frag[kk]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, flip ? nb0 : b0);
+      const bf16x8 v1 = __builtin_bit_cast(bf16x8, flip ? nb1 : b1);
+      acc[0][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][a], 0, 0, 0);
+      acc[1][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][a], 0, 0, 0);
+    }
+  }
+}
+
+// Output token (within the chunk) of accumulator register r of block a for this lane.
+__device__ __forceinline__ int acc_row(int a, int r) {
+  const int hk = (threadIdx.x & 63) >> 5;
+  return 32 * a + 8 * (r >> 2) + 4 * hk + (r & 3);
+}
+
+struct TileIter {
+  int64_t ntiles, nslab, nchunk;
+  __device__ TileIter(int64_t rows, int64_t cols) {
+    nslab = (cols + 63) / 64;
+    nchunk = rows / 128;
+    ntiles = nslab * nchunk;
+  }
+  // tiles run chunk-fastest so that consecutive tiles complete each column's output lines
+  __device__ void decode(int64_t tile, int64_t& chunk, int64_t& slab) const {
+    slab = tile / nchunk;
+    chunk = tile - slab * nchunk;
+  }
+};
+
+__device__ __forceinline__ int64_t wave_id() { return ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; }
+__device__ __forceinline__ int64_t wave_count() { return ((int64_t)gridDim.x * blockDim.x) >> 6; }
+
+// ---------------------------------------------------------------------------
+// Standalone transform (bf16 in, f32 out); inverse uses H without input signs
+// and applies s_t to the output rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                  RhtSigns sg, int inverse, float* __restrict__ y) {
+  u32x4 frag[8];
+  make_fragments(sg, !inverse, frag);
+  const TileIter it(rows, cols);
+  const int lane = threadIdx.x & 63;
+  for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
+    int64_t chunk, slab;
+    it.decode(tile, chunk, slab);
+    const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
+    const bool valid = colp < cols;
+    f32x16 acc[2][4];
+    rht_contract(x, cols, tok0, colp, valid, frag, acc);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = acc_row(a, r);
+        float v0 = acc[0][a][r] * kRhtScale, v1 = acc[1][a][r] * kRhtScale;
+        if (inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) { v0 = -v0; v1 = -v1; }
+        if (valid) *reinterpret_cast<float2*>(y + (tok0 + t) * cols + colp) = make_float2(v0, v1);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1 of the fused path: amax of the transformed tensor.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                  RhtSigns sg, float* __restrict__ amax) {
+  u32x4 frag[8];
+  make_fragments(sg, true, frag);
+  const TileIter it(rows, cols);
+  const int lane = threadIdx.x & 63;
+  float m = 0.0f;
+  for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
+    int64_t chunk, slab;
+    it.decode(tile, chunk, slab);
+    const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
+    const bool valid = colp < cols;
+    f32x16 acc[2][4];
+    rht_contract(x, cols, tok0, colp, valid, frag, acc);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = __builtin_fmaxf(m, __builtin_fabsf(acc[p][a][r]));
+  }
+  // max |fl(acc*k)| = fl(max|acc| * k): scaling is monotone
+  m = wave_max(m) * kRhtScale;
+  if (lane == 0) atomic_max_nonneg(amax, m);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: column-wise NVFP4 (blocks of 16 tokens) of the transformed tensor.
+// After the permlane32 swaps each lane holds 16 consecutive tokens of one column.
+// ---------------------------------------------------------------------------
+template <bool SR>
+__global__ __launch_bounds__(256) void k_rht_nvfp4_col(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                       RhtSigns sg, const float* __restrict__ amax,
+                                                       float* __restrict__ tensor_scale, uint8_t* __restrict__ ccodes,
+                                                       uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
+  const float gs = tensor_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  u32x4 frag[8];
+  make_fragments(sg, true, frag);
+  const TileIter it(rows, cols);
+  const int lane = threadIdx.x & 63, hk = lane >> 5;
+  const int64_t half_rows = rows >> 1, nb = rows >> 4;
+  for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
+    int64_t chunk, slab;
+    it.decode(tile, chunk, slab);
+    const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
+    const bool valid = colp < cols;
+    f32x16 acc[2][4];
+    rht_contract(x, cols, tok0, colp, valid, frag, acc);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      uint32_t scale_word = 0;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        // regroup: lanes < 32 take rows 0..15 of block a, lanes >= 32 rows 16..31
+        float t[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][a][j]),
+                                                      __float_as_uint(acc[p][a][8 + j]), false, false);
+          auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][a][4 + j]),
+                                                      __float_as_uint(acc[p][a][12 + j]), false, false);
+          t[j] = __uint_as_float(s02[0]);
+          t[4 + j] = __uint_as_float(s02[1]);
+          t[8 + j] = __uint_as_float(s13[0]);
+          t[12 + j] = __uint_as_float(s13[1]);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          t[k] = (t[k] * kRhtScale) * gs;
+          m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
+        }
+        const uint32_t sc = nvfp4_scale_code(m);
+        const float s = e4m3_decode(sc);
+        const float s_eff = s == 0.0f ? 1.0f : s;
+        const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) t[k] = div_rs(t[k], s_eff, rs);
+        const int64_t c = colp + p;
+        const int64_t tok = tok0 + 32 * a + 16 * hk;
+        uint32_t w0, w1;
+        if constexpr (SR) {
+          uint32_t r0[8], r1[8];
+          const uint64_t idx8 = (uint64_t)(c * rows + tok) >> 3;
+          sr_draws8(idx8, 1u, k0, k1, r0);
+          sr_draws8(idx8 + 1, 1u, k0, k1, r1);
+          w0 = pack8_sr(t, r0, 1.0f);
+          w1 = pack8_sr(t + 8, r1, 1.0f);
+        } else {
+          w0 = pack8_rtn(t, 1.0f);
+          w1 = pack8_rtn(t + 8, 1.0f);
+        }
+        if (valid) *reinterpret_cast<uint2*>(ccodes + c * half_rows + (tok >> 1)) = make_uint2(w0, w1);
+        scale_word |= sc << (8 * a);
+      }
+      // lane < 32 holds blocks 0,2,4,6 of the chunk and lane >= 32 blocks 1,3,5,7;
+      // interleave so each lane stores four consecutive scale bytes.
+      auto sw = __builtin_amdgcn_permlane32_swap(scale_word, scale_word, false, false);
+      const uint32_t lo = hk ? sw[0] : scale_word;      // blocks 0,2,4,6
+      const uint32_t hi = hk ? scale_word : sw[1];      // blocks 1,3,5,7
+      // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
+      const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
+      const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
+      if (valid) *reinterpret_cast<uint32_t*>(cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 input: VALU fast Walsh-Hadamard transform, one lane per (chunk, column),
+// 128 values in registers (7 butterfly stages).  Used for f32 forward/inverse.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rht_f32(const float* __restrict__ x, int64_t rows, int64_t cols, RhtSigns sg,
+                                                 int inverse, float* __restrict__ y) {
+  const int64_t nchunk = rows / 128;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= nchunk * cols) return;
+  const int64_t chunk = id / cols, j = id - chunk * cols;
+  const int64_t base = chunk * 128 * cols + j;
+  float v[128];
+#pragma unroll
+  for (int t = 0; t < 128; ++t) {
+    float a = x[base + (int64_t)t * cols];
+    if (!inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) a = -a;
+    v[t] = a;
+  }
+#pragma unroll
+  for (int h = 1; h < 128; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 128; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+#pragma unroll
+  for (int t = 0; t < 128; ++t) {
+    float o = v[t] * kRhtScale;
+    if (inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) o = -o;
+    y[base + (int64_t)t * cols] = o;
+  }
+}
+
+__global__ void k_zero1_rht(float* p) { *p = 0.0f; }
+
+static RhtSigns pack_signs(const uint32_t s[4]) {
+  RhtSigns r;
+  for (int i = 0; i < 4; ++i) r.w[i] = s[i];
+  return r;
+}
+
+static int rht_grid(int64_t rows, int64_t cols) {
+  const int64_t tiles = ((cols + 63) / 64) * (rows / 128);
+  const int64_t waves = tiles < 2048 ? tiles : 2048;     // about 8 waves per CU, persistent beyond
+  return (int)((waves + 3) / 4);
+}
+
+void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4], int inverse, float* y,
+                hipStream_t st) {
+  const RhtSigns sg = pack_signs(signs);
+  if (dtype == 1) {
+    k_rht_bf16<<<rht_grid(rows, cols), 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols, sg, inverse, y);
+  } else {
+    const int64_t n = rows / 128 * cols;
+    k_rht_f32<<<(int)((n + 255) / 256), 256, 0, st>>>(static_cast<const float*>(x), rows, cols, sg, inverse, y);
+  }
+}
+
+void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], float* amax,
+                     hipStream_t st) {
+  k_zero1_rht<<<1, 1, 0, st>>>(amax);
+  k_rht_amax<<<rht_grid(rows, cols), 256, 0, st>>>(x, rows, cols, pack_signs(signs), amax);
+}
+
+void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], bool sr,
+                          uint64_t seed, const float* amax, float* tensor_scale, uint8_t* col_codes,
+                          uint8_t* col_scales, hipStream_t st) {
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const RhtSigns sg = pack_signs(signs);
+  if (sr)
+    k_rht_nvfp4_col<true><<<rht_grid(rows, cols), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
+                                                                col_scales, k0, k1);
+  else
+    k_rht_nvfp4_col<false><<<rht_grid(rows, cols), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
+                                                                 col_scales, k0, k1);
+}
+
+}  // namespace fp4q

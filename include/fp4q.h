@@ -1,0 +1,176 @@
+/*
+ * fp4q.h -- C ABI of libfp4q: block-scaled FP4 quantization on MI355X (gfx950).
+ *
+ * Sources of the operations (page, then section):
+ *  [NV] qiita.com/nishiha/items/b98c2b931d588c4c81d5 (notes on NVIDIA's NVFP4
+ *       pretraining recipe): "NVFP4データの変換" (E2M1), "Blockwise" (1x16 blocks),
+ *       "誤差逆伝播と転置" (backprop needs the transposed operands), "2D scaling",
+ *       "ランダムアダマール変換" (RHT), "確率的丸め" (stochastic rounding),
+ *       "NVFP4の表現できる最大値", "scaleの導出" (tensor and block scales).
+ *  [GL] ultralytics.com/ja/glossary/fp4 (glossary "FP4"): "FP4の仕組み"
+ *       (MXFP4: 32 values + E8M0 scale; NVFP4: 16 values + E4M3 scale + FP32 scale).
+ *  [IF] gist.science/ja/paper/2603.28765 (explainer of "Adaptive Block-Scaled Data
+ *       Types"): "2. 提案手法：IF4" (FP4/INT4 per block, sign-bit flag, 6/7 rule).
+ *  [F6] blog.ast.moe/blog/2026-09-24 ("FP6から考えるLLM量子化"):
+ *       "FP6で隣り合う値の間隔を見てみる" (E8M0 scale with round-to-nearest-even).
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are HIP DEVICE pointers to dense row-major matrices (row stride
+ *    == cols).  `rows` x `cols` is the shape of the input matrix.
+ *  - Every device pointer must be 16-byte aligned (FP4Q_E_ALIGN otherwise).
+ *  - Inputs and outputs must not overlap.  The caller allocates every buffer and
+ *    keeps it alive until the work on `stream` has completed; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - A call validates its arguments on the host, enqueues its kernels on `stream`
+ *    (0 = the null stream) and returns without synchronizing.  On any validation
+ *    error nothing is enqueued.  Device faults surface at the caller's next sync.
+ *  - Inputs must be finite; codes for non-finite inputs are unspecified.
+ *  - All calls are reentrant; calls on different streams may run concurrently
+ *    when their output buffers are distinct.
+ *
+ * Packed layouts (all byte arrays):
+ *  - codes: element 2k of a logical row in bits 0-3 of byte k, element 2k+1 in
+ *    bits 4-7.  E2M1 nibble = sign(1) exp(2) man(1); IF4 INT4 nibble = two's
+ *    complement in -7..7.
+ *  - E4M3 scale byte: OCP e4m3fn, never negative; IF4 sets bit 7 for INT4 blocks.
+ *  - E8M0 scale byte: value 2^(byte-127), 0..254.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_E_NULL = 1,   /* a required pointer is NULL */
+    FP4Q_E_SHAPE = 2,  /* rows/cols <= 0 or not a multiple of the block (see each call) */
+    FP4Q_E_ALIGN = 3,  /* a device pointer is not 16-byte aligned */
+    FP4Q_E_ARG = 4,    /* invalid enum, empty layout mask, or an unsupported combination */
+    FP4Q_E_HIP = 5     /* the HIP runtime reported an error while enqueueing */
+} fp4q_status;
+
+typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
+typedef enum { FP4Q_RTN = 0, FP4Q_SR = 1 } fp4q_round;
+typedef enum { FP4Q_FMT_NVFP4 = 0, FP4Q_FMT_NVFP4_2D = 1, FP4Q_FMT_MXFP4 = 2, FP4Q_FMT_IF4 = 3 } fp4q_format;
+
+#define FP4Q_ROWWISE 1u
+#define FP4Q_COLWISE 2u
+
+/* amax_mode: COMPUTE = the call writes max|x| to *amax; GIVEN = *amax is read as the
+ * tensor's max magnitude (e.g. produced upstream) and not recomputed. */
+#define FP4Q_AMAX_COMPUTE 0u
+#define FP4Q_AMAX_GIVEN 1u
+
+/*
+ * NVFP4 with 1x16 blocks [NV "scaleの導出", "Blockwise", "誤差逆伝播と転置"; GL].
+ * Tensor scale gs = 2688 / amax (amax = 0 -> 1; overflow -> FLT_MAX), written to
+ * *tensor_scale.  Per 16-element block: s = E4M3(fl(fl(bamax * gs) / 6)); each element
+ * v = fl(fl(x * gs) / s) rounded onto E2M1 (RTN: nearest, ties to even code,
+ * saturating; SR: up iff frac + u >= 1 with a 16-bit Philox4x32-10 draw u keyed on
+ * (sr_seed, element index), [NV "確率的丸め"]).  A block whose scale is 0 gives
+ * signed zeros.
+ *   layouts   FP4Q_ROWWISE: blocks along rows;   row_codes [rows][cols/2], row_scales [rows][cols/16]
+ *             FP4Q_COLWISE: quantization of X^T; col_codes [cols][rows/2], col_scales [cols][rows/16]
+ *             Both bits may be set; both use the same gs.
+ *   rht_signs HOST pointer to 4 words (bit t of word t/32 set means sign -1) or NULL.
+ *             Non-NULL applies the 128x128 random Hadamard transform along rows in
+ *             chunks of 128 before quantizing [NV "ランダムアダマール変換"]; requires
+ *             layouts == FP4Q_COLWISE and rows % 128 == 0.  The amax and gs are then
+ *             those of the transformed matrix.
+ *   amax, tensor_scale  device float[1] each.
+ * Shapes: ROWWISE needs cols % 16 == 0; COLWISE needs rows % 16 == 0 and cols % 8 == 0.
+ * SR uses stream 0 for the row-wise output and stream 1 for the column-wise output;
+ * element index = row * lcols + col of the logical (output) matrix.
+ */
+fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
+                                unsigned layouts, fp4q_round rnd, uint64_t sr_seed,
+                                const uint32_t* rht_signs, unsigned amax_mode, float* amax,
+                                float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
+                                uint8_t* col_codes, uint8_t* col_scales, hipStream_t stream);
+
+/*
+ * NVFP4 with 16x16 blocks for weights [NV "2D scaling"]: one E4M3 scale per 16x16
+ * tile, so quantizing W^T gives exactly the transposed codes and scales.  RTN only.
+ *   codes [rows][cols/2], scales [rows/16][cols/16];
+ *   codes_t optional (NULL to skip): [cols][rows/2], the same codes in the layout of
+ *   W^T, i.e. the codes of q(W^T).
+ * Shapes: rows % 16 == 0, cols % 16 == 0.
+ */
+fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
+                                   unsigned amax_mode, float* amax, float* tensor_scale,
+                                   uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                                   hipStream_t stream);
+
+/*
+ * MXFP4: 32 elements + one E8M0 scale [GL "FP4の仕組み"; F6].  Per block the scale
+ * code is E8M0_RNE(fl(bamax / 6)) (nearest power of two, ties at significand 1.5 to
+ * the even code); elements are x * 2^(127 - code) rounded onto E2M1 (RTN or SR as
+ * above, stream 0).  No tensor scale.
+ *   codes [rows][cols/2], scales [rows][cols/32].   Shapes: cols % 32 == 0.
+ */
+fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
+                                fp4q_round rnd, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
+
+/*
+ * IF4 [IF "2. 提案手法：IF4"]: NVFP4 1x16 row-wise scaling, then per block the
+ * FP4 candidate and the INT4 candidate q = clamp(rint(fl(v * fl(7/6))), -7, 7)
+ * (restored as fl(q * fl(6/7))) are compared by sum_i fma-accumulated (v_i - r_i)^2,
+ * i ascending; INT4 is kept only if strictly lower and flagged in bit 7 of the
+ * block's E4M3 scale byte.  RTN only.
+ *   codes [rows][cols/2], scales [rows][cols/16].   Shapes: cols % 16 == 0.
+ */
+fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
+                              unsigned amax_mode, float* amax, float* tensor_scale,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * Random Hadamard transform along rows [NV "ランダムアダマール変換"], per chunk of
+ * 128 rows, R = S H / sqrt(128) with Sylvester H and S = diag(signs):
+ *   inverse == 0:  y = R^T x    (y[128c+i][j] = sum_t H[i][t] s_t x[128c+t][j] / sqrt(128))
+ *   inverse != 0:  y = R x      (undoes the forward transform)
+ * Contraction on MFMA (bf16 operands, fp32 accumulation); the forward transform is
+ * the one fp4q_quantize_nvfp4 applies, bit for bit.  The inverse takes an f32 input
+ * rounded to bf16 only if dt == FP4Q_BF16; with dt == FP4Q_F32 it runs on fp32 VALU.
+ *   signs  HOST pointer to 4 words.   y  device float [rows][cols].
+ * Shapes: rows % 128 == 0, cols % 8 == 0.
+ */
+fp4q_status fp4q_rht(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
+                     const uint32_t* signs, int inverse, float* y, hipStream_t stream);
+
+/*
+ * Dequantize packed codes back to values.  rows x cols is the LOGICAL shape of the
+ * quantized matrix (for a column-wise NVFP4 output pass (cols_in, rows_in)).
+ *   NVFP4, NVFP4_2D, IF4: x_hat = fl(fl(r * s) / gs), r = the E2M1 value, or for an
+ *     IF4 block flagged INT4 r = fl(q * fl(6/7)); gs = *tensor_scale (device float).
+ *   MXFP4: x_hat = r * 2^(code-127); tensor_scale may be NULL.
+ *   out_dt FP4Q_F32 writes float; FP4Q_BF16 writes bf16 = RNE(float result).
+ * Shapes as for the matching quantize call.
+ */
+fp4q_status fp4q_dequantize(fp4q_format fmt, const uint8_t* codes, const uint8_t* scales,
+                            const float* tensor_scale, int64_t rows, int64_t cols,
+                            fp4q_dtype out_dt, void* y, hipStream_t stream);
+
+/* max |x| over the whole matrix, written to device float *amax. */
+fp4q_status fp4q_amax(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, float* amax,
+                      hipStream_t stream);
+
+/* The RHT sign mask for a seed: one Philox4x32-10 call with counter {0,0,0,1} and key
+ * {lo32(seed), hi32(seed)}; its 128 output bits are the signs (host only). */
+void fp4q_rht_signs_from_seed(uint64_t seed, uint32_t signs[4]);
+
+const char* fp4q_status_string(fp4q_status status);
+int fp4q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

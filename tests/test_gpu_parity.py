@@ -1,0 +1,398 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Integer outputs (codes, scales, IF4 flags) must match bit for bit; amax and the
+tensor scale exactly; dequantized values at 0 ULP.  The random Hadamard transform
+runs on MFMA with fp32 accumulation, so its values are held to a 1e-5 relative
+tolerance (per 128-value chunk column, relative to the column's RMS), while the
+quantization that follows must match the oracle bit for bit when the oracle is fed
+the library's own transform output (two-stage check).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from block_scaled_fp4_05_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def dev_f32(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def make_input(kind: str, rows: int, cols: int, seed: int = 0):
+    """Returns (host array for the oracle, device tensor)."""
+    if kind == "bf16":
+        bits = si.activation(rows, cols, seed=seed)
+        return bits, dev_bf16(bits)
+    x = si.weight(rows, cols, seed=seed, std=1.0)
+    x[:, ::7] *= np.float32(25.0)
+    return x, dev_f32(x)
+
+
+def f32_bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+# ---------------------------------------------------------------------------------------
+# NVFP4 1x16
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(256, 512), (272, 400), (16, 16), (1040, 144)])
+def test_nvfp4_row_and_col_rtn(kind, shape):
+    rows, cols = shape
+    xh, xd = make_input(kind, rows, cols, seed=rows + cols)
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
+    rc, rs, gs = oracle.quantize_nvfp4(xh)
+    cc, cs, _ = oracle.quantize_nvfp4(xh, colwise=True)
+    assert host(out["amax"])[0] == np.float32(oracle.amax(xh))
+    assert host(out["tensor_scale"])[0] == gs
+    assert np.array_equal(host(out["row_codes"]), rc)
+    assert np.array_equal(host(out["row_scales"]), rs)
+    assert np.array_equal(host(out["col_codes"]), cc)
+    assert np.array_equal(host(out["col_scales"]), cs)
+
+
+@pytest.mark.parametrize("shape", [(37, 96), (1, 16), (129, 272)])
+def test_nvfp4_rowwise_ragged_rows(shape):
+    rows, cols = shape
+    xh, xd = make_input("bf16", rows, cols, seed=3)
+    out = B.quantize_nvfp4(xd, B.ROWWISE)
+    rc, rs, gs = oracle.quantize_nvfp4(xh)
+    assert np.array_equal(host(out["row_codes"]), rc)
+    assert np.array_equal(host(out["row_scales"]), rs)
+
+
+@pytest.mark.parametrize("shape", [(64, 40), (160, 8), (48, 136)])
+def test_nvfp4_colwise_only(shape):
+    rows, cols = shape
+    xh, xd = make_input("f32", rows, cols, seed=5)
+    out = B.quantize_nvfp4(xd, B.COLWISE)
+    cc, cs, gs = oracle.quantize_nvfp4(xh, colwise=True)
+    assert host(out["tensor_scale"])[0] == gs
+    assert np.array_equal(host(out["col_codes"]), cc)
+    assert np.array_equal(host(out["col_scales"]), cs)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+def test_nvfp4_stochastic_rounding_matches_philox_oracle(kind):
+    rows, cols = 272, 384
+    xh, xd = make_input(kind, rows, cols, seed=11)
+    seed = 0x1234_5678_9ABC
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, rnd=B.SR, sr_seed=seed)
+    rc, rs, gs = oracle.quantize_nvfp4(xh, rnd=oracle.SR, seed=seed)
+    cc, cs, _ = oracle.quantize_nvfp4(xh, colwise=True, rnd=oracle.SR, seed=seed)
+    assert np.array_equal(host(out["row_codes"]), rc)
+    assert np.array_equal(host(out["row_scales"]), rs)
+    assert np.array_equal(host(out["col_codes"]), cc)
+    assert np.array_equal(host(out["col_scales"]), cs)
+    # same seed -> same bits; another seed -> different draws
+    again = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, rnd=B.SR, sr_seed=seed)
+    assert torch.equal(again["row_codes"], out["row_codes"])
+    other = B.quantize_nvfp4(xd, B.ROWWISE, rnd=B.SR, sr_seed=seed + 1)
+    differ = np.count_nonzero(host(other["row_codes"]) != rc)
+    assert differ > rc.size // 10
+
+
+def test_nvfp4_amax_given():
+    rows, cols = 64, 128
+    xh, xd = make_input("bf16", rows, cols, seed=2)
+    given = torch.tensor([4.0 * oracle.amax(xh)], dtype=torch.float32, device=DEV)
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, amax=given)
+    gs = oracle.tensor_scale(float(host(given)[0]))
+    rc, rs, _ = oracle.quantize_nvfp4(xh, gs=gs)
+    cc, cs, _ = oracle.quantize_nvfp4(xh, colwise=True, gs=gs)
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    assert np.array_equal(host(out["row_codes"]), rc) and np.array_equal(host(out["row_scales"]), rs)
+    assert np.array_equal(host(out["col_codes"]), cc) and np.array_equal(host(out["col_scales"]), cs)
+
+
+def test_nvfp4_degenerate_inputs():
+    # all zeros: amax 0 -> gs 1, every code and scale 0
+    z = np.zeros((32, 32), np.float32)
+    out = B.quantize_nvfp4(dev_f32(z), B.ROWWISE | B.COLWISE)
+    assert host(out["tensor_scale"])[0] == 1.0
+    assert not host(out["row_codes"]).any() and not host(out["col_codes"]).any()
+    # signed zeros, zero-scale blocks (tiny values next to a large one) and huge values
+    x = np.zeros((32, 64), np.float32)
+    x[0, 0] = 3.0e38
+    x[1, :] = -0.0
+    x[2, 16:32] = np.float32(1e-30) * np.tile([1, -1], 8)
+    x[3, 32:48] = -np.float32(1e-3)
+    x[5:, :] = si.weight(27, 64, seed=1)
+    for lay, colwise in ((B.ROWWISE, False), (B.COLWISE, True)):
+        out = B.quantize_nvfp4(dev_f32(x), lay)
+        c, s, gs = oracle.quantize_nvfp4(x, colwise=colwise)
+        key = "col" if colwise else "row"
+        assert np.array_equal(host(out[key + "_codes"]), c)
+        assert np.array_equal(host(out[key + "_scales"]), s)
+
+
+def test_nvfp4_full_activation_config_sampled():
+    """bf16 [8192 x 4096], 1% columns x30, ROW|COL RTN: exact amax/gs, sampled rows and columns."""
+    bits = si.activation(8192, 4096, seed=2)
+    xd = dev_bf16(bits)
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
+    amax = oracle.amax(bits)
+    gs = oracle.tensor_scale(amax)
+    assert host(out["amax"])[0] == np.float32(amax)
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    rcg, rsg = host(out["row_codes"]), host(out["row_scales"])
+    ccg, csg = host(out["col_codes"]), host(out["col_scales"])
+    for r0 in (0, 127, 4096, 8176):
+        c, s = oracle.quantize_nvfp4_rows(bits, r0, 16, False, gs)
+        assert np.array_equal(rcg[r0:r0 + 16], c) and np.array_equal(rsg[r0:r0 + 16], s)
+    for j0 in (0, 1000, 2047, 4088):
+        c, s = oracle.quantize_nvfp4_rows(bits, j0, 8, True, gs)
+        assert np.array_equal(ccg[j0:j0 + 8], c) and np.array_equal(csg[j0:j0 + 8], s)
+
+
+# ---------------------------------------------------------------------------------------
+# NVFP4 16x16
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(96, 160), (16, 16), (528, 272)])
+def test_nvfp4_2d_and_transposed_codes(kind, shape):
+    rows, cols = shape
+    xh, xd = make_input(kind, rows, cols, seed=7)
+    out = B.quantize_nvfp4_2d(xd, transposed=True)
+    c, s, gs = oracle.quantize_nvfp4_2d(xh)
+    ct, st, _ = oracle.quantize_nvfp4_2d(np.ascontiguousarray(xh.T))
+    assert host(out["tensor_scale"])[0] == gs
+    assert np.array_equal(host(out["codes"]), c)
+    assert np.array_equal(host(out["scales"]), s)
+    assert np.array_equal(host(out["codes_t"]), ct)
+    assert np.array_equal(st, s.T)
+
+
+def test_nvfp4_2d_full_weight_config_sampled():
+    w = si.weight(8192, 8192, seed=3)
+    out = B.quantize_nvfp4_2d(dev_f32(w), transposed=True)
+    gs = oracle.tensor_scale(oracle.amax(w))
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    cg, sg, ctg = host(out["codes"]), host(out["scales"]), host(out["codes_t"])
+    for r0 in (0, 4096, 8176):
+        c, s, _ = oracle.quantize_nvfp4_2d(np.ascontiguousarray(w[r0:r0 + 16]), gs=gs)
+        assert np.array_equal(cg[r0:r0 + 16], c) and np.array_equal(sg[r0 // 16:r0 // 16 + 1], s)
+        ct, _, _ = oracle.quantize_nvfp4_2d(np.ascontiguousarray(w[:, r0:r0 + 16].T), gs=gs)
+        assert np.array_equal(ctg[r0:r0 + 16], ct)
+
+
+# ---------------------------------------------------------------------------------------
+# MXFP4
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_mxfp4(kind, rnd):
+    rows, cols = 96, 320
+    xh, xd = make_input(kind, rows, cols, seed=13)
+    out = B.quantize_mxfp4(xd, rnd=rnd, sr_seed=99)
+    c, s = oracle.quantize_mxfp4(xh, rnd=rnd, seed=99)
+    assert np.array_equal(host(out["codes"]), c)
+    assert np.array_equal(host(out["scales"]), s)
+
+
+def test_mxfp4_extreme_blocks():
+    x = np.zeros((4, 128), np.float32)
+    x[0, :32] = np.float32(1e-39) * np.arange(1, 33, dtype=np.float32)   # subnormal block -> code 0 region
+    x[1, :32] = 3.0e38
+    x[1, 32:64] = 1.5 * 6.0                                                 # bamax/6 = 1.5 exactly: tie
+    x[2, 64:96] = -0.0
+    x[3, :] = si.weight(1, 128, seed=4)
+    out = B.quantize_mxfp4(dev_f32(x))
+    c, s = oracle.quantize_mxfp4(x)
+    assert np.array_equal(host(out["scales"]), s)
+    assert np.array_equal(host(out["codes"]), c)
+
+
+def test_mxfp4_full_weight_config_sampled():
+    w = si.weight(8192, 8192, seed=3)
+    out = B.quantize_mxfp4(dev_f32(w))
+    cg, sg = host(out["codes"]), host(out["scales"])
+    for r0 in (0, 3000, 8184):
+        c, s = oracle.quantize_mxfp4(np.ascontiguousarray(w[r0:r0 + 8]))
+        assert np.array_equal(cg[r0:r0 + 8], c) and np.array_equal(sg[r0:r0 + 8], s)
+
+
+# ---------------------------------------------------------------------------------------
+# IF4
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(128, 256), (40, 48)])
+def test_if4(shape):
+    bits = si.if4_mix(*shape, seed=6)
+    out = B.quantize_if4(dev_bf16(bits))
+    c, s, gs = oracle.quantize_if4(bits)
+    assert host(out["tensor_scale"])[0] == gs
+    assert np.array_equal(host(out["scales"]), s)
+    assert np.array_equal(host(out["codes"]), c)
+    assert 0 < np.count_nonzero(s & 0x80) < s.size       # both block types occur
+
+
+def test_if4_full_config_sampled():
+    bits = si.if4_mix(32768, 8192, seed=5)
+    out = B.quantize_if4(dev_bf16(bits))
+    amax = oracle.amax(bits)
+    gs = oracle.tensor_scale(amax)
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    cg, sg = host(out["codes"]), host(out["scales"])
+    for r0 in (0, 16384, 24576, 32760):
+        c, s, _ = oracle.quantize_if4(np.ascontiguousarray(bits[r0:r0 + 8]), gs=gs)
+        assert np.array_equal(cg[r0:r0 + 8], c) and np.array_equal(sg[r0:r0 + 8], s)
+    # dequantize round trip of the sampled rows at 0 ULP
+    y = B.dequantize(B.FMT_IF4, out["codes"], out["scales"], out["tensor_scale"], 32768, 8192)
+    yh = host(y)
+    for r0 in (0, 24576):
+        ref = oracle.dequantize(oracle.FMT_IF4, cg[r0:r0 + 8], sg[r0:r0 + 8], gs, 8, 8192)
+        assert np.array_equal(f32_bits(yh[r0:r0 + 8]), f32_bits(ref))
+
+
+# ---------------------------------------------------------------------------------------
+# Dequantization
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4_2d", "mxfp4", "if4", "nvfp4_col"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_zero_ulp(fmt, out_dtype):
+    rows, cols = 96, 256
+    bits = si.if4_mix(rows, cols, seed=8)
+    xd = dev_bf16(bits)
+    if fmt == "nvfp4":
+        q = B.quantize_nvfp4(xd, B.ROWWISE)
+        args = (B.FMT_NVFP4, q["row_codes"], q["row_scales"], q["tensor_scale"], rows, cols)
+    elif fmt == "nvfp4_col":
+        q = B.quantize_nvfp4(xd, B.COLWISE)
+        args = (B.FMT_NVFP4, q["col_codes"], q["col_scales"], q["tensor_scale"], cols, rows)
+    elif fmt == "nvfp4_2d":
+        q = B.quantize_nvfp4_2d(xd)
+        args = (B.FMT_NVFP4_2D, q["codes"], q["scales"], q["tensor_scale"], rows, cols)
+    elif fmt == "mxfp4":
+        q = B.quantize_mxfp4(xd)
+        args = (B.FMT_MXFP4, q["codes"], q["scales"], None, rows, cols)
+    else:
+        q = B.quantize_if4(xd)
+        args = (B.FMT_IF4, q["codes"], q["scales"], q["tensor_scale"], rows, cols)
+    f, codes, scales, ts, r, c = args
+    gs = float(host(ts)[0]) if ts is not None else 1.0
+    ref = oracle.dequantize(f, host(codes), host(scales), gs, r, c)
+    if out_dtype == torch.float32:
+        y = host(B.dequantize(*args))
+        assert np.array_equal(f32_bits(y), f32_bits(ref))
+    else:
+        yb = host(B.dequantize(*args, out_dtype=torch.bfloat16).view(torch.int16)).view(np.uint16)
+        assert np.array_equal(yb, si.f32_to_bf16_bits(ref))
+
+
+# ---------------------------------------------------------------------------------------
+# Random Hadamard transform
+# ---------------------------------------------------------------------------------------
+
+def rht_close(y: np.ndarray, ref: np.ndarray, tol: float = 1e-5) -> bool:
+    """Per (128-row chunk, column): max |y - ref| <= tol * RMS(ref column chunk)."""
+    rows, cols = ref.shape
+    r = ref.reshape(rows // 128, 128, cols).astype(np.float64)
+    d = np.abs(y.reshape(rows // 128, 128, cols).astype(np.float64) - r).max(axis=1)
+    rms = np.sqrt((r ** 2).mean(axis=1))
+    return bool(np.all(d <= tol * rms + 1e-30))
+
+
+@pytest.mark.parametrize("kind", ["grad", "act"])
+def test_rht_standalone_within_tolerance(kind):
+    rows, cols = 384, 192
+    bits = si.wgrad_gradient(rows, cols, seed=1) if kind == "grad" else si.wgrad_activation(rows, cols, seed=1)
+    signs = oracle.rht_signs(4)
+    y = host(B.rht(dev_bf16(bits), signs.tolist()))
+    ref = oracle.rht(bits, signs)
+    assert rht_close(y, ref)
+    # inverse (bf16 MFMA path) and the f32 VALU path
+    back = host(B.rht(dev_f32(ref), signs.tolist(), inverse=True))
+    assert rht_close(back, si.bf16_bits_to_f32(bits))
+    yf = host(B.rht(dev_f32(si.bf16_bits_to_f32(bits)), signs.tolist()))
+    assert rht_close(yf, ref)
+
+
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_rht_fused_two_stage_exact(rnd):
+    """The fused RHT + column-wise NVFP4 equals the oracle quantizer fed with the
+    library's own transform output, bit for bit; against the all-oracle pipeline the
+    codes may differ only at rounding ties."""
+    rows, cols = 512, 256
+    bits = si.wgrad_gradient(rows, cols, seed=3)
+    signs = oracle.rht_signs(4)
+    xd = dev_bf16(bits)
+    out = B.quantize_nvfp4(xd, B.COLWISE, rnd=rnd, sr_seed=40, rht_signs=signs.tolist())
+    y = host(B.rht(xd, signs.tolist()))
+    amax_g, gs_g = host(out["amax"])[0], host(out["tensor_scale"])[0]
+    assert amax_g == np.max(np.abs(y))
+    assert gs_g == np.float32(oracle.tensor_scale(float(amax_g)))
+    c2, s2, _ = oracle.quantize_nvfp4(y, colwise=True, gs=float(gs_g), rnd=rnd, seed=40)
+    assert np.array_equal(host(out["col_codes"]), c2)
+    assert np.array_equal(host(out["col_scales"]), s2)
+    # all-oracle pipeline
+    yo = oracle.rht(bits, signs)
+    assert rht_close(y, yo)
+    c3, s3, _ = oracle.quantize_nvfp4(yo, colwise=True, rnd=rnd, seed=40)
+    mism = np.count_nonzero(host(out["col_codes"]) != c3)
+    assert mism <= max(2, c3.size * 2 * 1e-4)
+
+
+def test_rht_full_wgrad_config_sampled():
+    """Both Wgrad operands at [16384 x 4096]: gradient with SR, activation with RTN."""
+    signs = oracle.rht_signs(4)
+    for kind, rnd, seed in (("grad", 1, 40), ("act", 0, 41)):
+        bits = si.wgrad_gradient(16384, 4096, seed=4) if kind == "grad" else si.wgrad_activation(16384, 4096, seed=4)
+        xd = dev_bf16(bits)
+        out = B.quantize_nvfp4(xd, B.COLWISE, rnd=rnd, sr_seed=seed, rht_signs=signs.tolist())
+        y = B.rht(xd, signs.tolist())
+        amax_g = host(out["amax"])[0]
+        assert amax_g == host(y.abs().max().reshape(1))[0]
+        gs_g = float(host(out["tensor_scale"])[0])
+        ccg, csg = host(out["col_codes"]), host(out["col_scales"])
+        yh = host(y)
+        for j in (0, 777, 4095):
+            ref = oracle.rht_column(bits, j, signs)
+            assert rht_close(yh[:, j:j + 1].copy(), ref.reshape(-1, 1))
+            c2, s2 = oracle.quantize_nvfp4_rows(yh, j, 1, True, gs_g, rnd=rnd, seed=seed)
+            assert np.array_equal(ccg[j:j + 1], c2) and np.array_equal(csg[j:j + 1], s2)
+        del xd, y, out
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------
+# Streams, determinism, guard bytes
+# ---------------------------------------------------------------------------------------
+
+def test_non_default_stream_and_guard_bytes():
+    rows, cols = 128, 256
+    xh, xd = make_input("bf16", rows, cols, seed=21)
+    pad = 4096
+    guard = lambda n: torch.full((n + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    rc, rs = guard(rows * cols // 2), guard(rows * cols // 16)
+    cc, cs = guard(rows * cols // 2), guard(rows * cols // 16)
+    amax = torch.zeros(1, dtype=torch.float32, device=DEV)
+    ts = torch.zeros(1, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        B.fp4q_quantize_nvfp4(xd, B.BF16, rows, cols, B.ROWWISE | B.COLWISE, B.RTN, 0, None, B.AMAX_COMPUTE,
+                              amax, ts, rc[pad:], rs[pad:], cc[pad:], cs[pad:], stream=s)
+    s.synchronize()
+    for t, n in ((rc, rows * cols // 2), (rs, rows * cols // 16), (cc, rows * cols // 2), (cs, rows * cols // 16)):
+        h = host(t)
+        assert np.all(h[:pad] == 0xA5) and np.all(h[pad + n:] == 0xA5)
+    r_o, s_o, _ = oracle.quantize_nvfp4(xh)
+    assert np.array_equal(host(rc)[pad:pad + rows * cols // 2].reshape(rows, cols // 2), r_o)
