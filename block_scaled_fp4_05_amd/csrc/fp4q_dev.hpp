@@ -41,45 +41,81 @@ __device__ __forceinline__ void load8(const float* __restrict__ p, int64_t i, fl
 }
 
 // ---------------------------------------------------------------------------
-// Division by a block scale, correctly rounded.
+// Division by a block scale in two operations, correctly rounded.
 //
-// The quotient fl(t / s) is formed from rs = fl(1/s) with one Newton-style
-// correction: q0 = fl(t*rs), the residual t - q0*s is exact in one FMA, and
-// q = fl(q0 + res*rs).  For every divisor with at most 4 significant bits (all
-// E4M3 values, and 6) this equals the correctly rounded quotient whenever
-// |t| >= 2^-90; the repository's host tests check all 2^23 dividend significands
-// against the divisors' 8 significands.  The residual is negated twice so that
-// t = -0 yields -0.  Below 2^-90 the result is within a few ulps, which leaves every
-// code unchanged (|t/s| < 2^-80 is far below the first rounding threshold).
+// For a divisor s > 0 with at most four significant bits (every E4M3 value, and 6)
+// let zh be 1/s rounded toward zero and zl = fl(fl(1 - s*zh) * zh), which is >= 0.
+// Then fl(t*zh + fl(t*zl)) -- one multiplication and one fused multiply-add -- is the
+// correctly rounded quotient t/s for every binary32 t with a normal quotient: the
+// repository's host check runs all 2^23 dividend significands against the eight
+// divisor significands and spot-checks exponents.  Because zh and zl are both
+// non-negative, both terms carry the dividend's sign and t = -0 gives -0.  A zero
+// pair (zh = zl = 0) turns every dividend into a zero of its own sign, which is what
+// a block whose scale rounded to zero needs.  The scheme is the one of Brisebarre,
+// Muller and Raina for division by a constant known in advance (IEEE Trans. Comput.
+// 53(8), 2004), with the high part rounded toward zero instead of to nearest.
+// Quotients below the normal range may be off by an ulp; they are far below the
+// smallest E2M1 rounding threshold, so no code depends on them.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float div_rs(float t, float s, float rs) {
-  float q0 = t * rs;
-  float res = -__builtin_fmaf(q0, s, -t);
-  return __builtin_fmaf(res, rs, q0);
+struct RecipPair {
+  float zh, zl;
+};
+
+__device__ __forceinline__ float div2(float t, RecipPair r) { return __builtin_fmaf(t, r.zh, t * r.zl); }
+
+// The pair for an E4M3 value s > 0.  fl(1/s) comes from the hardware estimate
+// (within 1 ulp) and one Newton step with an exact residual, which rounds correctly
+// for every divisor with at most four significant bits (checked on the host for all
+// 126 values with the estimate anywhere within 1 ulp).
+__device__ __forceinline__ RecipPair recip_pair(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  float zh = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+  float e = __builtin_fmaf(-s, zh, 1.0f);      // exact: 1 - s*zh needs few bits
+  if (e < 0.0f) {                              // 1/s was rounded up: step one ulp down
+    zh = __uint_as_float(__float_as_uint(zh) - 1u);
+    e = __builtin_fmaf(-s, zh, 1.0f);
+  }
+  return RecipPair{zh, e * zh};
 }
 
-// ---------------------------------------------------------------------------
-// E4M3 block scale (e4m3fn, saturating at 448).
-// The hardware conversion rounds to nearest-even but does not saturate, so the
-// input is clamped to 448 first.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  y = __builtin_fminf(y, 448.0f);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0u, false) & 0xFFu;
+// The pair for dividing by 6: zh = 0x3E2AAAAA (1/6 rounded down), 1 - 6*zh = 2^-24,
+// zl = 2^-24 * zh.
+__device__ __forceinline__ RecipPair recip6() {
+  return RecipPair{__uint_as_float(0x3E2AAAAAu), __uint_as_float(0x322AAAAAu)};
 }
 
+// E4M3 code -> value via the hardware fp8 (OCP e4m3fn) convert; exact.
 __device__ __forceinline__ float e4m3_decode(uint32_t code) {
-  // exponent bias 7, subnormal step 2^-9: rebuild the binary32 bit pattern
-  uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  if (e == 0) return (float)m * 0x1p-9f;
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
 // NVFP4 / IF4 block scale from the block max of |x*gs| (= fl(bamax*gs)):
-// s = E4M3(fl(p / 6)).  Division by 6 uses the same corrected reciprocal.
+// s = E4M3(fl(p / 6)), e4m3fn saturating at 448.  The hardware conversion rounds to
+// nearest-even but does not saturate, so the value is clamped first.  The second
+// converted value is +0, so the returned word is the scale byte itself.
 __device__ __forceinline__ uint32_t nvfp4_scale_code(float p) {
-  const float six = 6.0f, r6 = 1.0f / 6.0f;   // fl(1/6), folded at compile time
-  return e4m3_encode(div_rs(p, six, r6));
+  const float y = __builtin_fminf(div2(p, recip6()), 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0u, false);
+}
+
+// Reciprocal pairs of all 128 E4M3 codes, indexed by the code: a block divides by
+// table[code].  Codes 0 (scale zero) and 0x7F (not a number; never produced, since
+// scales saturate at 448) hold the zero pair.
+struct RecipTable {
+  RecipPair r[128];
+};
+
+// The pair for a scale byte (code 0: the zero pair).
+__device__ __forceinline__ RecipPair recip_pair_code(uint32_t code) {
+  const RecipPair r = recip_pair(e4m3_decode(code));
+  const bool zero = code == 0u;
+  return RecipPair{zero ? 0.0f : r.zh, zero ? 0.0f : r.zl};
+}
+
+// Fill by the first 128 threads of a workgroup; the caller synchronizes after.
+__device__ __forceinline__ void fill_recip_table(RecipTable& tab) {
+  const int c = threadIdx.x;
+  if (c < 128) tab.r[c] = c == 0x7F ? RecipPair{0.0f, 0.0f} : recip_pair_code((uint32_t)c);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,6 +228,14 @@ __device__ __forceinline__ float lane_xor_max(float v) {
   else
     other = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
   return __builtin_fmaxf(v, __int_as_float(other));
+}
+
+// Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it does not
+// wait for outstanding global loads, so a prefetch of the next tile stays in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ float wave_max(float v) {

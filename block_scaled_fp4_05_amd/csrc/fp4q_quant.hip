@@ -22,12 +22,15 @@ namespace fp4q {
 
 __global__ void k_zero1(float* p) { *p = 0.0f; }
 
+// Same-address device atomics serialize at the memory side, so each workgroup
+// reduces its share (DPP/shuffle within waves, LDS across waves) and issues a single
+// atomic; the grid is sized to about one 1024-thread workgroup per CU.
 template <typename T>
-__global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t n8, float* __restrict__ amax) {
-  // n8 = number of 8-element groups; 4 groups in flight per thread per trip
+__global__ __launch_bounds__(1024) void k_amax(const T* __restrict__ x, int64_t n8, float* __restrict__ amax) {
+  __shared__ float wmax[16];
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  int64_t g = (int64_t)blockIdx.x * 1024 + threadIdx.x;
   for (; g + 3 * stride < n8; g += 4 * stride) {
     float a[8], b[8], c[8], d[8];
     load8(x, g * 8, a);
@@ -46,7 +49,14 @@ __global__ __launch_bounds__(256) void k_amax(const T* __restrict__ x, int64_t n
     for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(a[k]));
   }
   m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bm = 0.0f;
+    const int nw = (int)(blockDim.x >> 6);
+    for (int w = 0; w < nw; ++w) bm = __builtin_fmaxf(bm, wmax[w]);
+    atomic_max_nonneg(amax, bm);
+  }
 }
 
 // amax over a tail of fewer than 8 elements (only for fp4q_amax on odd sizes)
@@ -63,8 +73,8 @@ __global__ void k_amax_tail(const T* __restrict__ x, int64_t start, int64_t n, f
 }
 
 static int amax_grid(int64_t n8) {
-  int64_t blocks = (n8 + 255) / 256;
-  return (int)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048);
+  int64_t blocks = (n8 + 1023) / 1024;
+  return (int)(blocks < 256 ? (blocks > 0 ? blocks : 1) : 256);
 }
 
 template <typename T>
@@ -72,7 +82,7 @@ static void launch_amax_t(const void* x, int64_t n, float* amax, hipStream_t st)
   const T* xp = static_cast<const T*>(x);
   k_zero1<<<1, 1, 0, st>>>(amax);
   int64_t n8 = n / 8;
-  if (n8 > 0) k_amax<T><<<amax_grid(n8), 256, 0, st>>>(xp, n8, amax);
+  if (n8 > 0) k_amax<T><<<amax_grid(n8), 1024, 0, st>>>(xp, n8, amax);
   if (n8 * 8 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n8 * 8, n, amax);
 }
 
@@ -84,112 +94,320 @@ void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t s
 // ===========================================================================
 // NVFP4 1x16, row-wise and/or column-wise, one pass over x.
 //
-// Workgroup tile: 128 rows x 128 cols (4 waves of 32 rows).  Lane layout inside a
-// wave: quads of four lanes own a 16x16 sub-tile; lane bit 0 picks the upper or
-// lower 8 rows, lane bit 1 the left or right 8 columns, so every lane holds an 8x8
-// micro-tile.  A row block (16 columns) is the lane pair (lane ^ 2) and a column
-// block (16 rows) the pair (lane ^ 1): both block maxima are one DPP max away.
-// The product t = x*gs is formed once and serves both layouts.
+// A workgroup of four waves owns a 128 x 128 tile; wave w takes rows 32w..32w+31.
+// Lane layout inside a wave: quads of four lanes own a 16x16 sub-tile; lane bit 0
+// picks the upper or lower 8 rows and lane bit 1 the left or right 8 columns, so
+// every lane holds an 8x8 micro-tile as raw input words.  A row block (16 columns)
+// is the lane pair (lane ^ 2) and a column block (16 rows) the pair (lane ^ 1): both
+// block maxima are one DPP max away.  Each pass widens the raw words and forms
+// t = x*gs on the fly, which keeps the register footprint small.
+//
+// Codes and scales are staged in LDS for the whole tile, so every column's 64 bytes
+// of codes and 8 scale bytes leave contiguously, and rows' outputs leave as 16-byte
+// stores.  Tiles are dealt in groups of 16 x 16 tiles (2048 x 2048 elements): each
+// XCD (block b runs on XCD b % 8) gets a contiguous run of the group-major tile
+// sequence, so output cache lines that several tiles share are completed inside one
+// XCD's L2 while it works on the group.
 // ===========================================================================
 
-template <typename T, bool ROW, bool COL, bool SR>
-__global__ __launch_bounds__(256) void k_nvfp4_tile(
-    const T* __restrict__ x, int64_t rows, int64_t cols, int tiles_c, int tiles_total,
-    const float* __restrict__ amax, float* __restrict__ tensor_scale,
-    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
-    uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales,
-    uint32_t k0, uint32_t k1) {
-  const float gs = tensor_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
-
-  // XCD-aware order: consecutive block ids go round-robin over the 8 XCDs, so
-  // give each XCD a contiguous run of tiles (neighbouring outputs share its L2).
-  int b = blockIdx.x;
-  int tile = b;
-  if ((tiles_total & 7) == 0) tile = (b & 7) * (tiles_total >> 3) + (b >> 3);
-  const int tr = tile / tiles_c, tc = tile - tr * tiles_c;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane >> 2, h = (lane >> 1) & 1, vv = lane & 1;
-  const int64_t row0 = (int64_t)tr * 128 + wave * 32 + (q >> 3) * 16 + vv * 8;
-  const int64_t col0 = (int64_t)tc * 128 + (q & 7) * 16 + h * 8;
-  const bool col_ok = col0 < cols;
-
-  float t[8][8];
+template <typename T> struct Raw8x8;
+// Loads are unconditional, so no branch forces an early wait on them: rows past the
+// end and columns past the end read the last valid row / column group instead.  Such
+// values only ever enter row or column blocks whose outputs are not stored (blocks
+// never straddle the matrix edge), so they cannot change a stored code.
+template <> struct Raw8x8<uint16_t> {
+  uint4 r[8];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int row0, int col0, int rows, int cols) {
+    const int c = min(col0, cols - 8);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (col_ok && row0 + i < rows) {
-      load8(x, (row0 + i) * cols + col0, t[i]);
+    for (int i = 0; i < 8; ++i)
+      r[i] = *reinterpret_cast<const uint4*>(x + (int64_t)min(row0 + i, rows - 1) * cols + c);
+  }
+  __device__ __forceinline__ uint32_t word(int i, int k) const {
+    return k == 0 ? r[i].x : k == 1 ? r[i].y : k == 2 ? r[i].z : r[i].w;
+  }
+  // Hide the words' provenance from the optimizer (no instruction is emitted), so a
+  // second pass recomputes x*gs instead of keeping 64 products alive across passes.
+  // element (i, j) of the micro-tile times gs
+  __device__ __forceinline__ float at(int i, int j, float gs) const {
+    const uint32_t w = word(i, j >> 1);
+    return ((j & 1) ? bf16_hi(w) : bf16_lo(w)) * gs;
+  }
+};
+template <> struct Raw8x8<float> {
+  float4 r[16];
+  __device__ __forceinline__ void load(const float* __restrict__ x, int row0, int col0, int rows, int cols) {
+    const int c = min(col0, cols - 8);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[i][j] = t[i][j] * gs;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) t[i][j] = 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const float* p = x + (int64_t)min(row0 + i, rows - 1) * cols + c;
+      r[2 * i] = *reinterpret_cast<const float4*>(p);
+      r[2 * i + 1] = *reinterpret_cast<const float4*>(p + 4);
     }
   }
+  __device__ __forceinline__ float at(int i, int j, float gs) const {
+    const float4 v = r[2 * i + (j >> 2)];
+    const int k = j & 3;
+    return (k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w) * gs;
+  }
+};
+
+// Staging of one 128 x 128 tile's outputs.  Chunk positions are XOR swizzled so that
+// the 4-byte writes and the 16-byte reads avoid LDS bank conflicts (64 x 4 bytes).
+struct TileStage {
+  uint32_t rc[2048];   // row codes: 128 rows x 64 B (512 chunks of 16 B)
+  uint32_t cc[2048];   // column codes: 128 columns x 64 B (4 chunks of 32 tokens each)
+  uint8_t rs[1024];    // row scales: 128 rows x 8 blocks
+  uint8_t cs[1024];    // column scales: 128 columns x 8 blocks
+};
+
+// row r (0..127), 4-byte piece p (0..15) of its 64 bytes -> dword index in rc
+__device__ __forceinline__ int rc_dword(int r, int p) {
+  const int chunk = (r << 2) + (p >> 2);
+  return ((chunk ^ (((r >> 3) & 3) << 2)) << 2) + (p & 3);
+}
+__device__ __forceinline__ int rc_chunk_row(int ch) {   // inverse: chunk -> row
+  const int r0 = ch >> 2;
+  return r0 ^ ((r0 >> 3) & 3);
+}
+// column c (0..127), 16-byte piece w (0..3, tokens 32w..32w+31), 4-byte part p
+__device__ __forceinline__ int cc_dword(int c, int w, int p) {
+  return ((((c << 2) + w) ^ ((c >> 3) & 15)) << 2) + p;
+}
+__device__ __forceinline__ int cc_chunk_unswizzle(int ch) {   // swizzled chunk -> c*4 + w
+  return ch ^ ((ch >> 5) & 15);
+}
+
+__device__ __forceinline__ void store_u8x8(uint8_t* dst, uint2 v, int nvalid, bool aligned8) {
+  if (nvalid >= 8 && aligned8) {
+    *reinterpret_cast<uint2*>(dst) = v;
+  } else {
+    for (int e = 0; e < 8 && e < nvalid; ++e) dst[e] = (uint8_t)((e < 4 ? v.x : v.y) >> (8 * (e & 3)));
+  }
+}
+
+// This lane's 8x8 micro-tile of tile (trow0, tcol0).
+template <typename T>
+__device__ __forceinline__ void nvfp4_tile_load(const T* __restrict__ x, int trow0, int tcol0, int rows, int cols,
+                                                Raw8x8<T>& raw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 2, h = (lane >> 1) & 1, vv = lane & 1;
+  const int row0 = trow0 + wave * 32 + (q >> 3) * 16 + vv * 8, col0 = tcol0 + (q & 7) * 16 + h * 8;
+  raw.load(x, row0, col0, rows, cols);
+}
+
+template <typename T, bool ROW, bool COL, bool SR>
+__device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0, int rows, int cols, float gs,
+                                           TileStage& st, const RecipTable& rtab,
+                                           uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
+                                           uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales, uint32_t k0,
+                                           uint32_t k1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 2, h = (lane >> 1) & 1, vv = lane & 1, qr = q >> 3, qc = q & 7;
+  const int lrow0 = wave * 32 + qr * 16 + vv * 8, lcol0 = qc * 16 + h * 8;   // within the tile
+  const int row0 = trow0 + lrow0, col0 = tcol0 + lcol0;
+
+  // t = fl(x*gs) for the lane's 64 elements, formed once for both directions
+  float t[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[i][j] = raw.at(i, j, gs);
 
   if constexpr (ROW) {
-    const int64_t half_cols = cols >> 1, nb = cols >> 4;
+    const uint64_t idx0 = (uint64_t)row0 * (uint64_t)cols + (uint64_t)col0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
       m = lane_xor_max<2>(m);
-      const uint32_t sc = nvfp4_scale_code(m);
-      const float s = e4m3_decode(sc);
-      const float s_eff = s == 0.0f ? 1.0f : s;
-      const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+      const uint32_t code = nvfp4_scale_code(m);
+      const RecipPair rp = rtab.r[code];
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = div_rs(t[i][j], s_eff, rs);
-      const int64_t r = row0 + i;
+      for (int j = 0; j < 8; ++j) v[j] = div2(t[i][j], rp);
       uint32_t w;
       if constexpr (SR) {
         uint32_t rr[8];
-        sr_draws8((uint64_t)(r * cols + col0) >> 3, 0u, k0, k1, rr);
+        sr_draws8((idx0 + (uint64_t)i * (uint64_t)cols) >> 3, 0u, k0, k1, rr);
         w = pack8_sr(v, rr, 1.0f);
       } else {
         w = pack8_rtn(v, 1.0f);
       }
-      if (col_ok && r < rows) {
-        *reinterpret_cast<uint32_t*>(rcodes + r * half_cols + (col0 >> 1)) = w;
-        if (h == 0) rscales[r * nb + (col0 >> 4)] = (uint8_t)sc;
-      }
+      const int r = lrow0 + i;
+      st.rc[rc_dword(r, 2 * qc + h)] = w;
+      if (h == 0) st.rs[r * 8 + qc] = (uint8_t)code;
     }
   }
-
   if constexpr (COL) {
-    const int64_t half_rows = rows >> 1, nb = rows >> 4;
-    const bool ok = col_ok && row0 < rows;
+    const uint64_t idx0 = (uint64_t)col0 * (uint64_t)rows + (uint64_t)row0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
       m = lane_xor_max<1>(m);
-      const uint32_t sc = nvfp4_scale_code(m);
-      const float s = e4m3_decode(sc);
-      const float s_eff = s == 0.0f ? 1.0f : s;
-      const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+      const uint32_t code = nvfp4_scale_code(m);
+      const RecipPair rp = rtab.r[code];
       float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = div_rs(t[i][j], s_eff, rs);
-      const int64_t c = col0 + j;
+      for (int i = 0; i < 8; ++i) v[i] = div2(t[i][j], rp);
       uint32_t w;
       if constexpr (SR) {
         uint32_t rr[8];
-        sr_draws8((uint64_t)(c * rows + row0) >> 3, 1u, k0, k1, rr);
+        sr_draws8((idx0 + (uint64_t)j * (uint64_t)rows) >> 3, 1u, k0, k1, rr);
         w = pack8_sr(v, rr, 1.0f);
       } else {
         w = pack8_rtn(v, 1.0f);
       }
-      if (ok) {
-        *reinterpret_cast<uint32_t*>(ccodes + c * half_rows + (row0 >> 1)) = w;
-        if (vv == 0) cscales[c * nb + (row0 >> 4)] = (uint8_t)sc;
-      }
+      const int c = lcol0 + j;
+      st.cc[cc_dword(c, wave, 2 * qr + vv)] = w;
+      if (vv == 0) st.cs[c * 8 + 2 * wave + qr] = (uint8_t)code;
     }
   }
+  lds_barrier();
+  const int tid = threadIdx.x;
+  if constexpr (ROW) {
+    const int half_cols = cols >> 1, nb = cols >> 4;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ch = tid + 256 * k;                        // swizzled chunk
+      const int r = rc_chunk_row(ch), c4 = ch & 3;
+      const uint4 w = *reinterpret_cast<const uint4*>(&st.rc[ch * 4]);
+      const int grow = trow0 + r, gcol = tcol0 + c4 * 32;   // first column of this 32-column chunk
+      if (grow < rows && gcol < cols) {
+        uint8_t* dst = rcodes + (int64_t)grow * half_cols + (gcol >> 1);   // 8-byte aligned
+        if (gcol + 32 > cols) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);           // 16 valid columns
+        } else if ((half_cols & 15) == 0) {
+          *reinterpret_cast<uint4*>(dst) = w;
+        } else {
+          reinterpret_cast<uint2*>(dst)[0] = make_uint2(w.x, w.y);
+          reinterpret_cast<uint2*>(dst)[1] = make_uint2(w.z, w.w);
+        }
+      }
+    }
+    if (tid < 128) {
+      const int grow = trow0 + tid, blk0 = tcol0 >> 4;
+      if (grow < rows && blk0 < nb)
+        store_u8x8(rscales + (int64_t)grow * nb + blk0, *reinterpret_cast<const uint2*>(&st.rs[tid * 8]),
+                   nb - blk0, (nb & 7) == 0);
+    }
+  }
+  if constexpr (COL) {
+    const int half_rows = rows >> 1, nb = rows >> 4;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ch = tid + 256 * k;
+      const int cw = cc_chunk_unswizzle(ch), c = cw >> 2, w = cw & 3;
+      const uint4 v = *reinterpret_cast<const uint4*>(&st.cc[ch * 4]);
+      const int gcol = tcol0 + c, grow = trow0 + 32 * w;
+      if (gcol < cols && grow + 16 <= rows) {
+        uint8_t* dst = ccodes + (int64_t)gcol * half_rows + (grow >> 1);   // 8-byte aligned
+        if (grow + 32 > rows) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+        } else if ((half_rows & 15) == 0) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+          reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+        }
+      }
+    }
+    if (tid < 128) {
+      const int gcol = tcol0 + tid, blk0 = trow0 >> 4;
+      if (gcol < cols && blk0 < nb)
+        store_u8x8(cscales + (int64_t)gcol * nb + blk0, *reinterpret_cast<const uint2*>(&st.cs[tid * 8]),
+                   nb - blk0, (nb & 7) == 0);
+    }
+  }
+  lds_barrier();   // the next tile's staging writes must not overtake these reads
+}
+
+// Tile t of the group-major sequence -> (tile row, tile column).
+__device__ __forceinline__ void group_major_tile(int t, int tiles_r, int tiles_c, int& tr, int& tc) {
+  constexpr int G = 16;
+  const int full_rows_tiles = G * tiles_c;                 // tiles in one full group-row
+  const int gr = t / full_rows_tiles;
+  int rem = t - gr * full_rows_tiles;
+  const int gh = min(G, tiles_r - gr * G);                 // height of this group-row
+  const int gc = rem / (gh * G);
+  const int gw = min(G, tiles_c - gc * G);
+  rem -= gc * gh * G;
+  tr = gr * G + rem / gw;
+  tc = gc * G + rem % gw;
+}
+
+template <typename T, bool ROW, bool COL, bool SR>
+__global__ __launch_bounds__(256) void k_nvfp4_tile(
+    const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
+    const float* __restrict__ amax, float* __restrict__ tensor_scale,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
+    uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales,
+    uint32_t k0, uint32_t k1) {
+  __shared__ TileStage stage;
+  __shared__ RecipTable rtab;
+  fill_recip_table(rtab);
+  __syncthreads();
+  const float gs = tensor_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+
+  // tiles of XCD x (blocks b with b % 8 == x) form the contiguous band
+  // [x*per, (x+1)*per) of the group-major sequence; the band's blocks stride through it.
+  const int total = tiles_r * tiles_c;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, nx = (nblk + 7 - xcd) >> 3, lb = b >> 3;
+  const int per = (total + 7) >> 3;
+  const int band0 = xcd * per, band1 = min(total, band0 + per);
+  // ping-pong: the next tile's raw input is in flight while this one is computed
+  int t = band0 + lb;
+  if (t >= band1) return;
+  Raw8x8<T> ra, rb;
+  int tra, tca, trb, tcb;
+  group_major_tile(t, tiles_r, tiles_c, tra, tca);
+  nvfp4_tile_load<T>(x, tra * 128, tca * 128, rows, cols, ra);
+  // Each step is written out twice (with and without the next load) so that the
+  // compiler's wait before the compute only covers the current tile's loads.
+  while (true) {
+    const int t1 = t + nx;
+    if (t1 < band1) {
+      group_major_tile(t1, tiles_r, tiles_c, trb, tcb);
+      nvfp4_tile_load<T>(x, trb * 128, tcb * 128, rows, cols, rb);
+      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+                                  cscales, k0, k1);
+    } else {
+      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+                                  cscales, k0, k1);
+      break;
+    }
+    const int t2 = t1 + nx;
+    if (t2 < band1) {
+      group_major_tile(t2, tiles_r, tiles_c, tra, tca);
+      nvfp4_tile_load<T>(x, tra * 128, tca * 128, rows, cols, ra);
+      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+                                  cscales, k0, k1);
+    } else {
+      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+                                  cscales, k0, k1);
+      break;
+    }
+    t = t2;
+  }
+}
+
+static int g_num_cus = 0;
+
+static int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
 }
 
 template <typename T, bool ROW, bool COL, bool SR>
@@ -198,8 +416,10 @@ static void launch_nvfp4_t(const void* x, int64_t rows, int64_t cols, const floa
                            uint32_t k0, uint32_t k1, hipStream_t st) {
   const int tiles_r = (int)((rows + 127) / 128), tiles_c = (int)((cols + 127) / 128);
   const int total = tiles_r * tiles_c;
-  k_nvfp4_tile<T, ROW, COL, SR><<<total, 256, 0, st>>>(static_cast<const T*>(x), rows, cols, tiles_c,
-                                                       total, amax, tensor_scale, rc, rs, cc, cs, k0, k1);
+  const int want = num_cus() * 2;          // two resident 4-wave workgroups per CU, each walking tiles
+  const int grid = total < want ? total : want;
+  k_nvfp4_tile<T, ROW, COL, SR><<<grid, 256, 0, st>>>(static_cast<const T*>(x), (int)rows, (int)cols, tiles_r,
+                                                      tiles_c, amax, tensor_scale, rc, rs, cc, cs, k0, k1);
 }
 
 template <typename T>
@@ -335,13 +555,11 @@ __global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n1
     m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])));
   }
   const uint32_t sc = nvfp4_scale_code(m);
-  const float s = e4m3_decode(sc);
-  const float s_eff = s == 0.0f ? 1.0f : s;
-  const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+  const RecipPair rp = recip_pair_code(sc);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    a[k] = div_rs(a[k], s_eff, rs);
-    b[k] = div_rs(b[k], s_eff, rs);
+    a[k] = div2(a[k], rp);
+    b[k] = div2(b[k], rp);
   }
   const uint32_t fa = pack8_rtn(a, 1.0f), fb = pack8_rtn(b, 1.0f);
   float ra[8], rb[8];
@@ -412,13 +630,11 @@ __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64
   }
   m = max16_lanes(m);
   const uint32_t sc = nvfp4_scale_code(m);
-  const float s = e4m3_decode(sc);
-  const float s_eff = s == 0.0f ? 1.0f : s;
-  const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+  const RecipPair rp = recip_pair_code(sc);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    a[k] = div_rs(a[k], s_eff, rs);
-    b[k] = div_rs(b[k], s_eff, rs);
+    a[k] = div2(a[k], rp);
+    b[k] = div2(b[k], rp);
   }
   const uint32_t w0 = pack8_rtn(a, 1.0f), w1 = pack8_rtn(b, 1.0f);
   if (ok) {

@@ -220,11 +220,9 @@ __global__ __launch_bounds__(256) void k_rht_nvfp4_col(const uint16_t* __restric
           m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
         }
         const uint32_t sc = nvfp4_scale_code(m);
-        const float s = e4m3_decode(sc);
-        const float s_eff = s == 0.0f ? 1.0f : s;
-        const float rs = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+        const RecipPair rp = recip_pair_code(sc);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) t[k] = div_rs(t[k], s_eff, rs);
+        for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
         const int64_t c = colp + p;
         const int64_t tok = tok0 + 32 * a + 16 * hk;
         uint32_t w0, w1;
