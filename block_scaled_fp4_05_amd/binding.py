@@ -27,8 +27,9 @@ AMAX_COMPUTE, AMAX_GIVEN = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_E_NULL", 2: "FP4Q_E_SHAPE", 3: "FP4Q_E_ALIGN", 4: "FP4Q_E_ARG", 5: "FP4Q_E_HIP"}
 
 EXPORTS = ["fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_if4",
-           "fp4q_rht", "fp4q_dequantize", "fp4q_amax", "fp4q_rht_signs_from_seed", "fp4q_status_string",
-           "fp4q_abi_version"]
+           "fp4q_rht", "fp4q_dequantize", "fp4q_amax", "fp4q_set_onepass_wait", "fp4q_onepass_fallbacks",
+           "fp4q_rht_signs_from_seed",
+           "fp4q_status_string", "fp4q_abi_version"]
 
 
 class Fp4qError(RuntimeError):
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
             "fp4q_dequantize": [_I, _P, _P, _P, _I64, _I64, _I, _P, _P],
             "fp4q_amax": [_P, _I, _I64, _I64, _P, _P],
+            "fp4q_set_onepass_wait": [_U],
+            "fp4q_onepass_fallbacks": [_P, _P],
             "fp4q_rht_signs_from_seed": [_U64, _P],
             "fp4q_status_string": [_I],
             "fp4q_abi_version": [],
@@ -66,6 +69,7 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = _I
         L.fp4q_rht_signs_from_seed.restype = None
+        L.fp4q_set_onepass_wait.restype = None
         L.fp4q_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -139,6 +143,16 @@ def fp4q_dequantize(fmt, codes, scales, tensor_scale, rows, cols, out_dt, y, str
 
 def fp4q_amax(x, dt, rows, cols, amax, stream=None) -> int:
     return _check("fp4q_amax", lib().fp4q_amax(_p(x), dt, rows, cols, _p(amax), _s(stream)))
+
+
+def fp4q_set_onepass_wait(microseconds: int) -> None:
+    lib().fp4q_set_onepass_wait(microseconds)
+
+
+def fp4q_onepass_fallbacks(stream=None) -> int:
+    out = ctypes.c_uint32(0)
+    _check("fp4q_onepass_fallbacks", lib().fp4q_onepass_fallbacks(_s(stream), ctypes.addressof(out)))
+    return out.value
 
 
 def fp4q_rht_signs_from_seed(seed: int) -> list[int]:

@@ -54,6 +54,13 @@ const char* fp4q_status_string(fp4q_status s) {
   return "unknown status";
 }
 
+void fp4q_set_onepass_wait(uint32_t microseconds) { fp4q::set_fused_wait_us(microseconds); }
+
+fp4q_status fp4q_onepass_fallbacks(hipStream_t stream, uint32_t* count) {
+  if (!count) return FP4Q_E_NULL;
+  return fp4q::fused_fallbacks(stream, count) ? FP4Q_OK : FP4Q_E_HIP;
+}
+
 void fp4q_rht_signs_from_seed(uint64_t seed, uint32_t signs[4]) {
   const uint32_t ctr[4] = {0u, 0u, 0u, 1u};
   const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
@@ -97,7 +104,13 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
                                stream);
     return after_launch();
   }
-  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax(x, dt, rows * cols, amax, stream);
+  if (amax_mode == FP4Q_AMAX_COMPUTE) {
+    // one pass when the tensor fits a co-resident grid, else amax first
+    if (fp4q::launch_nvfp4_fused(x, dt, rows, cols, layouts, sr, amax, tensor_scale, row_codes, row_scales,
+                                 col_codes, col_scales, sr_seed, stream))
+      return after_launch();
+    fp4q::launch_amax(x, dt, rows * cols, amax, stream);
+  }
   fp4q::launch_nvfp4(x, dt, rows, cols, layouts, sr, amax, tensor_scale, row_codes, row_scales, col_codes,
                      col_scales, sr_seed, stream);
   return after_launch();

@@ -13,6 +13,17 @@ void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned
                   const float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
                   uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, hipStream_t st);
 
+// NVFP4 with amax computed in the same pass.  Returns false, having enqueued nothing,
+// when the tensor does not fit one co-resident grid.
+bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
+                        float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
+                        uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, hipStream_t st);
+// Wait limit of the one-pass kernel's exchange before a workgroup computes a missing
+// maximum itself, and the count of such fallbacks on a stream (synchronizes it).
+void set_fused_wait_us(uint32_t us);
+bool fused_fallbacks(hipStream_t st, uint32_t* count);
+constexpr int kFusedMaxWg = 2048;
+
 void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax,
                      float* tensor_scale, uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st);
 

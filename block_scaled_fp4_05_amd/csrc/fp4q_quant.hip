@@ -14,6 +14,10 @@
 #include "fp4q_dev.hpp"
 #include "fp4q_internal.hpp"
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 namespace fp4q {
 
 // ===========================================================================
@@ -99,8 +103,8 @@ void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t s
 // picks the upper or lower 8 rows and lane bit 1 the left or right 8 columns, so
 // every lane holds an 8x8 micro-tile as raw input words.  A row block (16 columns)
 // is the lane pair (lane ^ 2) and a column block (16 rows) the pair (lane ^ 1): both
-// block maxima are one DPP max away.  Each pass widens the raw words and forms
-// t = x*gs on the fly, which keeps the register footprint small.
+// block maxima are one DPP max away.  t = x*gs is formed once per element and
+// serves both directions.
 //
 // Codes and scales are staged in LDS for the whole tile, so every column's 64 bytes
 // of codes and 8 scale bytes leave contiguously, and rows' outputs leave as 16-byte
@@ -115,19 +119,25 @@ template <typename T> struct Raw8x8;
 // end and columns past the end read the last valid row / column group instead.  Such
 // values only ever enter row or column blocks whose outputs are not stored (blocks
 // never straddle the matrix edge), so they cannot change a stored code.
+// The input is read exactly once, so its loads are marked non-temporal: they do not
+// displace the output lines that neighbouring tiles are still completing in L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 template <> struct Raw8x8<uint16_t> {
   uint4 r[8];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int row0, int col0, int rows, int cols) {
     const int c = min(col0, cols - 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      r[i] = *reinterpret_cast<const uint4*>(x + (int64_t)min(row0 + i, rows - 1) * cols + c);
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(x + (int64_t)min(row0 + i, rows - 1) * cols + c));
+      r[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   }
   __device__ __forceinline__ uint32_t word(int i, int k) const {
     return k == 0 ? r[i].x : k == 1 ? r[i].y : k == 2 ? r[i].z : r[i].w;
   }
-  // Hide the words' provenance from the optimizer (no instruction is emitted), so a
-  // second pass recomputes x*gs instead of keeping 64 products alive across passes.
   // element (i, j) of the micro-tile times gs
   __device__ __forceinline__ float at(int i, int j, float gs) const {
     const uint32_t w = word(i, j >> 1);
@@ -141,8 +151,10 @@ template <> struct Raw8x8<float> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float* p = x + (int64_t)min(row0 + i, rows - 1) * cols + c;
-      r[2 * i] = *reinterpret_cast<const float4*>(p);
-      r[2 * i + 1] = *reinterpret_cast<const float4*>(p + 4);
+      const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+      const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+      r[2 * i] = make_float4(a.x, a.y, a.z, a.w);
+      r[2 * i + 1] = make_float4(b.x, b.y, b.z, b.w);
     }
   }
   __device__ __forceinline__ float at(int i, int j, float gs) const {
@@ -442,6 +454,374 @@ void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned
     launch_nvfp4_dt<uint16_t>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
   else
     launch_nvfp4_dt<float>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+}
+
+// ===========================================================================
+// NVFP4 1x16 with the tensor amax found in the same pass over x.
+//
+// The tensor scale depends on the maximum over the whole tensor, so a plain
+// implementation reads x twice (amax, then quantize).  When the tensor fits in the
+// register files of one co-resident grid (up to TPW tiles per workgroup), each
+// workgroup instead loads all of its tiles once and keeps them in registers,
+// publishes its partial maximum and meets the others at a grid-wide barrier; then
+// every workgroup reduces the partial maxima itself, forms gs and quantizes its
+// tiles from registers.  x leaves HBM once.
+//
+// The grid is sized from the occupancy query so that all workgroups are resident at
+// once; then the exchange of partial maxima costs about a microsecond.  Correctness
+// does not depend on it: every wait is bounded, and a workgroup whose wait runs out
+// reads the missing part of x itself (see grid_max).
+// ===========================================================================
+
+// Workspace of the one-pass kernel.  Values that cross workgroups travel in 64-bit
+// slots holding (epoch << 32) | float bits: a reader that sees the current launch's
+// epoch in a slot has the value in the same word, so no fence is needed and nothing
+// is ever reset.  The host numbers launches per stream (epoch 1, 2, ...), so slots
+// left by earlier launches never match.
+//
+// Workgroups form 8 groups, g = b % 8, and workgroup g leads group g.  Under the
+// default dispatch, workgroup b runs on XCD b % 8, so a group shares one L2: members
+// post their slots with workgroup-scope stores, which stop in that L2, and poll the
+// group's result there; only the 8 leaders exchange words through memory.  Placement
+// is a matter of speed only: a reader that cannot see a value in time computes it.
+struct FusedWs {
+  uint64_t local[8][kFusedMaxWg / 8 + 16];   // per group: members' slots, then the result
+  uint64_t group[8][16];                      // per group: its maximum, device scope
+  uint32_t fallbacks[32];                     // waits that ran out and were answered from x
+};
+
+__device__ __forceinline__ float raw_absmax(const Raw8x8<uint16_t>& raw) {
+  // |bf16| orders like its 15 magnitude bits, so a packed 16-bit max does two at once
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, raw.word(i, k) & 0x7FFF7FFFu));
+  const uint32_t b = m.x > m.y ? m.x : m.y;
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ float raw_absmax(const Raw8x8<float>& raw) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(raw.r[i].x), __builtin_fabsf(raw.r[i].y)),
+                                           __builtin_fmaxf(__builtin_fabsf(raw.r[i].z), __builtin_fabsf(raw.r[i].w))));
+  return m;
+}
+
+// Maximum over the workgroup of a per-thread value (every thread gets the result).
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ uint64_t pack_epoch(uint32_t epoch, float v) {
+  return ((uint64_t)epoch << 32) | __float_as_uint(v);
+}
+
+// Device-scope loads skip the CU's L1; a value a workgroup of the same XCD stored with
+// a workgroup-scope store is seen in the shared L2.
+__device__ __forceinline__ uint64_t load_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls `slot` until it carries `epoch`, for at most `wait_iters` rounds of a short
+// sleep (each at least 256 clocks).  Returns whether the value arrived (in *v).
+__device__ __forceinline__ bool poll_slot(const uint64_t* slot, uint32_t epoch, uint32_t wait_iters, float* v) {
+  uint64_t w = load_dev(slot);
+  for (uint32_t it = 0; (uint32_t)(w >> 32) != epoch; ++it) {
+    if (it >= wait_iters) return false;
+    __builtin_amdgcn_s_sleep(4);
+    w = load_dev(slot);
+  }
+  *v = __uint_as_float((uint32_t)w);
+  return true;
+}
+
+// max|x| over the tiles start, start + stride, ... (< end) of the group-major sequence,
+// by the whole workgroup; every thread gets the result.  Only the fallback uses it.
+template <typename T>
+__device__ __noinline__ float tiles_absmax(const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
+                                           int start, int stride, int end, float* red) {
+  float m = 0.0f;
+  for (int t = start; t < end; t += stride) {
+    int tr, tc;
+    group_major_tile(t, tiles_r, tiles_c, tr, tc);
+    Raw8x8<T> r;
+    nvfp4_tile_load<T>(x, tr * 128, tc * 128, rows, cols, r);
+    m = __builtin_fmaxf(m, raw_absmax(r));
+  }
+  return block_max256(m, red);
+}
+
+struct GridMaxShared {
+  float red[4];
+  uint32_t miss[8];   // bit j: slot j of the current wait did not arrive in time
+  float val;
+};
+
+// Grid-wide maximum of the workgroups' values v (thread 0's copy), returned to every
+// thread.  Members post their slot in the group area; leader g collects the group's
+// slots, posts the group maximum at device scope, collects the eight group maxima and
+// posts the result in the group area, where the members poll it.
+//
+// No wait depends on other workgroups making progress for correctness: a slot that
+// has not arrived after `wait_iters` polls is computed from x by the waiting
+// workgroup itself (one workgroup's tiles, a group's band, or a member's whole
+// tensor).  With the whole grid resident, which the launch size is chosen for, the
+// fallback never runs; without it, the grid still finishes with the exact maximum.
+template <typename T>
+__device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, uint32_t wait_iters,
+                                          const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
+                                          GridMaxShared& sh) {
+  const int b = blockIdx.x, nwg = gridDim.x, g = b & 7, ng = nwg >> 3;
+  const int tid = threadIdx.x;
+  const int total = tiles_r * tiles_c, per = (total + 7) >> 3;
+  uint64_t* local = ws->local[g];
+  uint64_t* result = local + kFusedMaxWg / 8;
+  if (tid < 8) sh.miss[tid] = 0u;
+  if (tid == 0 && b >= 8)   // one 64-bit store through this CU's L1 into the L2
+    __hip_atomic_store(&local[b >> 3], pack_epoch(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  if (b < 8) {                                        // leader of group g == b
+    float m = v;
+    for (int j = 1 + tid; j < ng; j += 256) {
+      float u;
+      if (poll_slot(&local[j], epoch, wait_iters, &u)) m = __builtin_fmaxf(m, u);
+      else atomicOr(&sh.miss[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    for (int j = 1; j < ng; ++j)                      // uniform: miss[] is shared
+      if (sh.miss[j >> 5] & (1u << (j & 31))) {
+        const int band0 = g * per;
+        m = __builtin_fmaxf(m, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, band0 + j, ng,
+                                               min(total, band0 + per), sh.red));
+        if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    m = block_max256(m, sh.red);
+    if (tid == 0)
+      __hip_atomic_store(&ws->group[g][0], pack_epoch(epoch, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 8) sh.miss[tid] = 0u;
+    __syncthreads();
+    float t = 0.0f;
+    if (tid < 8) {
+      float u;
+      if (poll_slot(&ws->group[tid][0], epoch, wait_iters, &u)) t = u;
+      else atomicOr(&sh.miss[0], 1u << tid);
+    }
+    __syncthreads();
+    for (int k = 0; k < 8; ++k)
+      if (sh.miss[0] & (1u << k)) {
+        t = __builtin_fmaxf(t, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, k * per, 1,
+                                               min(total, (k + 1) * per), sh.red));
+        if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    t = block_max256(t, sh.red);
+    if (tid == 0) __hip_atomic_store(result, pack_epoch(epoch, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return t;
+  }
+  if (tid == 0) {
+    float u;
+    if (poll_slot(result, epoch, wait_iters, &u)) sh.val = u;
+    else sh.miss[0] = 1u;
+  }
+  __syncthreads();
+  if (sh.miss[0]) {
+    if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, 0, 1, total, sh.red);
+  }
+  return sh.val;
+}
+
+// Tile K, then K+1, ... with compile-time indices, so the raw tiles stay in registers.
+template <typename T, int TPW, bool ROW, bool COL, bool SR, int K>
+__device__ __forceinline__ void fused_phase2(Raw8x8<T> (&raw)[TPW], const int (&tr)[TPW], const int (&tc)[TPW],
+                                             const bool (&ok)[TPW], int rows, int cols, float gs, TileStage& stage,
+                                             const RecipTable& rtab, uint8_t* __restrict__ rcodes,
+                                             uint8_t* __restrict__ rscales, uint8_t* __restrict__ ccodes,
+                                             uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
+  if (ok[K])
+    nvfp4_tile<T, ROW, COL, SR>(raw[K], tr[K] * 128, tc[K] * 128, rows, cols, gs, stage, rtab, rcodes, rscales,
+                                ccodes, cscales, k0, k1);
+  if constexpr (K + 1 < TPW)
+    fused_phase2<T, TPW, ROW, COL, SR, K + 1>(raw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+                                              cscales, k0, k1);
+}
+
+template <typename T, int TPW, bool ROW, bool COL, bool SR>
+__global__ __launch_bounds__(256) void k_nvfp4_fused(
+    const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c, FusedWs* __restrict__ ws,
+    uint32_t epoch, uint32_t wait_iters,
+    float* __restrict__ amax_out, float* __restrict__ tensor_scale,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
+    uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
+  __shared__ TileStage stage;
+  __shared__ RecipTable rtab;
+  __shared__ GridMaxShared gsh;
+  fill_recip_table(rtab);
+
+  // Same band layout as the streaming kernel: XCD x owns a contiguous run of the
+  // group-major tile sequence and its nx workgroups take every nx-th tile of it.
+  const int total = tiles_r * tiles_c;
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, nx = (nwg + 7 - xcd) >> 3, lb = b >> 3;
+  const int per = (total + 7) >> 3;
+  const int band0 = xcd * per, band1 = min(total, band0 + per);
+  const int last = band1 > band0 ? band1 - 1 : total - 1;
+
+  // phase 1: every tile load in flight at once; out-of-band slots reload a valid
+  // tile, which leaves the maximum unchanged and keeps the loads branch-free
+  Raw8x8<T> raw[TPW];
+  int tr[TPW], tc[TPW];
+  bool ok[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = band0 + lb + k * nx;
+    ok[k] = t < band1;
+    group_major_tile(ok[k] ? t : last, tiles_r, tiles_c, tr[k], tc[k]);
+    nvfp4_tile_load<T>(x, tr[k] * 128, tc[k] * 128, rows, cols, raw[k]);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) m = __builtin_fmaxf(m, raw_absmax(raw[k]));
+  m = block_max256(m, gsh.red);
+  const float g = grid_max<T>(ws, m, epoch, wait_iters, x, rows, cols, tiles_r, tiles_c, gsh);
+  const float gs = tensor_scale_from_amax(g);
+  if (b == 0 && threadIdx.x == 0) {
+    *amax_out = g;
+    *tensor_scale = gs;
+  }
+
+  // phase 2: quantize from registers
+  fused_phase2<T, TPW, ROW, COL, SR, 0>(raw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+                                        cscales, k0, k1);
+}
+
+namespace {
+
+std::atomic<uint32_t> g_wait_iters{2000u};   // polls of >= 256 clocks each: >= 200 us at 2.4 GHz
+
+struct WsEntry {
+  int dev;
+  hipStream_t stream;
+  FusedWs* ws;
+  uint32_t epoch;          // launches enqueued so far; the device words start at epoch 0
+};
+
+struct Launch {
+  FusedWs* ws;
+  uint32_t epoch;
+};
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+
+// The stream's workspace on the current device, allocated and zeroed on first use.
+FusedWs* find_ws(hipStream_t st, WsEntry** entry) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (WsEntry& e : g_ws)
+    if (e.dev == dev && e.stream == st) {
+      *entry = &e;
+      return e.ws;
+    }
+  FusedWs* ws = nullptr;
+  if (hipMalloc(&ws, sizeof(FusedWs)) != hipSuccess) return nullptr;
+  if (hipMemset(ws, 0, sizeof(FusedWs)) != hipSuccess) {
+    (void)hipFree(ws);
+    return nullptr;
+  }
+  g_ws.push_back(WsEntry{dev, st, ws, 0u});
+  *entry = &g_ws.back();
+  return ws;
+}
+
+// Reserves the next launch on the stream: its workspace and epoch.  An epoch only has
+// to differ from the one a slot held before, so launches may run in any order.
+bool reserve_launch(hipStream_t st, Launch* l) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  WsEntry* e = nullptr;
+  if (!find_ws(st, &e)) return false;
+  e->epoch += 1u;
+  if (e->epoch == 0u) e->epoch = 1u;   // 0 is the zeroed workspace's value
+  *l = Launch{e->ws, e->epoch};
+  return true;
+}
+
+template <typename T, int TPW, bool ROW, bool COL, bool SR>
+bool try_fused_t(const T* x, int rows, int cols, float* amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                 uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+  const int tiles_r = (rows + 127) / 128, tiles_c = (cols + 127) / 128, total = tiles_r * tiles_c;
+  const int per = (total + 7) / 8;
+  const int nwg = 8 * ((per + TPW - 1) / TPW);
+  auto kern = k_nvfp4_fused<T, TPW, ROW, COL, SR>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess) return false;
+  if (nwg > kFusedMaxWg || nwg > per_cu * num_cus()) return false;
+  Launch l;
+  if (!reserve_launch(st, &l)) return false;
+  kern<<<nwg, 256, 0, st>>>(x, rows, cols, tiles_r, tiles_c, l.ws, l.epoch, g_wait_iters.load(), amax, ts, rc, rs,
+                            cc, cs, k0, k1);
+  return true;
+}
+
+template <typename T, bool ROW, bool COL, bool SR>
+bool try_fused_rcs(const T* x, int rows, int cols, float* amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                   uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+  // fewest tiles per workgroup that still fit one co-resident grid
+  if (try_fused_t<T, 1, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)) return true;
+  if (try_fused_t<T, 2, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)) return true;
+  if constexpr (sizeof(T) == 2)
+    if (try_fused_t<T, 4, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)) return true;
+  return false;
+}
+
+template <typename T>
+bool try_fused_dt(const void* xv, int64_t rows, int64_t cols, unsigned layouts, bool sr, float* amax, float* ts,
+                  uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+  const T* x = static_cast<const T*>(xv);
+  const bool row = layouts & 1u, col = layouts & 2u;
+  const int r = (int)rows, c = (int)cols;
+#define FP4Q_FU(R, C, S) try_fused_rcs<T, R, C, S>(x, r, c, amax, ts, rc, rs, cc, cs, k0, k1, st)
+  if (row && col) return sr ? FP4Q_FU(true, true, true) : FP4Q_FU(true, true, false);
+  if (row) return sr ? FP4Q_FU(true, false, true) : FP4Q_FU(true, false, false);
+  return sr ? FP4Q_FU(false, true, true) : FP4Q_FU(false, true, false);
+#undef FP4Q_FU
+}
+
+}  // namespace
+
+bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
+                        float* amax, float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs,
+                        uint64_t seed, hipStream_t st) {
+  if (rows > (1 << 30) || cols > (1 << 30)) return false;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  if (dtype == 1)
+    return try_fused_dt<uint16_t>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+  return try_fused_dt<float>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+}
+
+void set_fused_wait_us(uint32_t us) {
+  const uint64_t t = (uint64_t)us * 10u;   // one poll round takes at least ~0.1 us
+  g_wait_iters.store(t > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)t);
+}
+
+bool fused_fallbacks(hipStream_t st, uint32_t* count) {
+  FusedWs* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry* e = nullptr;
+    ws = find_ws(st, &e);
+  }
+  if (!ws) return false;
+  return hipMemcpyAsync(count, &ws->fallbacks[0], 4, hipMemcpyDeviceToHost, st) == hipSuccess &&
+         hipStreamSynchronize(st) == hipSuccess;
 }
 
 // ===========================================================================

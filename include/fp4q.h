@@ -17,10 +17,13 @@
  * Conventions for every call:
  *  - Tensor pointers are HIP DEVICE pointers to dense row-major matrices (row stride
  *    == cols).  `rows` x `cols` is the shape of the input matrix.
- *  - Every device pointer must be 16-byte aligned (FP4Q_E_ALIGN otherwise).
+ *  - Tensor, code and scale pointers must be 16-byte aligned, the float[1] amax and
+ *    tensor_scale pointers 4-byte aligned (FP4Q_E_ALIGN otherwise).
  *  - Inputs and outputs must not overlap.  The caller allocates every buffer and
- *    keeps it alive until the work on `stream` has completed; the library
- *    allocates nothing and keeps no state between calls.
+ *    keeps it alive until the work on `stream` has completed.  The only memory the
+ *    library owns is a small per-(device, stream) workspace of the one-pass NVFP4
+ *    kernel (about 8 KB), allocated on the first such call on that stream and kept
+ *    until the process ends; that first call is therefore not graph-capturable.
  *  - A call validates its arguments on the host, enqueues its kernels on `stream`
  *    (0 = the null stream) and returns without synchronizing.  On any validation
  *    error nothing is enqueued.  Device faults surface at the caller's next sync.
@@ -165,6 +168,18 @@ fp4q_status fp4q_amax(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, 
 /* The RHT sign mask for a seed: one Philox4x32-10 call with counter {0,0,0,1} and key
  * {lo32(seed), hi32(seed)}; its 128 output bits are the signs (host only). */
 void fp4q_rht_signs_from_seed(uint64_t seed, uint32_t signs[4]);
+
+/* One-pass NVFP4 (AMAX_COMPUTE on a tensor that fits one resident grid): workgroups
+ * exchange partial maxima through the per-stream workspace, and a workgroup whose wait
+ * for a missing value exceeds this limit reads the corresponding part of x itself, so
+ * results never depend on every workgroup being resident.  Default 200 us; 0 makes
+ * every wait give up at once (slow, but exact).  Process-wide; applies to calls
+ * enqueued afterwards. */
+void fp4q_set_onepass_wait(uint32_t microseconds);
+
+/* Waits for `stream`, then stores in *count how many times one-pass calls on it fell
+ * back to reading x for a missing maximum (0 when the grid was resident). */
+fp4q_status fp4q_onepass_fallbacks(hipStream_t stream, uint32_t* count);
 
 const char* fp4q_status_string(fp4q_status status);
 int fp4q_abi_version(void);

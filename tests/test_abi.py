@@ -95,5 +95,6 @@ def test_other_entry_points_validate():
     assert L.fp4q_dequantize(2, A, A, None, 16, 48, 0, A, 0) == 2
     assert L.fp4q_dequantize(1, A, A, A2, 8, 64, 0, A, 0) == 2
     assert L.fp4q_dequantize(0, A, A, A2, 16, 64, 5, A, 0) == 4
+    assert L.fp4q_onepass_fallbacks(0, None) == 1
     assert L.fp4q_amax(None, 0, 4, 4, A2, 0) == 1
     assert L.fp4q_amax(A, 0, 0, 4, A2, 0) == 2

@@ -160,6 +160,112 @@ def test_nvfp4_full_activation_config_sampled():
         assert np.array_equal(ccg[j0:j0 + 8], c) and np.array_equal(csg[j0:j0 + 8], s)
 
 
+def _exact_given_amax(xh):
+    return torch.tensor([oracle.amax(xh)], dtype=torch.float32, device=DEV)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(256, 512), (272, 400), (1040, 144), (16, 16)])
+@pytest.mark.parametrize("rnd", [0, 1])
+def test_nvfp4_two_pass_streaming_kernel(kind, shape, rnd):
+    """AMAX_GIVEN skips the one-pass kernel: the streaming tile kernel alone, ragged tiles included."""
+    rows, cols = shape
+    xh, xd = make_input(kind, rows, cols, seed=rows * 3 + cols)
+    seed = 0xBEEF + rows
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, rnd=rnd, sr_seed=seed, amax=_exact_given_amax(xh))
+    rc, rs, gs = oracle.quantize_nvfp4(xh, rnd=rnd, seed=seed)
+    cc, cs, _ = oracle.quantize_nvfp4(xh, colwise=True, rnd=rnd, seed=seed)
+    assert host(out["tensor_scale"])[0] == gs
+    assert np.array_equal(host(out["row_codes"]), rc) and np.array_equal(host(out["row_scales"]), rs)
+    assert np.array_equal(host(out["col_codes"]), cc) and np.array_equal(host(out["col_scales"]), cs)
+
+
+@pytest.mark.parametrize("layouts", [3, 1, 2])
+def test_nvfp4_one_pass_mid_size(layouts):
+    """4000 x 2608 bf16 (32 x 21 tiles, ragged on both edges): more tiles than one per workgroup."""
+    rows, cols = 4000, 2608
+    xh, xd = make_input("bf16", rows, cols, seed=17)
+    out = B.quantize_nvfp4(xd, layouts)
+    if layouts & B.ROWWISE:
+        rc, rs, gs = oracle.quantize_nvfp4(xh)
+        assert np.array_equal(host(out["row_codes"]), rc) and np.array_equal(host(out["row_scales"]), rs)
+    if layouts & B.COLWISE:
+        cc, cs, gs = oracle.quantize_nvfp4(xh, colwise=True)
+        assert np.array_equal(host(out["col_codes"]), cc) and np.array_equal(host(out["col_scales"]), cs)
+    assert host(out["amax"])[0] == np.float32(oracle.amax(xh))
+    assert host(out["tensor_scale"])[0] == gs
+
+
+def test_nvfp4_one_pass_repeated_launches_agree():
+    """The grid barrier is reused launch after launch; results must not depend on it."""
+    rows, cols = 1024, 2048
+    xh, xd = make_input("bf16", rows, cols, seed=23)
+    first = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
+    for _ in range(5):
+        again = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
+        for k in ("row_codes", "row_scales", "col_codes", "col_scales", "amax", "tensor_scale"):
+            assert torch.equal(again[k], first[k])
+    rc, rs, gs = oracle.quantize_nvfp4(xh)
+    assert np.array_equal(host(first["row_codes"]), rc)
+
+
+@pytest.mark.parametrize("shape", [(1024, 2048), (4000, 2608), (8192, 4096)])
+def test_nvfp4_one_pass_grid_resident_no_fallback(shape):
+    """At the default wait limit the sized-to-fit grid is resident: no workgroup reads x twice."""
+    rows, cols = shape
+    xh, xd = make_input("bf16", rows, cols, seed=31)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        before = B.fp4q_onepass_fallbacks(stream=s)
+        out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, stream=s)
+        after = B.fp4q_onepass_fallbacks(stream=s)
+    assert after == before
+    assert host(out["amax"])[0] == np.float32(oracle.amax(xh))
+
+
+@pytest.mark.parametrize("shape", [(1024, 2048), (2048, 4096)])
+def test_nvfp4_one_pass_forced_fallback_is_exact(shape):
+    """Wait limit 0: every wait gives up at once and the workgroup reads the missing part of
+    x itself; codes, scales and amax must still match the oracle bit for bit."""
+    rows, cols = shape
+    xh, xd = make_input("bf16", rows, cols, seed=37)
+    s = torch.cuda.Stream()
+    try:
+        B.fp4q_set_onepass_wait(0)
+        with torch.cuda.stream(s):
+            before = B.fp4q_onepass_fallbacks(stream=s)
+            out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, stream=s)
+            after = B.fp4q_onepass_fallbacks(stream=s)
+    finally:
+        B.fp4q_set_onepass_wait(200)
+    assert after > before
+    rc, rs, gs = oracle.quantize_nvfp4(xh)
+    cc, cs, _ = oracle.quantize_nvfp4(xh, colwise=True)
+    assert host(out["amax"])[0] == np.float32(oracle.amax(xh))
+    assert host(out["tensor_scale"])[0] == gs
+    assert np.array_equal(host(out["row_codes"]), rc) and np.array_equal(host(out["row_scales"]), rs)
+    assert np.array_equal(host(out["col_codes"]), cc) and np.array_equal(host(out["col_scales"]), cs)
+
+
+def test_nvfp4_beyond_one_grid_falls_back_sampled():
+    """bf16 [16384 x 4096] has more tiles than one co-resident grid holds: amax pass + streaming pass."""
+    bits = si.activation(16384, 4096, seed=29)
+    xd = dev_bf16(bits)
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
+    amax = oracle.amax(bits)
+    gs = oracle.tensor_scale(amax)
+    assert host(out["amax"])[0] == np.float32(amax)
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    rcg, rsg = host(out["row_codes"]), host(out["row_scales"])
+    ccg, csg = host(out["col_codes"]), host(out["col_scales"])
+    for r0 in (0, 8192, 16368):
+        c, s = oracle.quantize_nvfp4_rows(bits, r0, 16, False, gs)
+        assert np.array_equal(rcg[r0:r0 + 16], c) and np.array_equal(rsg[r0:r0 + 16], s)
+    for j0 in (0, 2056, 4088):
+        c, s = oracle.quantize_nvfp4_rows(bits, j0, 8, True, gs)
+        assert np.array_equal(ccg[j0:j0 + 8], c) and np.array_equal(csg[j0:j0 + 8], s)
+
+
 # ---------------------------------------------------------------------------------------
 # NVFP4 16x16
 # ---------------------------------------------------------------------------------------
