@@ -308,7 +308,38 @@ class IF4RoundTrip(Workload):
                 "sample": f"IF4 of rows 0..{nrows - 1} ({nrows}x{self.cols}), single thread, {dt:.1f} s"}
 
 
+class DeviceCopy(Workload):
+    """Calibration, not a hot-path row: a plain device-to-device copy of 64 MiB.  It gives
+    the copy rate this machine reaches and the factor between rocprofv3's FETCH_SIZE /
+    WRITE_SIZE and bytes actually moved (each is known to be 64 MiB per launch)."""
+    name = "device_copy_64MiB"
+    nbytes = 64 << 20
+
+    def __init__(self):
+        self.elements = self.nbytes // 2
+        self.algo_bytes = 2 * self.nbytes
+        self.kernel = "copyBuffer"
+        self.kernel_bytes = self.algo_bytes
+
+    def setup(self, nbuf):
+        import torch
+        n = self.nbytes // 2
+        self.src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(nbuf)]
+        self.dst = [torch.empty_like(t) for t in self.src]
+
+    def step(self, i):
+        k = i % len(self.src)
+        self.dst[k].copy_(self.src[k])
+
+    def kernel_launch(self, i):
+        self.step(i)
+
+    def cpu_baseline(self, budget_s):
+        return None
+
+
 WORKLOADS = {"activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT, "if4": IF4RoundTrip}
+CALIBRATION = {"copy": DeviceCopy}
 
 
 # --------------------------------------------------------------------------------------
@@ -379,7 +410,9 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
         line["config"]["dequant_ms"] = dq
         line["config"]["dequant_GBps"] = (n // 2 + n // 16 + 4 * n) / (dq * 1e-3) / 1e9
     if cpu_budget > 0:
-        line["cpu_baseline"] = wl.cpu_baseline(cpu_budget)
+        cb = wl.cpu_baseline(cpu_budget)
+        if cb is not None:
+            line["cpu_baseline"] = cb
     return line
 
 
@@ -388,7 +421,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="activation", choices=list(WORKLOADS) + ["all"])
+    ap.add_argument("--config", default="activation", choices=list(WORKLOADS) + list(CALIBRATION) + ["all"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline (0: skip)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -403,7 +436,8 @@ def main(argv=None):
     B.lib()
     names = list(WORKLOADS) if a.config == "all" else [a.config]
     for n in names:
-        line = run(WORKLOADS[n](), a.steps, a.warmup, a.cpu_budget)
+        wl = WORKLOADS[n]() if n in WORKLOADS else CALIBRATION[n]()
+        line = run(wl, a.steps, a.warmup, a.cpu_budget)
         print(json.dumps(line), flush=True)
         torch.cuda.empty_cache()
     return 0
