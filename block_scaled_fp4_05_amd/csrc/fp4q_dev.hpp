@@ -16,6 +16,8 @@
 namespace fp4q {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // bf16 / f32 loads

@@ -76,15 +76,62 @@ __global__ void k_amax_tail(const T* __restrict__ x, int64_t start, int64_t n, f
   if (threadIdx.x == 0) atomic_max_nonneg(amax, m);
 }
 
+// Large tensors: two 256-thread workgroups per CU, each thread keeping four
+// non-temporal 16-byte loads in flight, and the maximum taken on magnitude bits
+// (|x| orders like its bits with the sign cleared; bf16 two at a time).
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_wide(const u32x4_t* __restrict__ x, int64_t n16,
+                                                   float* __restrict__ amax) {
+  __shared__ float wm[4];
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t m32 = 0;
+  u16x2 m16 = {0, 0};
+  auto fold = [&](const u32x4_t v) {
+    if constexpr (sizeof(T) == 2) {
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu));
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+      m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+    } else {
+      m32 = max(m32, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+  };
+  for (; g + 3 * stride < n16; g += 4 * stride) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(x + g + k * stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fold(v[k]);
+  }
+  for (; g < n16; g += stride) fold(__builtin_nontemporal_load(x + g));
+  float f;
+  if constexpr (sizeof(T) == 2) f = __uint_as_float((uint32_t)max(m16.x, m16.y) << 16);
+  else f = __uint_as_float(m32);
+  f = wave_max(f);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = f;
+  __syncthreads();
+  if (threadIdx.x == 0) atomic_max_nonneg(amax, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])));
+}
+
 static int amax_grid(int64_t n8) {
   int64_t blocks = (n8 + 1023) / 1024;
   return (int)(blocks < 256 ? (blocks > 0 ? blocks : 1) : 256);
 }
 
+static int num_cus();
+
 template <typename T>
 static void launch_amax_t(const void* x, int64_t n, float* amax, hipStream_t st) {
   const T* xp = static_cast<const T*>(x);
   k_zero1<<<1, 1, 0, st>>>(amax);
+  if ((int64_t)sizeof(T) * n >= ((int64_t)128 << 20)) {
+    const int64_t per16 = 16 / sizeof(T), n16 = n / per16;
+    k_amax_wide<T><<<2 * num_cus(), 256, 0, st>>>(static_cast<const u32x4_t*>(x), n16, amax);
+    if (n16 * per16 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n16 * per16, n, amax);
+    return;
+  }
   int64_t n8 = n / 8;
   if (n8 > 0) k_amax<T><<<amax_grid(n8), 1024, 0, st>>>(xp, n8, amax);
   if (n8 * 8 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n8 * 8, n, amax);
@@ -121,8 +168,6 @@ template <typename T> struct Raw8x8;
 // never straddle the matrix edge), so they cannot change a stored code.
 // The input is read exactly once, so its loads are marked non-temporal: they do not
 // displace the output lines that neighbouring tiles are still completing in L2.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <> struct Raw8x8<uint16_t> {
   uint4 r[8];

@@ -6,10 +6,10 @@
 //
 // bf16 inputs run the contraction on MFMA (v_mfma_f32_32x32x16_bf16): the +-1
 // matrix K[i][t] = H[i][t] s_t is exact in bf16 and the sum is accumulated in fp32.
-// One wave owns a tile of 128 tokens x 64 columns; lane l loads a 2-column x 8-token
-// micro-tile with 4-byte loads (lanes 0..31 read 128 contiguous bytes of a token
-// row) and transposes it in registers (v_perm) into the B operand, so no LDS is
-// needed.  Sylvester H factors as H_128[32a+u][32b+w] = H_4[a][b] H_32[u][w]: the A
+// One wave owns a tile of 128 tokens x 64 columns; lane l loads a 2-column x 64-token
+// slice with 4-byte loads (lanes 0..31 read 128 contiguous bytes of a token row), all
+// issued before the first MFMA, and transposes it in registers (v_perm) into the B
+// operands, so no LDS is needed.  Sylvester H factors as H_128[32a+u][32b+w] = H_4[a][b] H_32[u][w]: the A
 // operand of a K-step only depends on the H_32 part (folded with the signs, kept in
 // registers for the wave's lifetime), and the H_4 sign is applied by negating the B
 // operand for the output row-blocks that need it.
@@ -55,38 +55,53 @@ __device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_sig
   }
 }
 
-// Contract one tile: tokens tok0..tok0+127, columns colp and colp+1 for this lane
-// (colp = col_base + 2*(lane & 31)).  acc[p][a] is the 32x32 MFMA output block a
-// (output tokens 32a..32a+31) for column parity p.
-__device__ __forceinline__ void rht_contract(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0,
-                                             int64_t colp, bool valid, const u32x4 frag[8], f32x16 acc[2][4]) {
+// The 64 words one lane reads for a tile: tokens tok0 + 16kk + 8hk + r (r = 0..7) of
+// columns colp, colp+1.  All loads are issued before any MFMA and none sits under a
+// branch, so the tile costs one memory round trip: a lane past the last column reads
+// column pair 0 instead and its results are discarded by the caller.
+struct RhtRaw {
+  uint32_t v[8][8];
+};
+
+__device__ __forceinline__ void rht_load(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0, int64_t colp,
+                                         bool valid, RhtRaw& raw) {
   const uint32_t hk = (threadIdx.x & 63) >> 5;
+  const uint16_t* base = x + (tok0 + 8 * hk) * cols + (valid ? colp : 0);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      raw.v[kk][r] = *reinterpret_cast<const uint32_t*>(base + (int64_t)(16 * kk + r) * cols);
+}
+
+// Half H of one tile from its raw words: acc[p][a'] is the 32x32 MFMA output block
+// a = 2H + a' (output tokens 32a..32a+31) for column parity p of this lane's column
+// pair.  Working in halves keeps 64 accumulators live instead of 128, which lets two
+// waves share a SIMD.
+template <int H>
+__device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag[8], f32x16 acc[2][2]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) acc[p][a] = f32x16{};
+    for (int a = 0; a < 2; ++a) acc[p][a] = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    uint32_t rowv[8];
-    const int64_t tb = tok0 + 16 * kk + 8 * hk;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      rowv[r] = valid ? *reinterpret_cast<const uint32_t*>(x + (tb + r) * cols + colp) : 0u;
     u32x4 b0, b1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      b0[q] = __builtin_amdgcn_perm(rowv[2 * q + 1], rowv[2 * q], 0x05040100u);
-      b1[q] = __builtin_amdgcn_perm(rowv[2 * q + 1], rowv[2 * q], 0x07060302u);
+      b0[q] = __builtin_amdgcn_perm(raw.v[kk][2 * q + 1], raw.v[kk][2 * q], 0x05040100u);
+      b1[q] = __builtin_amdgcn_perm(raw.v[kk][2 * q + 1], raw.v[kk][2 * q], 0x07060302u);
     }
     const u32x4 nb0 = b0 ^ 0x80008000u, nb1 = b1 ^ 0x80008000u;
     const bf16x8 fa = __builtin_bit_cast(bf16x8, frag[kk]);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int ap = 0; ap < 2; ++ap) {
+      const int a = 2 * H + ap;
       const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, flip ? nb0 : b0);
       const bf16x8 v1 = __builtin_bit_cast(bf16x8, flip ? nb1 : b1);
-      acc[0][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][a], 0, 0, 0);
-      acc[1][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][a], 0, 0, 0);
+      acc[0][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][ap], 0, 0, 0);
+      acc[1][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][ap], 0, 0, 0);
     }
   }
 }
@@ -104,10 +119,12 @@ struct TileIter {
     nchunk = rows / 128;
     ntiles = nslab * nchunk;
   }
-  // tiles run chunk-fastest so that consecutive tiles complete each column's output lines
+  // tiles run slab-fastest: the waves in flight read whole token rows (every 64-column
+  // slab of the same chunks), which keeps DRAM pages open; the column-wise output
+  // lines they share (two chunks per 128-byte line) are completed within that window
   __device__ void decode(int64_t tile, int64_t& chunk, int64_t& slab) const {
-    slab = tile / nchunk;
-    chunk = tile - slab * nchunk;
+    chunk = tile / nslab;
+    slab = tile - chunk * nslab;
   }
 };
 
@@ -129,17 +146,24 @@ __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x
     it.decode(tile, chunk, slab);
     const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
     const bool valid = colp < cols;
-    f32x16 acc[2][4];
-    rht_contract(x, cols, tok0, colp, valid, frag, acc);
+    RhtRaw raw;
+    rht_load(x, cols, tok0, colp, valid, raw);
+    auto emit = [&](const f32x16 (&acc)[2][2], int a0) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int ap = 0; ap < 2; ++ap)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = acc_row(a, r);
-        float v0 = acc[0][a][r] * kRhtScale, v1 = acc[1][a][r] * kRhtScale;
-        if (inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) { v0 = -v0; v1 = -v1; }
-        if (valid) *reinterpret_cast<float2*>(y + (tok0 + t) * cols + colp) = make_float2(v0, v1);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int t = acc_row(a0 + ap, r);
+          float v0 = acc[0][ap][r] * kRhtScale, v1 = acc[1][ap][r] * kRhtScale;
+          if (inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) { v0 = -v0; v1 = -v1; }
+          if (valid) *reinterpret_cast<float2*>(y + (tok0 + t) * cols + colp) = make_float2(v0, v1);
+        }
+    };
+    f32x16 acc[2][2];
+    rht_mma_half<0>(raw, frag, acc);
+    emit(acc, 0);
+    rht_mma_half<1>(raw, frag, acc);
+    emit(acc, 2);
   }
 }
 
@@ -158,18 +182,33 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
     it.decode(tile, chunk, slab);
     const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
     const bool valid = colp < cols;
-    f32x16 acc[2][4];
-    rht_contract(x, cols, tok0, colp, valid, frag, acc);
+    RhtRaw raw;
+    rht_load(x, cols, tok0, colp, valid, raw);
+    float t = 0.0f;
+    auto fold = [&](const f32x16 (&acc)[2][2]) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = __builtin_fmaxf(m, __builtin_fabsf(acc[p][a][r]));
+          for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, __builtin_fabsf(acc[p][a][r]));
+    };
+    f32x16 acc[2][2];
+    rht_mma_half<0>(raw, frag, acc);
+    fold(acc);
+    rht_mma_half<1>(raw, frag, acc);
+    fold(acc);
+    if (valid) m = __builtin_fmaxf(m, t);
   }
-  // max |fl(acc*k)| = fl(max|acc| * k): scaling is monotone
-  m = wave_max(m) * kRhtScale;
-  if (lane == 0) atomic_max_nonneg(amax, m);
+  // max |fl(acc*k)| = fl(max|acc| * k): scaling is monotone.  One atomic per
+  // workgroup: same-address atomics serialize, so per-wave atomics would cost more
+  // than the transform.
+  __shared__ float wm[4];
+  m = wave_max(m);
+  if (lane == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomic_max_nonneg(amax, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])) * kRhtScale);
 }
 
 // ---------------------------------------------------------------------------
@@ -188,68 +227,110 @@ __global__ __launch_bounds__(256) void k_rht_nvfp4_col(const uint16_t* __restric
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63, hk = lane >> 5;
   const int64_t half_rows = rows >> 1, nb = rows >> 4;
-  for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
+  // The next tile's raw words are loaded while this one is transformed and
+  // quantized; each loop step is written out with and without the next load so
+  // the compiler's wait before the MFMAs covers only the current tile.
+  auto process = [&](const RhtRaw& raw, int64_t tile) {
     int64_t chunk, slab;
     it.decode(tile, chunk, slab);
     const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
     const bool valid = colp < cols;
-    f32x16 acc[2][4];
-    rht_contract(x, cols, tok0, colp, valid, frag, acc);
+    uint32_t scale_word[2] = {0u, 0u};
+    // quantize the 16-token column blocks of output blocks a0 and a0 + 1
+    auto quantize = [&](f32x16 (&acc)[2][2], int a0) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int ap = 0; ap < 2; ++ap) {
+          const int a = a0 + ap;
+          // regroup: lanes < 32 take rows 0..15 of block a, lanes >= 32 rows 16..31
+          float t[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][j]),
+                                                        __float_as_uint(acc[p][ap][8 + j]), false, false);
+            auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][4 + j]),
+                                                        __float_as_uint(acc[p][ap][12 + j]), false, false);
+            t[j] = __uint_as_float(s02[0]);
+            t[4 + j] = __uint_as_float(s02[1]);
+            t[8 + j] = __uint_as_float(s13[0]);
+            t[12 + j] = __uint_as_float(s13[1]);
+          }
+          float m = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            t[k] = (t[k] * kRhtScale) * gs;
+            m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
+          }
+          const uint32_t sc = nvfp4_scale_code(m);
+          const RecipPair rp = recip_pair_code(sc);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
+          const int64_t c = colp + p;
+          const int64_t tok = tok0 + 32 * a + 16 * hk;
+          uint32_t w0, w1;
+          if constexpr (SR) {
+            uint32_t r0[8], r1[8];
+            const uint64_t idx8 = (uint64_t)(c * rows + tok) >> 3;
+            sr_draws8(idx8, 1u, k0, k1, r0);
+            sr_draws8(idx8 + 1, 1u, k0, k1, r1);
+            w0 = pack8_sr(t, r0, 1.0f);
+            w1 = pack8_sr(t + 8, r1, 1.0f);
+          } else {
+            w0 = pack8_rtn(t, 1.0f);
+            w1 = pack8_rtn(t + 8, 1.0f);
+          }
+          if (valid) *reinterpret_cast<uint2*>(ccodes + c * half_rows + (tok >> 1)) = make_uint2(w0, w1);
+          scale_word[p] |= sc << (8 * a);
+        }
+    };
+    f32x16 acc[2][2];
+    rht_mma_half<0>(raw, frag, acc);
+    quantize(acc, 0);
+    rht_mma_half<1>(raw, frag, acc);
+    quantize(acc, 2);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      uint32_t scale_word = 0;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        // regroup: lanes < 32 take rows 0..15 of block a, lanes >= 32 rows 16..31
-        float t[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][a][j]),
-                                                      __float_as_uint(acc[p][a][8 + j]), false, false);
-          auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][a][4 + j]),
-                                                      __float_as_uint(acc[p][a][12 + j]), false, false);
-          t[j] = __uint_as_float(s02[0]);
-          t[4 + j] = __uint_as_float(s02[1]);
-          t[8 + j] = __uint_as_float(s13[0]);
-          t[12 + j] = __uint_as_float(s13[1]);
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          t[k] = (t[k] * kRhtScale) * gs;
-          m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
-        }
-        const uint32_t sc = nvfp4_scale_code(m);
-        const RecipPair rp = recip_pair_code(sc);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
-        const int64_t c = colp + p;
-        const int64_t tok = tok0 + 32 * a + 16 * hk;
-        uint32_t w0, w1;
-        if constexpr (SR) {
-          uint32_t r0[8], r1[8];
-          const uint64_t idx8 = (uint64_t)(c * rows + tok) >> 3;
-          sr_draws8(idx8, 1u, k0, k1, r0);
-          sr_draws8(idx8 + 1, 1u, k0, k1, r1);
-          w0 = pack8_sr(t, r0, 1.0f);
-          w1 = pack8_sr(t + 8, r1, 1.0f);
-        } else {
-          w0 = pack8_rtn(t, 1.0f);
-          w1 = pack8_rtn(t + 8, 1.0f);
-        }
-        if (valid) *reinterpret_cast<uint2*>(ccodes + c * half_rows + (tok >> 1)) = make_uint2(w0, w1);
-        scale_word |= sc << (8 * a);
-      }
       // lane < 32 holds blocks 0,2,4,6 of the chunk and lane >= 32 blocks 1,3,5,7;
       // interleave so each lane stores four consecutive scale bytes.
-      auto sw = __builtin_amdgcn_permlane32_swap(scale_word, scale_word, false, false);
-      const uint32_t lo = hk ? sw[0] : scale_word;      // blocks 0,2,4,6
-      const uint32_t hi = hk ? scale_word : sw[1];      // blocks 1,3,5,7
+      auto sw = __builtin_amdgcn_permlane32_swap(scale_word[p], scale_word[p], false, false);
+      const uint32_t lo = hk ? sw[0] : scale_word[p];   // blocks 0,2,4,6
+      const uint32_t hi = hk ? scale_word[p] : sw[1];   // blocks 1,3,5,7
       // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
       const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
       const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
       if (valid) *reinterpret_cast<uint32_t*>(cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
     }
+  };
+  auto fetch = [&](RhtRaw& raw, int64_t tile) {
+    int64_t chunk, slab;
+    it.decode(tile, chunk, slab);
+    const int64_t colp = slab * 64 + 2 * (lane & 31);
+    rht_load(x, cols, chunk * 128, colp, colp < cols, raw);
+  };
+  int64_t tile = wave_id();
+  const int64_t step = wave_count();
+  if (tile >= it.ntiles) return;
+  RhtRaw ra, rb;
+  fetch(ra, tile);
+  while (true) {
+    const int64_t t1 = tile + step;
+    if (t1 < it.ntiles) {
+      fetch(rb, t1);
+      process(ra, tile);
+    } else {
+      process(ra, tile);
+      break;
+    }
+    const int64_t t2 = t1 + step;
+    if (t2 < it.ntiles) {
+      fetch(ra, t2);
+      process(rb, t1);
+    } else {
+      process(rb, t1);
+      break;
+    }
+    tile = t2;
   }
 }
 
@@ -296,9 +377,13 @@ static RhtSigns pack_signs(const uint32_t s[4]) {
   return r;
 }
 
-static int rht_grid(int64_t rows, int64_t cols) {
+// Persistent grid of at most `per_simd` waves per SIMD (256 CUs x 4 SIMDs): the
+// transform-only kernels fit two waves per SIMD, the quantizing kernel, which keeps a
+// second tile in flight, one.
+static int rht_grid(int64_t rows, int64_t cols, int per_simd) {
   const int64_t tiles = ((cols + 63) / 64) * (rows / 128);
-  const int64_t waves = tiles < 2048 ? tiles : 2048;     // about 8 waves per CU, persistent beyond
+  const int64_t cap = (int64_t)1024 * per_simd;
+  const int64_t waves = tiles < cap ? tiles : cap;
   return (int)((waves + 3) / 4);
 }
 
@@ -306,7 +391,7 @@ void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint
                 hipStream_t st) {
   const RhtSigns sg = pack_signs(signs);
   if (dtype == 1) {
-    k_rht_bf16<<<rht_grid(rows, cols), 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols, sg, inverse, y);
+    k_rht_bf16<<<rht_grid(rows, cols, 1), 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols, sg, inverse, y);
   } else {
     const int64_t n = rows / 128 * cols;
     k_rht_f32<<<(int)((n + 255) / 256), 256, 0, st>>>(static_cast<const float*>(x), rows, cols, sg, inverse, y);
@@ -316,7 +401,7 @@ void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint
 void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], float* amax,
                      hipStream_t st) {
   k_zero1_rht<<<1, 1, 0, st>>>(amax);
-  k_rht_amax<<<rht_grid(rows, cols), 256, 0, st>>>(x, rows, cols, pack_signs(signs), amax);
+  k_rht_amax<<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, pack_signs(signs), amax);
 }
 
 void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], bool sr,
@@ -325,10 +410,10 @@ void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const u
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const RhtSigns sg = pack_signs(signs);
   if (sr)
-    k_rht_nvfp4_col<true><<<rht_grid(rows, cols), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
+    k_rht_nvfp4_col<true><<<rht_grid(rows, cols, 1), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
                                                                 col_scales, k0, k1);
   else
-    k_rht_nvfp4_col<false><<<rht_grid(rows, cols), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
+    k_rht_nvfp4_col<false><<<rht_grid(rows, cols, 1), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
                                                                  col_scales, k0, k1);
 }
 

@@ -266,6 +266,26 @@ def test_nvfp4_beyond_one_grid_falls_back_sampled():
         assert np.array_equal(ccg[j0:j0 + 8], c) and np.array_equal(csg[j0:j0 + 8], s)
 
 
+@pytest.mark.parametrize("kind,shape", [("f32", (8193, 4099)), ("bf16", (16385, 4097)), ("bf16", (37, 61)),
+                                        ("f32", (3, 5))])
+def test_amax_entry_point_small_and_wide_with_tails(kind, shape):
+    """fp4q_amax on sizes below and above the wide-kernel threshold (128 MB), with element
+    counts that leave a tail after the 16-byte vectors; the largest magnitude is planted
+    in the tail, in the body, and compared with the oracle's exact amax."""
+    rows, cols = shape
+    rng = np.random.default_rng(rows)
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    x.reshape(-1)[-1] = -37.5          # tail element
+    x.reshape(-1)[rows * cols // 3] = 41.25 if rows * cols > 64 else x.reshape(-1)[0]
+    if kind == "bf16":
+        bits = si.f32_to_bf16_bits(x)
+        xh, xd = bits, dev_bf16(bits)
+    else:
+        xh, xd = x, dev_f32(x)
+    a = B.amax(xd)
+    assert host(a)[0] == np.float32(oracle.amax(xh))
+
+
 # ---------------------------------------------------------------------------------------
 # NVFP4 16x16
 # ---------------------------------------------------------------------------------------
