@@ -379,7 +379,8 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
                    nb - blk0, (nb & 7) == 0);
     }
   }
-  lds_barrier();   // the next tile's staging writes must not overtake these reads
+  // No second barrier: the caller alternates between two staging buffers, and the
+  // next tile's barrier orders these reads before the buffer is written again.
 }
 
 // Tile t of the group-major sequence -> (tile row, tile column).
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile(
     uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
     uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales,
     uint32_t k0, uint32_t k1) {
-  __shared__ TileStage stage;
+  __shared__ TileStage stage[2];   // tile parity alternates the staging buffer
   __shared__ RecipTable rtab;
   fill_recip_table(rtab);
   __syncthreads();
@@ -431,10 +432,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile(
     if (t1 < band1) {
       group_major_tile(t1, tiles_r, tiles_c, trb, tcb);
       nvfp4_tile_load<T>(x, trb * 128, tcb * 128, rows, cols, rb);
-      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage[0], rtab, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
     } else {
-      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage[0], rtab, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
       break;
     }
@@ -442,10 +443,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile(
     if (t2 < band1) {
       group_major_tile(t2, tiles_r, tiles_c, tra, tca);
       nvfp4_tile_load<T>(x, tra * 128, tca * 128, rows, cols, ra);
-      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage[1], rtab, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
     } else {
-      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage[1], rtab, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
       break;
     }
@@ -688,12 +689,12 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
 // Tile K, then K+1, ... with compile-time indices, so the raw tiles stay in registers.
 template <typename T, int TPW, bool ROW, bool COL, bool SR, int K>
 __device__ __forceinline__ void fused_phase2(Raw8x8<T> (&raw)[TPW], const int (&tr)[TPW], const int (&tc)[TPW],
-                                             const bool (&ok)[TPW], int rows, int cols, float gs, TileStage& stage,
+                                             const bool (&ok)[TPW], int rows, int cols, float gs, TileStage (&stage)[2],
                                              const RecipTable& rtab, uint8_t* __restrict__ rcodes,
                                              uint8_t* __restrict__ rscales, uint8_t* __restrict__ ccodes,
                                              uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
   if (ok[K])
-    nvfp4_tile<T, ROW, COL, SR>(raw[K], tr[K] * 128, tc[K] * 128, rows, cols, gs, stage, rtab, rcodes, rscales,
+    nvfp4_tile<T, ROW, COL, SR>(raw[K], tr[K] * 128, tc[K] * 128, rows, cols, gs, stage[K & 1], rtab, rcodes, rscales,
                                 ccodes, cscales, k0, k1);
   if constexpr (K + 1 < TPW)
     fused_phase2<T, TPW, ROW, COL, SR, K + 1>(raw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
@@ -707,7 +708,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_fused(
     float* __restrict__ amax_out, float* __restrict__ tensor_scale,
     uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
     uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
-  __shared__ TileStage stage;
+  __shared__ TileStage stage[2];   // tile parity alternates the staging buffer
   __shared__ RecipTable rtab;
   __shared__ GridMaxShared gsh;
   fill_recip_table(rtab);
