@@ -196,7 +196,9 @@ __device__ __forceinline__ void sr_draws8(uint64_t idx8, uint32_t stream, uint32
 // bits 4k..4k+3).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack8_rtn(const float v[8], float scale) {
-  uint32_t w = 0;
+  // The four converts overwrite all four bytes, so the starting value of the word is
+  // irrelevant; starting from v[0]'s bits (dead after this) saves a register clear.
+  uint32_t w = __float_as_uint(v[0]);
   w = FP4Q_CVT_RTN(w, v[0], v[1], scale, 0);
   w = FP4Q_CVT_RTN(w, v[2], v[3], scale, 1);
   w = FP4Q_CVT_RTN(w, v[4], v[5], scale, 2);
@@ -220,16 +222,18 @@ __device__ __forceinline__ uint32_t pack8_sr(const float v[8], const uint32_t r3
 // ---------------------------------------------------------------------------
 // Cross-lane helpers (wave64).
 // ---------------------------------------------------------------------------
+// Maximum with the partner lane (lane ^ 1 or lane ^ 2 within each quad, by DPP) of a
+// value that is >= 0: non-negative floats order like their bit patterns, so the
+// comparison is an integer max (a float max would first canonicalize the moved value).
 template <int XOR>
 __device__ __forceinline__ float lane_xor_max(float v) {
-  // quad_perm DPP for xor 1 / xor 2 within groups of four lanes
-  int iv = __float_as_int(v);
+  const int iv = __float_as_int(v);
   int other;
   if constexpr (XOR == 1)
     other = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
   else
     other = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
-  return __builtin_fmaxf(v, __int_as_float(other));
+  return __uint_as_float(max((uint32_t)iv, (uint32_t)other));
 }
 
 // Workgroup barrier that orders LDS traffic only: unlike __syncthreads() it does not

@@ -294,7 +294,7 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
       }
       const int r = lrow0 + i;
       st.rc[rc_dword(r, 2 * qc + h)] = w;
-      if (h == 0) st.rs[r * 8 + qc] = (uint8_t)code;
+      st.rs[r * 8 + qc] = (uint8_t)code;   // both lanes of the block write the same byte
     }
   }
   if constexpr (COL) {
@@ -320,7 +320,7 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
       }
       const int c = lcol0 + j;
       st.cc[cc_dword(c, wave, 2 * qr + vv)] = w;
-      if (vv == 0) st.cs[c * 8 + 2 * wave + qr] = (uint8_t)code;
+      st.cs[c * 8 + 2 * wave + qr] = (uint8_t)code;   // both lanes of the block write the same byte
     }
   }
   lds_barrier();
@@ -1018,10 +1018,11 @@ void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const floa
 __device__ __forceinline__ float max16_lanes(float v) {
   v = lane_xor_max<1>(v);
   v = lane_xor_max<2>(v);
-  // rotate within rows of 16 lanes by 4 and 8
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));
-  return v;
+  // rotate within rows of 16 lanes by 4 and 8 (v >= 0: integer max on the bits)
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x124, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, false));
+  return __uint_as_float(u);
 }
 
 template <typename T, bool TRANS>
