@@ -325,6 +325,35 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
   }
   lds_barrier();
   const int tid = threadIdx.x;
+  // Interior tile of a 128-aligned matrix (uniform test): every store is whole and
+  // aligned, so none needs a per-lane bounds check.
+  if (((rows | cols) & 127) == 0 && trow0 + 128 <= rows && tcol0 + 128 <= cols) {
+    if constexpr (ROW) {
+      const int half_cols = cols >> 1, nb = cols >> 4;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ch = tid + 256 * k, r = rc_chunk_row(ch), c4 = ch & 3;
+        *reinterpret_cast<uint4*>(rcodes + (int64_t)(trow0 + r) * half_cols + ((tcol0 + c4 * 32) >> 1)) =
+            *reinterpret_cast<const uint4*>(&st.rc[ch * 4]);
+      }
+      if (tid < 128)
+        *reinterpret_cast<uint2*>(rscales + (int64_t)(trow0 + tid) * nb + (tcol0 >> 4)) =
+            *reinterpret_cast<const uint2*>(&st.rs[tid * 8]);
+    }
+    if constexpr (COL) {
+      const int half_rows = rows >> 1, nb = rows >> 4;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ch = tid + 256 * k, cw = cc_chunk_unswizzle(ch), c = cw >> 2, w = cw & 3;
+        *reinterpret_cast<uint4*>(ccodes + (int64_t)(tcol0 + c) * half_rows + ((trow0 + 32 * w) >> 1)) =
+            *reinterpret_cast<const uint4*>(&st.cc[ch * 4]);
+      }
+      if (tid < 128)
+        *reinterpret_cast<uint2*>(cscales + (int64_t)(tcol0 + tid) * nb + (trow0 >> 4)) =
+            *reinterpret_cast<const uint2*>(&st.cs[tid * 8]);
+    }
+    return;
+  }
   if constexpr (ROW) {
     const int half_cols = cols >> 1, nb = cols >> 4;
 #pragma unroll
