@@ -209,6 +209,91 @@ template <> struct Raw8x8<float> {
   }
 };
 
+// Maxima of |x| over the lane's 16-element blocks, found from the raw words before
+// the tensor scale is known (the one-pass kernel does this while it waits for the
+// other workgroups): for row i (i = 0..7) of the lane's micro-tile the row block
+// (16 columns, this lane and lane ^ 2), for column j the column block (16 rows, this
+// lane and lane ^ 1).  Then max|fl(x*gs)| over a block = fl(bamax*gs), since the
+// product rounds monotonically.  bf16 keeps the magnitude bits two per word.
+template <typename T> struct BlockMax;
+template <> struct BlockMax<uint16_t> {
+  uint32_t row[4], col[4];   // row[k]: rows 2k (low half), 2k+1; col[k]: columns 2k, 2k+1
+  __device__ __forceinline__ void compute(const Raw8x8<uint16_t>& raw) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[i][k] = __builtin_bit_cast(u16x2, raw.word(i, k) & 0x7FFF7FFFu);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t r[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * k + e;
+        const u16x2 a = __builtin_elementwise_max(__builtin_elementwise_max(m[i][0], m[i][1]),
+                                                  __builtin_elementwise_max(m[i][2], m[i][3]));
+        r[e] = a.x > a.y ? a.x : a.y;
+      }
+      const uint32_t w = r[0] | (r[1] << 16);
+      const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+      row[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, w),
+                                                                       __builtin_bit_cast(u16x2, o)));
+      u16x2 c = m[0][k];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) c = __builtin_elementwise_max(c, m[i][k]);
+      const uint32_t cw = __builtin_bit_cast(uint32_t, c);
+      const uint32_t co = (uint32_t)__builtin_amdgcn_mov_dpp((int)cw, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+      col[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(c, __builtin_bit_cast(u16x2, co)));
+    }
+  }
+  __device__ __forceinline__ float rowmax(int i) const {
+    return __uint_as_float((i & 1) ? (row[i >> 1] & 0xFFFF0000u) : (row[i >> 1] << 16));
+  }
+  __device__ __forceinline__ float colmax(int j) const {
+    return __uint_as_float((j & 1) ? (col[j >> 1] & 0xFFFF0000u) : (col[j >> 1] << 16));
+  }
+  // maximum over every element of the micro-tile (any block covers its rows)
+  __device__ __forceinline__ float lanemax() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, max(row[k] << 16, row[k] & 0xFFFF0000u));
+    return __uint_as_float(m);
+  }
+};
+template <> struct BlockMax<float> {
+  uint32_t row[8], col[8];   // magnitude bits
+  __device__ __forceinline__ void compute(const Raw8x8<float>& raw) {
+    uint32_t m[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[i][j] = __float_as_uint(raw.at(i, j, 1.0f)) & 0x7FFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a = max(a, m[i][j]);
+      row[i] = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t a = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = max(a, m[i][j]);
+      col[j] = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false));
+    }
+  }
+  __device__ __forceinline__ float rowmax(int i) const { return __uint_as_float(row[i]); }
+  __device__ __forceinline__ float colmax(int j) const { return __uint_as_float(col[j]); }
+  __device__ __forceinline__ float lanemax() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, row[i]);
+    return __uint_as_float(m);
+  }
+};
+
 // Staging of one 128 x 128 tile's outputs.  Chunk positions are XOR swizzled so that
 // the 4-byte writes and the 16-byte reads avoid LDS bank conflicts (64 x 4 bytes).
 struct TileStage {
@@ -253,9 +338,9 @@ __device__ __forceinline__ void nvfp4_tile_load(const T* __restrict__ x, int tro
   raw.load(x, row0, col0, rows, cols);
 }
 
-template <typename T, bool ROW, bool COL, bool SR>
+template <typename T, bool ROW, bool COL, bool SR, bool PRE = false>
 __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0, int rows, int cols, float gs,
-                                           TileStage& st, const RecipTable& rtab,
+                                           TileStage& st, const RecipTable& rtab, const BlockMax<T>* bm,
                                            uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
                                            uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales, uint32_t k0,
                                            uint32_t k1) {
@@ -276,9 +361,13 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float m = 0.0f;
+      if constexpr (PRE) {
+        m = bm->rowmax(i) * gs;
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
-      m = lane_xor_max<2>(m);
+        for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
+        m = lane_xor_max<2>(m);
+      }
       const uint32_t code = nvfp4_scale_code(m);
       const RecipPair rp = rtab.r[code];
       float v[8];
@@ -302,9 +391,13 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float m = 0.0f;
+      if constexpr (PRE) {
+        m = bm->colmax(j) * gs;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
-      m = lane_xor_max<1>(m);
+        for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(t[i][j]));
+        m = lane_xor_max<1>(m);
+      }
       const uint32_t code = nvfp4_scale_code(m);
       const RecipPair rp = rtab.r[code];
       float v[8];
@@ -461,10 +554,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile(
     if (t1 < band1) {
       group_major_tile(t1, tiles_r, tiles_c, trb, tcb);
       nvfp4_tile_load<T>(x, trb * 128, tcb * 128, rows, cols, rb);
-      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage[0], rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage[0], rtab, nullptr, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
     } else {
-      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage[0], rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(ra, tra * 128, tca * 128, rows, cols, gs, stage[0], rtab, nullptr, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
       break;
     }
@@ -472,10 +565,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile(
     if (t2 < band1) {
       group_major_tile(t2, tiles_r, tiles_c, tra, tca);
       nvfp4_tile_load<T>(x, tra * 128, tca * 128, rows, cols, ra);
-      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage[1], rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage[1], rtab, nullptr, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
     } else {
-      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage[1], rtab, rcodes, rscales, ccodes,
+      nvfp4_tile<T, ROW, COL, SR>(rb, trb * 128, tcb * 128, rows, cols, gs, stage[1], rtab, nullptr, rcodes, rscales, ccodes,
                                   cscales, k0, k1);
       break;
     }
@@ -716,17 +809,27 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
 }
 
 // Tile K, then K+1, ... with compile-time indices, so the raw tiles stay in registers.
+template <typename T> constexpr int kBlockMaxWords = sizeof(BlockMax<T>) / 4;
+
 template <typename T, int TPW, bool ROW, bool COL, bool SR, int K>
-__device__ __forceinline__ void fused_phase2(Raw8x8<T> (&raw)[TPW], const int (&tr)[TPW], const int (&tc)[TPW],
+__device__ __forceinline__ void fused_phase2(Raw8x8<T> (&raw)[TPW],
+                                             const uint32_t (&bmw)[TPW][kBlockMaxWords<T>][256],
+                                             const int (&tr)[TPW], const int (&tc)[TPW],
                                              const bool (&ok)[TPW], int rows, int cols, float gs, TileStage (&stage)[2],
                                              const RecipTable& rtab, uint8_t* __restrict__ rcodes,
                                              uint8_t* __restrict__ rscales, uint8_t* __restrict__ ccodes,
                                              uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
-  if (ok[K])
-    nvfp4_tile<T, ROW, COL, SR>(raw[K], tr[K] * 128, tc[K] * 128, rows, cols, gs, stage[K & 1], rtab, rcodes, rscales,
+  if (ok[K]) {
+    BlockMax<T> bm;
+    uint32_t* w = reinterpret_cast<uint32_t*>(&bm);
+#pragma unroll
+    for (int e = 0; e < kBlockMaxWords<T>; ++e) w[e] = bmw[K][e][threadIdx.x];
+    nvfp4_tile<T, ROW, COL, SR, true>(raw[K], tr[K] * 128, tc[K] * 128, rows, cols, gs, stage[K & 1], rtab, &bm,
+                                      rcodes, rscales,
                                 ccodes, cscales, k0, k1);
+  }
   if constexpr (K + 1 < TPW)
-    fused_phase2<T, TPW, ROW, COL, SR, K + 1>(raw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+    fused_phase2<T, TPW, ROW, COL, SR, K + 1>(raw, bmw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
                                               cscales, k0, k1);
 }
 
@@ -763,9 +866,19 @@ __global__ __launch_bounds__(256) void k_nvfp4_fused(
     group_major_tile(ok[k] ? t : last, tiles_r, tiles_c, tr[k], tc[k]);
     nvfp4_tile_load<T>(x, tr[k] * 128, tc[k] * 128, rows, cols, raw[k]);
   }
+  // The block maxima do not depend on the tensor scale: find them now, while the
+  // loads and the exchange leave the ALUs idle, and park them in LDS for phase 2.
+  __shared__ uint32_t bmw[TPW][kBlockMaxWords<T>][256];
   float m = 0.0f;
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) m = __builtin_fmaxf(m, raw_absmax(raw[k]));
+  for (int k = 0; k < TPW; ++k) {
+    BlockMax<T> bm;
+    bm.compute(raw[k]);
+    m = __builtin_fmaxf(m, bm.lanemax());
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&bm);
+#pragma unroll
+    for (int e = 0; e < kBlockMaxWords<T>; ++e) bmw[k][e][threadIdx.x] = w[e];
+  }
   m = block_max256(m, gsh.red);
   const float g = grid_max<T>(ws, m, epoch, wait_iters, x, rows, cols, tiles_r, tiles_c, gsh);
   const float gs = tensor_scale_from_amax(g);
@@ -775,7 +888,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_fused(
   }
 
   // phase 2: quantize from registers
-  fused_phase2<T, TPW, ROW, COL, SR, 0>(raw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
+  fused_phase2<T, TPW, ROW, COL, SR, 0>(raw, bmw, tr, tc, ok, rows, cols, gs, stage, rtab, rcodes, rscales, ccodes,
                                         cscales, k0, k1);
 }
 
