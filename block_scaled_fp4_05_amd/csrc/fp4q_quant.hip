@@ -647,13 +647,12 @@ void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned
 // is ever reset.  The host numbers launches per stream (epoch 1, 2, ...), so slots
 // left by earlier launches never match.
 //
-// Workgroups form 8 groups, g = b % 8, and workgroup g leads group g.  Under the
-// default dispatch, workgroup b runs on XCD b % 8, so a group shares one L2: members
-// post their slots with workgroup-scope stores, which stop in that L2, and poll the
-// group's result there; only the 8 leaders exchange words through memory.  Placement
-// is a matter of speed only: a reader that cannot see a value in time computes it.
+// Workgroups form 8 groups, g = b % 8, and workgroup g leads group g: members post
+// their slots, the leader combines them and posts the group maximum, and every
+// workgroup reads the eight group maxima.  All of it is device-scope traffic, so no
+// step relies on where a workgroup runs.
 struct FusedWs {
-  uint64_t local[8][kFusedMaxWg / 8 + 16];   // per group: members' slots, then the result
+  uint64_t local[8][kFusedMaxWg / 8 + 16];   // per group: members' slots
   uint64_t group[8][16];                      // per group: its maximum, device scope
   uint32_t fallbacks[32];                     // waits that ran out and were answered from x
 };
@@ -694,8 +693,7 @@ __device__ __forceinline__ uint64_t pack_epoch(uint32_t epoch, float v) {
   return ((uint64_t)epoch << 32) | __float_as_uint(v);
 }
 
-// Device-scope loads skip the CU's L1; a value a workgroup of the same XCD stored with
-// a workgroup-scope store is seen in the shared L2.
+// Device-scope (single-location coherent) load of a slot.
 __device__ __forceinline__ uint64_t load_dev(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -737,14 +735,14 @@ struct GridMaxShared {
 
 // Grid-wide maximum of the workgroups' values v (thread 0's copy), returned to every
 // thread.  Members post their slot in the group area; leader g collects the group's
-// slots, posts the group maximum at device scope, collects the eight group maxima and
-// posts the result in the group area, where the members poll it.
+// slots and posts the group maximum at device scope; every workgroup then reads the
+// eight group maxima itself (eight lines, polled by eight lanes).
 //
 // No wait depends on other workgroups making progress for correctness: a slot that
 // has not arrived after `wait_iters` polls is computed from x by the waiting
-// workgroup itself (one workgroup's tiles, a group's band, or a member's whole
-// tensor).  With the whole grid resident, which the launch size is chosen for, the
-// fallback never runs; without it, the grid still finishes with the exact maximum.
+// workgroup itself (one workgroup's tiles, or a group's band).  With the whole grid
+// resident, which the launch size is chosen for, the fallback never runs; without
+// it, the grid still finishes with the exact maximum.
 template <typename T>
 __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, uint32_t wait_iters,
                                           const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
@@ -753,10 +751,9 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
   const int tid = threadIdx.x;
   const int total = tiles_r * tiles_c, per = (total + 7) >> 3;
   uint64_t* local = ws->local[g];
-  uint64_t* result = local + kFusedMaxWg / 8;
   if (tid < 8) sh.miss[tid] = 0u;
-  if (tid == 0 && b >= 8)   // one 64-bit store through this CU's L1 into the L2
-    __hip_atomic_store(&local[b >> 3], pack_epoch(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (tid == 0 && b >= 8)
+    __hip_atomic_store(&local[b >> 3], pack_epoch(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (b < 8) {                                        // leader of group g == b
     float m = v;
@@ -778,34 +775,21 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
       __hip_atomic_store(&ws->group[g][0], pack_epoch(epoch, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid < 8) sh.miss[tid] = 0u;
     __syncthreads();
-    float t = 0.0f;
-    if (tid < 8) {
-      float u;
-      if (poll_slot(&ws->group[tid][0], epoch, wait_iters, &u)) t = u;
-      else atomicOr(&sh.miss[0], 1u << tid);
-    }
-    __syncthreads();
-    for (int k = 0; k < 8; ++k)
-      if (sh.miss[0] & (1u << k)) {
-        t = __builtin_fmaxf(t, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, k * per, 1,
-                                               min(total, (k + 1) * per), sh.red));
-        if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    t = block_max256(t, sh.red);
-    if (tid == 0) __hip_atomic_store(result, pack_epoch(epoch, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return t;
   }
-  if (tid == 0) {
+  float t = 0.0f;
+  if (tid < 8) {
     float u;
-    if (poll_slot(result, epoch, wait_iters, &u)) sh.val = u;
-    else sh.miss[0] = 1u;
+    if (poll_slot(&ws->group[tid][0], epoch, wait_iters, &u)) t = u;
+    else atomicOr(&sh.miss[0], 1u << tid);
   }
   __syncthreads();
-  if (sh.miss[0]) {
-    if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, 0, 1, total, sh.red);
-  }
-  return sh.val;
+  for (int k = 0; k < 8; ++k)
+    if (sh.miss[0] & (1u << k)) {
+      t = __builtin_fmaxf(t, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, k * per, 1, min(total, (k + 1) * per),
+                                             sh.red));
+      if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  return block_max256(t, sh.red);
 }
 
 // Tile K, then K+1, ... with compile-time indices, so the raw tiles stay in registers.
