@@ -80,6 +80,17 @@ __device__ __forceinline__ RecipPair recip_pair(float s) {
   return RecipPair{zh, e * zh};
 }
 
+// Division by an arbitrary FP32 divisor y given rs = fl(1/y): q0 = fl(t*rs) is
+// corrected once with the exact residual t - q0*y (Markstein).  Correct rounding is
+// not guaranteed for every dividend, only for the dividend significands a caller has
+// shown to be safe; the residual is written as -(q0*y - t) so zero dividends keep
+// their sign.
+__device__ __forceinline__ float div_rs(float t, float y, float rs) {
+  const float q0 = t * rs;
+  const float res = -__builtin_fmaf(q0, y, -t);
+  return __builtin_fmaf(res, rs, q0);
+}
+
 // The pair for dividing by 6: zh = 0x3E2AAAAA (1/6 rounded down), 1 - 6*zh = 2^-24,
 // zl = 2^-24 * zh.
 __device__ __forceinline__ RecipPair recip6() {

@@ -1,0 +1,110 @@
+/* Host check of the division the dequantization kernel uses instead of IEEE
+ * division by the FP32 tensor scale.
+ *
+ *  t   = fl(r * s)       r: decoded element (E2M1 value, or q * fl(6/7) for an INT4
+ *                         block, q in -8..7), s: decoded E4M3 block scale
+ *  out = fl(t / gs)      wanted, correctly rounded
+ *  div_rs(t, gs, rg) = fma(-fma(q0, gs, -t), rg, q0),  q0 = fl(t * rg),  rg = fl(1 / gs)
+ *
+ * The kernel takes div_rs only when ratio = fl(s * rg) lies in [2^-98, 2^96], and
+ * IEEE division otherwise. Claims checked (exit status 0 only if all hold):
+ *  1. Over all element codes and all E4M3 scale codes, the nonzero dividends t have
+ *     few distinct significands; div_rs is correctly rounded for each of them against
+ *     every one of the 2^23 divisor significands, in both quotient binades.
+ *  2. Random spot checks across the exponent range the ratio predicate admits
+ *     (real codes, random gs), both signs, reproduce IEEE division bit for bit.
+ *  3. Zero dividends of either sign keep their sign.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+static float div_rs(float t, float s, float rs)
+{
+    float q0 = t * rs;
+    float res = -fmaf(q0, s, -t);
+    return fmaf(res, rs, q0);
+}
+
+static float e4m3(int code)
+{
+    int e = (code >> 3) & 15, m = code & 7;
+    return e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+}
+
+/* element value of a 4-bit code: E2M1 (fmt 0) or INT4 times fl(6/7) (fmt 1) */
+static float element(int fmt, int nib)
+{
+    static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    if (fmt == 0) return (nib & 8) ? -mag[nib & 7] : mag[nib & 7];
+    const float c67 = 6.0f / 7.0f;
+    return (float)(((nib ^ 8) - 8)) * c67;
+}
+
+static int same(float a, float b) { return memcmp(&a, &b, 4) == 0; }
+
+int main(void)
+{
+    float sig[512];
+    int nsig = 0;
+    for (int fmt = 0; fmt < 2; ++fmt)
+        for (int nib = 0; nib < 16; ++nib)
+            for (int code = 1; code <= 0x7E; ++code) {
+                float t = fabsf(element(fmt, nib) * e4m3(code));
+                if (t == 0.0f) continue;
+                int e;
+                float m = 2.0f * frexpf(t, &e); /* [1, 2) */
+                int dup = 0;
+                for (int k = 0; k < nsig && !dup; ++k) dup = sig[k] == m;
+                if (!dup) sig[nsig++] = m;
+            }
+
+    long checked = 0, bad = 0;
+    for (uint32_t mant = 0; mant < (1u << 23); ++mant) {
+        uint32_t bits = 0x3F800000u | mant;
+        float y;
+        memcpy(&y, &bits, 4);
+        float ry = 1.0f / y;
+        for (int k = 0; k < nsig; ++k) {
+            float t = sig[k], t2 = 2.0f * sig[k];
+            if (!same(div_rs(t, y, ry), t / y)) ++bad;
+            if (!same(div_rs(t2, y, ry), t2 / y)) ++bad;
+            checked += 2;
+        }
+    }
+
+    /* 2: spot checks over the admitted exponent range */
+    long spot = 0, spot_bad = 0;
+    uint32_t lcg = 2463534242u;
+    for (int k = 0; k < 6000000; ++k) {
+        lcg = lcg * 1664525u + 1013904223u;
+        uint32_t mant = lcg >> 9;
+        lcg = lcg * 1664525u + 1013904223u;
+        int ex = (int)(lcg % 230u) - 115;
+        int code = 1 + (int)((lcg >> 8) % 126u);
+        int nib = (int)((lcg >> 16) & 15u), fmt = (int)((lcg >> 20) & 1u);
+        uint32_t bits = 0x3F800000u | mant;
+        float gs;
+        memcpy(&gs, &bits, 4);
+        gs = ldexpf(gs, ex);
+        if (lcg & 0x80000000u) gs = -gs; /* negative scales must take the slow path */
+        float s = e4m3(code), rg = 1.0f / gs, ratio = s * rg;
+        if (!(ratio >= 0x1p-98f && ratio <= 0x1p+96f)) continue;
+        float t = element(fmt, nib) * s;
+        if (!same(div_rs(t, gs, rg), t / gs)) ++spot_bad;
+        ++spot;
+    }
+
+    /* 3: signed zeros */
+    int zero_bad = 0;
+    for (int code = 1; code <= 0x7E; ++code) {
+        float gs = e4m3(code) * 3.7f, rg = 1.0f / gs;
+        float a = div_rs(-0.0f, gs, rg), b = div_rs(0.0f, gs, rg);
+        if (!(a == 0.0f && signbit(a) && b == 0.0f && !signbit(b))) ++zero_bad;
+    }
+
+    printf("%d dividend significands; exhaustive checked %ld, mismatches %ld; spot checked %ld, "
+           "mismatches %ld; signed-zero failures %d\n", nsig, checked, bad, spot, spot_bad, zero_bad);
+    return (bad == 0 && spot_bad == 0 && zero_bad == 0 && spot > 1000000) ? 0 : 1;
+}
