@@ -1224,7 +1224,9 @@ void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const
 
 // ===========================================================================
 // Dequantize: x_hat = fl(fl(r*s)/gs) (NVFP4, 2D, IF4) or r*2^(code-127) (MXFP4).
-// One lane per 16 output elements.
+// The lanes of a wave write consecutive 16-byte chunks, so each store instruction
+// covers one contiguous span of 1 KiB; a lane handles 16 elements of a 1024-element
+// wave span, in four steps of four fp32 outputs or two steps of eight bf16 outputs.
 // ===========================================================================
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -1236,82 +1238,95 @@ template <int FMT, bool BF16OUT>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                                  const float* __restrict__ tensor_scale, int64_t rows, int64_t cols,
                                                  void* __restrict__ y) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-element group
-  const int64_t n16 = rows * cols / 16;
-  if (g >= n16) return;
-  const uint2 w = *reinterpret_cast<const uint2*>(codes + g * 8);
-  float out[16];
-  if constexpr (FMT == 2) {
-    const uint32_t code = scales[g >> 1];
-    const float scale = __uint_as_float(code << 23);
-    decode8_fp4(w.x, scale, out);
-    decode8_fp4(w.y, scale, out + 8);
-  } else {
-    const float gs = *tensor_scale;
-    const float rgs = __fdiv_rn(1.0f, gs);
-    uint32_t sc;
-    if constexpr (FMT == 1) {
-      const int64_t e = g * 16, r = e / cols, c = e - r * cols;
-      sc = scales[(r >> 4) * (cols >> 4) + (c >> 4)];
-    } else {
-      sc = scales[g];
-    }
-    const float s = e4m3_decode(sc & 0x7Fu);
-    float rv[16];
-    if (FMT == 3 && (sc & 0x80u)) {
-      const float c67 = 6.0f / 7.0f;
+  constexpr int EPL = BF16OUT ? 8 : 4;          // elements per lane and step
+  constexpr int STEPS = 16 / EPL;
+  const int lane = threadIdx.x & 63;
+  const int64_t n = rows * cols;                // a multiple of 16
+  const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 1024 + lane * EPL;
+  if (e0 >= n) return;
+
+  // loads first, from clamped addresses, so all of them are in flight together
+  uint32_t cw[STEPS], sc[STEPS];
+  int64_t r = 0, c = 0;
+  if constexpr (FMT == 1) { r = e0 / cols; c = e0 - r * cols; }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t word = k < 8 ? w.x : w.y;
-        const int nib = (int)((word >> (4 * (k & 7))) & 0xFu);
-        const int qv = (nib ^ 8) - 8;
-        rv[k] = (float)qv * c67;
-      }
+  for (int j = 0; j < STEPS; ++j) {
+    const int64_t e = min(e0 + (int64_t)j * 64 * EPL, n - EPL);
+    if constexpr (EPL == 4) cw[j] = *reinterpret_cast<const uint16_t*>(codes + (e >> 1));
+    else cw[j] = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
+    if constexpr (FMT == 2) {
+      sc[j] = scales[e >> 5];
+    } else if constexpr (FMT == 1) {
+      const int64_t rr = min(r, rows - 1);
+      sc[j] = scales[(rr >> 4) * (cols >> 4) + (c >> 4)];
+      c += 64 * EPL;
+      while (c >= cols) { c -= cols; ++r; }
     } else {
-      decode8_fp4(w.x, 1.0f, rv);
-      decode8_fp4(w.y, 1.0f, rv + 8);
-    }
-    // fl(t/gs) for t = fl(r*s): over all element and scale codes t has only 29
-    // significands, and for each of them the corrected-reciprocal division is
-    // correctly rounded against every divisor significand (checked exhaustively on
-    // the host).  That carries over to every exponent while no intermediate leaves
-    // the normal range, which s/gs in [2^-98, 2^96] (with |r| in [0.5, 48/7])
-    // guarantees; other blocks, and non-finite or negative scales, divide exactly.
-    const float ratio = s * rgs;
-    if (ratio >= 0x1p-98f && ratio <= 0x1p+96f) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) out[k] = div_rs(rv[k] * s, gs, rgs);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) out[k] = __fdiv_rn(rv[k] * s, gs);
+      sc[j] = scales[e >> 4];
     }
   }
-  if constexpr (BF16OUT) {
-    uint4 o0, o1;
-    o0.x = f32_to_bf16_rne(out[0]) | (f32_to_bf16_rne(out[1]) << 16);
-    o0.y = f32_to_bf16_rne(out[2]) | (f32_to_bf16_rne(out[3]) << 16);
-    o0.z = f32_to_bf16_rne(out[4]) | (f32_to_bf16_rne(out[5]) << 16);
-    o0.w = f32_to_bf16_rne(out[6]) | (f32_to_bf16_rne(out[7]) << 16);
-    o1.x = f32_to_bf16_rne(out[8]) | (f32_to_bf16_rne(out[9]) << 16);
-    o1.y = f32_to_bf16_rne(out[10]) | (f32_to_bf16_rne(out[11]) << 16);
-    o1.z = f32_to_bf16_rne(out[12]) | (f32_to_bf16_rne(out[13]) << 16);
-    o1.w = f32_to_bf16_rne(out[14]) | (f32_to_bf16_rne(out[15]) << 16);
-    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
-    p[0] = o0;
-    p[1] = o1;
-  } else {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + g * 16);
-    p[0] = make_float4(out[0], out[1], out[2], out[3]);
-    p[1] = make_float4(out[4], out[5], out[6], out[7]);
-    p[2] = make_float4(out[8], out[9], out[10], out[11]);
-    p[3] = make_float4(out[12], out[13], out[14], out[15]);
+  float gs = 1.0f, rgs = 1.0f;
+  if constexpr (FMT != 2) { gs = *tensor_scale; rgs = __fdiv_rn(1.0f, gs); }
+
+#pragma unroll
+  for (int j = 0; j < STEPS; ++j) {
+    const int64_t e = e0 + (int64_t)j * 64 * EPL;
+    if (e >= n) break;
+    float rv[EPL], out[EPL];
+    if (FMT == 3 && (sc[j] & 0x80u)) {
+      const float c67 = 6.0f / 7.0f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) rv[k] = (float)((int)(((cw[j] >> (4 * k)) & 0xFu) ^ 8u) - 8) * c67;
+    } else {
+      f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 0);
+      rv[0] = d[0]; rv[1] = d[1];
+      d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 1);
+      rv[2] = d[0]; rv[3] = d[1];
+      if constexpr (EPL == 8) {
+        d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 2);
+        rv[4] = d[0]; rv[5] = d[1];
+        d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 3);
+        rv[6] = d[0]; rv[7] = d[1];
+      }
+    }
+    if constexpr (FMT == 2) {
+      // E8M0: exact power-of-two scaling, subnormal and overflowing results included
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) out[k] = __builtin_ldexpf(rv[k], (int)sc[j] - 127);
+    } else {
+      // fl(t/gs) for t = fl(r*s): over all element and scale codes t has only 29
+      // significands, and for each of them the corrected-reciprocal division is
+      // correctly rounded against every divisor significand (checked exhaustively on
+      // the host).  That carries over to every exponent while no intermediate leaves
+      // the normal range, which s/gs in [2^-98, 2^96] (with |r| in [0.5, 48/7])
+      // guarantees; other blocks, and non-finite or negative scales, divide exactly.
+      const float s = e4m3_decode(sc[j] & 0x7Fu);
+      const float ratio = s * rgs;
+      if (ratio >= 0x1p-98f && ratio <= 0x1p+96f) {
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) out[k] = div_rs(rv[k] * s, gs, rgs);
+      } else {
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) out[k] = __fdiv_rn(rv[k] * s, gs);
+      }
+    }
+    if constexpr (BF16OUT) {
+      uint4 o;
+      o.x = f32_to_bf16_rne(out[0]) | (f32_to_bf16_rne(out[1]) << 16);
+      o.y = f32_to_bf16_rne(out[2]) | (f32_to_bf16_rne(out[3]) << 16);
+      o.z = f32_to_bf16_rne(out[4]) | (f32_to_bf16_rne(out[5]) << 16);
+      o.w = f32_to_bf16_rne(out[6]) | (f32_to_bf16_rne(out[7]) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + e) = o;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(y) + e) = make_float4(out[0], out[1], out[2], out[3]);
+    }
   }
 }
 
 void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t rows,
                     int64_t cols, int out_dtype, void* y, hipStream_t st) {
-  const int64_t n16 = rows * cols / 16;
-  const int grid = (int)((n16 + 255) / 256);
+  const int64_t n = rows * cols;
+  const int grid = (int)((n + 4095) / 4096);
 #define FP4Q_DQ(F) \
   if (out_dtype == 1) k_dequant<F, true><<<grid, 256, 0, st>>>(codes, scales, tensor_scale, rows, cols, y); \
   else k_dequant<F, false><<<grid, 256, 0, st>>>(codes, scales, tensor_scale, rows, cols, y)

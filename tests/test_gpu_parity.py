@@ -424,25 +424,39 @@ def test_dequantize_zero_ulp(fmt, out_dtype):
         assert np.array_equal(yb, si.f32_to_bf16_bits(ref))
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("gs", [1.0, 3.7e-3, 0.6180339, 7.1e25, 2.3e-28, -2.5, 1.0e-40])
-@pytest.mark.parametrize("fmt", ["nvfp4", "if4"])
-def test_dequantize_arbitrary_codes_and_tensor_scales(fmt, gs):
+@pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4_2d", "mxfp4", "if4"])
+def test_dequantize_arbitrary_codes_and_tensor_scales(fmt, gs, out_dtype):
     """Every code byte, every finite E4M3 scale code (with and without the INT4 flag for
-    IF4) and tensor scales that send blocks down both division paths: in range, so
-    large or small that quotients leave the normal range, negative, subnormal."""
-    rows, cols = 64, 512
+    IF4), every E8M0 code for MXFP4 (2^-127 and overflow included), and tensor scales
+    that send blocks down both division paths: in range, so large or small that
+    quotients leave the normal range, negative, subnormal.  Shapes include element
+    counts that end inside a wave's span."""
+    f = {"nvfp4": B.FMT_NVFP4, "nvfp4_2d": B.FMT_NVFP4_2D, "mxfp4": B.FMT_MXFP4, "if4": B.FMT_IF4}[fmt]
+    shapes = {"nvfp4_2d": [(64, 512), (16, 272), (48, 80)],
+              "mxfp4": [(64, 512), (16, 288), (3, 96)]}.get(fmt, [(64, 512), (16, 272), (3, 96)])
     rng = np.random.default_rng(97)
-    codes = rng.integers(0, 256, size=rows * cols // 2, dtype=np.uint8)
-    scales = rng.integers(0, 0x7F, size=rows * cols // 16, dtype=np.uint8)   # 0x7F is NaN
-    if fmt == "if4":
-        scales |= (rng.integers(0, 2, size=scales.size, dtype=np.uint8) << 7).astype(np.uint8)
-    f = B.FMT_NVFP4 if fmt == "nvfp4" else B.FMT_IF4
     gs32 = np.float32(gs)
-    ts = torch.tensor([gs32], dtype=torch.float32, device="cuda")
-    ref = oracle.dequantize(f, codes, scales, float(gs32), rows, cols)
-    y = host(B.dequantize(f, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), ts,
-                          rows, cols))
-    assert np.array_equal(f32_bits(y), f32_bits(ref))
+    for rows, cols in shapes:
+        codes = rng.integers(0, 256, size=rows * cols // 2, dtype=np.uint8)
+        if fmt == "mxfp4":
+            scales = rng.integers(0, 256, size=rows * cols // 32, dtype=np.uint8)
+        elif fmt == "nvfp4_2d":
+            scales = rng.integers(0, 0x7F, size=rows * cols // 256, dtype=np.uint8)  # 0x7F is NaN
+        else:
+            scales = rng.integers(0, 0x7F, size=rows * cols // 16, dtype=np.uint8)
+        if fmt == "if4":
+            scales |= (rng.integers(0, 2, size=scales.size, dtype=np.uint8) << 7).astype(np.uint8)
+        ts = None if fmt == "mxfp4" else torch.tensor([gs32], dtype=torch.float32, device="cuda")
+        ref = oracle.dequantize(f, codes, scales, float(gs32) if ts is not None else 1.0, rows, cols)
+        args = (f, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), ts, rows, cols)
+        if out_dtype == torch.float32:
+            y = host(B.dequantize(*args))
+            assert np.array_equal(f32_bits(y), f32_bits(ref)), (rows, cols)
+        else:
+            yb = host(B.dequantize(*args, out_dtype=torch.bfloat16).view(torch.int16)).view(np.uint16)
+            assert np.array_equal(yb, si.f32_to_bf16_bits(ref)), (rows, cols)
 
 
 # ---------------------------------------------------------------------------------------
