@@ -648,12 +648,15 @@ void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned
 // left by earlier launches never match.
 //
 // Workgroups form 8 groups, g = b % 8, and workgroup g leads group g: members post
-// their slots, the leader combines them and posts the group maximum, and every
-// workgroup reads the eight group maxima.  All of it is device-scope traffic, so no
-// step relies on where a workgroup runs.
+// their slots, the leader combines them and posts the group maximum, the eight
+// leaders read each other's group maxima, and each leader hands the result to its
+// members through one mailbox word per member.  No line is polled by more than 16
+// workgroups, so the polls do not queue behind each other.  All of it is
+// device-scope traffic, so no step relies on where a workgroup runs.
 struct FusedWs {
   uint64_t local[8][kFusedMaxWg / 8 + 16];   // per group: members' slots
   uint64_t group[8][16];                      // per group: its maximum, device scope
+  uint64_t mail[8][kFusedMaxWg / 8 + 16];    // per group: the grid maximum, per member
   uint32_t fallbacks[32];                     // waits that ran out and were answered from x
 };
 
@@ -729,20 +732,54 @@ __device__ __noinline__ float tiles_absmax(const T* __restrict__ x, int rows, in
 
 struct GridMaxShared {
   float red[4];
-  uint32_t miss[8];   // bit j: slot j of the current wait did not arrive in time
+  alignas(16) uint32_t miss[8];   // bit j: slot j of the current wait did not arrive in time
   float val;
 };
 
+// The eight miss words, read with two 16-byte LDS loads (one round trip).
+__device__ __forceinline__ void read_miss(const GridMaxShared& sh, uint32_t (&w)[8]) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(&sh.miss[0]);
+  const uint4 hi = *reinterpret_cast<const uint4*>(&sh.miss[4]);
+  w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+  w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+}
+
 // Grid-wide maximum of the workgroups' values v (thread 0's copy), returned to every
 // thread.  Members post their slot in the group area; leader g collects the group's
-// slots and posts the group maximum at device scope; every workgroup then reads the
-// eight group maxima itself (eight lines, polled by eight lanes).
+// slots, posts the group maximum, reads the eight group maxima and writes the grid
+// maximum into each member's mailbox; members wait on their own mailbox only.
 //
 // No wait depends on other workgroups making progress for correctness: a slot that
 // has not arrived after `wait_iters` polls is computed from x by the waiting
-// workgroup itself (one workgroup's tiles, or a group's band).  With the whole grid
-// resident, which the launch size is chosen for, the fallback never runs; without
-// it, the grid still finishes with the exact maximum.
+// workgroup itself (one workgroup's tiles, or a group's band), and a member whose
+// mailbox stays empty reads the group maxima itself, with the same fallback.  With
+// the whole grid resident, which the launch size is chosen for, no fallback runs;
+// without it, the grid still finishes with the exact maximum.
+template <typename T>
+__device__ __forceinline__ float all_groups_max(FusedWs* ws, uint32_t epoch, uint32_t wait_iters,
+                                                const T* __restrict__ x, int rows, int cols, int tiles_r,
+                                                int tiles_c, GridMaxShared& sh) {
+  const int tid = threadIdx.x;
+  const int total = tiles_r * tiles_c, per = (total + 7) >> 3;
+  if (tid < 8) sh.miss[tid] = 0u;
+  __syncthreads();
+  float t = 0.0f;
+  if (tid < 8) {
+    float u;
+    if (poll_slot(&ws->group[tid][0], epoch, wait_iters, &u)) t = u;
+    else atomicOr(&sh.miss[0], 1u << tid);
+  }
+  __syncthreads();
+  const uint32_t miss = sh.miss[0];                  // uniform; one LDS read, not one per group
+  for (int k = 0; k < 8; ++k)
+    if (miss & (1u << k)) {
+      t = __builtin_fmaxf(t, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, k * per, 1, min(total, (k + 1) * per),
+                                             sh.red));
+      if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  return block_max256(t, sh.red);
+}
+
 template <typename T>
 __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, uint32_t wait_iters,
                                           const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
@@ -751,6 +788,7 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
   const int tid = threadIdx.x;
   const int total = tiles_r * tiles_c, per = (total + 7) >> 3;
   uint64_t* local = ws->local[g];
+  uint64_t* mail = ws->mail[g];
   if (tid < 8) sh.miss[tid] = 0u;
   if (tid == 0 && b >= 8)
     __hip_atomic_store(&local[b >> 3], pack_epoch(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -763,33 +801,40 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
       else atomicOr(&sh.miss[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
-    for (int j = 1; j < ng; ++j)                      // uniform: miss[] is shared
-      if (sh.miss[j >> 5] & (1u << (j & 31))) {
-        const int band0 = g * per;
-        m = __builtin_fmaxf(m, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, band0 + j, ng,
-                                               min(total, band0 + per), sh.red));
-        if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    // miss[] is shared, so the words are uniform; read them at once, since a loop that
+    // re-read LDS per member would cost one LDS round trip per member
+    uint32_t mw[8];
+    read_miss(sh, mw);
+    if ((mw[0] | mw[1] | mw[2] | mw[3] | mw[4] | mw[5] | mw[6] | mw[7]) != 0u) {
+      for (int w = 0; w < 8; ++w)
+        for (uint32_t bits = mw[w]; bits != 0u; bits &= bits - 1u) {
+          const int j = w * 32 + __builtin_ctz(bits);
+          const int band0 = g * per;
+          m = __builtin_fmaxf(m, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, band0 + j, ng,
+                                                 min(total, band0 + per), sh.red));
+          if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     m = block_max256(m, sh.red);
     if (tid == 0)
       __hip_atomic_store(&ws->group[g][0], pack_epoch(epoch, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < 8) sh.miss[tid] = 0u;
-    __syncthreads();
+    const float gmax = all_groups_max<T>(ws, epoch, wait_iters, x, rows, cols, tiles_r, tiles_c, sh);
+    for (int j = 1 + tid; j < ng; j += 256)
+      __hip_atomic_store(&mail[j], pack_epoch(epoch, gmax), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return gmax;
   }
-  float t = 0.0f;
-  if (tid < 8) {
+  if (tid == 0) {
     float u;
-    if (poll_slot(&ws->group[tid][0], epoch, wait_iters, &u)) t = u;
-    else atomicOr(&sh.miss[0], 1u << tid);
+    const bool got = poll_slot(&mail[b >> 3], epoch, wait_iters, &u);
+    sh.val = u;
+    sh.miss[0] = got ? 0u : 1u;
   }
   __syncthreads();
-  for (int k = 0; k < 8; ++k)
-    if (sh.miss[0] & (1u << k)) {
-      t = __builtin_fmaxf(t, tiles_absmax<T>(x, rows, cols, tiles_r, tiles_c, k * per, 1, min(total, (k + 1) * per),
-                                             sh.red));
-      if (tid == 0) __hip_atomic_fetch_add(&ws->fallbacks[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  return block_max256(t, sh.red);
+  const bool got = sh.miss[0] == 0u;
+  const float r = sh.val;
+  __syncthreads();                                    // everyone has read sh before it is reused
+  if (got) return r;
+  return all_groups_max<T>(ws, epoch, wait_iters, x, rows, cols, tiles_r, tiles_c, sh);
 }
 
 // Tile K, then K+1, ... with compile-time indices, so the raw tiles stay in registers.

@@ -22,7 +22,7 @@
  *  - Inputs and outputs must not overlap.  The caller allocates every buffer and
  *    keeps it alive until the work on `stream` has completed.  The only memory the
  *    library owns is a small per-(device, stream) workspace of the one-pass NVFP4
- *    kernel (about 8 KB), allocated on the first such call on that stream and kept
+ *    kernel (about 36 KB), allocated on the first such call on that stream and kept
  *    until the process ends; that first call is therefore not graph-capturable.
  *  - A call validates its arguments on the host, enqueues its kernels on `stream`
  *    (0 = the null stream) and returns without synchronizing.  On any validation
