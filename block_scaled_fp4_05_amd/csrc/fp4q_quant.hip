@@ -294,31 +294,23 @@ template <> struct BlockMax<float> {
   }
 };
 
-// Staging of one 128 x 128 tile's outputs.  Chunk positions are XOR swizzled so that
-// the 4-byte writes and the 16-byte reads avoid LDS bank conflicts (64 x 4 bytes).
+// Staging of one 128 x 128 tile's outputs.  A row's 64 bytes of codes sit at dword
+// r*16 + (r/8)*16 and a column's at c*16 + (c/8)*4: the padding after every eight
+// rows / columns sends the lanes of one 4-byte write (four row groups, or sixteen
+// column groups, at one i or j) to distinct banks, and it depends on r/8 and c/8 only,
+// which are fixed for a lane's eight rows and columns, so the row or column index
+// is a constant offset from one per-lane base.  16-byte chunks stay aligned.
 struct TileStage {
-  uint32_t rc[2048];   // row codes: 128 rows x 64 B (512 chunks of 16 B)
-  uint32_t cc[2048];   // column codes: 128 columns x 64 B (4 chunks of 32 tokens each)
-  uint8_t rs[1024];    // row scales: 128 rows x 8 blocks
-  uint8_t cs[1024];    // column scales: 128 columns x 8 blocks
+  uint32_t rc[128 * 16 + 16 * 16];   // row codes: 128 rows x 64 B, 64 B pad per 8 rows
+  uint32_t cc[128 * 16 + 16 * 4];    // column codes: 128 columns x 64 B (4 chunks of 32 tokens), 16 B pad per 8
+  uint8_t rs[1024];                  // row scales: 128 rows x 8 blocks
+  uint8_t cs[1024];                  // column scales: 128 columns x 8 blocks
 };
 
 // row r (0..127), 4-byte piece p (0..15) of its 64 bytes -> dword index in rc
-__device__ __forceinline__ int rc_dword(int r, int p) {
-  const int chunk = (r << 2) + (p >> 2);
-  return ((chunk ^ (((r >> 3) & 3) << 2)) << 2) + (p & 3);
-}
-__device__ __forceinline__ int rc_chunk_row(int ch) {   // inverse: chunk -> row
-  const int r0 = ch >> 2;
-  return r0 ^ ((r0 >> 3) & 3);
-}
+__device__ __forceinline__ int rc_dword(int r, int p) { return r * 16 + (r >> 3) * 16 + p; }
 // column c (0..127), 16-byte piece w (0..3, tokens 32w..32w+31), 4-byte part p
-__device__ __forceinline__ int cc_dword(int c, int w, int p) {
-  return ((((c << 2) + w) ^ ((c >> 3) & 15)) << 2) + p;
-}
-__device__ __forceinline__ int cc_chunk_unswizzle(int ch) {   // swizzled chunk -> c*4 + w
-  return ch ^ ((ch >> 5) & 15);
-}
+__device__ __forceinline__ int cc_dword(int c, int w, int p) { return c * 16 + (c >> 3) * 4 + w * 4 + p; }
 
 __device__ __forceinline__ void store_u8x8(uint8_t* dst, uint2 v, int nvalid, bool aligned8) {
   if (nvalid >= 8 && aligned8) {
@@ -348,6 +340,12 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
   const int q = lane >> 2, h = (lane >> 1) & 1, vv = lane & 1, qr = q >> 3, qc = q & 7;
   const int lrow0 = wave * 32 + qr * 16 + vv * 8, lcol0 = qc * 16 + h * 8;   // within the tile
   const int row0 = trow0 + lrow0, col0 = tcol0 + lcol0;
+
+  // staging addresses of row lrow0 + i and column lcol0 + j: base + constant
+  uint32_t* const rc_lane = &st.rc[rc_dword(lrow0, 2 * qc + h)];
+  uint8_t* const rs_lane = &st.rs[lrow0 * 8 + qc];
+  uint32_t* const cc_lane = &st.cc[cc_dword(lcol0, wave, 2 * qr + vv)];
+  uint8_t* const cs_lane = &st.cs[lcol0 * 8 + 2 * wave + qr];
 
   // t = fl(x*gs) for the lane's 64 elements, formed once for both directions
   float t[8][8];
@@ -381,9 +379,8 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
       } else {
         w = pack8_rtn(v, 1.0f);
       }
-      const int r = lrow0 + i;
-      st.rc[rc_dword(r, 2 * qc + h)] = w;
-      st.rs[r * 8 + qc] = (uint8_t)code;   // both lanes of the block write the same byte
+      rc_lane[i * 16] = w;
+      rs_lane[i * 8] = (uint8_t)code;   // both lanes of the block write the same byte
     }
   }
   if constexpr (COL) {
@@ -411,9 +408,8 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
       } else {
         w = pack8_rtn(v, 1.0f);
       }
-      const int c = lcol0 + j;
-      st.cc[cc_dword(c, wave, 2 * qr + vv)] = w;
-      st.cs[c * 8 + 2 * wave + qr] = (uint8_t)code;   // both lanes of the block write the same byte
+      cc_lane[j * 16] = w;
+      cs_lane[j * 8] = (uint8_t)code;   // both lanes of the block write the same byte
     }
   }
   lds_barrier();
@@ -425,9 +421,9 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
       const int half_cols = cols >> 1, nb = cols >> 4;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int ch = tid + 256 * k, r = rc_chunk_row(ch), c4 = ch & 3;
+        const int ch = tid + 256 * k, r = ch >> 2, c4 = ch & 3;
         *reinterpret_cast<uint4*>(rcodes + (int64_t)(trow0 + r) * half_cols + ((tcol0 + c4 * 32) >> 1)) =
-            *reinterpret_cast<const uint4*>(&st.rc[ch * 4]);
+            *reinterpret_cast<const uint4*>(&st.rc[rc_dword(r, c4 * 4)]);
       }
       if (tid < 128)
         *reinterpret_cast<uint2*>(rscales + (int64_t)(trow0 + tid) * nb + (tcol0 >> 4)) =
@@ -437,9 +433,9 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
       const int half_rows = rows >> 1, nb = rows >> 4;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int ch = tid + 256 * k, cw = cc_chunk_unswizzle(ch), c = cw >> 2, w = cw & 3;
+        const int ch = tid + 256 * k, c = ch >> 2, w = ch & 3;
         *reinterpret_cast<uint4*>(ccodes + (int64_t)(tcol0 + c) * half_rows + ((trow0 + 32 * w) >> 1)) =
-            *reinterpret_cast<const uint4*>(&st.cc[ch * 4]);
+            *reinterpret_cast<const uint4*>(&st.cc[cc_dword(c, w, 0)]);
       }
       if (tid < 128)
         *reinterpret_cast<uint2*>(cscales + (int64_t)(tcol0 + tid) * nb + (trow0 >> 4)) =
@@ -451,9 +447,9 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
     const int half_cols = cols >> 1, nb = cols >> 4;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int ch = tid + 256 * k;                        // swizzled chunk
-      const int r = rc_chunk_row(ch), c4 = ch & 3;
-      const uint4 w = *reinterpret_cast<const uint4*>(&st.rc[ch * 4]);
+      const int ch = tid + 256 * k;                        // chunk: row ch / 4, 32 columns
+      const int r = ch >> 2, c4 = ch & 3;
+      const uint4 w = *reinterpret_cast<const uint4*>(&st.rc[rc_dword(r, c4 * 4)]);
       const int grow = trow0 + r, gcol = tcol0 + c4 * 32;   // first column of this 32-column chunk
       if (grow < rows && gcol < cols) {
         uint8_t* dst = rcodes + (int64_t)grow * half_cols + (gcol >> 1);   // 8-byte aligned
@@ -479,8 +475,8 @@ __device__ __forceinline__ void nvfp4_tile(Raw8x8<T>& raw, int trow0, int tcol0,
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int ch = tid + 256 * k;
-      const int cw = cc_chunk_unswizzle(ch), c = cw >> 2, w = cw & 3;
-      const uint4 v = *reinterpret_cast<const uint4*>(&st.cc[ch * 4]);
+      const int c = ch >> 2, w = ch & 3;
+      const uint4 v = *reinterpret_cast<const uint4*>(&st.cc[cc_dword(c, w, 0)]);
       const int gcol = tcol0 + c, grow = trow0 + 32 * w;
       if (gcol < cols && grow + 16 <= rows) {
         uint8_t* dst = ccodes + (int64_t)gcol * half_rows + (grow >> 1);   // 8-byte aligned
