@@ -74,6 +74,42 @@ __device__ __forceinline__ void rht_load(const uint16_t* __restrict__ x, int64_t
       raw.v[kk][r] = *reinterpret_cast<const uint32_t*>(base + (int64_t)(16 * kk + r) * cols);
 }
 
+// LDS staging for the fused passes.  A wave's tile (128 tokens x 64 columns of bf16,
+// 16 KB) goes from HBM to its own LDS buffer by 16 direct loads of 16 bytes per lane
+// (lane l of load i carries token 8i + l/8, columns 8(l%8)..+7, and lands at byte
+// 16 l of that load's 1 KB, so the buffer is the tile in row-major order).  No VGPR
+// holds the data in flight, so a wave keeps a whole tile in the air while it works
+// on the previous one, and two waves fit on each SIMD.  The wave then reads the same
+// 64 words per lane as rht_load from LDS.  Chunks past the last column read column
+// chunk 0 of the same token instead; only lanes whose results are discarded use them.
+struct RhtStage {
+  uint32_t w[128 * 32];
+};
+
+__device__ __forceinline__ void rht_issue(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0, int64_t col0,
+                                          RhtStage& st) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = col0 + 8 * (lane & 7);
+  const uint16_t* base = x + (tok0 + (lane >> 3)) * cols + (c < cols ? c : 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    __builtin_amdgcn_global_load_lds(base + (int64_t)(8 * i) * cols, &st.w[i * 256], 16, 0, 0);
+}
+
+// The direct loads are invisible to the compiler's wait counting: wait for every
+// outstanding vector memory operation before the buffer is read, and for the LDS
+// reads before it is refilled.
+__device__ __forceinline__ void rht_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void rht_wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void rht_read(const RhtStage& st, RhtRaw& raw) {
+  const int lane = threadIdx.x & 63, n = lane & 31, hk = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) raw.v[kk][r] = st.w[(16 * kk + 8 * hk + r) * 32 + n];
+}
+
 // Half H of one tile from its raw words: acc[p][a'] is the 32x32 MFMA output block
 // a = 2H + a' (output tokens 32a..32a+31) for column parity p of this lane's column
 // pair.  Working in halves keeps 64 accumulators live instead of 128, which lets two
@@ -170,20 +206,36 @@ __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x
 // ---------------------------------------------------------------------------
 // Pass 1 of the fused path: amax of the transformed tensor.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                   RhtSigns sg, float* __restrict__ amax) {
+  __shared__ RhtStage stage[4];
+  RhtStage& st = stage[threadIdx.x >> 6];
   u32x4 frag[8];
   make_fragments(sg, true, frag);
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63;
   float m = 0.0f;
-  for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
+  int64_t tile = wave_id();
+  const int64_t step = wave_count();
+  if (tile < it.ntiles) {
     int64_t chunk, slab;
     it.decode(tile, chunk, slab);
-    const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
+    rht_issue(x, cols, chunk * 128, slab * 64, st);
+  }
+  for (; tile < it.ntiles; tile += step) {
+    int64_t chunk, slab;
+    it.decode(tile, chunk, slab);
+    const int64_t colp = slab * 64 + 2 * (lane & 31);
     const bool valid = colp < cols;
     RhtRaw raw;
-    rht_load(x, cols, tok0, colp, valid, raw);
+    rht_wait_loads();
+    rht_read(st, raw);
+    rht_wait_lds();
+    if (tile + step < it.ntiles) {
+      int64_t c2, s2;
+      it.decode(tile + step, c2, s2);
+      rht_issue(x, cols, c2 * 128, s2 * 64, st);
+    }
     float t = 0.0f;
     auto fold = [&](const f32x16 (&acc)[2][2]) {
 #pragma unroll
@@ -216,10 +268,12 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
 // After the permlane32 swaps each lane holds 16 consecutive tokens of one column.
 // ---------------------------------------------------------------------------
 template <bool SR>
-__global__ __launch_bounds__(256) void k_rht_nvfp4_col(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_nvfp4_col(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                        RhtSigns sg, const float* __restrict__ amax,
                                                        float* __restrict__ tensor_scale, uint8_t* __restrict__ ccodes,
                                                        uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
+  __shared__ RhtStage stage[4];
+  RhtStage& st = stage[threadIdx.x >> 6];
   const float gs = tensor_scale_from_amax(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
   u32x4 frag[8];
@@ -227,9 +281,8 @@ __global__ __launch_bounds__(256) void k_rht_nvfp4_col(const uint16_t* __restric
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63, hk = lane >> 5;
   const int64_t half_rows = rows >> 1, nb = rows >> 4;
-  // The next tile's raw words are loaded while this one is transformed and
-  // quantized; each loop step is written out with and without the next load so
-  // the compiler's wait before the MFMAs covers only the current tile.
+  // The next tile streams into the wave's LDS buffer while this one, already read
+  // into registers, is transformed and quantized.
   auto process = [&](const RhtRaw& raw, int64_t tile) {
     int64_t chunk, slab;
     it.decode(tile, chunk, slab);
@@ -302,35 +355,22 @@ __global__ __launch_bounds__(256) void k_rht_nvfp4_col(const uint16_t* __restric
       if (valid) *reinterpret_cast<uint32_t*>(cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
     }
   };
-  auto fetch = [&](RhtRaw& raw, int64_t tile) {
+  auto issue = [&](int64_t tile) {
     int64_t chunk, slab;
     it.decode(tile, chunk, slab);
-    const int64_t colp = slab * 64 + 2 * (lane & 31);
-    rht_load(x, cols, chunk * 128, colp, colp < cols, raw);
+    rht_issue(x, cols, chunk * 128, slab * 64, st);
   };
   int64_t tile = wave_id();
   const int64_t step = wave_count();
   if (tile >= it.ntiles) return;
-  RhtRaw ra, rb;
-  fetch(ra, tile);
-  while (true) {
-    const int64_t t1 = tile + step;
-    if (t1 < it.ntiles) {
-      fetch(rb, t1);
-      process(ra, tile);
-    } else {
-      process(ra, tile);
-      break;
-    }
-    const int64_t t2 = t1 + step;
-    if (t2 < it.ntiles) {
-      fetch(ra, t2);
-      process(rb, t1);
-    } else {
-      process(rb, t1);
-      break;
-    }
-    tile = t2;
+  issue(tile);
+  for (; tile < it.ntiles; tile += step) {
+    RhtRaw raw;
+    rht_wait_loads();
+    rht_read(st, raw);
+    rht_wait_lds();
+    if (tile + step < it.ntiles) issue(tile + step);   // in flight while this tile is worked on
+    process(raw, tile);
   }
 }
 
@@ -377,9 +417,7 @@ static RhtSigns pack_signs(const uint32_t s[4]) {
   return r;
 }
 
-// Persistent grid of at most `per_simd` waves per SIMD (256 CUs x 4 SIMDs): the
-// transform-only kernels fit two waves per SIMD, the quantizing kernel, which keeps a
-// second tile in flight, one.
+// Persistent grid of at most `per_simd` waves per SIMD (256 CUs x 4 SIMDs).
 static int rht_grid(int64_t rows, int64_t cols, int per_simd) {
   const int64_t tiles = ((cols + 63) / 64) * (rows / 128);
   const int64_t cap = (int64_t)1024 * per_simd;
@@ -410,10 +448,10 @@ void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const u
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const RhtSigns sg = pack_signs(signs);
   if (sr)
-    k_rht_nvfp4_col<true><<<rht_grid(rows, cols, 1), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
+    k_rht_nvfp4_col<true><<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
                                                                 col_scales, k0, k1);
   else
-    k_rht_nvfp4_col<false><<<rht_grid(rows, cols, 1), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
+    k_rht_nvfp4_col<false><<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
                                                                  col_scales, k0, k1);
 }
 
