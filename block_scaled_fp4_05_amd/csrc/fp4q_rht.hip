@@ -11,8 +11,8 @@
 // issued before the first MFMA, and transposes it in registers (v_perm) into the B
 // operands, so no LDS is needed.  Sylvester H factors as H_128[32a+u][32b+w] = H_4[a][b] H_32[u][w]: the A
 // operand of a K-step only depends on the H_32 part (folded with the signs, kept in
-// registers for the wave's lifetime), and the H_4 sign is applied by negating the B
-// operand for the output row-blocks that need it.
+// registers for the wave's lifetime, with a negated copy), and the H_4 sign picks the
+// negated A operand for the output row-blocks that need it.
 //
 // The same contraction routine feeds the standalone transform, the amax pass and
 // the fused column-wise NVFP4 pass, so all three see bitwise identical values
@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t parity(uint32_t v) { return __builtin_popcou
 
 // A-operand fragments: lane (il = lane & 31, hk = lane >> 5), K-step kk holds
 // K[32a + il][16kk + 8hk + e] without the H_4 factor, e = 0..7.
-__device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_signs, u32x4 frag[8]) {
+__device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_signs, u32x4 frag[8], u32x4 nfrag[8]) {
   const uint32_t lane = threadIdx.x & 63, il = lane & 31, hk = lane >> 5;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -52,6 +52,7 @@ __device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_sig
       d[q] = half[0] | (half[1] << 16);
     }
     frag[kk] = u32x4{d[0], d[1], d[2], d[3]};
+    nfrag[kk] = frag[kk] ^ 0x80008000u;
   }
 }
 
@@ -115,7 +116,8 @@ __device__ __forceinline__ void rht_read(const RhtStage& st, RhtRaw& raw) {
 // pair.  Working in halves keeps 64 accumulators live instead of 128, which lets two
 // waves share a SIMD.
 template <int H>
-__device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag[8], f32x16 acc[2][2]) {
+__device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag[8], const u32x4 nfrag[8],
+                                             f32x16 acc[2][2]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -128,14 +130,12 @@ __device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag
       b0[q] = __builtin_amdgcn_perm(raw.v[kk][2 * q + 1], raw.v[kk][2 * q], 0x05040100u);
       b1[q] = __builtin_amdgcn_perm(raw.v[kk][2 * q + 1], raw.v[kk][2 * q], 0x07060302u);
     }
-    const u32x4 nb0 = b0 ^ 0x80008000u, nb1 = b1 ^ 0x80008000u;
-    const bf16x8 fa = __builtin_bit_cast(bf16x8, frag[kk]);
+    const bf16x8 v0 = __builtin_bit_cast(bf16x8, b0), v1 = __builtin_bit_cast(bf16x8, b1);
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap) {
       const int a = 2 * H + ap;
       const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
-      const bf16x8 v0 = __builtin_bit_cast(bf16x8, flip ? nb0 : b0);
-      const bf16x8 v1 = __builtin_bit_cast(bf16x8, flip ? nb1 : b1);
+      const bf16x8 fa = __builtin_bit_cast(bf16x8, flip ? nfrag[kk] : frag[kk]);
       acc[0][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][ap], 0, 0, 0);
       acc[1][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][ap], 0, 0, 0);
     }
@@ -173,8 +173,8 @@ __device__ __forceinline__ int64_t wave_count() { return ((int64_t)gridDim.x * b
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                   RhtSigns sg, int inverse, float* __restrict__ y) {
-  u32x4 frag[8];
-  make_fragments(sg, !inverse, frag);
+  u32x4 frag[8], nfrag[8];
+  make_fragments(sg, !inverse, frag, nfrag);
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63;
   for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
@@ -196,9 +196,9 @@ __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x
         }
     };
     f32x16 acc[2][2];
-    rht_mma_half<0>(raw, frag, acc);
+    rht_mma_half<0>(raw, frag, nfrag, acc);
     emit(acc, 0);
-    rht_mma_half<1>(raw, frag, acc);
+    rht_mma_half<1>(raw, frag, nfrag, acc);
     emit(acc, 2);
   }
 }
@@ -210,8 +210,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                   RhtSigns sg, float* __restrict__ amax) {
   __shared__ RhtStage stage[4];
   RhtStage& st = stage[threadIdx.x >> 6];
-  u32x4 frag[8];
-  make_fragments(sg, true, frag);
+  u32x4 frag[8], nfrag[8];
+  make_fragments(sg, true, frag, nfrag);
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63;
   float m = 0.0f;
@@ -246,9 +246,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, __builtin_fabsf(acc[p][a][r]));
     };
     f32x16 acc[2][2];
-    rht_mma_half<0>(raw, frag, acc);
+    rht_mma_half<0>(raw, frag, nfrag, acc);
     fold(acc);
-    rht_mma_half<1>(raw, frag, acc);
+    rht_mma_half<1>(raw, frag, nfrag, acc);
     fold(acc);
     if (valid) m = __builtin_fmaxf(m, t);
   }
@@ -273,11 +273,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                        float* __restrict__ tensor_scale, uint8_t* __restrict__ ccodes,
                                                        uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
   __shared__ RhtStage stage[4];
+  __shared__ RecipTable rtab;
   RhtStage& st = stage[threadIdx.x >> 6];
+  fill_recip_table(rtab);
+  __syncthreads();
   const float gs = tensor_scale_from_amax(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
-  u32x4 frag[8];
-  make_fragments(sg, true, frag);
+  u32x4 frag[8], nfrag[8];
+  make_fragments(sg, true, frag, nfrag);
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63, hk = lane >> 5;
   const int64_t half_rows = rows >> 1, nb = rows >> 4;
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
           }
           const uint32_t sc = nvfp4_scale_code(m);
-          const RecipPair rp = recip_pair_code(sc);
+          const RecipPair rp = rtab.r[sc];
 #pragma unroll
           for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
           const int64_t c = colp + p;
@@ -338,9 +341,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
     f32x16 acc[2][2];
-    rht_mma_half<0>(raw, frag, acc);
+    rht_mma_half<0>(raw, frag, nfrag, acc);
     quantize(acc, 0);
-    rht_mma_half<1>(raw, frag, acc);
+    rht_mma_half<1>(raw, frag, nfrag, acc);
     quantize(acc, 2);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
