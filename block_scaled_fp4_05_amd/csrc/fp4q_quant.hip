@@ -1112,7 +1112,7 @@ __device__ __forceinline__ void decode8_fp4(uint32_t w, float scale, float r[8])
 // as fl(q*fl(6/7)); accumulates both squared-error sums in element order.
 __device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[8], float& e_fp, float& e_int) {
   const float c76 = 7.0f / 6.0f, c67 = 6.0f / 7.0f, magic = 12582912.0f;
-  uint32_t w = 0;
+  uint32_t yb[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     float wv = v[k] * c76;
@@ -1120,13 +1120,17 @@ __device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[
     const float y = wv + magic;
     const float qf = y - magic;
     const float ri = qf * c67;
-    w |= (__float_as_uint(y) & 0xFu) << (4 * k);
+    yb[k] = __float_as_uint(y);
     const float dfp = v[k] - rf[k];
     const float dint = v[k] - ri;
     e_fp = __builtin_fmaf(dfp, dfp, e_fp);
     e_int = __builtin_fmaf(dint, dint, e_int);
   }
-  return w;
+  // nibble k = low nibble of yb[k]: gather the low bytes of the even and the odd
+  // elements (byte permutes), then merge the two nibble planes in one bit select
+  const uint32_t ev = __builtin_amdgcn_perm(yb[2], yb[0], 0x0C0C0400u) | __builtin_amdgcn_perm(yb[6], yb[4], 0x04000C0Cu);
+  const uint32_t od = __builtin_amdgcn_perm(yb[3], yb[1], 0x0C0C0400u) | __builtin_amdgcn_perm(yb[7], yb[5], 0x04000C0Cu);
+  return __builtin_amdgcn_bitop3_b32(ev, od << 4, 0x0F0F0F0Fu, 0xE4);   // (ev & m) | (od<<4 & ~m)
 }
 
 template <typename T>
