@@ -203,14 +203,17 @@ def quantize_nvfp4(x: torch.Tensor, layouts: int = ROWWISE | COLWISE, rnd: int =
     return out
 
 
-def quantize_nvfp4_2d(x: torch.Tensor, transposed: bool = False, stream=None) -> dict:
+def quantize_nvfp4_2d(x: torch.Tensor, transposed: bool = False, amax: torch.Tensor | None = None,
+                      stream=None) -> dict:
+    """NVFP4 16x16.  If `amax` is given it is used as the tensor amax (AMAX_GIVEN)."""
     rows, cols = x.shape
     dev = x.device
-    out = {"amax": torch.empty(1, dtype=torch.float32, device=dev),
+    mode = AMAX_GIVEN if amax is not None else AMAX_COMPUTE
+    out = {"amax": amax if amax is not None else torch.empty(1, dtype=torch.float32, device=dev),
            "tensor_scale": torch.empty(1, dtype=torch.float32, device=dev),
            "codes": _u8(rows, cols // 2, device=dev), "scales": _u8(rows // 16, cols // 16, device=dev),
            "codes_t": _u8(cols, rows // 2, device=dev) if transposed else None}
-    fp4q_quantize_nvfp4_2d(x, _dt(x), rows, cols, AMAX_COMPUTE, out["amax"], out["tensor_scale"], out["codes"],
+    fp4q_quantize_nvfp4_2d(x, _dt(x), rows, cols, mode, out["amax"], out["tensor_scale"], out["codes"],
                            out["scales"], out["codes_t"], stream)
     return out
 
@@ -223,13 +226,15 @@ def quantize_mxfp4(x: torch.Tensor, rnd: int = RTN, sr_seed: int = 0, stream=Non
     return out
 
 
-def quantize_if4(x: torch.Tensor, stream=None) -> dict:
+def quantize_if4(x: torch.Tensor, amax: torch.Tensor | None = None, stream=None) -> dict:
+    """IF4.  If `amax` is given it is used as the tensor amax (AMAX_GIVEN)."""
     rows, cols = x.shape
     dev = x.device
-    out = {"amax": torch.empty(1, dtype=torch.float32, device=dev),
+    mode = AMAX_GIVEN if amax is not None else AMAX_COMPUTE
+    out = {"amax": amax if amax is not None else torch.empty(1, dtype=torch.float32, device=dev),
            "tensor_scale": torch.empty(1, dtype=torch.float32, device=dev),
            "codes": _u8(rows, cols // 2, device=dev), "scales": _u8(rows, cols // 16, device=dev)}
-    fp4q_quantize_if4(x, _dt(x), rows, cols, AMAX_COMPUTE, out["amax"], out["tensor_scale"], out["codes"],
+    fp4q_quantize_if4(x, _dt(x), rows, cols, mode, out["amax"], out["tensor_scale"], out["codes"],
                       out["scales"], stream)
     return out
 

@@ -13,6 +13,19 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool valid_dtype(int d) { return d == FP4Q_F32 || d == FP4Q_BF16; }
 bool valid_round(int r) { return r == FP4Q_RTN || r == FP4Q_SR; }
 
+// Sink of a two-pass call's amax pass and the matching source for its quantizer: the
+// stream's workspace word when it can be had (no zeroing launch), else the caller's float.
+fp4q::AmaxSink amax_sink(float* amax, hipStream_t st, fp4q::AmaxSource* src) {
+  uint64_t* slot = nullptr;
+  uint32_t epoch = 0u;
+  if (fp4q::reserve_amax_slot(st, &slot, &epoch)) {
+    *src = fp4q::AmaxSource{nullptr, slot, amax};
+    return fp4q::AmaxSink{nullptr, slot, epoch};
+  }
+  *src = fp4q::AmaxSource{amax, nullptr, nullptr};
+  return fp4q::AmaxSink{amax, nullptr, 0u};
+}
+
 fp4q_status after_launch() {
   return hipGetLastError() == hipSuccess ? FP4Q_OK : FP4Q_E_HIP;
 }
@@ -99,19 +112,24 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
   const bool sr = rnd == FP4Q_SR;
   if (rht_signs) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_rht_amax(xb, rows, cols, rht_signs, amax, stream);
-    fp4q::launch_rht_nvfp4_col(xb, rows, cols, rht_signs, sr, sr_seed, amax, tensor_scale, col_codes, col_scales,
+    fp4q::AmaxSource src{amax, nullptr, nullptr};
+    if (amax_mode == FP4Q_AMAX_COMPUTE) {
+      const fp4q::AmaxSink sink = amax_sink(amax, stream, &src);
+      fp4q::launch_rht_amax(xb, rows, cols, rht_signs, sink, stream);
+    }
+    fp4q::launch_rht_nvfp4_col(xb, rows, cols, rht_signs, sr, sr_seed, src, tensor_scale, col_codes, col_scales,
                                stream);
     return after_launch();
   }
+  fp4q::AmaxSource src{amax, nullptr, nullptr};
   if (amax_mode == FP4Q_AMAX_COMPUTE) {
     // one pass when the tensor fits a co-resident grid, else amax first
     if (fp4q::launch_nvfp4_fused(x, dt, rows, cols, layouts, sr, amax, tensor_scale, row_codes, row_scales,
                                  col_codes, col_scales, sr_seed, stream))
       return after_launch();
-    fp4q::launch_amax(x, dt, rows * cols, amax, stream);
+    fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, stream, &src), stream);
   }
-  fp4q::launch_nvfp4(x, dt, rows, cols, layouts, sr, amax, tensor_scale, row_codes, row_scales, col_codes,
+  fp4q::launch_nvfp4(x, dt, rows, cols, layouts, sr, src, tensor_scale, row_codes, row_scales, col_codes,
                      col_scales, sr_seed, stream);
   return after_launch();
 }
@@ -125,8 +143,9 @@ fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, i
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(amax) || !aligned4(tensor_scale) ||
       (codes_t && !aligned16(codes_t)))
     return FP4Q_E_ALIGN;
-  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax(x, dt, rows * cols, amax, stream);
-  fp4q::launch_nvfp4_2d(x, dt, rows, cols, amax, tensor_scale, codes, scales, codes_t, stream);
+  fp4q::AmaxSource src{amax, nullptr, nullptr};
+  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, stream, &src), stream);
+  fp4q::launch_nvfp4_2d(x, dt, rows, cols, src, tensor_scale, codes, scales, codes_t, stream);
   return after_launch();
 }
 
@@ -148,8 +167,9 @@ fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_
   if (rows <= 0 || cols <= 0 || cols % 16 != 0) return FP4Q_E_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(amax) || !aligned4(tensor_scale))
     return FP4Q_E_ALIGN;
-  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax(x, dt, rows * cols, amax, stream);
-  fp4q::launch_if4(x, dt, rows, cols, amax, tensor_scale, codes, scales, stream);
+  fp4q::AmaxSource src{amax, nullptr, nullptr};
+  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, stream, &src), stream);
+  fp4q::launch_if4(x, dt, rows, cols, src, tensor_scale, codes, scales, stream);
   return after_launch();
 }
 

@@ -9,6 +9,7 @@
 // same IEEE binary32 roundings as the reference definition (no contraction; this
 // file is compiled with -ffp-contract=off and uses fmaf only where stated).
 #pragma once
+#include "fp4q_internal.hpp"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -272,6 +273,35 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
 __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
   // non-negative floats order like their bit patterns
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+// Where an amax pass posts its workgroup maxima, and where a quantizer finds the
+// tensor amax.  A pass posts either into a float the caller zeroed (atomic max on
+// its bits) or into a 64-bit word of a per-stream workspace holding
+// (epoch << 32) | bits, where the host numbers the launches on the stream: the
+// first post of a launch replaces whatever an earlier launch left (its epoch is
+// larger), so the word needs no reset between calls.
+// (AmaxSink and AmaxSource are declared with the launchers.)
+__device__ __forceinline__ void post_amax(const AmaxSink& s, float m) {
+  if (s.slot)
+    __hip_atomic_fetch_max(s.slot, ((uint64_t)s.epoch << 32) | __float_as_uint(m), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  else
+    atomic_max_nonneg(s.f, m);
+}
+__device__ __forceinline__ float read_amax(const AmaxSource& s) {
+  return s.slot ? __uint_as_float((uint32_t)*s.slot) : *s.f;
+}
+// The tensor scale from the source; workgroup 0's first thread publishes it (and the
+// amax, when it came from a pass of this call).
+__device__ __forceinline__ float tensor_scale_publish(const AmaxSource& s, float* tensor_scale) {
+  const float a = read_amax(s);
+  const float gs = tensor_scale_from_amax(a);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *tensor_scale = gs;
+    if (s.out) *s.out = a;
+  }
+  return gs;
 }
 
 }  // namespace fp4q

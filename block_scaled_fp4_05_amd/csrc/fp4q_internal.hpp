@@ -7,10 +7,28 @@
 
 namespace fp4q {
 
+// Where an amax pass posts (a zeroed float, or a per-stream workspace word with an
+// epoch) and where a quantizer reads the tensor amax from (device side in fp4q_dev.hpp).
+struct AmaxSink {
+  float* f;
+  uint64_t* slot;
+  uint32_t epoch;
+};
+struct AmaxSource {
+  const float* f;         // tensor amax given by the caller, or
+  const uint64_t* slot;   // the word an amax pass of the same stream posted into
+  float* out;             // with `slot`: the caller's amax output, written by one thread
+};
+
+// amax of x into a zeroed-first float (the standalone entry point) or a sink
 void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t st);
+void launch_amax_to(const void* x, int dtype, int64_t n, const AmaxSink& sink, hipStream_t st);
+// The stream's workspace word for a two-pass call and the call's epoch (false if the
+// workspace cannot be allocated; callers then use the caller's float instead).
+bool reserve_amax_slot(hipStream_t st, uint64_t** slot, uint32_t* epoch);
 
 void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
-                  const float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
+                  const AmaxSource& amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
                   uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, hipStream_t st);
 
 // NVFP4 with amax computed in the same pass.  Returns false, having enqueued nothing,
@@ -24,13 +42,13 @@ void set_fused_wait_us(uint32_t us);
 bool fused_fallbacks(hipStream_t st, uint32_t* count);
 constexpr int kFusedMaxWg = 2048;
 
-void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax,
+void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                      float* tensor_scale, uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st);
 
 void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
                   uint8_t* scales, uint64_t seed, hipStream_t st);
 
-void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax,
+void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                 float* tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t st);
 
 void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
@@ -40,9 +58,9 @@ void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const 
 void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
                 int inverse, float* y, hipStream_t st);
 void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4],
-                     float* amax, hipStream_t st);
+                     const AmaxSink& sink, hipStream_t st);
 void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4],
-                          bool sr, uint64_t seed, const float* amax, float* tensor_scale,
+                          bool sr, uint64_t seed, const AmaxSource& amax, float* tensor_scale,
                           uint8_t* col_codes, uint8_t* col_scales, hipStream_t st);
 
 }  // namespace fp4q

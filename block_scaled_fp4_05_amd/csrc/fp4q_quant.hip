@@ -30,7 +30,7 @@ __global__ void k_zero1(float* p) { *p = 0.0f; }
 // reduces its share (DPP/shuffle within waves, LDS across waves) and issues a single
 // atomic; the grid is sized to about one 1024-thread workgroup per CU.
 template <typename T>
-__global__ __launch_bounds__(1024) void k_amax(const T* __restrict__ x, int64_t n8, float* __restrict__ amax) {
+__global__ __launch_bounds__(1024) void k_amax(const T* __restrict__ x, int64_t n8, AmaxSink sink) {
   __shared__ float wmax[16];
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * 1024;
@@ -59,13 +59,13 @@ __global__ __launch_bounds__(1024) void k_amax(const T* __restrict__ x, int64_t 
     float bm = 0.0f;
     const int nw = (int)(blockDim.x >> 6);
     for (int w = 0; w < nw; ++w) bm = __builtin_fmaxf(bm, wmax[w]);
-    atomic_max_nonneg(amax, bm);
+    post_amax(sink, bm);
   }
 }
 
 // amax over a tail of fewer than 8 elements (only for fp4q_amax on odd sizes)
 template <typename T>
-__global__ void k_amax_tail(const T* __restrict__ x, int64_t start, int64_t n, float* __restrict__ amax) {
+__global__ void k_amax_tail(const T* __restrict__ x, int64_t start, int64_t n, AmaxSink sink) {
   int64_t i = start + threadIdx.x;
   float m = 0.0f;
   if (i < n) {
@@ -73,15 +73,14 @@ __global__ void k_amax_tail(const T* __restrict__ x, int64_t start, int64_t n, f
     else m = __builtin_fabsf(x[i]);
   }
   m = wave_max(m);
-  if (threadIdx.x == 0) atomic_max_nonneg(amax, m);
+  if (threadIdx.x == 0) post_amax(sink, m);
 }
 
 // Large tensors: two 256-thread workgroups per CU, each thread keeping four
 // non-temporal 16-byte loads in flight, and the maximum taken on magnitude bits
 // (|x| orders like its bits with the sign cleared; bf16 two at a time).
 template <typename T>
-__global__ __launch_bounds__(256) void k_amax_wide(const u32x4_t* __restrict__ x, int64_t n16,
-                                                   float* __restrict__ amax) {
+__global__ __launch_bounds__(256) void k_amax_wide(const u32x4_t* __restrict__ x, int64_t n16, AmaxSink sink) {
   __shared__ float wm[4];
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(256) void k_amax_wide(const u32x4_t* __restrict__ x
   f = wave_max(f);
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = f;
   __syncthreads();
-  if (threadIdx.x == 0) atomic_max_nonneg(amax, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])));
+  if (threadIdx.x == 0) post_amax(sink, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])));
 }
 
 static int amax_grid(int64_t n8) {
@@ -123,23 +122,27 @@ static int amax_grid(int64_t n8) {
 static int num_cus();
 
 template <typename T>
-static void launch_amax_t(const void* x, int64_t n, float* amax, hipStream_t st) {
+static void launch_amax_t(const void* x, int64_t n, const AmaxSink& sink, hipStream_t st) {
   const T* xp = static_cast<const T*>(x);
-  k_zero1<<<1, 1, 0, st>>>(amax);
+  if (!sink.slot) k_zero1<<<1, 1, 0, st>>>(sink.f);
   if ((int64_t)sizeof(T) * n >= ((int64_t)128 << 20)) {
     const int64_t per16 = 16 / sizeof(T), n16 = n / per16;
-    k_amax_wide<T><<<2 * num_cus(), 256, 0, st>>>(static_cast<const u32x4_t*>(x), n16, amax);
-    if (n16 * per16 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n16 * per16, n, amax);
+    k_amax_wide<T><<<2 * num_cus(), 256, 0, st>>>(static_cast<const u32x4_t*>(x), n16, sink);
+    if (n16 * per16 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n16 * per16, n, sink);
     return;
   }
   int64_t n8 = n / 8;
-  if (n8 > 0) k_amax<T><<<amax_grid(n8), 1024, 0, st>>>(xp, n8, amax);
-  if (n8 * 8 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n8 * 8, n, amax);
+  if (n8 > 0) k_amax<T><<<amax_grid(n8), 1024, 0, st>>>(xp, n8, sink);
+  if (n8 * 8 < n) k_amax_tail<T><<<1, 64, 0, st>>>(xp, n8 * 8, n, sink);
+}
+
+void launch_amax_to(const void* x, int dtype, int64_t n, const AmaxSink& sink, hipStream_t st) {
+  if (dtype == 1) launch_amax_t<uint16_t>(x, n, sink, st);
+  else launch_amax_t<float>(x, n, sink, st);
 }
 
 void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t st) {
-  if (dtype == 1) launch_amax_t<uint16_t>(x, n, amax, st);
-  else launch_amax_t<float>(x, n, amax, st);
+  launch_amax_to(x, dtype, n, AmaxSink{amax, nullptr, 0u}, st);
 }
 
 // ===========================================================================
@@ -518,7 +521,7 @@ __device__ __forceinline__ void group_major_tile(int t, int tiles_r, int tiles_c
 template <typename T, bool ROW, bool COL, bool SR>
 __global__ __launch_bounds__(256) void k_nvfp4_tile(
     const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
-    const float* __restrict__ amax, float* __restrict__ tensor_scale,
+    AmaxSource amax, float* __restrict__ tensor_scale,
     uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
     uint8_t* __restrict__ ccodes, uint8_t* __restrict__ cscales,
     uint32_t k0, uint32_t k1) {
@@ -526,8 +529,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile(
   __shared__ RecipTable rtab;
   fill_recip_table(rtab);
   __syncthreads();
-  const float gs = tensor_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  const float gs = tensor_scale_publish(amax, tensor_scale);
 
   // tiles of XCD x (blocks b with b % 8 == x) form the contiguous band
   // [x*per, (x+1)*per) of the group-major sequence; the band's blocks stride through it.
@@ -587,7 +589,7 @@ static int num_cus() {
 }
 
 template <typename T, bool ROW, bool COL, bool SR>
-static void launch_nvfp4_t(const void* x, int64_t rows, int64_t cols, const float* amax,
+static void launch_nvfp4_t(const void* x, int64_t rows, int64_t cols, const AmaxSource& amax,
                            float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs,
                            uint32_t k0, uint32_t k1, hipStream_t st) {
   const int tiles_r = (int)((rows + 127) / 128), tiles_c = (int)((cols + 127) / 128);
@@ -600,7 +602,7 @@ static void launch_nvfp4_t(const void* x, int64_t rows, int64_t cols, const floa
 
 template <typename T>
 static void launch_nvfp4_dt(const void* x, int64_t rows, int64_t cols, unsigned layouts, bool sr,
-                            const float* amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                            const AmaxSource& amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
                             uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
   const bool row = layouts & 1u, col = layouts & 2u;
 #define FP4Q_NV(R, C, S) launch_nvfp4_t<T, R, C, S>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)
@@ -611,7 +613,7 @@ static void launch_nvfp4_dt(const void* x, int64_t rows, int64_t cols, unsigned 
 }
 
 void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
-                  const float* amax, float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                  const AmaxSource& amax, float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc,
                   uint8_t* cs, uint64_t seed, hipStream_t st) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   if (dtype == 1)
@@ -654,6 +656,7 @@ struct FusedWs {
   uint64_t group[8][16];                      // per group: its maximum, device scope
   uint64_t mail[8][kFusedMaxWg / 8 + 16];    // per group: the grid maximum, per member
   uint32_t fallbacks[32];                     // waits that ran out and were answered from x
+  uint64_t amax_slot[16];                     // two-pass calls: (epoch << 32) | amax bits, by atomic max
 };
 
 __device__ __forceinline__ float raw_absmax(const Raw8x8<uint16_t>& raw) {
@@ -962,7 +965,12 @@ bool reserve_launch(hipStream_t st, Launch* l) {
   WsEntry* e = nullptr;
   if (!find_ws(st, &e)) return false;
   e->epoch += 1u;
-  if (e->epoch == 0u) e->epoch = 1u;   // 0 is the zeroed workspace's value
+  if (e->epoch == 0u) {
+    // After 2^32 launches the numbers repeat: clear every word first, so neither a
+    // stale slot nor a larger old epoch can be taken for the current launch's.
+    if (hipMemsetAsync(e->ws, 0, sizeof(FusedWs), st) != hipSuccess) return false;
+    e->epoch = 1u;
+  }
   *l = Launch{e->ws, e->epoch};
   return true;
 }
@@ -1018,6 +1026,14 @@ bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, un
   if (dtype == 1)
     return try_fused_dt<uint16_t>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
   return try_fused_dt<float>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+}
+
+bool reserve_amax_slot(hipStream_t st, uint64_t** slot, uint32_t* epoch) {
+  Launch l;
+  if (!reserve_launch(st, &l)) return false;
+  *slot = &l.ws->amax_slot[0];
+  *epoch = l.epoch;
+  return true;
 }
 
 void set_fused_wait_us(uint32_t us) {
@@ -1134,11 +1150,10 @@ __device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n16, const float* __restrict__ amax,
+__global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n16, AmaxSource amax,
                                              float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
                                              uint8_t* __restrict__ scales) {
-  const float gs = tensor_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  const float gs = tensor_scale_publish(amax, tensor_scale);
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= n16) return;
   float a[8], b[8];
@@ -1170,7 +1185,7 @@ __global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n1
   scales[g] = (uint8_t)(sc | (use_int ? 0x80u : 0u));
 }
 
-void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax, float* tensor_scale,
+void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax, float* tensor_scale,
                 uint8_t* codes, uint8_t* scales, hipStream_t st) {
   const int64_t n16 = rows * cols / 16;
   const int grid = (int)((n16 + 255) / 256);
@@ -1198,12 +1213,11 @@ __device__ __forceinline__ float max16_lanes(float v) {
 
 template <typename T, bool TRANS>
 __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64_t rows, int64_t cols,
-                                                  const float* __restrict__ amax, float* __restrict__ tensor_scale,
+                                                  AmaxSource amax, float* __restrict__ tensor_scale,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                   uint8_t* __restrict__ codes_t) {
   __shared__ uint32_t lds[16][16][2];   // [tile in block][row][8 bytes]
-  const float gs = tensor_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  const float gs = tensor_scale_publish(amax, tensor_scale);
   const int64_t tiles_c = cols >> 4, tiles = (rows >> 4) * tiles_c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tin = lane >> 4, i = lane & 15;                 // tile within wave, row within tile
@@ -1256,7 +1270,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64
   }
 }
 
-void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const float* amax, float* tensor_scale,
+void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax, float* tensor_scale,
                      uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st) {
   const int64_t tiles = (rows >> 4) * (cols >> 4);
   const int grid = (int)((tiles + 15) / 16);

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x
 // Pass 1 of the fused path: amax of the transformed tensor.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                  RhtSigns sg, float* __restrict__ amax) {
+                                                  RhtSigns sg, AmaxSink sink) {
   __shared__ RhtStage stage[4];
   RhtStage& st = stage[threadIdx.x >> 6];
   u32x4 frag[8], nfrag[8];
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (lane == 0) wm[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0)
-    atomic_max_nonneg(amax, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])) * kRhtScale);
+    post_amax(sink, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])) * kRhtScale);
 }
 
 // ---------------------------------------------------------------------------
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ---------------------------------------------------------------------------
 template <bool SR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_nvfp4_col(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                       RhtSigns sg, const float* __restrict__ amax,
+                                                       RhtSigns sg, AmaxSource amax,
                                                        float* __restrict__ tensor_scale, uint8_t* __restrict__ ccodes,
                                                        uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
   __shared__ RhtStage stage[4];
@@ -277,8 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   RhtStage& st = stage[threadIdx.x >> 6];
   fill_recip_table(rtab);
   __syncthreads();
-  const float gs = tensor_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = gs;
+  const float gs = tensor_scale_publish(amax, tensor_scale);
   u32x4 frag[8], nfrag[8];
   make_fragments(sg, true, frag, nfrag);
   const TileIter it(rows, cols);
@@ -439,14 +438,14 @@ void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint
   }
 }
 
-void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], float* amax,
+void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], const AmaxSink& sink,
                      hipStream_t st) {
-  k_zero1_rht<<<1, 1, 0, st>>>(amax);
-  k_rht_amax<<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, pack_signs(signs), amax);
+  if (!sink.slot) k_zero1_rht<<<1, 1, 0, st>>>(sink.f);
+  k_rht_amax<<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, pack_signs(signs), sink);
 }
 
 void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], bool sr,
-                          uint64_t seed, const float* amax, float* tensor_scale, uint8_t* col_codes,
+                          uint64_t seed, const AmaxSource& amax, float* tensor_scale, uint8_t* col_codes,
                           uint8_t* col_scales, hipStream_t st) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const RhtSigns sg = pack_signs(signs);

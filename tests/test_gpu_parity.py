@@ -537,6 +537,66 @@ def test_rht_full_wgrad_config_sampled():
 
 
 # ---------------------------------------------------------------------------------------
+# Two-pass calls: amax computed by a separate pass, or given by the caller
+# ---------------------------------------------------------------------------------------
+
+def _same_outputs(a: dict, b: dict):
+    for k, v in a.items():
+        if v is None or k == "amax":
+            continue
+        assert np.array_equal(host(v), host(b[k])), k
+
+
+def test_given_amax_reproduces_computed_amax():
+    """Each two-pass entry point, called with the amax its compute mode reported,
+    produces the same tensor scale, codes and scales; the compute mode's amax is the
+    exact maximum."""
+    bits = si.if4_mix(256, 512, seed=31)
+    xd = dev_bf16(bits)
+    xf = dev_f32(si.bf16_bits_to_f32(bits))
+    ref_amax = np.float32(np.max(np.abs(si.bf16_bits_to_f32(bits))))
+    # 16x16 2D (fp32 and bf16) and IF4
+    for fn, args in ((B.quantize_nvfp4_2d, (xf,)), (B.quantize_nvfp4_2d, (xd,)), (B.quantize_if4, (xd,))):
+        c = fn(*args)
+        assert host(c["amax"])[0] == ref_amax
+        g = fn(*args, amax=c["amax"].clone())
+        _same_outputs(c, g)
+    # RHT + column-wise NVFP4 (SR)
+    signs = oracle.rht_signs(4).tolist()
+    c = B.quantize_nvfp4(xd, B.COLWISE, rnd=1, sr_seed=9, rht_signs=signs)
+    assert host(c["amax"])[0] == host(B.rht(xd, signs).abs().max().reshape(1))[0]
+    g = B.quantize_nvfp4(xd, B.COLWISE, rnd=1, sr_seed=9, rht_signs=signs, amax=c["amax"].clone())
+    _same_outputs(c, g)
+
+
+def test_two_pass_amax_does_not_leak_between_calls():
+    """Two-pass calls on one stream share a workspace word: a call on a tensor with a
+    small amax right after one with a large amax, through different entry points,
+    still reports and uses its own amax."""
+    big = si.if4_mix(256, 512, seed=32)
+    small = si.f32_to_bf16_bits(si.bf16_bits_to_f32(big) * np.float32(1.0 / 1024.0))
+    amax_big = np.float32(np.max(np.abs(si.bf16_bits_to_f32(big))))
+    amax_small = np.float32(np.max(np.abs(si.bf16_bits_to_f32(small))))
+    assert amax_small < amax_big
+    signs = oracle.rht_signs(4).tolist()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            a = B.quantize_if4(dev_bf16(big), stream=s)
+            b = B.quantize_nvfp4_2d(dev_bf16(small), stream=s)
+            c = B.quantize_if4(dev_bf16(small), stream=s)
+            d = B.quantize_nvfp4(dev_bf16(big), B.COLWISE, rht_signs=signs, stream=s)
+            e = B.quantize_nvfp4(dev_bf16(small), B.COLWISE, rht_signs=signs, stream=s)
+    s.synchronize()
+    assert host(a["amax"])[0] == amax_big
+    assert host(b["amax"])[0] == amax_small and host(c["amax"])[0] == amax_small
+    assert host(e["amax"])[0] < host(d["amax"])[0]
+    assert host(b["tensor_scale"])[0] == np.float32(oracle.tensor_scale(float(amax_small)))
+    c_ref, s_ref, _ = oracle.quantize_if4(small)
+    assert np.array_equal(host(c["codes"]), c_ref) and np.array_equal(host(c["scales"]), s_ref)
+
+
+# ---------------------------------------------------------------------------------------
 # Streams, determinism, guard bytes
 # ---------------------------------------------------------------------------------------
 
