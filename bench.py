@@ -116,6 +116,11 @@ class ActivationNVFP4(Workload):
     def kernel_launch(self, i):
         self._call(i, self.B.AMAX_COMPUTE)
 
+    def given_launch(self, i):
+        # the same call with the tensor amax supplied (AMAX_GIVEN): the streaming tile
+        # kernel alone; the amax buffers hold the values a compute-mode call wrote
+        self._call(i, self.B.AMAX_GIVEN)
+
     def cpu_baseline(self, budget_s):
         import numpy as np
         import oracle
@@ -393,6 +398,31 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
                      "kernel_ms_mean": k_mean, "kernel_launches_timed": nk,
                      "algorithmic_bytes_per_launch": wl.kernel_bytes},
     }
+    # distribution of single steps: a separate pass, each step between its own events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        wl.step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    st = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: st[min(len(st) - 1, int(q * (len(st) - 1) + 0.5))]
+    line["config"]["step_ms_p10"], line["config"]["step_ms_p50"], line["config"]["step_ms_p90"] = (
+        pick(0.1), pick(0.5), pick(0.9))
+    # the call with the tensor amax given by the caller (no amax pass)
+    given = getattr(wl, "given_launch", wl.kernel_launch)
+    for i in range(4):
+        wl.step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(nk):
+        given(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    g_ms = e0.elapsed_time(e1) / nk
+    line["config"]["amax_given_ms"] = g_ms
+    line["config"]["amax_given_GBps"] = wl.kernel_bytes / (g_ms * 1e-3) / 1e9
     if isinstance(wl, WgradRHT):
         flops = 2 * 128 * (wl.rows * wl.cols)            # dense 128x128 contraction over one operand
         line["roofline"]["mfma_tflops_in_kernel"] = flops / (k_mean * 1e-3) / 1e12
