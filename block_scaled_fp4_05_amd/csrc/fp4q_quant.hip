@@ -646,15 +646,12 @@ void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned
 // left by earlier launches never match.
 //
 // Workgroups form 8 groups, g = b % 8, and workgroup g leads group g: members post
-// their slots, the leader combines them and posts the group maximum, the eight
-// leaders read each other's group maxima, and each leader hands the result to its
-// members through one mailbox word per member.  No line is polled by more than 16
-// workgroups, so the polls do not queue behind each other.  All of it is
-// device-scope traffic, so no step relies on where a workgroup runs.
+// their slots, the leader combines them and posts the group maximum, and every
+// workgroup reads the eight group maxima.  All of it is device-scope traffic, so no
+// step relies on where a workgroup runs.
 struct FusedWs {
   uint64_t local[8][kFusedMaxWg / 8 + 16];   // per group: members' slots
   uint64_t group[8][16];                      // per group: its maximum, device scope
-  uint64_t mail[8][kFusedMaxWg / 8 + 16];    // per group: the grid maximum, per member
   uint32_t fallbacks[32];                     // waits that ran out and were answered from x
   uint64_t amax_slot[16];                     // two-pass calls: (epoch << 32) | amax bits, by atomic max
 };
@@ -745,15 +742,14 @@ __device__ __forceinline__ void read_miss(const GridMaxShared& sh, uint32_t (&w)
 
 // Grid-wide maximum of the workgroups' values v (thread 0's copy), returned to every
 // thread.  Members post their slot in the group area; leader g collects the group's
-// slots, posts the group maximum, reads the eight group maxima and writes the grid
-// maximum into each member's mailbox; members wait on their own mailbox only.
+// slots and posts the group maximum; every workgroup then reads the eight group
+// maxima itself (eight lines, polled by eight lanes).
 //
 // No wait depends on other workgroups making progress for correctness: a slot that
 // has not arrived after `wait_iters` polls is computed from x by the waiting
-// workgroup itself (one workgroup's tiles, or a group's band), and a member whose
-// mailbox stays empty reads the group maxima itself, with the same fallback.  With
-// the whole grid resident, which the launch size is chosen for, no fallback runs;
-// without it, the grid still finishes with the exact maximum.
+// workgroup itself (one workgroup's tiles, or a group's band).  With the whole grid
+// resident, which the launch size is chosen for, no fallback runs; without it, the
+// grid still finishes with the exact maximum.
 template <typename T>
 __device__ __forceinline__ float all_groups_max(FusedWs* ws, uint32_t epoch, uint32_t wait_iters,
                                                 const T* __restrict__ x, int rows, int cols, int tiles_r,
@@ -787,7 +783,6 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
   const int tid = threadIdx.x;
   const int total = tiles_r * tiles_c, per = (total + 7) >> 3;
   uint64_t* local = ws->local[g];
-  uint64_t* mail = ws->mail[g];
   if (tid < 8) sh.miss[tid] = 0u;
   if (tid == 0 && b >= 8)
     __hip_atomic_store(&local[b >> 3], pack_epoch(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -817,22 +812,7 @@ __device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, 
     m = block_max256(m, sh.red);
     if (tid == 0)
       __hip_atomic_store(&ws->group[g][0], pack_epoch(epoch, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float gmax = all_groups_max<T>(ws, epoch, wait_iters, x, rows, cols, tiles_r, tiles_c, sh);
-    for (int j = 1 + tid; j < ng; j += 256)
-      __hip_atomic_store(&mail[j], pack_epoch(epoch, gmax), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return gmax;
   }
-  if (tid == 0) {
-    float u;
-    const bool got = poll_slot(&mail[b >> 3], epoch, wait_iters, &u);
-    sh.val = u;
-    sh.miss[0] = got ? 0u : 1u;
-  }
-  __syncthreads();
-  const bool got = sh.miss[0] == 0u;
-  const float r = sh.val;
-  __syncthreads();                                    // everyone has read sh before it is reused
-  if (got) return r;
   return all_groups_max<T>(ws, epoch, wait_iters, x, rows, cols, tiles_r, tiles_c, sh);
 }
 

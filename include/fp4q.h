@@ -21,7 +21,7 @@
  *    tensor_scale pointers 4-byte aligned (FP4Q_E_ALIGN otherwise).
  *  - Inputs and outputs must not overlap.  The caller allocates every buffer and
  *    keeps it alive until the work on `stream` has completed.  The only memory the
- *    library owns is a small per-(device, stream) workspace (about 36 KB) used by the
+ *    library owns is a small per-(device, stream) workspace (about 18 KB) used by the
  *    calls that compute a tensor amax (the one-pass NVFP4 kernel's exchange, and the
  *    word a separate amax pass posts into for the quantizer that follows it),
  *    allocated on the first such call on that stream and kept until the process ends;
