@@ -1091,7 +1091,7 @@ void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr,
 }
 
 // ===========================================================================
-// IF4: flat kernel, one lane per 16-element row block.
+// IF4: flat kernel, one lane per 16-element row block (four blocks per lane).
 // ===========================================================================
 
 // Eight E2M1 nibbles -> values times 2^exponent(scale) (exact).
@@ -1129,46 +1129,64 @@ __device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[
   return __builtin_amdgcn_bitop3_b32(ev, od << 4, 0x0F0F0F0Fu, 0xE4);   // (ev & m) | (od<<4 & ~m)
 }
 
+// Each lane takes kIf4Blocks blocks, one from each of the workgroup's consecutive
+// 256-block chunks (so every load instruction stays contiguous across the wave); all
+// their loads are issued before any block is encoded, and the per-launch work (tensor
+// scale, reciprocal table) is shared by the four.
+constexpr int kIf4Blocks = 4;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n16, AmaxSource amax,
                                              float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
                                              uint8_t* __restrict__ scales) {
+  __shared__ RecipTable rtab;
+  fill_recip_table(rtab);
+  __syncthreads();
   const float gs = tensor_scale_publish(amax, tensor_scale);
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= n16) return;
-  float a[8], b[8];
-  load8(x, g * 16, a);
-  load8(x, g * 16 + 8, b);
-  float m = 0.0f;
+  const int64_t g0 = (int64_t)blockIdx.x * (256 * kIf4Blocks) + threadIdx.x;
+  float a[kIf4Blocks][8], b[kIf4Blocks][8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    a[k] = a[k] * gs;
-    b[k] = b[k] * gs;
-    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])));
+  for (int j = 0; j < kIf4Blocks; ++j) {
+    const int64_t g = min(g0 + 256 * j, n16 - 1);   // past the end: reload the last block, not stored
+    load8(x, g * 16, a[j]);
+    load8(x, g * 16 + 8, b[j]);
   }
-  const uint32_t sc = nvfp4_scale_code(m);
-  const RecipPair rp = recip_pair_code(sc);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    a[k] = div2(a[k], rp);
-    b[k] = div2(b[k], rp);
+  for (int j = 0; j < kIf4Blocks; ++j) {
+    const int64_t g = g0 + 256 * j;
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[j][k] = a[j][k] * gs;
+      b[j][k] = b[j][k] * gs;
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[j][k]), __builtin_fabsf(b[j][k])));
+    }
+    const uint32_t sc = nvfp4_scale_code(m);
+    const RecipPair rp = rtab.r[sc];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[j][k] = div2(a[j][k], rp);
+      b[j][k] = div2(b[j][k], rp);
+    }
+    const uint32_t fa = pack8_rtn(a[j], 1.0f), fb = pack8_rtn(b[j], 1.0f);
+    float ra[8], rb[8];
+    decode8_fp4(fa, 1.0f, ra);
+    decode8_fp4(fb, 1.0f, rb);
+    float e_fp = 0.0f, e_int = 0.0f;
+    const uint32_t ia = if4_block8(a[j], ra, e_fp, e_int);
+    const uint32_t ib = if4_block8(b[j], rb, e_fp, e_int);
+    const bool use_int = e_int < e_fp;
+    if (g < n16) {
+      *reinterpret_cast<uint2*>(codes + g * 8) = use_int ? make_uint2(ia, ib) : make_uint2(fa, fb);
+      scales[g] = (uint8_t)(sc | (use_int ? 0x80u : 0u));
+    }
   }
-  const uint32_t fa = pack8_rtn(a, 1.0f), fb = pack8_rtn(b, 1.0f);
-  float ra[8], rb[8];
-  decode8_fp4(fa, 1.0f, ra);
-  decode8_fp4(fb, 1.0f, rb);
-  float e_fp = 0.0f, e_int = 0.0f;
-  const uint32_t ia = if4_block8(a, ra, e_fp, e_int);
-  const uint32_t ib = if4_block8(b, rb, e_fp, e_int);
-  const bool use_int = e_int < e_fp;
-  *reinterpret_cast<uint2*>(codes + g * 8) = use_int ? make_uint2(ia, ib) : make_uint2(fa, fb);
-  scales[g] = (uint8_t)(sc | (use_int ? 0x80u : 0u));
 }
 
 void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax, float* tensor_scale,
                 uint8_t* codes, uint8_t* scales, hipStream_t st) {
   const int64_t n16 = rows * cols / 16;
-  const int grid = (int)((n16 + 255) / 256);
+  const int grid = (int)((n16 + 256 * kIf4Blocks - 1) / (256 * kIf4Blocks));
   if (dtype == 1)
     k_if4<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, amax, tensor_scale, codes, scales);
   else
