@@ -1209,69 +1209,88 @@ __device__ __forceinline__ float max16_lanes(float v) {
   return __uint_as_float(u);
 }
 
+// A workgroup takes k2dSteps consecutive runs of 16 tiles (each wave four
+// horizontally adjacent tiles per run); all of a lane's row loads are issued before
+// any tile is encoded.
+constexpr int k2dSteps = 4;
+
 template <typename T, bool TRANS>
 __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                   AmaxSource amax, float* __restrict__ tensor_scale,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                   uint8_t* __restrict__ codes_t) {
-  __shared__ uint32_t lds[16][16][2];   // [tile in block][row][8 bytes]
+  __shared__ uint32_t lds[k2dSteps][16][16][2];   // [run][tile in run][row][8 bytes]
+  __shared__ RecipTable rtab;
+  fill_recip_table(rtab);
+  __syncthreads();
   const float gs = tensor_scale_publish(amax, tensor_scale);
   const int64_t tiles_c = cols >> 4, tiles = (rows >> 4) * tiles_c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tin = lane >> 4, i = lane & 15;                 // tile within wave, row within tile
-  const int64_t tile = ((int64_t)blockIdx.x * 4 + wave) * 4 + tin;
-  const bool ok = tile < tiles;
-  const int64_t br = ok ? tile / tiles_c : 0, bc = ok ? tile - br * tiles_c : 0;
-  const int64_t r = br * 16 + i, c0 = bc * 16;
-  float a[8], b[8];
-  if (ok) {
-    load8(x, r * cols + c0, a);
-    load8(x, r * cols + c0 + 8, b);
-  } else {
+  float a[k2dSteps][8], b[k2dSteps][8];
+  int64_t br[k2dSteps], bc[k2dSteps];
+  bool ok[k2dSteps];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] = b[k] = 0.0f;
+  for (int j = 0; j < k2dSteps; ++j) {
+    const int64_t tile = ((int64_t)blockIdx.x * k2dSteps + j) * 16 + wave * 4 + tin;
+    ok[j] = tile < tiles;
+    const int64_t t = ok[j] ? tile : tiles - 1;            // past the end: reload the last tile
+    br[j] = t / tiles_c;
+    bc[j] = t - br[j] * tiles_c;
+    const int64_t r = br[j] * 16 + i, c0 = bc[j] * 16;
+    load8(x, r * cols + c0, a[j]);
+    load8(x, r * cols + c0 + 8, b[j]);
   }
-  float m = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    a[k] = a[k] * gs;
-    b[k] = b[k] * gs;
-    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[k]), __builtin_fabsf(b[k])));
-  }
-  m = max16_lanes(m);
-  const uint32_t sc = nvfp4_scale_code(m);
-  const RecipPair rp = recip_pair_code(sc);
+  for (int j = 0; j < k2dSteps; ++j) {
+    float m = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    a[k] = div2(a[k], rp);
-    b[k] = div2(b[k], rp);
-  }
-  const uint32_t w0 = pack8_rtn(a, 1.0f), w1 = pack8_rtn(b, 1.0f);
-  if (ok) {
-    *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c0 >> 1)) = make_uint2(w0, w1);
-    if (i == 0) scales[br * tiles_c + bc] = (uint8_t)sc;
+    for (int k = 0; k < 8; ++k) {
+      a[j][k] = a[j][k] * gs;
+      b[j][k] = b[j][k] * gs;
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[j][k]), __builtin_fabsf(b[j][k])));
+    }
+    m = max16_lanes(m);
+    const uint32_t sc = nvfp4_scale_code(m);
+    const RecipPair rp = rtab.r[sc];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[j][k] = div2(a[j][k], rp);
+      b[j][k] = div2(b[j][k], rp);
+    }
+    const uint32_t w0 = pack8_rtn(a[j], 1.0f), w1 = pack8_rtn(b[j], 1.0f);
+    const int64_t r = br[j] * 16 + i, c0 = bc[j] * 16;
+    if (ok[j]) {
+      *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c0 >> 1)) = make_uint2(w0, w1);
+      if (i == 0) scales[br[j] * tiles_c + bc[j]] = (uint8_t)sc;
+    }
+    if constexpr (TRANS) {
+      lds[j][wave * 4 + tin][i][0] = w0;
+      lds[j][wave * 4 + tin][i][1] = w1;
+    }
   }
   if constexpr (TRANS) {
-    const int tb = wave * 4 + tin;
-    lds[tb][i][0] = w0;
-    lds[tb][i][1] = w1;
     __syncthreads();
     // lane i now gathers column i of its tile: nibble i of every row
-    uint32_t o0 = 0, o1 = 0;
-    const int word = i >> 3, sh = (i & 7) * 4;
+    const int tb = wave * 4 + tin, word = i >> 3, sh = (i & 7) * 4;
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      o0 |= ((lds[tb][rr][word] >> sh) & 0xFu) << (4 * rr);
-      o1 |= ((lds[tb][rr + 8][word] >> sh) & 0xFu) << (4 * rr);
+    for (int j = 0; j < k2dSteps; ++j) {
+      uint32_t o0 = 0, o1 = 0;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        o0 |= ((lds[j][tb][rr][word] >> sh) & 0xFu) << (4 * rr);
+        o1 |= ((lds[j][tb][rr + 8][word] >> sh) & 0xFu) << (4 * rr);
+      }
+      const int64_t c0 = bc[j] * 16;
+      if (ok[j]) *reinterpret_cast<uint2*>(codes_t + (c0 + i) * (rows >> 1) + (br[j] * 16 >> 1)) = make_uint2(o0, o1);
     }
-    if (ok) *reinterpret_cast<uint2*>(codes_t + (c0 + i) * (rows >> 1) + (br * 16 >> 1)) = make_uint2(o0, o1);
   }
 }
 
 void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax, float* tensor_scale,
                      uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st) {
   const int64_t tiles = (rows >> 4) * (cols >> 4);
-  const int grid = (int)((tiles + 15) / 16);
+  const int grid = (int)((tiles + 16 * k2dSteps - 1) / (16 * k2dSteps));
 #define FP4Q_2D(T, TR) k_nvfp4_2d<T, TR><<<grid, 256, 0, st>>>(static_cast<const T*>(x), rows, cols, amax, \
                                                               tensor_scale, codes, scales, codes_t)
   if (dtype == 1) { if (codes_t) FP4Q_2D(uint16_t, true); else FP4Q_2D(uint16_t, false); }
