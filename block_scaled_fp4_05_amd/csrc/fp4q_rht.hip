@@ -164,8 +164,39 @@ struct TileIter {
   }
 };
 
-__device__ __forceinline__ int64_t wave_id() { return ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; }
+// The wave's index in the grid, uniform (a scalar register) so that the tile
+// arithmetic below stays off the vector ALUs.
+__device__ __forceinline__ int64_t wave_id() {
+  return (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 __device__ __forceinline__ int64_t wave_count() { return ((int64_t)gridDim.x * blockDim.x) >> 6; }
+
+// A wave's tiles wave_id(), wave_id() + step, ... with (chunk, slab) advanced by a
+// fixed stride and one carry, so the loop divides only once.
+struct TileWalk {
+  int64_t nslab, ntiles, step, step_chunk, step_slab;
+  int64_t tile, chunk, slab;
+  __device__ TileWalk(int64_t rows, int64_t cols) {
+    nslab = (cols + 63) / 64;
+    ntiles = nslab * (rows / 128);
+    step = wave_count();
+    step_chunk = step / nslab;
+    step_slab = step - step_chunk * nslab;
+    tile = wave_id();
+    chunk = tile / nslab;
+    slab = tile - chunk * nslab;
+  }
+  __device__ bool valid() const { return tile < ntiles; }
+  __device__ void next() {
+    tile += step;
+    chunk += step_chunk;
+    slab += step_slab;
+    if (slab >= nslab) {
+      slab -= nslab;
+      ++chunk;
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Standalone transform (bf16 in, f32 out); inverse uses H without input signs
@@ -212,30 +243,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   RhtStage& st = stage[threadIdx.x >> 6];
   u32x4 frag[8], nfrag[8];
   make_fragments(sg, true, frag, nfrag);
-  const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63;
   float m = 0.0f;
-  int64_t tile = wave_id();
-  const int64_t step = wave_count();
-  if (tile < it.ntiles) {
-    int64_t chunk, slab;
-    it.decode(tile, chunk, slab);
-    rht_issue(x, cols, chunk * 128, slab * 64, st);
-  }
-  for (; tile < it.ntiles; tile += step) {
-    int64_t chunk, slab;
-    it.decode(tile, chunk, slab);
-    const int64_t colp = slab * 64 + 2 * (lane & 31);
+  TileWalk w(rows, cols);
+  if (w.valid()) rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
+  for (; w.valid(); w.next()) {
+    const int64_t colp = w.slab * 64 + 2 * (lane & 31);
     const bool valid = colp < cols;
     RhtRaw raw;
     rht_wait_loads();
     rht_read(st, raw);
     rht_wait_lds();
-    if (tile + step < it.ntiles) {
-      int64_t c2, s2;
-      it.decode(tile + step, c2, s2);
-      rht_issue(x, cols, c2 * 128, s2 * 64, st);
-    }
+    TileWalk nw = w;
+    nw.next();
+    if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
     float t = 0.0f;
     auto fold = [&](const f32x16 (&acc)[2][2]) {
 #pragma unroll
@@ -280,14 +301,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float gs = tensor_scale_publish(amax, tensor_scale);
   u32x4 frag[8], nfrag[8];
   make_fragments(sg, true, frag, nfrag);
-  const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63, hk = lane >> 5;
   const int64_t half_rows = rows >> 1, nb = rows >> 4;
   // The next tile streams into the wave's LDS buffer while this one, already read
   // into registers, is transformed and quantized.
-  auto process = [&](const RhtRaw& raw, int64_t tile) {
-    int64_t chunk, slab;
-    it.decode(tile, chunk, slab);
+  auto process = [&](const RhtRaw& raw, int64_t chunk, int64_t slab) {
     const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
     const bool valid = colp < cols;
     uint32_t scale_word[2] = {0u, 0u};
@@ -357,22 +375,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (valid) *reinterpret_cast<uint32_t*>(cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
     }
   };
-  auto issue = [&](int64_t tile) {
-    int64_t chunk, slab;
-    it.decode(tile, chunk, slab);
-    rht_issue(x, cols, chunk * 128, slab * 64, st);
-  };
-  int64_t tile = wave_id();
-  const int64_t step = wave_count();
-  if (tile >= it.ntiles) return;
-  issue(tile);
-  for (; tile < it.ntiles; tile += step) {
+  TileWalk w(rows, cols);
+  if (!w.valid()) return;
+  rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
+  for (; w.valid(); w.next()) {
     RhtRaw raw;
     rht_wait_loads();
     rht_read(st, raw);
     rht_wait_lds();
-    if (tile + step < it.ntiles) issue(tile + step);   // in flight while this tile is worked on
-    process(raw, tile);
+    TileWalk nw = w;
+    nw.next();
+    if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);   // in flight while this tile is worked on
+    process(raw, w.chunk, w.slab);
   }
 }
 
