@@ -288,6 +288,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Pass 2: column-wise NVFP4 (blocks of 16 tokens) of the transformed tensor.
 // After the permlane32 swaps each lane holds 16 consecutive tokens of one column.
 // ---------------------------------------------------------------------------
+// One operand of a column-wise pass: its tensor, shape, outputs, tensor scale and SR key.
+struct RhtColOp {
+  const uint16_t* x;
+  int64_t rows, cols;
+  uint8_t* ccodes;
+  uint8_t* cscales;
+  float gs;
+  uint32_t k0, k1;
+};
+
+// Transform and quantize one tile (tokens 128*chunk.., columns 64*slab..) whose raw
+// words are in registers.
+template <bool SR>
+__device__ __forceinline__ void rht_quant_tile(const RhtRaw& raw, int64_t chunk, int64_t slab, const RhtColOp& o,
+                                               const u32x4 (&frag)[8], const u32x4 (&nfrag)[8],
+                                               const RecipTable& rtab) {
+  const int lane = threadIdx.x & 63, hk = lane >> 5;
+  const int64_t half_rows = o.rows >> 1, nb = o.rows >> 4;
+  const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
+  const bool valid = colp < o.cols;
+  const float gs = o.gs;
+  uint32_t scale_word[2] = {0u, 0u};
+  // quantize the 16-token column blocks of output blocks a0 and a0 + 1
+  auto quantize = [&](f32x16 (&acc)[2][2], int a0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap) {
+        const int a = a0 + ap;
+        // regroup: lanes < 32 take rows 0..15 of block a, lanes >= 32 rows 16..31
+        float t[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][j]),
+                                                      __float_as_uint(acc[p][ap][8 + j]), false, false);
+          auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][4 + j]),
+                                                      __float_as_uint(acc[p][ap][12 + j]), false, false);
+          t[j] = __uint_as_float(s02[0]);
+          t[4 + j] = __uint_as_float(s02[1]);
+          t[8 + j] = __uint_as_float(s13[0]);
+          t[12 + j] = __uint_as_float(s13[1]);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          t[k] = (t[k] * kRhtScale) * gs;
+          m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
+        }
+        const uint32_t sc = nvfp4_scale_code(m);
+        const RecipPair rp = rtab.r[sc];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
+        const int64_t c = colp + p;
+        const int64_t tok = tok0 + 32 * a + 16 * hk;
+        uint32_t w0, w1;
+        if constexpr (SR) {
+          uint32_t r0[8], r1[8];
+          const uint64_t idx8 = (uint64_t)(c * o.rows + tok) >> 3;
+          sr_draws8(idx8, 1u, o.k0, o.k1, r0);
+          sr_draws8(idx8 + 1, 1u, o.k0, o.k1, r1);
+          w0 = pack8_sr(t, r0, 1.0f);
+          w1 = pack8_sr(t + 8, r1, 1.0f);
+        } else {
+          w0 = pack8_rtn(t, 1.0f);
+          w1 = pack8_rtn(t + 8, 1.0f);
+        }
+        if (valid) *reinterpret_cast<uint2*>(o.ccodes + c * half_rows + (tok >> 1)) = make_uint2(w0, w1);
+        scale_word[p] |= sc << (8 * a);
+      }
+  };
+  f32x16 acc[2][2];
+  rht_mma_half<0>(raw, frag, nfrag, acc);
+  quantize(acc, 0);
+  rht_mma_half<1>(raw, frag, nfrag, acc);
+  quantize(acc, 2);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    // lane < 32 holds blocks 0,2,4,6 of the chunk and lane >= 32 blocks 1,3,5,7;
+    // interleave so each lane stores four consecutive scale bytes.
+    auto sw = __builtin_amdgcn_permlane32_swap(scale_word[p], scale_word[p], false, false);
+    const uint32_t lo = hk ? sw[0] : scale_word[p];   // blocks 0,2,4,6
+    const uint32_t hi = hk ? scale_word[p] : sw[1];   // blocks 1,3,5,7
+    // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
+    const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
+    const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
+    if (valid) *reinterpret_cast<uint32_t*>(o.cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
+  }
+}
+
 template <bool SR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_nvfp4_col(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                        RhtSigns sg, AmaxSource amax,
@@ -298,83 +387,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   RhtStage& st = stage[threadIdx.x >> 6];
   fill_recip_table(rtab);
   __syncthreads();
-  const float gs = tensor_scale_publish(amax, tensor_scale);
+  const RhtColOp op{x, rows, cols, ccodes, cscales, tensor_scale_publish(amax, tensor_scale), k0, k1};
   u32x4 frag[8], nfrag[8];
   make_fragments(sg, true, frag, nfrag);
-  const int lane = threadIdx.x & 63, hk = lane >> 5;
-  const int64_t half_rows = rows >> 1, nb = rows >> 4;
   // The next tile streams into the wave's LDS buffer while this one, already read
   // into registers, is transformed and quantized.
-  auto process = [&](const RhtRaw& raw, int64_t chunk, int64_t slab) {
-    const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
-    const bool valid = colp < cols;
-    uint32_t scale_word[2] = {0u, 0u};
-    // quantize the 16-token column blocks of output blocks a0 and a0 + 1
-    auto quantize = [&](f32x16 (&acc)[2][2], int a0) {
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int ap = 0; ap < 2; ++ap) {
-          const int a = a0 + ap;
-          // regroup: lanes < 32 take rows 0..15 of block a, lanes >= 32 rows 16..31
-          float t[16];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][j]),
-                                                        __float_as_uint(acc[p][ap][8 + j]), false, false);
-            auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][4 + j]),
-                                                        __float_as_uint(acc[p][ap][12 + j]), false, false);
-            t[j] = __uint_as_float(s02[0]);
-            t[4 + j] = __uint_as_float(s02[1]);
-            t[8 + j] = __uint_as_float(s13[0]);
-            t[12 + j] = __uint_as_float(s13[1]);
-          }
-          float m = 0.0f;
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            t[k] = (t[k] * kRhtScale) * gs;
-            m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
-          }
-          const uint32_t sc = nvfp4_scale_code(m);
-          const RecipPair rp = rtab.r[sc];
-#pragma unroll
-          for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
-          const int64_t c = colp + p;
-          const int64_t tok = tok0 + 32 * a + 16 * hk;
-          uint32_t w0, w1;
-          if constexpr (SR) {
-            uint32_t r0[8], r1[8];
-            const uint64_t idx8 = (uint64_t)(c * rows + tok) >> 3;
-            sr_draws8(idx8, 1u, k0, k1, r0);
-            sr_draws8(idx8 + 1, 1u, k0, k1, r1);
-            w0 = pack8_sr(t, r0, 1.0f);
-            w1 = pack8_sr(t + 8, r1, 1.0f);
-          } else {
-            w0 = pack8_rtn(t, 1.0f);
-            w1 = pack8_rtn(t + 8, 1.0f);
-          }
-          if (valid) *reinterpret_cast<uint2*>(ccodes + c * half_rows + (tok >> 1)) = make_uint2(w0, w1);
-          scale_word[p] |= sc << (8 * a);
-        }
-    };
-    f32x16 acc[2][2];
-    rht_mma_half<0>(raw, frag, nfrag, acc);
-    quantize(acc, 0);
-    rht_mma_half<1>(raw, frag, nfrag, acc);
-    quantize(acc, 2);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      // lane < 32 holds blocks 0,2,4,6 of the chunk and lane >= 32 blocks 1,3,5,7;
-      // interleave so each lane stores four consecutive scale bytes.
-      auto sw = __builtin_amdgcn_permlane32_swap(scale_word[p], scale_word[p], false, false);
-      const uint32_t lo = hk ? sw[0] : scale_word[p];   // blocks 0,2,4,6
-      const uint32_t hi = hk ? scale_word[p] : sw[1];   // blocks 1,3,5,7
-      // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
-      const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
-      const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
-      if (valid) *reinterpret_cast<uint32_t*>(cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
-    }
-  };
   TileWalk w(rows, cols);
   if (!w.valid()) return;
   rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     TileWalk nw = w;
     nw.next();
     if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);   // in flight while this tile is worked on
-    process(raw, w.chunk, w.slab);
+    rht_quant_tile<SR>(raw, w.chunk, w.slab, op, frag, nfrag, rtab);
   }
 }
 
