@@ -6,17 +6,19 @@
 //
 // bf16 inputs run the contraction on MFMA (v_mfma_f32_32x32x16_bf16): the +-1
 // matrix K[i][t] = H[i][t] s_t is exact in bf16 and the sum is accumulated in fp32.
-// One wave owns a tile of 128 tokens x 64 columns; lane l loads a 2-column x 64-token
-// slice with 4-byte loads (lanes 0..31 read 128 contiguous bytes of a token row), all
-// issued before the first MFMA, and transposes it in registers (v_perm) into the B
-// operands, so no LDS is needed.  Sylvester H factors as H_128[32a+u][32b+w] = H_4[a][b] H_32[u][w]: the A
-// operand of a K-step only depends on the H_32 part (folded with the signs, kept in
-// registers for the wave's lifetime, with a negated copy), and the H_4 sign picks the
-// negated A operand for the output row-blocks that need it.
+// One wave owns a tile of 128 tokens x 64 columns.  The B operands (8 consecutive
+// tokens of one column per lane) come either from registers -- the standalone
+// transform loads a 2-column x 64-token slice per lane with 4-byte loads and pairs
+// the tokens with v_perm -- or, in the fused passes, from the tile staged in LDS by
+// direct loads and read back with transposing LDS reads (ds_read_b64_tr_b16).
+// Sylvester H factors as H_128[32a+u][32b+w] = H_4[a][b] H_32[u][w]: the A operand of
+// a K-step only depends on the H_32 part (folded with the signs, kept in registers for
+// the wave's lifetime, with a negated copy), and the H_4 sign picks the negated A
+// operand for the output row-blocks that need it.
 //
-// The same contraction routine feeds the standalone transform, the amax pass and
-// the fused column-wise NVFP4 pass, so all three see bitwise identical values
-// B = fl(acc * fl(1/sqrt(128))).
+// The standalone transform, the amax pass and the fused column-wise NVFP4 pass issue
+// the same MFMA sequence for every output element (only the column's MFMA slot
+// differs), so all three see bitwise identical values B = fl(acc * fl(1/sqrt(128))).
 #include "fp4q_dev.hpp"
 #include "fp4q_internal.hpp"
 
@@ -76,21 +78,25 @@ __device__ __forceinline__ void rht_load(const uint16_t* __restrict__ x, int64_t
 }
 
 // LDS staging for the fused passes.  A wave's tile (128 tokens x 64 columns of bf16,
-// 16 KB) goes from HBM to its own LDS buffer by 16 direct loads of 16 bytes per lane
-// (lane l of load i carries token 8i + l/8, columns 8(l%8)..+7, and lands at byte
-// 16 l of that load's 1 KB, so the buffer is the tile in row-major order).  No VGPR
-// holds the data in flight, so a wave keeps a whole tile in the air while it works
-// on the previous one, and two waves fit on each SIMD.  The wave then reads the same
-// 64 words per lane as rht_load from LDS.  Chunks past the last column read column
-// chunk 0 of the same token instead; only lanes whose results are discarded use them.
+// 16 KB) goes from HBM to its own LDS buffer by 16 direct loads of 16 bytes per lane:
+// lane l of load i lands at byte 16 l of that load's 1 KB, i.e. at token row
+// r = 8i + l/8, chunk position l%8 of the row's 128 bytes, and it carries the row's
+// column chunk (l%8) ^ swz(r) (8 columns).  No VGPR holds the data in flight, so a
+// wave keeps a whole tile in the air while it works on the previous one, and two
+// waves fit on each SIMD.  Chunks past the last column read column chunk 0 of the same
+// token instead; only lanes whose results are discarded use them.
 struct RhtStage {
   uint32_t w[128 * 32];
 };
 
+// Chunk swizzle of staged row r: it depends on r % 4 only, and it spreads the
+// transposed reads below over distinct LDS banks (with 32 or 64 banks).
+__device__ __forceinline__ uint32_t rht_swz(uint32_t r) { return ((r & 1u) * 3u) | (((r >> 1) & 1u) << 2); }
+
 __device__ __forceinline__ void rht_issue(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0, int64_t col0,
                                           RhtStage& st) {
   const int lane = threadIdx.x & 63;
-  const int64_t c = col0 + 8 * (lane & 7);
+  const int64_t c = col0 + 8 * ((lane & 7) ^ rht_swz((lane >> 3) & 3));
   const uint16_t* base = x + (tok0 + (lane >> 3)) * cols + (c < cols ? c : 0);
 #pragma unroll
   for (int i = 0; i < 16; ++i)
@@ -103,12 +109,39 @@ __device__ __forceinline__ void rht_issue(const uint16_t* __restrict__ x, int64_
 __device__ __forceinline__ void rht_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void rht_wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void rht_read(const RhtStage& st, RhtRaw& raw) {
-  const int lane = threadIdx.x & 63, n = lane & 31, hk = lane >> 5;
+// MFMA B operands of a staged tile, read transposed from LDS.  In the fused passes
+// MFMA column slot n of pass p is tile column 32p + n.  The B operand of K-step kk
+// holds, in lane (n, hk), tokens 16kk + 8hk + 0..7 of that column, two per dword.
+// ds_read_b64_tr_b16 hands output lane i of each 16-lane group element i%4 of the
+// 8-byte reads of source lanes i/4 + 4e (e = 0..3, one 16-bit element per e), so
+// source lane 4e + a reads token k0 + e, columns c0 + 4a..4a+3, and output lane i
+// receives tokens k0..k0+3 of column c0 + i: two such reads (k0 and k0 + 4) make one
+// operand.
+struct RhtB {
+  u32x4 b[8][2];   // [kk][p]
+};
+
+typedef short rht_v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void rht_read_b(const RhtStage& st, RhtB& B) {
+  const uint32_t lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15, e = j >> 2, a = j & 3;
+  const uint32_t hk = g >> 1, nb = g & 1, row = 8 * hk + e, f = rht_swz(e);
+  const char* base = reinterpret_cast<const char*>(st.w);
+  uint32_t off[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) off[p] = row * 128 + 16 * ((4 * p + 2 * nb + (a >> 1)) ^ f) + 8 * (a & 1);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) raw.v[kk][r] = st.w[(16 * kk + 8 * hk + r) * 32 + n];
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const rht_v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) rht_v4s*)(base + off[p] + kk * 2048 + h * 512));
+        const uint2 w = __builtin_bit_cast(uint2, v);
+        B.b[kk][p][2 * h] = w.x;
+        B.b[kk][p][2 * h + 1] = w.y;
+      }
 }
 
 // Half H of one tile from its raw words: acc[p][a'] is the 32x32 MFMA output block
@@ -131,6 +164,29 @@ __device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag
       b1[q] = __builtin_amdgcn_perm(raw.v[kk][2 * q + 1], raw.v[kk][2 * q], 0x07060302u);
     }
     const bf16x8 v0 = __builtin_bit_cast(bf16x8, b0), v1 = __builtin_bit_cast(bf16x8, b1);
+#pragma unroll
+    for (int ap = 0; ap < 2; ++ap) {
+      const int a = 2 * H + ap;
+      const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
+      const bf16x8 fa = __builtin_bit_cast(bf16x8, flip ? nfrag[kk] : frag[kk]);
+      acc[0][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][ap], 0, 0, 0);
+      acc[1][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][ap], 0, 0, 0);
+    }
+  }
+}
+
+// The same contraction from ready B operands (column slot n of pass p is tile column
+// 32p + n); per output element the MFMA sums are the same as above.
+template <int H>
+__device__ __forceinline__ void rht_mma_half_b(const RhtB& B, const u32x4 frag[8], const u32x4 nfrag[8],
+                                               f32x16 acc[2][2]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) acc[p][a] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 v0 = __builtin_bit_cast(bf16x8, B.b[kk][0]), v1 = __builtin_bit_cast(bf16x8, B.b[kk][1]);
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap) {
       const int a = 2 * H + ap;
@@ -248,30 +304,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   TileWalk w(rows, cols);
   if (w.valid()) rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
   for (; w.valid(); w.next()) {
-    const int64_t colp = w.slab * 64 + 2 * (lane & 31);
-    const bool valid = colp < cols;
-    RhtRaw raw;
+    const int64_t col = w.slab * 64 + (lane & 31);   // column of pass 0; pass 1 is col + 32
+    RhtB B;
     rht_wait_loads();
-    rht_read(st, raw);
+    rht_read_b(st, B);
     rht_wait_lds();
     TileWalk nw = w;
     nw.next();
     if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
-    float t = 0.0f;
+    float t[2] = {0.0f, 0.0f};
     auto fold = [&](const f32x16 (&acc)[2][2]) {
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t = __builtin_fmaxf(t, __builtin_fabsf(acc[p][a][r]));
+          for (int r = 0; r < 16; ++r) t[p] = __builtin_fmaxf(t[p], __builtin_fabsf(acc[p][a][r]));
     };
     f32x16 acc[2][2];
-    rht_mma_half<0>(raw, frag, nfrag, acc);
+    rht_mma_half_b<0>(B, frag, nfrag, acc);
     fold(acc);
-    rht_mma_half<1>(raw, frag, nfrag, acc);
+    rht_mma_half_b<1>(B, frag, nfrag, acc);
     fold(acc);
-    if (valid) m = __builtin_fmaxf(m, t);
+    if (col < cols) m = __builtin_fmaxf(m, t[0]);
+    if (col + 32 < cols) m = __builtin_fmaxf(m, t[1]);
   }
   // max |fl(acc*k)| = fl(max|acc| * k): scaling is monotone.  One atomic per
   // workgroup: same-address atomics serialize, so per-wave atomics would cost more
@@ -298,16 +354,20 @@ struct RhtColOp {
   uint32_t k0, k1;
 };
 
-// Transform and quantize one tile (tokens 128*chunk.., columns 64*slab..) whose raw
-// words are in registers.
+// Transform and quantize one tile (tokens 128*chunk.., columns 64*slab..) whose B
+// operands are in registers.  Lane (n, hk) quantizes columns 64*slab + n (pass 0) and
+// + 32 (pass 1).
 template <bool SR>
-__device__ __forceinline__ void rht_quant_tile(const RhtRaw& raw, int64_t chunk, int64_t slab, const RhtColOp& o,
+__device__ __forceinline__ void rht_quant_tile(const RhtB& B, int64_t chunk, int64_t slab, const RhtColOp& o,
                                                const u32x4 (&frag)[8], const u32x4 (&nfrag)[8],
                                                const RecipTable& rtab) {
   const int lane = threadIdx.x & 63, hk = lane >> 5;
   const int64_t half_rows = o.rows >> 1, nb = o.rows >> 4;
-  const int64_t tok0 = chunk * 128, colp = slab * 64 + 2 * (lane & 31);
-  const bool valid = colp < o.cols;
+  const int64_t tok0 = chunk * 128, col = slab * 64 + (lane & 31);
+  const bool valid[2] = {col < o.cols, col + 32 < o.cols};
+  // this lane's codes of pass p, block a: code_base[p] + 16 a (bytes)
+  uint8_t* const code_base0 = o.ccodes + col * half_rows + (tok0 >> 1) + 8 * hk;
+  uint8_t* const code_base[2] = {code_base0, code_base0 + 32 * half_rows};
   const float gs = o.gs;
   uint32_t scale_word[2] = {0u, 0u};
   // quantize the 16-token column blocks of output blocks a0 and a0 + 1
@@ -340,12 +400,10 @@ __device__ __forceinline__ void rht_quant_tile(const RhtRaw& raw, int64_t chunk,
         const RecipPair rp = rtab.r[sc];
 #pragma unroll
         for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
-        const int64_t c = colp + p;
-        const int64_t tok = tok0 + 32 * a + 16 * hk;
         uint32_t w0, w1;
         if constexpr (SR) {
           uint32_t r0[8], r1[8];
-          const uint64_t idx8 = (uint64_t)(c * o.rows + tok) >> 3;
+          const uint64_t idx8 = (uint64_t)((col + 32 * p) * o.rows + tok0 + 32 * a + 16 * hk) >> 3;
           sr_draws8(idx8, 1u, o.k0, o.k1, r0);
           sr_draws8(idx8 + 1, 1u, o.k0, o.k1, r1);
           w0 = pack8_sr(t, r0, 1.0f);
@@ -354,14 +412,14 @@ __device__ __forceinline__ void rht_quant_tile(const RhtRaw& raw, int64_t chunk,
           w0 = pack8_rtn(t, 1.0f);
           w1 = pack8_rtn(t + 8, 1.0f);
         }
-        if (valid) *reinterpret_cast<uint2*>(o.ccodes + c * half_rows + (tok >> 1)) = make_uint2(w0, w1);
+        if (valid[p]) *reinterpret_cast<uint2*>(code_base[p] + 16 * a) = make_uint2(w0, w1);
         scale_word[p] |= sc << (8 * a);
       }
   };
   f32x16 acc[2][2];
-  rht_mma_half<0>(raw, frag, nfrag, acc);
+  rht_mma_half_b<0>(B, frag, nfrag, acc);
   quantize(acc, 0);
-  rht_mma_half<1>(raw, frag, nfrag, acc);
+  rht_mma_half_b<1>(B, frag, nfrag, acc);
   quantize(acc, 2);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -373,7 +431,8 @@ __device__ __forceinline__ void rht_quant_tile(const RhtRaw& raw, int64_t chunk,
     // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
     const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
     const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
-    if (valid) *reinterpret_cast<uint32_t*>(o.cscales + (colp + p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
+    if (valid[p])
+      *reinterpret_cast<uint32_t*>(o.cscales + (col + 32 * p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
   }
 }
 
@@ -396,14 +455,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (!w.valid()) return;
   rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
   for (; w.valid(); w.next()) {
-    RhtRaw raw;
+    RhtB B;
     rht_wait_loads();
-    rht_read(st, raw);
+    rht_read_b(st, B);
     rht_wait_lds();
     TileWalk nw = w;
     nw.next();
     if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);   // in flight while this tile is worked on
-    rht_quant_tile<SR>(raw, w.chunk, w.slab, op, frag, nfrag, rtab);
+    rht_quant_tile<SR>(B, w.chunk, w.slab, op, frag, nfrag, rtab);
   }
 }
 
