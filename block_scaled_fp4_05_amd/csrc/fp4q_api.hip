@@ -104,7 +104,7 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
   if (rows <= 0 || cols <= 0) return FP4Q_E_SHAPE;
   if (row && cols % 16 != 0) return FP4Q_E_SHAPE;
   if (col && (rows % 16 != 0 || cols % 8 != 0)) return FP4Q_E_SHAPE;
-  if (rht_signs && rows % 128 != 0) return FP4Q_E_SHAPE;
+  if (rht_signs && (rows % 128 != 0 || cols >= (int64_t(1) << 27))) return FP4Q_E_SHAPE;
   if (!aligned16(x) || !aligned4(amax) || !aligned4(tensor_scale)) return FP4Q_E_ALIGN;
   if (row && (!aligned16(row_codes) || !aligned16(row_scales))) return FP4Q_E_ALIGN;
   if (col && (!aligned16(col_codes) || !aligned16(col_scales))) return FP4Q_E_ALIGN;

@@ -93,14 +93,19 @@ struct RhtStage {
 // transposed reads below over distinct LDS banks (with 32 or 64 banks).
 __device__ __forceinline__ uint32_t rht_swz(uint32_t r) { return ((r & 1u) * 3u) | (((r >> 1) & 1u) << 2); }
 
+// The address of load i is the uniform row base of tokens tok0 + 8i (scalar registers)
+// plus this lane's byte offset, which fits 32 bits because cols < 2^27 (checked by the
+// caller); with the buffer picked by a uniform wave index, the per-load address and
+// LDS base steps run on the scalar unit.
 __device__ __forceinline__ void rht_issue(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0, int64_t col0,
                                           RhtStage& st) {
-  const int lane = threadIdx.x & 63;
+  const uint32_t lane = threadIdx.x & 63;
   const int64_t c = col0 + 8 * ((lane & 7) ^ rht_swz((lane >> 3) & 3));
-  const uint16_t* base = x + (tok0 + (lane >> 3)) * cols + (c < cols ? c : 0);
+  const uint32_t off = 2u * ((lane >> 3) * (uint32_t)cols + (uint32_t)(c < cols ? c : 0));
+  const char* rows0 = reinterpret_cast<const char*>(x + tok0 * cols);
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    __builtin_amdgcn_global_load_lds(base + (int64_t)(8 * i) * cols, &st.w[i * 256], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rows0 + (int64_t)(16 * i) * cols + off, &st.w[i * 256], 16, 0, 0);
 }
 
 // The direct loads are invisible to the compiler's wait counting: wait for every
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                   RhtSigns sg, AmaxSink sink) {
   __shared__ RhtStage stage[4];
-  RhtStage& st = stage[threadIdx.x >> 6];
+  RhtStage& st = stage[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
   u32x4 frag[8], nfrag[8];
   make_fragments(sg, true, frag, nfrag);
   const int lane = threadIdx.x & 63;
@@ -370,8 +375,49 @@ __device__ __forceinline__ void rht_quant_tile(const RhtB& B, int64_t chunk, int
   uint8_t* const code_base[2] = {code_base0, code_base0 + 32 * half_rows};
   const float gs = o.gs;
   uint32_t scale_word[2] = {0u, 0u};
-  // quantize the 16-token column blocks of output blocks a0 and a0 + 1
-  auto quantize = [&](f32x16 (&acc)[2][2], int a0) {
+  // RTN: the lane keeps its 8 values of each of the two 16-token blocks of output block
+  // a (tokens 32a + 0..15: A, 16..31: B; registers 0..7 and 8..15) and trades three
+  // words with the lane 32 away instead of regrouping the values: the partial maxima,
+  // the scale codes and the packed codes.  Lane hk then owns block hk's outputs.
+  auto quantize_rtn = [&](f32x16 (&acc)[2][2], int a0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap) {
+        const int a = a0 + ap;
+        float t[16];
+        float mA = 0.0f, mB = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          t[k] = (acc[p][ap][k] * kRhtScale) * gs;
+          if (k < 8) mA = __builtin_fmaxf(mA, __builtin_fabsf(t[k]));
+          else mB = __builtin_fmaxf(mB, __builtin_fabsf(t[k]));
+        }
+        // lane hk = 0 receives the partner's A maximum, lane hk = 1 the partner's B one
+        auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mA), __float_as_uint(mB), false, false);
+        const float m = __builtin_fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));
+        const uint32_t sc = nvfp4_scale_code(m);   // scale of block hk
+        auto scs = __builtin_amdgcn_permlane32_swap(sc, sc, false, false);   // every lane: (code A, code B)
+        const RecipPair rpA = rtab.r[scs[0]], rpB = rtab.r[scs[1]];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          t[k] = div2(t[k], rpA);
+          t[8 + k] = div2(t[8 + k], rpB);
+        }
+        // nibbles of A: tokens 4hk + 0..3 then 8 + 4hk + 0..3; likewise for B
+        const uint32_t wA = pack8_rtn(t, 1.0f), wB = pack8_rtn(t + 8, 1.0f);
+        // lane hk = 0 now holds A's words of both halves, lane hk = 1 B's: the own
+        // block's tokens 0..3 / 8..11 in the first word, 4..7 / 12..15 in the second
+        auto wx = __builtin_amdgcn_permlane32_swap(wA, wB, false, false);
+        const uint32_t lo = __builtin_amdgcn_perm(wx[1], wx[0], 0x05040100u);   // tokens 0..7
+        const uint32_t hi = __builtin_amdgcn_perm(wx[1], wx[0], 0x07060302u);   // tokens 8..15
+        if (valid[p]) *reinterpret_cast<uint2*>(code_base[p] + 16 * a) = make_uint2(lo, hi);
+        scale_word[p] |= sc << (8 * a);
+      }
+  };
+  // SR: regroup so that each lane holds 16 consecutive tokens of one block, whose draws
+  // come from two Philox evaluations.
+  auto quantize_sr = [&](f32x16 (&acc)[2][2], int a0) {
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -418,9 +464,9 @@ __device__ __forceinline__ void rht_quant_tile(const RhtB& B, int64_t chunk, int
   };
   f32x16 acc[2][2];
   rht_mma_half_b<0>(B, frag, nfrag, acc);
-  quantize(acc, 0);
+  if constexpr (SR) quantize_sr(acc, 0); else quantize_rtn(acc, 0);
   rht_mma_half_b<1>(B, frag, nfrag, acc);
-  quantize(acc, 2);
+  if constexpr (SR) quantize_sr(acc, 2); else quantize_rtn(acc, 2);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     // lane < 32 holds blocks 0,2,4,6 of the chunk and lane >= 32 blocks 1,3,5,7;
@@ -443,7 +489,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                        uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
   __shared__ RhtStage stage[4];
   __shared__ RecipTable rtab;
-  RhtStage& st = stage[threadIdx.x >> 6];
+  RhtStage& st = stage[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
   fill_recip_table(rtab);
   __syncthreads();
   const RhtColOp op{x, rows, cols, ccodes, cscales, tensor_scale_publish(amax, tensor_scale), k0, k1};

@@ -87,8 +87,8 @@ typedef enum { FP4Q_FMT_NVFP4 = 0, FP4Q_FMT_NVFP4_2D = 1, FP4Q_FMT_MXFP4 = 2, FP
  *   rht_signs HOST pointer to 4 words (bit t of word t/32 set means sign -1) or NULL.
  *             Non-NULL applies the 128x128 random Hadamard transform along rows in
  *             chunks of 128 before quantizing [NV "ランダムアダマール変換"]; requires
- *             layouts == FP4Q_COLWISE and rows % 128 == 0.  The amax and gs are then
- *             those of the transformed matrix.
+ *             layouts == FP4Q_COLWISE, rows % 128 == 0 and cols < 2^27.  The amax and
+ *             gs are then those of the transformed matrix.
  *   amax, tensor_scale  device float[1] each.
  * Shapes: ROWWISE needs cols % 16 == 0; COLWISE needs rows % 16 == 0 and cols % 8 == 0.
  * SR uses stream 0 for the row-wise output and stream 1 for the column-wise output;

@@ -62,6 +62,8 @@ def _nv(**kw):
     (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, dt=B.F32), 4),  # RHT needs bf16
     (dict(rows=0), 2), (dict(cols=-16), 2), (dict(cols=40), 2), (dict(rows=40), 2),
     (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, rows=64), 2),   # rows % 128
+    (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, rows=128, cols=1 << 27), 2),   # RHT: cols < 2^27
+    (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, rows=128, cols=(1 << 27) - 8, x=MIS), 3),  # shape ok
     (dict(x=MIS), 3), (dict(row_codes=MIS), 3), (dict(col_scales=MIS), 3), (dict(amax=A2 + 2), 3),
 ])
 def test_nvfp4_validation(kw, status):
