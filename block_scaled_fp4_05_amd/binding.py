@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "fp4q_quantize_nvfp4": [_P, _I, _I64, _I64, _U, _I, _U64, _P, _U, _P, _P, _P, _P, _P, _P, _P],
             "fp4q_quantize_nvfp4_2d": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P],
-            "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P],
+            "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P, _P],
             "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P],
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
             "fp4q_dequantize": [_I, _P, _P, _P, _I64, _I64, _I, _P, _P],
@@ -121,9 +121,9 @@ def fp4q_quantize_nvfp4_2d(x, dt, rows, cols, amax_mode, amax, tensor_scale, cod
         _s(stream)))
 
 
-def fp4q_quantize_mxfp4(x, dt, rows, cols, rnd, sr_seed, codes, scales, stream=None) -> int:
+def fp4q_quantize_mxfp4(x, dt, rows, cols, rnd, sr_seed, codes, scales, amax=None, stream=None) -> int:
     return _check("fp4q_quantize_mxfp4", lib().fp4q_quantize_mxfp4(
-        _p(x), dt, rows, cols, rnd, sr_seed, _p(codes), _p(scales), _s(stream)))
+        _p(x), dt, rows, cols, rnd, sr_seed, _p(codes), _p(scales), _p(amax), _s(stream)))
 
 
 def fp4q_quantize_if4(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, scales, stream=None) -> int:
@@ -218,11 +218,14 @@ def quantize_nvfp4_2d(x: torch.Tensor, transposed: bool = False, amax: torch.Ten
     return out
 
 
-def quantize_mxfp4(x: torch.Tensor, rnd: int = RTN, sr_seed: int = 0, stream=None) -> dict:
+def quantize_mxfp4(x: torch.Tensor, rnd: int = RTN, sr_seed: int = 0, with_amax: bool = False,
+                   stream=None) -> dict:
     rows, cols = x.shape
     dev = x.device
     out = {"codes": _u8(rows, cols // 2, device=dev), "scales": _u8(rows, cols // 32, device=dev)}
-    fp4q_quantize_mxfp4(x, _dt(x), rows, cols, rnd, sr_seed, out["codes"], out["scales"], stream)
+    if with_amax:
+        out["amax"] = torch.empty(1, dtype=torch.float32, device=dev)
+    fp4q_quantize_mxfp4(x, _dt(x), rows, cols, rnd, sr_seed, out["codes"], out["scales"], out.get("amax"), stream)
     return out
 
 

@@ -150,12 +150,14 @@ fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, i
 }
 
 fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, fp4q_round rnd,
-                                uint64_t sr_seed, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                                uint64_t sr_seed, uint8_t* codes, uint8_t* scales, float* amax,
+                                hipStream_t stream) {
   if (!x || !codes || !scales) return FP4Q_E_NULL;
   if (!valid_dtype(dt) || !valid_round(rnd)) return FP4Q_E_ARG;
   if (rows <= 0 || cols <= 0 || cols % 32 != 0) return FP4Q_E_SHAPE;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FP4Q_E_ALIGN;
-  fp4q::launch_mxfp4(x, dt, rows, cols, rnd == FP4Q_SR, codes, scales, sr_seed, stream);
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (amax && !aligned4(amax))) return FP4Q_E_ALIGN;
+  if (!fp4q::launch_mxfp4(x, dt, rows, cols, rnd == FP4Q_SR, codes, scales, sr_seed, amax, stream))
+    return FP4Q_E_HIP;
   return after_launch();
 }
 

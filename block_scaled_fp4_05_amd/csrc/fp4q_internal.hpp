@@ -41,12 +41,16 @@ bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, un
 void set_fused_wait_us(uint32_t us);
 bool fused_fallbacks(hipStream_t st, uint32_t* count);
 constexpr int kFusedMaxWg = 2048;
+constexpr int kAmaxSpread = 128;   // cache lines an amax-reporting pass spreads its posts over
 
 void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                      float* tensor_scale, uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st);
 
-void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
-                  uint8_t* scales, uint64_t seed, hipStream_t st);
+// amax: NULL, or a device float that receives max|x| over the tensor (a second,
+// one-workgroup launch folds the workgroups' spread posts).  False if the per-stream
+// workspace could not be set up (nothing launched then).
+bool launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
+                  uint8_t* scales, uint64_t seed, float* amax, hipStream_t st);
 
 void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                 float* tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t st);

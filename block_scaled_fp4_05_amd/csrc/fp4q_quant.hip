@@ -654,6 +654,7 @@ struct FusedWs {
   uint64_t group[8][16];                      // per group: its maximum, device scope
   uint32_t fallbacks[32];                     // waits that ran out and were answered from x
   uint64_t amax_slot[16];                     // two-pass calls: (epoch << 32) | amax bits, by atomic max
+  uint64_t spread[kAmaxSpread][16];           // MXFP4 amax: (epoch << 32) | magnitude bits, one line each
 };
 
 __device__ __forceinline__ float raw_absmax(const Raw8x8<uint16_t>& raw) {
@@ -1016,6 +1017,14 @@ bool reserve_amax_slot(hipStream_t st, uint64_t** slot, uint32_t* epoch) {
   return true;
 }
 
+bool reserve_amax_spread(hipStream_t st, uint64_t** slots, uint32_t* epoch) {
+  Launch l;
+  if (!reserve_launch(st, &l)) return false;
+  *slots = &l.ws->spread[0][0];
+  *epoch = l.epoch;
+  return true;
+}
+
 void set_fused_wait_us(uint32_t us) {
   const uint64_t t = (uint64_t)us * 10u;   // one poll round takes at least ~0.1 us
   g_wait_iters.store(t > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)t);
@@ -1038,10 +1047,15 @@ bool fused_fallbacks(hipStream_t st, uint32_t* count) {
 // the pair (lane ^ 1) shares the block maximum.
 // ===========================================================================
 
-template <typename T, bool SR>
+// AMAX: the workgroup also posts max|x| over its elements (magnitude bits compared as
+// integers, so a NaN wins as it does in the amax pass) into spread slot b % kAmaxSpread,
+// tagged with the launch's epoch; k_spread_max folds the slots afterwards.  Spreading
+// the posts over kAmaxSpread cache lines keeps same-address atomics from queueing.
+template <typename T, bool SR, bool AMAX>
 __global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t n16,
                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                               uint32_t k0, uint32_t k1) {
+                                               uint32_t k0, uint32_t k1, uint64_t* __restrict__ spread,
+                                               uint32_t epoch) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-element group
   const bool ok = g < n16;
   float a[8], b[8];
@@ -1051,6 +1065,21 @@ __global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t 
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) a[k] = b[k] = 0.0f;
+  }
+  if constexpr (AMAX) {
+    __shared__ uint32_t wm[4];
+    uint32_t mb = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      mb = max(mb, max(__float_as_uint(a[k]) & 0x7FFFFFFFu, __float_as_uint(b[k]) & 0x7FFFFFFFu));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mb;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_max(&spread[(blockIdx.x % kAmaxSpread) * 16],
+                             ((uint64_t)epoch << 32) | max(max(wm[0], wm[1]), max(wm[2], wm[3])), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
   float m = 0.0f;
 #pragma unroll
@@ -1076,18 +1105,43 @@ __global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t 
   }
 }
 
-void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
-                  uint8_t* scales, uint64_t seed, hipStream_t st) {
+// The tensor amax from the spread slots of launch `epoch` (slots this launch did not
+// reach hold an older epoch and count as 0).
+__global__ __launch_bounds__(256) void k_spread_max(const uint64_t* __restrict__ spread, uint32_t epoch,
+                                                    float* __restrict__ amax) {
+  __shared__ uint32_t wm[4];
+  uint32_t mb = 0;
+  for (int i = threadIdx.x; i < kAmaxSpread; i += 256) {
+    const uint64_t w = __hip_atomic_load(&spread[i * 16], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == epoch) mb = max(mb, (uint32_t)w);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mb;
+  __syncthreads();
+  if (threadIdx.x == 0) *amax = __uint_as_float(max(max(wm[0], wm[1]), max(wm[2], wm[3])));
+}
+
+bool launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
+                  uint8_t* scales, uint64_t seed, float* amax, hipStream_t st) {
   const int64_t n16 = rows * cols / 16;
   const int grid = (int)((n16 + 255) / 256);
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  uint64_t* spread = nullptr;
+  uint32_t epoch = 0;
+  if (amax && !reserve_amax_spread(st, &spread, &epoch)) return false;
+#define FP4Q_MX(TY, S, A) \
+  k_mxfp4<TY, S, A><<<grid, 256, 0, st>>>(static_cast<const TY*>(x), n16, codes, scales, k0, k1, spread, epoch)
   if (dtype == 1) {
-    if (sr) k_mxfp4<uint16_t, true><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, codes, scales, k0, k1);
-    else k_mxfp4<uint16_t, false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, codes, scales, k0, k1);
+    if (amax) { if (sr) FP4Q_MX(uint16_t, true, true); else FP4Q_MX(uint16_t, false, true); }
+    else      { if (sr) FP4Q_MX(uint16_t, true, false); else FP4Q_MX(uint16_t, false, false); }
   } else {
-    if (sr) k_mxfp4<float, true><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, codes, scales, k0, k1);
-    else k_mxfp4<float, false><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, codes, scales, k0, k1);
+    if (amax) { if (sr) FP4Q_MX(float, true, true); else FP4Q_MX(float, false, true); }
+    else      { if (sr) FP4Q_MX(float, true, false); else FP4Q_MX(float, false, false); }
   }
+#undef FP4Q_MX
+  if (amax) k_spread_max<<<1, 256, 0, st>>>(spread, epoch, amax);
+  return true;
 }
 
 // ===========================================================================

@@ -21,11 +21,12 @@
  *    tensor_scale pointers 4-byte aligned (FP4Q_E_ALIGN otherwise).
  *  - Inputs and outputs must not overlap.  The caller allocates every buffer and
  *    keeps it alive until the work on `stream` has completed.  The only memory the
- *    library owns is a small per-(device, stream) workspace (about 18 KB) used by the
- *    calls that compute a tensor amax (the one-pass NVFP4 kernel's exchange, and the
- *    word a separate amax pass posts into for the quantizer that follows it),
- *    allocated on the first such call on that stream and kept until the process ends;
- *    that first call is therefore not graph-capturable.
+ *    library owns is a small per-(device, stream) workspace (about 35 KB) used by the
+ *    calls that compute a tensor amax (the one-pass NVFP4 kernel's exchange, the word
+ *    a separate amax pass posts into for the quantizer that follows it, and the lines
+ *    an MXFP4 call that reports the amax spreads its posts over), allocated on the
+ *    first such call on that stream and kept until the process ends; that first call
+ *    is therefore not graph-capturable.
  *  - A call validates its arguments on the host, enqueues its kernels on `stream`
  *    (0 = the null stream) and returns without synchronizing.  On any validation
  *    error nothing is enqueued.  Device faults surface at the caller's next sync.
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 typedef enum {
     FP4Q_OK = 0,
@@ -119,10 +120,15 @@ fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, i
  * the even code); elements are x * 2^(127 - code) rounded onto E2M1 (RTN or SR as
  * above, stream 0).  No tensor scale.
  *   codes [rows][cols/2], scales [rows][cols/32].   Shapes: cols % 32 == 0.
+ *   amax  device float[1] or NULL.  Non-NULL also writes max|x| over the tensor, the
+ *         value fp4q_amax returns, from the same read of x: a caller that quantizes
+ *         one tensor to MXFP4 and to an amax-scaled format passes it on with
+ *         FP4Q_AMAX_GIVEN instead of running an amax pass.  Uses the stream's
+ *         workspace (see the conventions above); FP4Q_E_HIP if it cannot be allocated.
  */
 fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
                                 fp4q_round rnd, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream);
+                                float* amax, hipStream_t stream);
 
 /*
  * IF4 [IF "2. 提案手法：IF4"]: NVFP4 1x16 row-wise scaling, then per block the

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 1
+    assert B.fp4q_abi_version() == 2
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -82,9 +82,11 @@ def test_other_entry_points_validate():
     assert L.fp4q_quantize_nvfp4_2d(A, B.F32, 40, 48, 0, A2, A2, A, A, None, 0) == 2
     assert L.fp4q_quantize_nvfp4_2d(None, B.F32, 32, 48, 0, A2, A2, A, A, None, 0) == 1
     assert L.fp4q_quantize_nvfp4_2d(A, B.F32, 32, 48, 0, A2, A2, A, A, MIS, 0) == 3
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 48, 0, 0, A, A, 0) == 2
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 2, 0, A, A, 0) == 4
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, None, A, 0) == 1
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 48, 0, 0, A, A, None, 0) == 2
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 2, 0, A, A, None, 0) == 4
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, None, A, None, 0) == 1
+    assert L.fp4q_quantize_mxfp4(MIS, B.BF16, 4, 64, 0, 0, A, A, None, 0) == 3
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, A, A, A2 + 2, 0) == 3   # misaligned amax
     assert L.fp4q_quantize_if4(A, B.BF16, 4, 40, 0, A2, A2, A, A, 0) == 2
     assert L.fp4q_quantize_if4(A, 3, 4, 48, 0, A2, A2, A, A, 0) == 4
     sig = (ctypes.c_uint32 * 4)(1, 2, 3, 4)

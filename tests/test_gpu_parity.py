@@ -333,6 +333,35 @@ def test_mxfp4(kind, rnd):
     assert np.array_equal(host(out["scales"]), s)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 32), (96, 320), (1000, 1024), (4100, 4096)])
+def test_mxfp4_reports_tensor_amax(kind, shape):
+    # from 1 workgroup to about 4 K (128 spread lines, up to 33 posts each); the amax
+    # equals the oracle's and the codes do not change when it is requested
+    rows, cols = shape
+    xh, xd = make_input(kind, rows, cols, seed=17)
+    out = B.quantize_mxfp4(xd, with_amax=True)
+    assert host(out["amax"])[0] == np.float32(oracle.amax(xh))
+    if rows * cols <= 96 * 320:
+        c, s = oracle.quantize_mxfp4(xh)
+        assert np.array_equal(host(out["codes"]), c) and np.array_equal(host(out["scales"]), s)
+    plain = B.quantize_mxfp4(xd)
+    assert torch.equal(plain["codes"], out["codes"]) and torch.equal(plain["scales"], out["scales"])
+
+
+def test_mxfp4_amax_does_not_leak_between_calls():
+    # a later call with a smaller maximum, and one over fewer workgroups than spread
+    # lines, must not see the earlier call's posts
+    big = si.weight(2048, 2048, seed=21)
+    big[77, 5] = np.float32(123.0)
+    small = si.weight(16, 64, seed=22)
+    assert B.quantize_mxfp4(dev_f32(big), with_amax=True)["amax"].item() == np.float32(123.0)
+    got = B.quantize_mxfp4(dev_f32(small), with_amax=True)["amax"].item()
+    assert got == np.float32(oracle.amax(small))
+    z = np.zeros((8, 64), np.float32)
+    assert B.quantize_mxfp4(dev_f32(z), with_amax=True)["amax"].item() == 0.0
+
+
 def test_mxfp4_extreme_blocks():
     x = np.zeros((4, 128), np.float32)
     x[0, :32] = np.float32(1e-39) * np.arange(1, 33, dtype=np.float32)   # subnormal block -> code 0 region
