@@ -399,6 +399,34 @@ def test_if4(shape):
     assert 0 < np.count_nonzero(s & 0x80) < s.size       # both block types occur
 
 
+def test_if4_subnormal_scale_blocks():
+    # Blocks whose E4M3 scale is subnormal (codes 1..7) can round far below bamax/6, so
+    # their INT4 candidate needs the clamp to [-7, 7]; the kernel drops the clamp only in
+    # waves without such blocks.  Rows 0..31 (workgroup 0) are all normal, rows 32..63
+    # mix normal blocks with tiny ones placed to round their scale down.
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    x[0, 0] = 100.0                                  # amax: gs = 26.88
+    gs = np.float32(oracle.tensor_scale(100.0))
+    for r in (33, 40, 47, 58):
+        for cb in (0, 5, 17, 31):
+            for k, y in enumerate((1.4, 1.9, 2.45, 5.3)):   # fl(bamax*gs)/6 = y * 2^-9
+                if (cb + k) % 4 == 0:
+                    m = np.float32(6.0 * y * 2.0 ** -9) / gs
+                    blk = rng.uniform(-1.0, 1.0, 16).astype(np.float32) * m
+                    blk[rng.integers(16)] = m
+                    x[r, cb * 16:cb * 16 + 16] = blk
+    bits = si.f32_to_bf16_bits(x)
+    out = B.quantize_if4(dev_bf16(bits))
+    c, s, g = oracle.quantize_if4(bits)
+    assert host(out["tensor_scale"])[0] == g
+    assert np.array_equal(host(out["scales"]), s)
+    assert np.array_equal(host(out["codes"]), c)
+    codes = s & 0x7F
+    assert np.count_nonzero((codes >= 1) & (codes <= 7)) >= 8      # subnormal scales occur
+    assert not np.any((codes[:32] >= 1) & (codes[:32] <= 7))       # workgroup 0 has none
+
+
 def test_if4_full_config_sampled():
     bits = si.if4_mix(32768, 8192, seed=5)
     out = B.quantize_if4(dev_bf16(bits))
