@@ -158,14 +158,17 @@ __device__ __forceinline__ uint32_t e8m0_encode(float y) {
 #define FP4Q_CVT_RTN(old, a, b, scale, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), (scale), (sel))
 
 // SR: the first element of v_cvt_scalef32_sr_pk_fp4_f32 rounds up iff
-// frac + r/2^32 >= 1 on its E2M1 interval, where r is the 32-bit random operand.
-// A 16-bit draw placed in the top half (low half zero) therefore gives exactly
-// "up iff frac + r16/2^16 >= 1".  The second element of a pair would consume r << 1,
-// so each element is converted alone with a second source of +0 (code 0).  Only
-// byte 0 of the result is defined: the builtin does not carry the old destination
-// value through, so the other bytes are whatever the register held.
-#define FP4Q_CVT_SR1(a, r32, scale) \
-  __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{(a), 0.0f}, (r32), (scale), 0)
+// frac + r/2^32 >= 1 on its E2M1 interval, where r is the 32-bit random operand, and the
+// second element uses r << 1 (bit 31 dropped).  A 16-bit draw in the top half with the
+// low half zero therefore gives exactly "up iff frac + r16/2^16 >= 1": the first element
+// of a pair gets its draw as r = w & 0xFFFF0000 (the high half of a Philox word), the
+// second as r = w << 15, so that r << 1 = w << 16 (the low half).  Each pair is
+// converted twice from the same two values, keeping the first nibble of one result and
+// the second of the other.  Only byte 0 of a result is defined: the builtin does not
+// carry the old destination value through, so the other bytes are whatever the register
+// held.
+#define FP4Q_CVT_SR2(a, b, r32, scale) \
+  __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2{(a), (b)}, (r32), (scale), 0)
 
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon et al., SC'11): multipliers 0xD2511F53 / 0xCD9E8D57,
@@ -192,16 +195,16 @@ __device__ __forceinline__ U4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, ui
   return U4{c0, c1, c2, c3};
 }
 
-// Draws for the eight elements idx8*8 .. idx8*8+7 of SR stream `stream`:
-// element e uses the 16-bit half (e & 1) of word e >> 1, returned already placed in
-// the top 16 bits of a 32-bit word as the SR convert expects.
+// Draws for the eight elements idx8*8 .. idx8*8+7 of SR stream `stream`: element e
+// uses the high 16-bit half of word e >> 1 when e is even and the low half when e is
+// odd, returned as the random operands the pair convert expects (see above).
 __device__ __forceinline__ void sr_draws8(uint64_t idx8, uint32_t stream, uint32_t k0, uint32_t k1,
                                           uint32_t r32[8]) {
   U4 w = philox10((uint32_t)idx8, (uint32_t)(idx8 >> 32), stream, 0u, k0, k1);
-  r32[0] = w.x << 16; r32[1] = w.x & 0xFFFF0000u;
-  r32[2] = w.y << 16; r32[3] = w.y & 0xFFFF0000u;
-  r32[4] = w.z << 16; r32[5] = w.z & 0xFFFF0000u;
-  r32[6] = w.w << 16; r32[7] = w.w & 0xFFFF0000u;
+  r32[0] = w.x & 0xFFFF0000u; r32[1] = w.x << 15;
+  r32[2] = w.y & 0xFFFF0000u; r32[3] = w.y << 15;
+  r32[4] = w.z & 0xFFFF0000u; r32[5] = w.z << 15;
+  r32[6] = w.w & 0xFFFF0000u; r32[7] = w.w << 15;
 }
 
 // ---------------------------------------------------------------------------
@@ -223,9 +226,9 @@ __device__ __forceinline__ uint32_t pack8_sr(const float v[8], const uint32_t r3
   uint32_t t[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = FP4Q_CVT_SR1(v[2 * k], r32[2 * k], scale);
-    const uint32_t hi = FP4Q_CVT_SR1(v[2 * k + 1], r32[2 * k + 1], scale);
-    t[k] = (hi << 4) | lo;                      // byte 0 = code(2k) | code(2k+1) << 4
+    const uint32_t first = FP4Q_CVT_SR2(v[2 * k], v[2 * k + 1], r32[2 * k], scale);       // low nibble valid
+    const uint32_t second = FP4Q_CVT_SR2(v[2 * k], v[2 * k + 1], r32[2 * k + 1], scale);  // high nibble valid
+    t[k] = __builtin_amdgcn_bitop3_b32(first, second, 0x0F0F0F0Fu, 0xE4);   // (first & m) | (second & ~m)
   }
   const uint32_t u = __builtin_amdgcn_perm(t[1], t[0], 0x0C0C0400u);   // [t0.b0, t1.b0, 0, 0]
   const uint32_t w = __builtin_amdgcn_perm(t[3], t[2], 0x04000C0Cu);   // [0, 0, t2.b0, t3.b0]

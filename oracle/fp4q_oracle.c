@@ -71,8 +71,8 @@ void ora_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
  * in the logical quantized matrix) of stream `stream` (0: row-wise, 2D and MXFP4
  * outputs; 1: the column-wise output, i.e. the matrix X^T).  One Philox call serves
  * eight consecutive elements: counter {lo32(idx/8), hi32(idx/8), stream, 0}, key
- * {lo32(seed), hi32(seed)}; element idx takes 16-bit half (idx & 1) of word
- * (idx / 2) & 3, low half first. */
+ * {lo32(seed), hi32(seed)}; element idx takes a 16-bit half of word (idx / 2) & 3,
+ * the high half for even idx and the low half for odd idx. */
 uint32_t ora_sr_bits16(uint64_t seed, uint32_t stream, uint64_t idx)
 {
     uint64_t group = idx >> 3;
@@ -81,7 +81,7 @@ uint32_t ora_sr_bits16(uint64_t seed, uint32_t stream, uint64_t idx)
     uint32_t out[4];
     ora_philox4x32_10(ctr, key, out);
     uint32_t word = out[(idx >> 1) & 3];
-    return (idx & 1) ? (word >> 16) : (word & 0xFFFFu);
+    return (idx & 1) ? (word & 0xFFFFu) : (word >> 16);
 }
 
 /* The RHT's random diagonal S: 128 signs from one Philox call with counter

@@ -66,7 +66,7 @@ def test_sr_draws_and_rht_signs_use_the_stated_counters(rocrand_ref):
         got = oracle.sr_bits16(seed, stream, idx)
         for n, i in enumerate(idx.tolist()):
             word = int(ref[k + n][(i >> 1) & 3])
-            expect = (word >> 16) if (i & 1) else (word & 0xFFFF)
+            expect = (word & 0xFFFF) if (i & 1) else (word >> 16)
             assert got[n] == expect
         k += len(idx)
     sref = rocrand_ref(np.array([[0, 0, 0, 1] + key], dtype=np.uint32))[0]
