@@ -93,7 +93,11 @@ typedef enum { FP4Q_FMT_NVFP4 = 0, FP4Q_FMT_NVFP4_2D = 1, FP4Q_FMT_MXFP4 = 2, FP
  *   amax, tensor_scale  device float[1] each.
  * Shapes: ROWWISE needs cols % 16 == 0; COLWISE needs rows % 16 == 0 and cols % 8 == 0.
  * SR uses stream 0 for the row-wise output and stream 1 for the column-wise output;
- * element index = row * lcols + col of the logical (output) matrix.
+ * element index idx = row * lcols + col of the logical (output) matrix.  One
+ * Philox4x32-10 call, counter {lo32(idx/8), hi32(idx/8), stream, 0} and key
+ * {lo32(sr_seed), hi32(sr_seed)}, serves the 8 elements idx/8*8 .. +7: element idx
+ * takes the high 16 bits of output word (idx/2) % 4 when idx is even, the low 16 bits
+ * when idx is odd, as u = draw / 2^16 (MXFP4 uses the same layout with stream 0).
  */
 fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
                                 unsigned layouts, fp4q_round rnd, uint64_t sr_seed,
