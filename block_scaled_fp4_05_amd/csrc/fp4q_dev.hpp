@@ -109,7 +109,9 @@ __device__ __forceinline__ float e4m3_decode(uint32_t code) {
 // converted value is +0, so the returned word is the scale byte itself.
 __device__ __forceinline__ uint32_t nvfp4_scale_code(float p) {
   const float y = __builtin_fminf(div2(p, recip6()), 448.0f);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0u, false);
+  // the convert writes bits 0..15 (y, then +0) and keeps bits 16..31 of its old operand:
+  // any dead value does, and the mask lets uses that read 16 bits fold it away
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, __float_as_uint(y), false) & 0xFFFFu;
 }
 
 // Reciprocal pairs of all 128 E4M3 codes, indexed by the code: a block divides by
