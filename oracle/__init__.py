@@ -74,6 +74,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "ora_quantize_mxfp4": (None, [_P, _I, _I64, _I64, _I, _U64, _P, _P]),
         "ora_quantize_if4": (None, [_P, _I, _I64, _I64, _F, _P, _P]),
         "ora_dequantize": (None, [_I, _P, _P, _F, _I64, _I64, _P]),
+        "ora_gemm_mxfp4": (None, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
         "ora_hadamard_entry": (_I, [_I, _I]),
         "ora_rht": (None, [_P, _I, _I64, _I64, _P, _I, _P]),
         "ora_rht_column": (None, [_P, _I, _I64, _I64, _I64, _P, _P]),
@@ -254,6 +255,20 @@ def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, gs: float, rows:
     y = np.zeros((rows, cols), dtype=np.float32)
     lib().ora_dequantize(fmt, _ptr(codes), _ptr(scales), gs, rows, cols, _ptr(y))
     return y
+
+
+def gemm_mxfp4(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b_scales: np.ndarray):
+    """C = A B^T over two row-wise MXFP4 operands (A [m][k], B [n][k]), exact sum in
+    binary64.  Returns (C, sum of |products|) as float64 [m][n]."""
+    a_codes, a_scales = np.ascontiguousarray(a_codes), np.ascontiguousarray(a_scales)
+    b_codes, b_scales = np.ascontiguousarray(b_codes), np.ascontiguousarray(b_scales)
+    m, k = a_codes.shape[0], a_codes.shape[1] * 2
+    n = b_codes.shape[0]
+    assert b_codes.shape == (n, k // 2) and a_scales.shape == (m, k // 32) and b_scales.shape == (n, k // 32)
+    c = np.zeros((m, n), dtype=np.float64)
+    cabs = np.zeros((m, n), dtype=np.float64)
+    lib().ora_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), m, n, k, _ptr(c), _ptr(cabs))
+    return c, cabs
 
 
 def hadamard_entry(i: int, t: int) -> int:

@@ -13,11 +13,13 @@
  *
  * Sources (cited by page and section, nothing else):
  *  [NV]  qiita.com/nishiha/items/b98c2b931d588c4c81d5 -- notes on NVIDIA's NVFP4
- *        pretraining recipe; sections "NVFP4データの変換" (E2M1), "2D scaling",
+ *        pretraining recipe; sections "NVFP4フロー図" (the three GEMMs on quantized
+ *        operands), "NVFP4データの変換" (E2M1), "2D scaling",
  *        "ランダムアダマール変換" (RHT), "確率的丸め" (SR), "NVFP4の表現できる最大値",
  *        "scaleの導出" (two-level scale).
  *  [GL]  ultralytics.com/ja/glossary/fp4 -- glossary "FP4"; section "FP4の仕組み"
- *        (MXFP4 / NVFP4 definitions and the block-size MAE snippet).
+ *        (MXFP4 / NVFP4 definitions and the block-size MAE snippet), section
+ *        "FP4による推論と学習" (FP4 products accumulated in higher precision).
  *  [IF]  gist.science/ja/paper/2603.28765 -- explainer of "Adaptive Block-Scaled
  *        Data Types"; section "2. 提案手法：IF4" (IF4, the sign-bit flag, the 6/7
  *        rule) and section "3. 主要な貢献" (Table 1).
@@ -483,6 +485,40 @@ void ora_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, float 
                 out = p / gs;
             }
             y[r * cols + c] = out;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* FP4 GEMM consumer [NV "NVFP4フロー図"], [GL "FP4による推論と学習"]             */
+/* ------------------------------------------------------------------------- */
+
+/* The products that follow quantization (forward, data-gradient and weight-gradient
+ * GEMMs) take two operands quantized along the reduction dimension K and accumulate
+ * in higher precision.  Reading: both operands are row-wise MXFP4 along K, A is
+ * [m][k] and B is [n][k], and
+ *     C[i][j] = sum_k a(i,k) * b(j,k),   a(i,k) = E2M1(nibble) * 2^(e8m0 - 127).
+ * Each product and the running sum (k ascending) are binary64; with E2M1 values of at
+ * most two significant bits, the products are exact and so is the sum while the
+ * operands' exponents stay within binary64's 53-bit window, which holds for the
+ * scales quantization produces.  cabs[i][j] = sum_k |a(i,k) * b(j,k)| is returned
+ * for error bounds.  Row strides: codes k/2 bytes, scales k/32 bytes. */
+void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                    const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, double* c, double* cabs)
+{
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                double av = ldexp((double)ora_e2m1_decode(get_nibble(a_codes, k, i, t)),
+                                  (int)a_scales[i * (k / 32) + t / 32] - 127);
+                double bv = ldexp((double)ora_e2m1_decode(get_nibble(b_codes, k, j, t)),
+                                  (int)b_scales[j * (k / 32) + t / 32] - 127);
+                acc += av * bv;
+                mag += fabs(av * bv);
+            }
+            c[i * n + j] = acc;
+            if (cabs) cabs[i * n + j] = mag;
         }
     }
 }
