@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4q.so")
-SOURCES = ["fp4q_api.hip", "fp4q_quant.hip", "fp4q_rht.hip"]
+SOURCES = ["fp4q_api.hip", "fp4q_quant.hip", "fp4q_rht.hip", "fp4q_gemm.hip"]
 
 ARCH = "gfx950"
 CXXFLAGS = [

@@ -67,4 +67,9 @@ void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const u
                           bool sr, uint64_t seed, const AmaxSource& amax, float* tensor_scale,
                           uint8_t* col_codes, uint8_t* col_scales, hipStream_t st);
 
+// MXFP4 GEMM C = A B^T (fp32 accumulate; fp32 or bf16 out) -- fp4q_gemm.hip.  k % 128 == 0.
+bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                       const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,
+                       hipStream_t st);
+
 }  // namespace fp4q

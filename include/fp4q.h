@@ -4,11 +4,14 @@
  * Sources of the operations (page, then section):
  *  [NV] qiita.com/nishiha/items/b98c2b931d588c4c81d5 (notes on NVIDIA's NVFP4
  *       pretraining recipe): "NVFP4データの変換" (E2M1), "Blockwise" (1x16 blocks),
- *       "誤差逆伝播と転置" (backprop needs the transposed operands), "2D scaling",
+ *       "誤差逆伝播と転置" (backprop needs the transposed operands), "NVFP4フロー図"
+ *       (the forward, data- and weight-gradient GEMMs on quantized operands), "2D scaling",
  *       "ランダムアダマール変換" (RHT), "確率的丸め" (stochastic rounding),
  *       "NVFP4の表現できる最大値", "scaleの導出" (tensor and block scales).
  *  [GL] ultralytics.com/ja/glossary/fp4 (glossary "FP4"): "FP4の仕組み"
- *       (MXFP4: 32 values + E8M0 scale; NVFP4: 16 values + E4M3 scale + FP32 scale).
+ *       (MXFP4: 32 values + E8M0 scale; NVFP4: 16 values + E4M3 scale + FP32 scale),
+ *       "FP4による推論と学習" (FP4 products accumulated in higher precision),
+ *       "FP4モデルのデプロイ" (MXFP4 native on the MI350 family).
  *  [IF] gist.science/ja/paper/2603.28765 (explainer of "Adaptive Block-Scaled Data
  *       Types"): "2. 提案手法：IF4" (FP4/INT4 per block, sign-bit flag, 6/7 rule).
  *  [F6] blog.ast.moe/blog/2026-09-24 ("FP6から考えるLLM量子化"):
@@ -51,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 2
+#define FP4Q_ABI_VERSION 3
 
 typedef enum {
     FP4Q_OK = 0,
@@ -159,6 +162,22 @@ fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_
  */
 fp4q_status fp4q_rht(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
                      const uint32_t* signs, int inverse, float* y, hipStream_t stream);
+
+/*
+ * FP4 GEMM consumer [NV "NVFP4フロー図"; GL "FP4による推論と学習"]: the product that
+ * follows quantization, on two operands quantized along the reduction dimension k:
+ *   c[i][j] = sum_t a(i,t) * b(j,t),   a(i,t) = E2M1 * 2^(a_scale - 127), likewise b,
+ * i.e. C = A B^T with A [m][k] and B [n][k] both row-wise MXFP4 as fp4q_quantize_mxfp4
+ * writes them (codes [rows][k/2], E8M0 scales [rows][k/32]).  For Y = X W^T pass the
+ * activation X as A and the weight W as B.  Products and sums run on the block-scaled
+ * MFMA with fp32 accumulation; the summation order is the hardware's.
+ *   out_dt FP4Q_F32: c is float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
+ * Shapes: m >= 1, n >= 1, k >= 128 with k % 128 == 0 and k < 2^31, m, n < 2^31.
+ */
+fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* b_codes, const uint8_t* b_scales,
+                            int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
+                            hipStream_t stream);
 
 /*
  * Dequantize packed codes back to values.  rows x cols is the LOGICAL shape of the
