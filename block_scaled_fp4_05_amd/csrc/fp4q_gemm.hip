@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fp4q_internal.hpp"
 
@@ -35,13 +36,29 @@ typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmTile = 256;     // rows of A and of B per workgroup tile
 constexpr int kGemmStages = 4;
-constexpr int kLoadsPerStep = 10;  // global_load_lds per wave and K step: 4 + 4 code chunks, 2 scale words
+constexpr int kLoadsPerStep = 10;  // global_load_lds per wave and K step: 4 + 4 code chunks, 2 scale slices
 
 struct GemmStage {
   u32x4_g a[kGemmTile * 4];   // 256 rows x four 16-byte chunks (swizzled)
   u32x4_g b[kGemmTile * 4];
-  uint32_t as[kGemmTile];     // the four scales of each row for this K step
-  uint32_t bs[kGemmTile];
+};
+
+// Scales travel in chunks of four K steps: 16 bytes per row (row-major input keeps a
+// row's scales for consecutive steps together, so one access per row brings four
+// steps; a word per row and step would touch a cache line per row on every step).
+// Three chunk buffers; the chunk for steps 4C..4C+3 is loaded in four slices of 64
+// rows, one with each of the code loads of steps 4C-4 .. 4C-1, so every step issues
+// the same number of loads.  Within a row, the word of step 4C+d sits at position
+// d ^ scale_swz(row), spreading 32 consecutive rows over distinct banks.
+struct GemmScales {
+  uint32_t a[kGemmTile * 4];
+  uint32_t b[kGemmTile * 4];
+};
+__device__ __forceinline__ uint32_t scale_swz(uint32_t r) { return (r >> 3) & 3u; }
+
+struct GemmLds {
+  GemmStage st[kGemmStages];
+  GemmScales sc[3];
 };
 
 // 16-byte chunk c of staged row r sits at position c ^ swz(r).  A fragment read takes
@@ -55,7 +72,12 @@ __device__ __forceinline__ uint32_t gemm_swz(uint32_t r) {
 // wait for all of them).  What it has to order is explicit: each wave has waited for
 // its own loads of the step about to be read (wait_vm), and every read of the stage
 // about to be refilled fed an MFMA of the previous step, so it has completed.
-__device__ __forceinline__ void gemm_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The LDS wait goes through the builtin so that the compiler's own wait insertion knows
+// every earlier LDS read is complete and adds no later wait for them.
+__device__ __forceinline__ void gemm_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -83,30 +105,41 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <int SUB>
-__device__ __forceinline__ void gemm_substep(const GemmStage& s, uint32_t offA, uint32_t offB, const uint32_t sa[4],
-                                             const uint32_t sb[4], v16f_t acc[4][4]) {
+// One 64-element K sub-step of a wave's 128 x 128 block: the 4 A and 4 B fragments.
+struct GemmFrags {
   v8i_t a[4], b[4];
+};
+
+__device__ __forceinline__ void gemm_read(const GemmStage& s, uint32_t offA, uint32_t offB, GemmFrags& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4_g va = *reinterpret_cast<const u32x4_g*>(reinterpret_cast<const char*>(s.a) + offA + i * 32 * 64);
     const u32x4_g vb = *reinterpret_cast<const u32x4_g*>(reinterpret_cast<const char*>(s.b) + offB + i * 32 * 64);
-    a[i] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-    b[i] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
+    f.a[i] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
+    f.b[i] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
   }
+}
+
+// The scale words of the lane's A and B rows, shifted so that byte 2 sub holds the
+// scale of the lane's K block in sub-step sub (block 2 sub + fh of the step).
+template <int SUB>
+__device__ __forceinline__ void gemm_mma(const GemmFrags& f, const uint32_t sa[4], const uint32_t sb[4],
+                                         v16f_t acc[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 2 * SUB, (int)sa[i],
-                                                                  2 * SUB, (int)sb[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 2 * SUB,
+                                                                  (int)sa[i], 2 * SUB, (int)sb[j]);
 }
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
     const uint8_t* __restrict__ bs, int M, int N, int K, int tiles_m, int tiles_n, void* __restrict__ cout) {
-  __shared__ GemmStage st[kGemmStages];
+  __shared__ GemmLds lds_;
+  GemmStage* st = lds_.st;
+  GemmScales* sc = lds_.sc;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
@@ -127,18 +160,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     pa[j] = ac + (int64_t)min(m0 + 64 * j + lr, M - 1) * ldq + gch * 16;
     pb[j] = bc + (int64_t)min(n0 + 64 * j + lr, N - 1) * ldq + gch * 16;
   }
-  const uint8_t* psa = as + (int64_t)min(m0 + tid, M - 1) * lds;
-  const uint8_t* psb = bs + (int64_t)min(n0 + tid, N - 1) * lds;
-
+  // Scale slice j of a chunk: this lane fetches row 64 j + 16 wave + lane/4, position
+  // lane % 4, i.e. the word of step 4C + (lane % 4) ^ scale_swz(row), clamped to the
+  // last step so that a partial last chunk stays inside the row.
+  const int srow = 16 * wave + (lane >> 2);   // row within the slice, + 64 j
+  const int sd = (lane & 3) ^ (int)scale_swz((uint32_t)srow);   // the same for every j
+  auto issue_scales = [&](int chunk, int j) {
+    GemmScales& c = sc[chunk % 3];
+    const int stp = min(4 * chunk + sd, nk - 1);
+    const int r = 64 * j + srow;
+    __builtin_amdgcn_global_load_lds(as + (int64_t)min(m0 + r, M - 1) * lds + 4 * stp, &c.a[(64 * j + 16 * wave) * 4],
+                                     4, 0, 0);
+    __builtin_amdgcn_global_load_lds(bs + (int64_t)min(n0 + r, N - 1) * lds + 4 * stp, &c.b[(64 * j + 16 * wave) * 4],
+                                     4, 0, 0);
+  };
   auto issue = [&](int ks) {
     GemmStage& s = st[ks % kGemmStages];
-    const int64_t ko = (int64_t)ks * 64, so = (int64_t)ks * 4;
+    const int64_t ko = (int64_t)ks * 64;
 #pragma unroll
     for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(pa[j] + ko, &s.a[j * 256 + wave * 64], 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(pb[j] + ko, &s.b[j * 256 + wave * 64], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(psa + so, &s.as[wave * 64], 4, 0, 0);
-    __builtin_amdgcn_global_load_lds(psb + so, &s.bs[wave * 64], 4, 0, 0);
+    issue_scales((ks >> 2) + 1, ks & 3);
   };
 
   // Fragment reads: row wm*128 + 32 i + fr, chunk (2 sub + fh) ^ swz(fr).
@@ -154,32 +197,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f_t{};
 
+  // Pipeline: while the 16 MFMAs of one sub-step run, the fragments of the next one
+  // are already being read.  The barrier that publishes step ks+1 sits between the two
+  // sub-steps of step ks, so the MFMAs never wait for it; right after it the loads of
+  // step ks+3 go into the stage step ks-1 used (its last reads fed MFMAs issued before
+  // the barrier), leaving two steps in flight behind the one being consumed.
+  // The scale word of step ks for the lane's rows wm*128 + 32 i + fr (A) and
+  // wn*128 + 32 i + fr (B): position ((ks & 3) ^ scale_swz(row)) of the row, and
+  // scale_swz depends only on fr for these rows.
+  const uint32_t fsw = scale_swz((uint32_t)fr);
+  const uint32_t posA = (uint32_t)(wm * 128 + fr) * 4, posB = (uint32_t)(wn * 128 + fr) * 4;
+  auto scales_of = [&](int ks, uint32_t sa_[4], uint32_t sb_[4]) {
+    const GemmScales& c = sc[(ks >> 2) % 3];
+    const uint32_t d = ((uint32_t)ks & 3u) ^ fsw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa_[i] = c.a[posA + d + 32 * 4 * i] >> (8 * fh);
+      sb_[i] = c.b[posB + d + 32 * 4 * i] >> (8 * fh);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) issue_scales(0, j);
 #pragma unroll
   for (int p = 0; p < kGemmStages - 1; ++p)
     if (p < nk) issue(p);
+  if (nk >= 3) wait_vm<2 * kLoadsPerStep>();
+  else if (nk == 2) wait_vm<kLoadsPerStep>();
+  else wait_vm<0>();
+  gemm_barrier();
+  GemmFrags cur, nxt;
+  uint32_t sa[4], sb[4];
+  gemm_read(st[0], rowA + pos0, rowB + pos0, cur);
+  scales_of(0, sa, sb);
 
-  for (int ks = 0; ks < nk; ++ks) {
-    // Step ks has landed once at most the loads of the steps issued after it remain.
-    const int after = min(kGemmStages - 2, nk - 1 - ks);
-    if (after >= 2) wait_vm<2 * kLoadsPerStep>();
-    else if (after == 1) wait_vm<kLoadsPerStep>();
-    else wait_vm<0>();
-    gemm_barrier();    // every wave's share of step ks is in LDS; step ks-1's stage is free
-    if (ks + kGemmStages - 1 < nk) issue(ks + kGemmStages - 1);
-
+  // One K step; MODE 0: steps ks+1 .. ks+3 exist (refill with ks+3), 3: ks+1 and ks+2
+  // exist, 1: only ks+1, 2: ks is the last.  The body has no branch.  With one wave
+  // per SIMD the matrix core idles whenever the wave issues anything else between two
+  // MFMAs for longer than one MFMA lasts, so the reads and loads are interleaved one by
+  // one with the MFMAs (scheduling groups); only the wait and the barrier stand alone.
+  auto step = [&](int ks, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
     const GemmStage& s = st[ks % kGemmStages];
-    uint32_t sa[4], sb[4];
+    gemm_read(s, rowA + pos1, rowB + pos1, nxt);
+    gemm_mma<0>(cur, sa, sb, acc);
+    uint32_t sa1[4], sb1[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = s.as[wm * 128 + 32 * i + fr] >> (8 * fh);   // byte 2 sub of the shifted word: block 2 sub + fh
-      sb[i] = s.bs[wn * 128 + 32 * i + fr] >> (8 * fh);
+    for (int i = 0; i < 4; ++i) sa1[i] = sa[i], sb1[i] = sb[i];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    gemm_substep<0>(s, rowA + pos0, rowB + pos0, sa, sb, acc);
-    gemm_substep<1>(s, rowA + pos1, rowB + pos1, sa, sb, acc);
-  }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MODE != 2) {
+      // step ks+1 has landed once at most step ks+2's loads remain
+      if constexpr (MODE == 0 || MODE == 3) wait_vm<kLoadsPerStep>();
+      else wait_vm<0>();
+      gemm_barrier();
+      if constexpr (MODE == 0) issue(ks + 3);
+      const GemmStage& s1 = st[(ks + 1) % kGemmStages];
+      scales_of(ks + 1, sa, sb);
+      gemm_read(s1, rowA + pos0, rowB + pos0, cur);
+    }
+    gemm_mma<1>(nxt, sa1, sb1, acc);
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int g = 0; g < 10; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
+      }
+#pragma unroll
+      for (int g = 0; g < 6; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    } else if constexpr (MODE != 2) {
+#pragma unroll
+      for (int g = 0; g < 12; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int ks = 0;
+  for (; ks + 3 < nk; ++ks) step(ks, std::integral_constant<int, 0>{});
+  if (ks + 2 < nk) step(ks++, std::integral_constant<int, 3>{});
+  if (ks + 1 < nk) step(ks++, std::integral_constant<int, 1>{});
+  step(ks, std::integral_constant<int, 2>{});
 
   // Epilogue: register q of block (i, j) is C row m0 + wm*128 + 32 i + 8(q/4) + 4 fh + q%4,
   // column n0 + wn*128 + 32 j + fr.
+  if constexpr (BF16OUT) {
+    // The 128 x 128 bf16 block goes through LDS, row-major, so that a store writes 16
+    // bytes and four whole 256-byte rows per instruction (the registers hold one column
+    // per lane, which would write half cache lines).  Each wave uses its own 32 KB once
+    // every wave has finished reading the stages; pieces that cross the edge of C, or
+    // rows not 16-byte aligned (n % 8 != 0), are stored element by element.
+    gemm_barrier();
+    const int br = m0 + wm * 128, bc = n0 + wn * 128;
+    uint16_t* e = reinterpret_cast<uint16_t*>(&lds_) + wave * 128 * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          e[(32 * i + 8 * (q >> 2) + 4 * fh + (q & 3)) * 128 + 32 * j + fr] = bf16_rne(acc[i][j][q]);
+        __builtin_amdgcn_sched_barrier(0);   // one block at a time keeps few values live
+      }
+    uint16_t* c16 = static_cast<uint16_t*>(cout);
+    const bool vec = (N & 7) == 0;
+    for (int it = 0; it < 32; ++it) {
+      const int row = 4 * it + (lane >> 4), c8 = (lane & 15) * 8;
+      if (br + row >= M) continue;
+      uint16_t* dst = c16 + (int64_t)(br + row) * N + bc + c8;
+      const uint16_t* src = e + row * 128 + c8;
+      if (vec && bc + c8 + 8 <= N) {
+        *reinterpret_cast<u32x4_g*>(dst) = *reinterpret_cast<const u32x4_g*>(src);
+      } else {
+        for (int x = 0; x < 8 && bc + c8 + x < N; ++x) dst[x] = src[x];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -190,10 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fh + (q & 3);
         if (row < M && col < N) {
           const int64_t o = (int64_t)row * N + col;
-          if constexpr (BF16OUT)
-            static_cast<uint16_t*>(cout)[o] = bf16_rne(acc[i][j][q]);
-          else
-            static_cast<float*>(cout)[o] = acc[i][j][q];
+          static_cast<float*>(cout)[o] = acc[i][j][q];
         }
       }
     }

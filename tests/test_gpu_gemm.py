@@ -62,7 +62,7 @@ def test_gemm_random_codes_fp32_out(shape):
     _check(got, exact, cabs, k)
 
 
-@pytest.mark.parametrize("shape", [(256, 256, 256), (390, 200, 512)])
+@pytest.mark.parametrize("shape", [(256, 256, 256), (390, 200, 512), (257, 130, 256), (600, 1000, 384)])
 def test_gemm_random_codes_bf16_out(shape):
     m, n, k = shape
     rng = np.random.default_rng(99 + m + n + k)
