@@ -16,10 +16,9 @@
 // lane does not matter, since both operands use the same packing.
 //
 // Workgroup: a 256 x 256 tile of C, four waves of 128 x 128 (4 x 4 MFMA blocks, 256
-// accumulator registers, one wave per SIMD).  A K step is 128 elements: 64 bytes of
-// codes and one dword of four scales per row of each operand, copied straight into LDS
-// by global_load_lds into one of four stages, so three steps are in flight while one
-// is consumed.
+// accumulator registers, one wave per SIMD).  A K step is 256 elements: 128 bytes of
+// codes per row of each operand, copied straight into LDS by global_load_lds into one
+// of two stages while the other is consumed, plus the scales in chunks of two steps.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -35,21 +34,25 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmTile = 256;     // rows of A and of B per workgroup tile
-constexpr int kGemmStages = 4;
-constexpr int kLoadsPerStep = 10;  // global_load_lds per wave and K step: 4 + 4 code chunks, 2 scale slices
+constexpr int kGemmStages = 2;
+constexpr int kLoadsPerStep = 20;  // global_load_lds per wave and K step: 8 + 8 code chunks, 4 scale slices
 
+// A K step is 256 elements, 128 bytes of codes per row, so every load fetches whole
+// 128-byte lines: with 64 bytes per row and step, each line was fetched twice (once
+// per step) and the L2-to-LDS stream ran about 40 % slower.
 struct GemmStage {
-  u32x4_g a[kGemmTile * 4];   // 256 rows x four 16-byte chunks (swizzled)
-  u32x4_g b[kGemmTile * 4];
+  u32x4_g a[kGemmTile * 8];   // 256 rows x eight 16-byte chunks (swizzled)
+  u32x4_g b[kGemmTile * 8];
 };
 
-// Scales travel in chunks of four K steps: 16 bytes per row (row-major input keeps a
-// row's scales for consecutive steps together, so one access per row brings four
-// steps; a word per row and step would touch a cache line per row on every step).
-// Three chunk buffers; the chunk for steps 4C..4C+3 is loaded in four slices of 64
-// rows, one with each of the code loads of steps 4C-4 .. 4C-1, so every step issues
-// the same number of loads.  Within a row, the word of step 4C+d sits at position
-// d ^ scale_swz(row), spreading 32 consecutive rows over distinct banks.
+// Scales travel in chunks of two K steps: 16 bytes per row, eight E8M0 bytes per step.
+// Row-major input keeps a row's scales for consecutive steps together, so one access
+// per row brings two steps; a word per row and step would touch a cache line per row
+// every time.  Three chunk buffers; the chunk for steps 2C and 2C+1 is loaded in four
+// slices of 64 rows, two with the code loads of step 2C-2 and two with those of step
+// 2C-1, so every step issues the same number of loads.  Word d of a row's 16 bytes
+// (d = 2 (step % 2) + half of the step) sits at position d ^ scale_swz(row), which
+// spreads 32 consecutive rows over distinct banks.
 struct GemmScales {
   uint32_t a[kGemmTile * 4];
   uint32_t b[kGemmTile * 4];
@@ -61,19 +64,18 @@ struct GemmLds {
   GemmScales sc[3];
 };
 
-// 16-byte chunk c of staged row r sits at position c ^ swz(r).  A fragment read takes
-// 16 consecutive rows at one chunk; with this swizzle (a function of r % 16) their
-// chunks fall in distinct bank groups whether LDS serves 8 or 16 such lanes per pass.
+// 16-byte chunk c of staged row r sits at position c ^ gemm_swz(r).  A fragment read
+// takes 16 consecutive rows at one chunk; with this swizzle (a function of r % 16) they
+// fall in distinct bank groups whether LDS serves 8 or 16 such lanes per pass.
 __device__ __forceinline__ uint32_t gemm_swz(uint32_t r) {
-  return ((r >> 2) & 1u) | ((((r >> 1) ^ (r >> 3)) & 1u) << 1);
+  return ((r >> 1) & 1u) | (((r >> 2) & 1u) << 1) | (((r ^ (r >> 3)) & 1u) << 2);
 }
 
-// Workgroup barrier that leaves the later steps' loads in flight (a memory fence would
+// Workgroup barrier that leaves the next step's loads in flight (a memory fence would
 // wait for all of them).  What it has to order is explicit: each wave has waited for
 // its own loads of the step about to be read (wait_vm), and every read of the stage
-// about to be refilled fed an MFMA of the previous step, so it has completed.
-// The LDS wait goes through the builtin so that the compiler's own wait insertion knows
-// every earlier LDS read is complete and adds no later wait for them.
+// about to be refilled has completed (the LDS wait).  The LDS wait goes through the
+// builtin so that the compiler's own wait insertion knows every earlier LDS read is done.
 __device__ __forceinline__ void gemm_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
   asm volatile("s_barrier" ::: "memory");
@@ -113,15 +115,15 @@ struct GemmFrags {
 __device__ __forceinline__ void gemm_read(const GemmStage& s, uint32_t offA, uint32_t offB, GemmFrags& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4_g va = *reinterpret_cast<const u32x4_g*>(reinterpret_cast<const char*>(s.a) + offA + i * 32 * 64);
-    const u32x4_g vb = *reinterpret_cast<const u32x4_g*>(reinterpret_cast<const char*>(s.b) + offB + i * 32 * 64);
+    const u32x4_g va = *reinterpret_cast<const u32x4_g*>(reinterpret_cast<const char*>(s.a) + offA + i * 32 * 128);
+    const u32x4_g vb = *reinterpret_cast<const u32x4_g*>(reinterpret_cast<const char*>(s.b) + offB + i * 32 * 128);
     f.a[i] = v8i_t{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
     f.b[i] = v8i_t{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
   }
 }
 
-// The scale words of the lane's A and B rows, shifted so that byte 2 sub holds the
-// scale of the lane's K block in sub-step sub (block 2 sub + fh of the step).
+// 16 MFMAs of one sub-step.  sa/sb hold the scale words of the lane's rows shifted by
+// 8 * (lane / 32), so byte 2 (SUB % 2) is the scale of the lane's K block.
 template <int SUB>
 __device__ __forceinline__ void gemm_mma(const GemmFrags& f, const uint32_t sa[4], const uint32_t sb[4],
                                          v16f_t acc[4][4]) {
@@ -129,8 +131,19 @@ __device__ __forceinline__ void gemm_mma(const GemmFrags& f, const uint32_t sa[4
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 2 * SUB,
-                                                                  (int)sa[i], 2 * SUB, (int)sb[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 2 * (SUB & 1),
+                                                                  (int)sa[i], 2 * (SUB & 1), (int)sb[j]);
+}
+
+// Scheduling groups: one MFMA, then up to V global loads and D LDS reads, N times.
+template <int N, int V, int D>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int g = 0; g < N; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+  }
 }
 
 template <bool BF16OUT>
@@ -146,50 +159,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
   const int64_t ldq = K / 2, lds = K / 32;   // row strides of codes and scales, bytes
-  const int nk = K / 128;
+  const int nb = K / 128;                     // 128-element halves of a step
+  const int nk = (nb + 1) / 2;                // steps; with nb odd the last one is half
+  const int last_chunk_byte = (int)ldq - 16;  // last 16 bytes of a row of codes
 
-  // Loader: chunk p = 256 j + tid of a stage is row 64 j + tid / 4, position tid % 4,
-  // which holds global chunk (tid % 4) ^ swz(row); rows past the matrix read its last
-  // row (their products land in C rows or columns that are not stored).
-  const int lr = tid >> 2;
-  const uint32_t gch = (uint32_t)(tid & 3) ^ gemm_swz((uint32_t)lr);
-  const uint8_t* pa[4];
-  const uint8_t* pb[4];
+  // Loader: chunk p = 256 j + tid of a stage is row 32 j + tid / 8, position tid % 8,
+  // which holds global chunk (tid % 8) ^ gemm_swz(row) (gemm_swz depends on row % 16 =
+  // (tid / 8) % 16 only).  Rows past the matrix read its last row (their products land
+  // in C rows or columns that are not stored); chunks past k, in a half last step, read
+  // the row's last 16 bytes (their MFMAs are skipped).
+  const int lr = tid >> 3;
+  const int gch = (tid & 7) ^ (int)gemm_swz((uint32_t)lr);
+  // Row group j starts at the uniform row min(m0 + 32 j, M - 1) (scalar base); the
+  // lane adds the 32-bit offset of its own (clamped) row, < 32 rows of ldq bytes.
+  uint32_t oa[8], ob[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    pa[j] = ac + (int64_t)min(m0 + 64 * j + lr, M - 1) * ldq + gch * 16;
-    pb[j] = bc + (int64_t)min(n0 + 64 * j + lr, N - 1) * ldq + gch * 16;
+  for (int j = 0; j < 8; ++j) {
+    oa[j] = (uint32_t)((min(m0 + 32 * j + lr, M - 1) - min(m0 + 32 * j, M - 1)) * (int)ldq);
+    ob[j] = (uint32_t)((min(n0 + 32 * j + lr, N - 1) - min(n0 + 32 * j, N - 1)) * (int)ldq);
   }
   // Scale slice j of a chunk: this lane fetches row 64 j + 16 wave + lane/4, position
-  // lane % 4, i.e. the word of step 4C + (lane % 4) ^ scale_swz(row), clamped to the
-  // last step so that a partial last chunk stays inside the row.
-  const int srow = 16 * wave + (lane >> 2);   // row within the slice, + 64 j
-  const int sd = (lane & 3) ^ (int)scale_swz((uint32_t)srow);   // the same for every j
+  // lane % 4, i.e. row word 4C + ((lane % 4) ^ scale_swz(row)), clamped to the row's
+  // last word so that a partial last chunk stays inside the row.
+  const int srow = 16 * wave + (lane >> 2);                      // row within the slice, + 64 j
+  const int sd = (lane & 3) ^ (int)scale_swz((uint32_t)srow);    // the same for every j
   auto issue_scales = [&](int chunk, int j) {
     GemmScales& c = sc[chunk % 3];
-    const int stp = min(4 * chunk + sd, nk - 1);
+    const int word = min(4 * chunk + sd, nb - 1);
     const int r = 64 * j + srow;
-    __builtin_amdgcn_global_load_lds(as + (int64_t)min(m0 + r, M - 1) * lds + 4 * stp, &c.a[(64 * j + 16 * wave) * 4],
-                                     4, 0, 0);
-    __builtin_amdgcn_global_load_lds(bs + (int64_t)min(n0 + r, N - 1) * lds + 4 * stp, &c.b[(64 * j + 16 * wave) * 4],
-                                     4, 0, 0);
+    __builtin_amdgcn_global_load_lds(as + (int64_t)min(m0 + r, M - 1) * lds + 4 * word,
+                                     &c.a[(64 * j + 16 * wave) * 4], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(bs + (int64_t)min(n0 + r, N - 1) * lds + 4 * word,
+                                     &c.b[(64 * j + 16 * wave) * 4], 4, 0, 0);
   };
   auto issue = [&](int ks) {
     GemmStage& s = st[ks % kGemmStages];
-    const int64_t ko = (int64_t)ks * 64;
+    const uint32_t off = (uint32_t)min(ks * 128 + gch * 16, last_chunk_byte);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(pa[j] + ko, &s.a[j * 256 + wave * 64], 16, 0, 0);
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(ac + (int64_t)min(m0 + 32 * j, M - 1) * ldq + (oa[j] + off),
+                                       &s.a[j * 256 + wave * 64], 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(pb[j] + ko, &s.b[j * 256 + wave * 64], 16, 0, 0);
-    issue_scales((ks >> 2) + 1, ks & 3);
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds(bc + (int64_t)min(n0 + 32 * j, N - 1) * ldq + (ob[j] + off),
+                                       &s.b[j * 256 + wave * 64], 16, 0, 0);
+    issue_scales((ks >> 1) + 1, 2 * (ks & 1));
+    issue_scales((ks >> 1) + 1, 2 * (ks & 1) + 1);
   };
 
-  // Fragment reads: row wm*128 + 32 i + fr, chunk (2 sub + fh) ^ swz(fr).
+  // Fragment reads for sub-step u: row wm*128 + 32 i + fr, chunk (2u + fh) ^ gemm_swz(fr).
   const int wm = wave & 1, wn = wave >> 1;
   const int fr = lane & 31, fh = lane >> 5;
   const uint32_t sw = gemm_swz((uint32_t)fr);
-  const uint32_t rowA = (uint32_t)(wm * 128 + fr) * 64, rowB = (uint32_t)(wn * 128 + fr) * 64;
-  const uint32_t pos0 = (((uint32_t)fh) ^ sw) * 16, pos1 = (((uint32_t)(2 + fh)) ^ sw) * 16;
+  const uint32_t rowA = (uint32_t)(wm * 128 + fr) * 128, rowB = (uint32_t)(wn * 128 + fr) * 128;
+  uint32_t pos[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pos[u] = (((uint32_t)(2 * u + fh)) ^ sw) * 16;
+
+  // Scale words of step ks for the lane's rows (wm*128 + 32 i + fr for A, likewise B):
+  // word 2 (ks % 2) + h (h = 0 for sub-steps 0-1, 1 for 2-3) at position ^ scale_swz(row),
+  // which depends only on fr for these rows.
+  const uint32_t fsw = scale_swz((uint32_t)fr);
+  const uint32_t posA = (uint32_t)(wm * 128 + fr) * 4, posB = (uint32_t)(wn * 128 + fr) * 4;
+  auto scales_of = [&](int ks, uint32_t sa_[2][4], uint32_t sb_[2][4]) {
+    const GemmScales& c = sc[(ks >> 1) % 3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t d = ((uint32_t)(2 * (ks & 1) + h)) ^ fsw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa_[h][i] = c.a[posA + d + 32 * 4 * i] >> (8 * fh);
+        sb_[h][i] = c.b[posB + d + 32 * 4 * i] >> (8 * fh);
+      }
+    }
+  };
 
   v16f_t acc[4][4];
 #pragma unroll
@@ -197,96 +240,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f_t{};
 
-  // Pipeline: while the 16 MFMAs of one sub-step run, the fragments of the next one
-  // are already being read.  The barrier that publishes step ks+1 sits between the two
-  // sub-steps of step ks, so the MFMAs never wait for it; right after it the loads of
-  // step ks+3 go into the stage step ks-1 used (its last reads fed MFMAs issued before
-  // the barrier), leaving two steps in flight behind the one being consumed.
-  // The scale word of step ks for the lane's rows wm*128 + 32 i + fr (A) and
-  // wn*128 + 32 i + fr (B): position ((ks & 3) ^ scale_swz(row)) of the row, and
-  // scale_swz depends only on fr for these rows.
-  const uint32_t fsw = scale_swz((uint32_t)fr);
-  const uint32_t posA = (uint32_t)(wm * 128 + fr) * 4, posB = (uint32_t)(wn * 128 + fr) * 4;
-  auto scales_of = [&](int ks, uint32_t sa_[4], uint32_t sb_[4]) {
-    const GemmScales& c = sc[(ks >> 2) % 3];
-    const uint32_t d = ((uint32_t)ks & 3u) ^ fsw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa_[i] = c.a[posA + d + 32 * 4 * i] >> (8 * fh);
-      sb_[i] = c.b[posB + d + 32 * 4 * i] >> (8 * fh);
-    }
-  };
+  // Pipeline: while the 16 MFMAs of one sub-step run, the fragments of the next are
+  // read.  The barrier that publishes step ks+1 sits before the last sub-step of step
+  // ks, after every fragment of step ks is in registers; right after it the loads of
+  // step ks+2 go into the stage step ks used, so one step is in flight behind the one
+  // being consumed.  With one wave per SIMD the matrix core idles whenever the wave
+  // issues anything else between two MFMAs for longer than one MFMA lasts, so reads
+  // and loads are interleaved one by one with the MFMAs (scheduling groups).
+  // Every step runs the same body: the last two issue loads past k at clamped, in-bounds
+  // addresses and read a stage nobody fills with data that is never used, which keeps
+  // the accumulators out of joins that made the compiler shuffle and spill them.  With
+  // k % 256 == 128 the last step has two sub-steps: the other two take zero codes.
 #pragma unroll
   for (int j = 0; j < 4; ++j) issue_scales(0, j);
-#pragma unroll
-  for (int p = 0; p < kGemmStages - 1; ++p)
-    if (p < nk) issue(p);
-  if (nk >= 3) wait_vm<2 * kLoadsPerStep>();
-  else if (nk == 2) wait_vm<kLoadsPerStep>();
-  else wait_vm<0>();
+  issue(0);
+  issue(1);
+  wait_vm<kLoadsPerStep>();
   gemm_barrier();
-  GemmFrags cur, nxt;
-  uint32_t sa[4], sb[4];
-  gemm_read(st[0], rowA + pos0, rowB + pos0, cur);
+  GemmFrags f0, f1;
+  uint32_t sa[2][4], sb[2][4];
+  gemm_read(st[0], rowA + pos[0], rowB + pos[0], f0);
   scales_of(0, sa, sb);
+  const int half_step = (nb & 1) ? nk - 1 : -1;
 
-  // One K step; MODE 0: steps ks+1 .. ks+3 exist (refill with ks+3), 3: ks+1 and ks+2
-  // exist, 1: only ks+1, 2: ks is the last.  The body has no branch.  With one wave
-  // per SIMD the matrix core idles whenever the wave issues anything else between two
-  // MFMAs for longer than one MFMA lasts, so the reads and loads are interleaved one by
-  // one with the MFMAs (scheduling groups); only the wait and the barrier stand alone.
-  auto step = [&](int ks, auto mode) {
-    constexpr int MODE = decltype(mode)::value;
+  for (int ks = 0; ks < nk; ++ks) {
     const GemmStage& s = st[ks % kGemmStages];
-    gemm_read(s, rowA + pos1, rowB + pos1, nxt);
-    gemm_mma<0>(cur, sa, sb, acc);
+    gemm_read(s, rowA + pos[1], rowB + pos[1], f1);
+    gemm_mma<0>(f0, sa[0], sb[0], acc);
+    interleave<8, 0, 1>();
+    interleave<8, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_read(s, rowA + pos[2], rowB + pos[2], f0);
+    gemm_mma<1>(f1, sa[0], sb[0], acc);
+    interleave<8, 0, 1>();
+    interleave<8, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_read(s, rowA + pos[3], rowB + pos[3], f1);
+    {
+      const int keep = ks == half_step ? 0 : -1;   // uniform; an AND, not a branch
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f0.a[i] &= keep, f1.a[i] &= keep;
+    }
+    gemm_mma<2>(f0, sa[1], sb[1], acc);
+    interleave<8, 0, 1>();
+    interleave<8, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t sa1[4], sb1[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa1[i] = sa[i], sb1[i] = sb[i];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    for (int i = 0; i < 4; ++i) sa1[i] = sa[1][i], sb1[i] = sb[1][i];
+    wait_vm<0>();      // step ks+1 has landed (no later step has been issued yet)
+    gemm_barrier();
+    issue(ks + 2);
+    scales_of(ks + 1, sa, sb);
+    gemm_read(st[(ks + 1) % kGemmStages], rowA + pos[0], rowB + pos[0], f0);
+    gemm_mma<3>(f1, sa1, sb1, acc);
+    interleave<10, 2, 1>();
+    interleave<6, 0, 1>();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MODE != 2) {
-      // step ks+1 has landed once at most step ks+2's loads remain
-      if constexpr (MODE == 0 || MODE == 3) wait_vm<kLoadsPerStep>();
-      else wait_vm<0>();
-      gemm_barrier();
-      if constexpr (MODE == 0) issue(ks + 3);
-      const GemmStage& s1 = st[(ks + 1) % kGemmStages];
-      scales_of(ks + 1, sa, sb);
-      gemm_read(s1, rowA + pos0, rowB + pos0, cur);
-    }
-    gemm_mma<1>(nxt, sa1, sb1, acc);
-    if constexpr (MODE == 0) {
-#pragma unroll
-      for (int g = 0; g < 10; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
-      }
-#pragma unroll
-      for (int g = 0; g < 6; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    } else if constexpr (MODE != 2) {
-#pragma unroll
-      for (int g = 0; g < 12; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  int ks = 0;
-  for (; ks + 3 < nk; ++ks) step(ks, std::integral_constant<int, 0>{});
-  if (ks + 2 < nk) step(ks++, std::integral_constant<int, 3>{});
-  if (ks + 1 < nk) step(ks++, std::integral_constant<int, 1>{});
-  step(ks, std::integral_constant<int, 2>{});
+  }
+  wait_vm<0>();   // the loads issued past k land in LDS before anything reuses it
 
   // Epilogue: register q of block (i, j) is C row m0 + wm*128 + 32 i + 8(q/4) + 4 fh + q%4,
   // column n0 + wn*128 + 32 j + fr.
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // every wave has finished reading the stages; pieces that cross the edge of C, or
     // rows not 16-byte aligned (n % 8 != 0), are stored element by element.
     gemm_barrier();
-    const int br = m0 + wm * 128, bc = n0 + wn * 128;
+    const int br = m0 + wm * 128, bc0 = n0 + wn * 128;
     uint16_t* e = reinterpret_cast<uint16_t*>(&lds_) + wave * 128 * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -313,12 +325,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int it = 0; it < 32; ++it) {
       const int row = 4 * it + (lane >> 4), c8 = (lane & 15) * 8;
       if (br + row >= M) continue;
-      uint16_t* dst = c16 + (int64_t)(br + row) * N + bc + c8;
+      uint16_t* dst = c16 + (int64_t)(br + row) * N + bc0 + c8;
       const uint16_t* src = e + row * 128 + c8;
-      if (vec && bc + c8 + 8 <= N) {
+      if (vec && bc0 + c8 + 8 <= N) {
         *reinterpret_cast<u32x4_g*>(dst) = *reinterpret_cast<const u32x4_g*>(src);
       } else {
-        for (int x = 0; x < 8 && bc + c8 + x < N; ++x) dst[x] = src[x];
+        for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) dst[x] = src[x];
       }
     }
     return;
@@ -331,10 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fh + (q & 3);
-        if (row < M && col < N) {
-          const int64_t o = (int64_t)row * N + col;
-          static_cast<float*>(cout)[o] = acc[i][j][q];
-        }
+        if (row < M && col < N) static_cast<float*>(cout)[(int64_t)row * N + col] = acc[i][j][q];
       }
     }
   }
