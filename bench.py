@@ -10,7 +10,9 @@ data from cache.
 
 Other workloads (`--config`): weight [8192 x 8192] fp32 NVFP4 16x16 + MXFP4
 ("weight"), the Wgrad pair with the 128x128 RHT ("wgrad"), IF4 + dequantize on
-[32768 x 8192] ("if4").  Each prints one JSON line; `--config all` prints one per
+[32768 x 8192] ("if4"), and the GEMM that consumes MXFP4 operands, Y = X W^T with
+8192 x 8192 x 8192 and bf16 output ("gemm"; measured in FLOP/s against the dense
+FP4 matrix-core peak).  Each prints one JSON line; `--config all` prints one per
 workload.
 
 The roofline object reports the dominant kernel: algorithmic bytes per launch
@@ -33,12 +35,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0
+PEAK_MFMA_FP4_TFLOPS = 10100.0
 
 
-def source_digest() -> str:
+# The sources each profiled kernel is built from; a change to any other file leaves its
+# recorded counters valid.
+KERNEL_SOURCES = {
+    "k_nvfp4_fused": ["fp4q_quant.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
+    "k_gemm_mxfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
+}
+
+
+def source_digest(kernel: str | None = None) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp4_05_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = KERNEL_SOURCES.get(kernel) or sorted(os.listdir(csrc))
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -52,7 +64,7 @@ def counter_traffic(kernel: str):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get("kernels", {}).get(kernel)
-    if not ent or ent.get("source_digest") != source_digest():
+    if not ent or ent.get("source_digest") != source_digest(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -315,6 +327,72 @@ class IF4RoundTrip(Workload):
                 "sample": f"IF4 of rows 0..{nrows - 1} ({nrows}x{self.cols}), single thread, {dt:.1f} s"}
 
 
+class GemmMXFP4(Workload):
+    """Y = X W^T on MXFP4 operands (the forward GEMM after quantization): X an activation
+    [8192 tokens x 8192] drawn as the activation workload's (N(0,1), 1% of the columns
+    x30, bf16), W the weight workload's [8192 x 8192] N(0, 0.02^2) fp32; both quantized
+    by fp4q_quantize_mxfp4 during setup, Y in bf16."""
+    name = "fprop_gemm_mxfp4_8192x8192x8192_bf16_out"
+    m = n = k = 8192
+    bound, peak, unit = "mfma", PEAK_MFMA_FP4_TFLOPS, "TFLOP/s"
+    dtype = "fp4"   # E2M1 x E2M1 products, fp32 accumulation
+    metric = "MXFP4 GEMM FLOP/s and % of MI355X dense FP4 matrix-core peak"
+
+    def __init__(self):
+        self.flops = 2 * self.m * self.n * self.k
+        self.elements = self.flops
+        self.algo_bytes = (self.m + self.n) * (self.k // 2 + self.k // 32) + 2 * self.m * self.n
+        self.kernel = "k_gemm_mxfp4"
+        self.kernel_bytes = self.algo_bytes
+
+    def setup(self, nbuf):
+        import numpy as np
+        import torch
+        import synth_inputs as si
+        from block_scaled_fp4_05_amd import binding as B
+        self.B = B
+        xb = si.activation(self.m, self.k, seed=2)
+        w = si.weight(self.n, self.k, seed=3)
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to("cuda")
+        qa = B.quantize_mxfp4(x)
+        qb = B.quantize_mxfp4(torch.from_numpy(w).to("cuda"))
+        torch.cuda.synchronize()
+        self.host = {key: t.cpu().numpy() for key, t in (("ac", qa["codes"]), ("as", qa["scales"]),
+                                                        ("bc", qb["codes"]), ("bs", qb["scales"]))}
+        del x
+        nbuf = min(nbuf, 2)   # 67 MB of operands + 134 MB of output per set: two sets exceed the cache
+        self.ops = [(qa, qb)] + [({k: v.clone() for k, v in qa.items()}, {k: v.clone() for k, v in qb.items()})
+                                 for _ in range(nbuf - 1)]
+        self.y = [torch.empty(self.m, self.n, dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+
+    def step(self, i):
+        B = self.B
+        qa, qb = self.ops[i % len(self.ops)]
+        B.fp4q_gemm_mxfp4(qa["codes"], qa["scales"], qb["codes"], qb["scales"], self.m, self.n, self.k, B.BF16,
+                          self.y[i % len(self.y)])
+
+    def kernel_launch(self, i):
+        self.step(i)
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        import oracle
+        h = self.host
+        oracle.lib()                                  # load (and if needed build) before timing
+        t0 = time.perf_counter()
+        oracle.gemm_mxfp4(h["ac"][:1], h["as"][:1], h["bc"][:32], h["bs"][:32])
+        per_out = (time.perf_counter() - t0) / 32
+        nout = int(max(64, min(self.m * 64, budget_s / per_out)))
+        rows, cols = max(1, nout // 64), 64
+        t0 = time.perf_counter()
+        oracle.gemm_mxfp4(np.ascontiguousarray(h["ac"][:rows]), np.ascontiguousarray(h["as"][:rows]),
+                          np.ascontiguousarray(h["bc"][:cols]), np.ascontiguousarray(h["bs"][:cols]))
+        dt = time.perf_counter() - t0
+        return {"value": 2.0 * rows * cols * self.k / dt, "unit": "FLOP/s", "cores": 1, "kind": "oracle",
+                "sample": f"outputs [0..{rows - 1}] x [0..{cols - 1}] of Y (k = {self.k}), exact binary64 sums, "
+                          f"single thread, {dt:.1f} s"}
+
+
 class DeviceCopy(Workload):
     """Calibration, not a hot-path row: a plain device-to-device copy of 64 MiB.  It gives
     the copy rate this machine reaches and the factor between rocprofv3's FETCH_SIZE /
@@ -345,7 +423,8 @@ class DeviceCopy(Workload):
         return None
 
 
-WORKLOADS = {"activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT, "if4": IF4RoundTrip}
+WORKLOADS = {"activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT, "if4": IF4RoundTrip,
+             "gemm": GemmMXFP4}
 CALIBRATION = {"copy": DeviceCopy}
 
 
@@ -377,12 +456,18 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
     e1.record(stream)
     torch.cuda.synchronize()
     k_mean = e0.elapsed_time(e1) / nk
-    achieved = wl.kernel_bytes / (k_mean * 1e-3) / 1e9
+    mfma = getattr(wl, "bound", "hbm") == "mfma"
+    if mfma:
+        achieved = wl.flops / (k_mean * 1e-3) / 1e12
+        peak, unit = wl.peak, wl.unit
+    else:
+        achieved = wl.kernel_bytes / (k_mean * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBPS, "GB/s"
     value = wl.elements / (ms_per_step * 1e-3)
     line = {
-        "metric": "FP4-quantized elements/s and achieved HBM GB/s (% of MI355X peak)",
+        "metric": getattr(wl, "metric", "FP4-quantized elements/s and achieved HBM GB/s (% of MI355X peak)"),
         "value": value,
-        "unit": "elements/s",
+        "unit": "FLOP/s" if mfma else "elements/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
@@ -390,13 +475,13 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": getattr(wl, "dtype", "f32"),
         "data": "synthetic",
         "config": {"workload": wl.name, "elements_per_step": wl.elements, "algorithmic_bytes_per_step": wl.algo_bytes,
                    "whole_step_GBps": wl.algo_bytes / (ms_per_step * 1e-3) / 1e9,
                    "whole_step_frac_of_hbm_peak": wl.algo_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS},
-        "roofline": {"bound": "hbm", "kernel": wl.kernel, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": counter_traffic(wl.kernel),
+        "roofline": {"bound": "mfma" if mfma else "hbm", "kernel": wl.kernel, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": counter_traffic(wl.kernel),
                      "kernel_ms_mean": k_mean, "kernel_launches_timed": nk,
                      "algorithmic_bytes_per_launch": wl.kernel_bytes},
     }
@@ -411,6 +496,15 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
     pick = lambda q: st[min(len(st) - 1, int(q * (len(st) - 1) + 0.5))]
     line["config"]["step_ms_p10"], line["config"]["step_ms_p50"], line["config"]["step_ms_p90"] = (
         pick(0.1), pick(0.5), pick(0.9))
+    if mfma:
+        flops_s = wl.flops / (ms_per_step * 1e-3)
+        line["config"]["whole_step_TFLOPs"] = flops_s / 1e12
+        line["config"]["whole_step_frac_of_fp4_peak"] = flops_s / 1e12 / wl.peak
+        if cpu_budget > 0:
+            cb = wl.cpu_baseline(cpu_budget)
+            if cb is not None:
+                line["cpu_baseline"] = cb
+        return line
     # the call with the tensor amax given by the caller (no amax pass)
     given = getattr(wl, "given_launch", wl.kernel_launch)
     for i in range(4):
