@@ -75,6 +75,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "ora_quantize_if4": (None, [_P, _I, _I64, _I64, _F, _P, _P]),
         "ora_dequantize": (None, [_I, _P, _P, _F, _I64, _I64, _P]),
         "ora_gemm_mxfp4": (None, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+        "ora_gemm_nvfp4": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _I64, _P, _P]),
         "ora_hadamard_entry": (_I, [_I, _I]),
         "ora_rht": (None, [_P, _I, _I64, _I64, _P, _I, _P]),
         "ora_rht_column": (None, [_P, _I, _I64, _I64, _I64, _P, _P]),
@@ -268,6 +269,21 @@ def gemm_mxfp4(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b
     c = np.zeros((m, n), dtype=np.float64)
     cabs = np.zeros((m, n), dtype=np.float64)
     lib().ora_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), m, n, k, _ptr(c), _ptr(cabs))
+    return c, cabs
+
+
+def gemm_nvfp4(a_codes, a_scales, gs_a, b_codes, b_scales, gs_b):
+    """C = A B^T over two row-wise NVFP4 1x16 operands with tensor scales gs_a, gs_b:
+    (sum of exact products r s r' s') / (gs_a gs_b).  Returns (C, sum |products| / same)."""
+    a_codes, a_scales = np.ascontiguousarray(a_codes), np.ascontiguousarray(a_scales)
+    b_codes, b_scales = np.ascontiguousarray(b_codes), np.ascontiguousarray(b_scales)
+    m, k = a_codes.shape[0], a_codes.shape[1] * 2
+    n = b_codes.shape[0]
+    assert b_codes.shape == (n, k // 2) and a_scales.shape == (m, k // 16) and b_scales.shape == (n, k // 16)
+    c = np.zeros((m, n), dtype=np.float64)
+    cabs = np.zeros((m, n), dtype=np.float64)
+    lib().ora_gemm_nvfp4(_ptr(a_codes), _ptr(a_scales), float(gs_a), _ptr(b_codes), _ptr(b_scales), float(gs_b),
+                         m, n, k, _ptr(c), _ptr(cabs))
     return c, cabs
 
 

@@ -523,6 +523,36 @@ void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
     }
 }
 
+/* The same product over two row-wise NVFP4 1x16 operands [NV "NVFP4フロー図"], whose
+ * dequantized values are r * s / gs (r the E2M1 value, s the block's E4M3 scale, gs
+ * the operand's tensor encode scale) [NV "scaleの導出"]:
+ *     C[i][j] = (sum_t (r_a s_a)(r_b s_b)) / (gs_a * gs_b).
+ * r * s has at most six significant bits, so every product and (for the scales that
+ * quantization produces) the binary64 sum are exact; the one division by the binary64
+ * product gs_a * gs_b (exact: two 24-bit significands) rounds once.  cabs is the sum of
+ * |products| over the same divisor.  Scale row strides: k/16 bytes. */
+void ora_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float gs_a, const uint8_t* b_codes,
+                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, double* c,
+                    double* cabs)
+{
+    const double g = (double)gs_a * (double)gs_b;
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                double av = (double)ora_e2m1_decode(get_nibble(a_codes, k, i, t)) *
+                            (double)ora_e4m3_decode(a_scales[i * (k / 16) + t / 16]);
+                double bv = (double)ora_e2m1_decode(get_nibble(b_codes, k, j, t)) *
+                            (double)ora_e4m3_decode(b_scales[j * (k / 16) + t / 16]);
+                acc += av * bv;
+                mag += fabs(av * bv);
+            }
+            c[i * n + j] = acc / g;
+            if (cabs) cabs[i * n + j] = mag / g;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Random Hadamard transform [NV "ランダムアダマール変換"]                         */
 /* ------------------------------------------------------------------------- */

@@ -45,6 +45,9 @@ void ora_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, float 
 
 void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                     const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, double* c, double* cabs);
+void ora_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float gs_a, const uint8_t* b_codes,
+                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, double* c,
+                    double* cabs);
 int ora_hadamard_entry(int i, int t);
 void ora_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
              int inverse, float* y);

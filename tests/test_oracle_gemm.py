@@ -90,3 +90,63 @@ def test_gemm_of_quantized_gaussians_tracks_the_float_product():
     # E2M1 with a per-32 power-of-two scale keeps each element within about 1/6 of its
     # block maximum; two independently quantized operands give roughly 0.1 relative error.
     assert 0.02 < rel < 0.2
+
+
+# --- NVFP4 1x16 operands ------------------------------------------------------------
+
+def _nv_operand(rng, rows, k):
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, size=(rows, k // 16), dtype=np.uint8)   # positive, finite e4m3fn codes
+    return codes, scales
+
+
+def _e4m3_exact(code: int) -> Fraction:
+    # independent decode: torch's own float8_e4m3fn interpretation of the byte
+    import torch
+    v = torch.tensor([code], dtype=torch.uint8).view(torch.float8_e4m3fn).float().item()
+    return Fraction(v)
+
+
+def test_nvfp4_gemm_brute_force_with_exact_rationals():
+    rng = np.random.default_rng(14)
+    m, n, k = 2, 3, 64
+    ac, as_ = _nv_operand(rng, m, k)
+    bc, bs = _nv_operand(rng, n, k)
+    gs_a, gs_b = np.float32(37.25), np.float32(1234.5678)
+    c, cabs = oracle.gemm_nvfp4(ac, as_, gs_a, bc, bs, gs_b)
+
+    def val(codes, scales, r, t):
+        byte = int(codes[r, t // 2])
+        nib = (byte >> 4) if (t & 1) else (byte & 15)
+        return _e2m1_exact(nib) * _e4m3_exact(int(scales[r, t // 16]))
+
+    g = Fraction(float(gs_a)) * Fraction(float(gs_b))
+    for i in range(m):
+        for j in range(n):
+            exact = sum(val(ac, as_, i, t) * val(bc, bs, j, t) for t in range(k)) / g
+            assert abs(Fraction(c[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 52)   # one binary64 rounding
+            mag = sum(abs(val(ac, as_, i, t) * val(bc, bs, j, t)) for t in range(k)) / g
+            assert abs(Fraction(cabs[i, j]) - mag) <= mag * Fraction(1, 2 ** 52)
+
+
+def test_nvfp4_gemm_equals_matmul_of_the_dequantized_operands_at_unit_tensor_scale():
+    rng = np.random.default_rng(15)
+    m, n, k = 19, 23, 256
+    ac, as_ = _nv_operand(rng, m, k)
+    bc, bs = _nv_operand(rng, n, k)
+    c, _ = oracle.gemm_nvfp4(ac, as_, 1.0, bc, bs, 1.0)
+    a = oracle.dequantize(0, ac, as_, 1.0, m, k).astype(np.float64)   # r * s, exact at gs = 1
+    b = oracle.dequantize(0, bc, bs, 1.0, n, k).astype(np.float64)
+    assert np.array_equal(c, a @ b.T)
+
+
+def test_nvfp4_gemm_of_quantized_gaussians_tracks_the_float_product():
+    m, n, k = 40, 48, 1024
+    x = si.weight(m, k, seed=23, std=1.0)
+    w = si.weight(n, k, seed=24, std=0.02)
+    ac, as_, gsa = oracle.quantize_nvfp4(x)
+    bc, bs, gsb = oracle.quantize_nvfp4(w)
+    c, _ = oracle.gemm_nvfp4(ac, as_, gsa, bc, bs, gsb)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    rel = np.linalg.norm(c - ref) / np.linalg.norm(ref)
+    assert 0.01 < rel < 0.15      # 16-element blocks with E4M3 scales: tighter than MXFP4
