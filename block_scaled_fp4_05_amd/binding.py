@@ -27,7 +27,7 @@ AMAX_COMPUTE, AMAX_GIVEN = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_E_NULL", 2: "FP4Q_E_SHAPE", 3: "FP4Q_E_ALIGN", 4: "FP4Q_E_ARG", 5: "FP4Q_E_HIP"}
 
 EXPORTS = ["fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_if4",
-           "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_dequantize", "fp4q_amax", "fp4q_set_onepass_wait", "fp4q_onepass_fallbacks",
+           "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax", "fp4q_set_onepass_wait", "fp4q_onepass_fallbacks",
            "fp4q_rht_signs_from_seed",
            "fp4q_status_string", "fp4q_abi_version"]
 
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
             "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P],
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
             "fp4q_gemm_mxfp4": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P],
+            "fp4q_gemm_nvfp4": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P],
             "fp4q_dequantize": [_I, _P, _P, _P, _I64, _I64, _I, _P, _P],
             "fp4q_amax": [_P, _I, _I64, _I64, _P, _P],
             "fp4q_set_onepass_wait": [_U],
@@ -140,6 +141,11 @@ def fp4q_rht(x, dt, rows, cols, signs, inverse, y, stream=None) -> int:
 def fp4q_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m, n, k, out_dt, c, stream=None) -> int:
     return _check("fp4q_gemm_mxfp4", lib().fp4q_gemm_mxfp4(
         _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), m, n, k, out_dt, _p(c), _s(stream)))
+
+
+def fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, out_dt, c, stream=None) -> int:
+    return _check("fp4q_gemm_nvfp4", lib().fp4q_gemm_nvfp4(
+        _p(a_codes), _p(a_scales), _p(a_ts), _p(b_codes), _p(b_scales), _p(b_ts), m, n, k, out_dt, _p(c), _s(stream)))
 
 
 def fp4q_dequantize(fmt, codes, scales, tensor_scale, rows, cols, out_dt, y, stream=None) -> int:
@@ -260,6 +266,14 @@ def gemm_mxfp4(a: dict, b: dict, out_dtype=torch.float32, stream=None) -> torch.
     m, n, k = a["codes"].shape[0], b["codes"].shape[0], a["codes"].shape[1] * 2
     c = torch.empty(m, n, dtype=out_dtype, device=a["codes"].device)
     fp4q_gemm_mxfp4(a["codes"], a["scales"], b["codes"], b["scales"], m, n, k, _dt(c), c, stream)
+    return c
+
+
+def gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """C = A B^T / (gs_a gs_b) for two row-wise NVFP4 operands (codes, scales, tensor scale)."""
+    m, n, k = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    c = torch.empty(m, n, dtype=out_dtype, device=a_codes.device)
+    fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, _dt(c), c, stream)
     return c
 
 

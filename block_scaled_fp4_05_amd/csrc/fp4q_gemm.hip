@@ -349,6 +349,208 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// NVFP4 1x16 operands: the scaled MFMA takes only power-of-two (E8M0) block scales, and an
+// E4M3 scale has a 3-bit significand, so each element is decoded to r * s (at most six
+// significant bits: exact in bf16) and multiplied on the bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16); the tensor scales are applied once to the fp32 sums.
+// The scaled FP4 convert applies only the exponent of its scale operand (checked on the
+// box with non-power-of-two scales), so the decode converts with scale 1 and multiplies
+// by s in fp32.
+// ---------------------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+constexpr int kNvStages = 4;
+constexpr int kNvLoads = 12;   // per wave and K step: 4 + 4 code chunks, 4 scale pieces
+
+// A K step is 128 elements: 64 bytes of codes and 8 scale bytes per row.
+struct NvStage {
+  u32x4_g a[kGemmTile * 4];   // 256 rows x four 16-byte chunks (swizzled)
+  u32x4_g b[kGemmTile * 4];
+  uint32_t sa[kGemmTile * 2]; // the row's two scale words of the step
+  uint32_t sb[kGemmTile * 2];
+};
+
+// Chunk c of staged row r at position c ^ nv_swz(r): 16 consecutive rows at one chunk
+// fall in distinct bank groups with 32 or 64 banks.
+__device__ __forceinline__ uint32_t nv_swz(uint32_t r) { return ((r >> 2) & 1u) | ((((r >> 1) ^ (r >> 3)) & 1u) << 1); }
+
+// Eight E2M1 codes (one word, element 2i in the low nibble of byte i) times the block
+// scale s -> eight bf16 in element order.  r * s is exact in fp32 and in bf16, so taking
+// the high half of each fp32 is exact.
+__device__ __forceinline__ uint32_t nv_pair(v2f_t p, float s) {
+  return __builtin_amdgcn_perm(__float_as_uint(p.y * s), __float_as_uint(p.x * s), 0x07060302u);
+}
+__device__ __forceinline__ bf16x8_t nv_decode(uint32_t w, float s) {
+  const uint32_t o0 = nv_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), s);
+  const uint32_t o1 = nv_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), s);
+  const uint32_t o2 = nv_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), s);
+  const uint32_t o3 = nv_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), s);
+  return __builtin_bit_cast(bf16x8_t, u32x4_g{o0, o1, o2, o3});
+}
+
+__device__ __forceinline__ float e4m3_byte(uint32_t w, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+
+// C = (A B^T) / (gs_a gs_b).  v_mfma_f32_32x32x16_bf16 takes, per lane, eight
+// consecutive K elements of row l % 32 in its half l / 32 of the instruction's 16; K
+// order inside a step is free as long as A and B agree, so MFMA q (0..7) of a step
+// gives lane half 0 the row's code word q (elements 8q..8q+7, block q/2) and half 1 the
+// word 8 + q (block 4 + q/2): a lane reads 32 contiguous bytes of codes and one scale
+// word (blocks 4 fh .. 4 fh + 3) per row and step.
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ gsa,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ gsb, int M, int N,
+    int K, int tiles_m, int tiles_n, void* __restrict__ cout) {
+  __shared__ NvStage st[kNvStages];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  gemm_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * kGemmTile, n0 = tn * kGemmTile;
+  const int64_t ldq = K / 2, lds = K / 16;   // row strides of codes and scales, bytes
+  const int nk = K / 128;
+
+  // Codes: chunk p = 256 j + tid of a stage is row 64 j + tid / 4, position tid % 4,
+  // holding global chunk (tid % 4) ^ nv_swz(row).  Rows past the matrix read its last
+  // row; steps past k (issued by the last iterations) read the last step.
+  const int lr = tid >> 2;
+  const int gch = (tid & 3) ^ (int)nv_swz((uint32_t)lr);
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    oa[j] = (uint32_t)((min(m0 + 64 * j + lr, M - 1) - min(m0 + 64 * j, M - 1)) * (int)ldq);
+    ob[j] = (uint32_t)((min(n0 + 64 * j + lr, N - 1) - min(n0 + 64 * j, N - 1)) * (int)ldq);
+  }
+  // Scales: piece g (0..7) of an operand is rows 32 g .. 32 g + 31, two words each;
+  // wave w loads pieces 2w and 2w+1 of A and of B.
+  auto issue = [&](int ks) {
+    NvStage& s = st[ks % kNvStages];
+    const int kc = min(ks, nk - 1);
+    const uint32_t off = (uint32_t)(kc * 64 + gch * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(ac + (int64_t)min(m0 + 64 * j, M - 1) * ldq + (oa[j] + off),
+                                       &s.a[j * 256 + wave * 64], 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(bc + (int64_t)min(n0 + 64 * j, N - 1) * ldq + (ob[j] + off),
+                                       &s.b[j * 256 + wave * 64], 16, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = 2 * wave + h, row = 32 * g + (lane >> 1);
+      const int64_t so = (int64_t)kc * 8 + 4 * (lane & 1);
+      __builtin_amdgcn_global_load_lds(as + (int64_t)min(m0 + row, M - 1) * lds + so, &s.sa[64 * g], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(bs + (int64_t)min(n0 + row, N - 1) * lds + so, &s.sb[64 * g], 4, 0, 0);
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  const uint32_t sw = nv_swz((uint32_t)fr);
+  const uint32_t rowA = (uint32_t)(wm * 128 + fr) * 64, rowB = (uint32_t)(wn * 128 + fr) * 64;
+  const uint32_t p0 = (((uint32_t)(2 * fh)) ^ sw) * 16, p1 = (((uint32_t)(2 * fh + 1)) ^ sw) * 16;
+  const int srA = (wm * 128 + fr) * 2 + fh, srB = (wn * 128 + fr) * 2 + fh;
+
+  v16f_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f_t{};
+
+  // Every step runs the same body (loads past k are clamped and never read), so the
+  // wait count is the same everywhere: step ks has landed once at most the loads of
+  // steps ks+1 and ks+2 remain.
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int ks = 0; ks < nk; ++ks) {
+    wait_vm<2 * kNvLoads>();
+    gemm_barrier();   // step ks is in LDS for every wave; step ks-1's stage is free
+    issue(ks + 3);
+    const NvStage& s = st[ks % kNvStages];
+    u32x4_g ra[4][2], rb[4][2];
+    uint32_t wa[4], wb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* pa = reinterpret_cast<const char*>(s.a) + rowA + i * 32 * 64;
+      const char* pb = reinterpret_cast<const char*>(s.b) + rowB + i * 32 * 64;
+      ra[i][0] = *reinterpret_cast<const u32x4_g*>(pa + p0);
+      ra[i][1] = *reinterpret_cast<const u32x4_g*>(pa + p1);
+      rb[i][0] = *reinterpret_cast<const u32x4_g*>(pb + p0);
+      rb[i][1] = *reinterpret_cast<const u32x4_g*>(pb + p1);
+      wa[i] = s.sa[srA + 64 * i];
+      wb[i] = s.sb[srB + 64 * i];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      bf16x8_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
+        fb[i] = nv_decode(rb[i][q >> 2][q & 3], e4m3_byte(wb[i], q >> 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vm<0>();   // the loads issued past k land before anything reuses LDS
+
+  // Tensor scales: C = sum / (gs_a gs_b), applied as one multiply by fl(1 / fl(gs_a gs_b)).
+  const float inv = 1.0f / (gsa[0] * gsb[0]);
+  if constexpr (BF16OUT) {
+    gemm_barrier();
+    const int br = m0 + wm * 128, bc0 = n0 + wn * 128;
+    uint16_t* e = reinterpret_cast<uint16_t*>(&st[0]) + wave * 128 * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          e[(32 * i + 8 * (q >> 2) + 4 * fh + (q & 3)) * 128 + 32 * j + fr] = bf16_rne(acc[i][j][q] * inv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    uint16_t* c16 = static_cast<uint16_t*>(cout);
+    const bool vec = (N & 7) == 0;
+    for (int it = 0; it < 32; ++it) {
+      const int row = 4 * it + (lane >> 4), c8 = (lane & 15) * 8;
+      if (br + row >= M) continue;
+      uint16_t* dst = c16 + (int64_t)(br + row) * N + bc0 + c8;
+      const uint16_t* src = e + row * 128 + c8;
+      if (vec && bc0 + c8 + 8 <= N) {
+        *reinterpret_cast<u32x4_g*>(dst) = *reinterpret_cast<const u32x4_g*>(src);
+      } else {
+        for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) dst[x] = src[x];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + 32 * j + fr;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fh + (q & 3);
+        if (row < M && col < N) static_cast<float*>(cout)[(int64_t)row * N + col] = acc[i][j][q] * inv;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 bool launch_gemm_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, int64_t m,
@@ -360,6 +562,16 @@ bool launch_gemm_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, 
     k_gemm_mxfp4<true><<<(unsigned)total, 256, 0, st>>>(ac, as, bc, bs, (int)m, (int)n, (int)k, tiles_m, tiles_n, c);
   else
     k_gemm_mxfp4<false><<<(unsigned)total, 256, 0, st>>>(ac, as, bc, bs, (int)m, (int)n, (int)k, tiles_m, tiles_n, c);
+  return true;
+}
+
+bool launch_gemm_nvfp4(const uint8_t* ac, const uint8_t* as, const float* gsa, const uint8_t* bc, const uint8_t* bs,
+                       const float* gsb, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c, hipStream_t st) {
+  const int tiles_m = (int)((m + kGemmTile - 1) / kGemmTile), tiles_n = (int)((n + kGemmTile - 1) / kGemmTile);
+  const int64_t total = (int64_t)tiles_m * tiles_n;
+  if (total > 0x7FFFFFFF) return false;
+  auto kern = bf16_out ? k_gemm_nvfp4<true> : k_gemm_nvfp4<false>;
+  kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c);
   return true;
 }
 

@@ -71,5 +71,9 @@ void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const u
 bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,
                        hipStream_t st);
+// NVFP4 1x16 GEMM C = A B^T / (gs_a gs_b) on the bf16 MFMA -- fp4q_gemm.hip.  k % 128 == 0.
+bool launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const float* b_ts, int64_t m, int64_t n, int64_t k, bool bf16_out,
+                       void* c, hipStream_t st);
 
 }  // namespace fp4q

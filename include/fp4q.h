@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 3
+#define FP4Q_ABI_VERSION 4
 
 typedef enum {
     FP4Q_OK = 0,
@@ -172,10 +172,28 @@ fp4q_status fp4q_rht(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
  * activation X as A and the weight W as B.  Products and sums run on the block-scaled
  * MFMA with fp32 accumulation; the summation order is the hardware's.
  *   out_dt FP4Q_F32: c is float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
- * Shapes: m >= 1, n >= 1, k >= 128 with k % 128 == 0 and k < 2^31, m, n < 2^31.
+ * Shapes: m >= 1, n >= 1, k >= 128 with k % 128 == 0 and k <= 2^25, m, n < 2^31.
  */
 fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales,
+                            int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
+                            hipStream_t stream);
+
+/*
+ * The same product over two row-wise NVFP4 1x16 operands [NV "NVFP4フロー図";
+ * NV "scaleの導出"], whose dequantized values are r * s / gs:
+ *   c[i][j] = (sum_t (r_a s_a)(r_b s_b)) / (gs_a gs_b),
+ * with codes [rows][k/2], E4M3 scales [rows][k/16] as fp4q_quantize_nvfp4 writes them
+ * (row-wise, or the column-wise output of the transposed operand, e.g. the Wgrad pair
+ * after the RHT), and gs_a = *a_tensor_scale, gs_b = *b_tensor_scale (device floats,
+ * the encode scales the quantizer stored).  Each r * s (at most six significant bits)
+ * is decoded exactly to bf16 and multiplied on the bf16 MFMA with fp32 accumulation;
+ * the sums are multiplied by fl(1 / fl(gs_a gs_b)).
+ *   out_dt FP4Q_F32: float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
+ * Shapes as fp4q_gemm_mxfp4.  NVFP4 16x16 (2D) scale layouts are not accepted.
+ */
+fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                            const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
                             int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
                             hipStream_t stream);
 

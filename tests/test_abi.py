@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 3
+    assert B.fp4q_abi_version() == 4
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -110,6 +110,13 @@ def test_other_entry_points_validate():
     assert L.fp4q_gemm_mxfp4(A, A, A, A, 1 << 31, 64, 128, 0, A2, 0) == 2
     assert L.fp4q_gemm_mxfp4(A, MIS, A, A, 64, 64, 128, 0, A2, 0) == 3
     assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 256, 1, MIS, 0) == 3
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, (1 << 25) + 128, 0, A2, 0) == 2
+    # NVFP4 GEMM: tensor scales are device floats (4-byte aligned)
+    assert L.fp4q_gemm_nvfp4(A, A, None, A, A, A2, 64, 64, 128, 0, A2, 0) == 1
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 192, 0, A2, 0) == 2
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 5, A2, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, A2, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, A2, 0) == 3
     assert L.fp4q_onepass_fallbacks(0, None) == 1
     assert L.fp4q_amax(None, 0, 4, 4, A2, 0) == 1
     assert L.fp4q_amax(A, 0, 0, 4, A2, 0) == 2

@@ -121,3 +121,93 @@ def test_gemm_full_size_sampled():
     exact, cabs = oracle.gemm_mxfp4(ac[rows], as_[rows], bc[cols], bs[cols])
     got = c[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy()
     _check(got.astype(np.float64), exact, cabs, k, bf16=True)
+
+
+# ---------------------------------------------------------------------------------------
+# NVFP4 operands (bf16 MFMA after an exact decode).  Each product of two decoded values
+# r s has at most twelve significant bits, exact in fp32; an instruction sums 16, so the
+# summation depth is at most 4 + k/16.  The tensor scales add three roundings
+# (fl(gs_a gs_b), its reciprocal, the product): 3 u |C|.
+# ---------------------------------------------------------------------------------------
+
+def _nv_operand(rng, rows, k):
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, size=(rows, k // 16), dtype=np.uint8)   # positive finite e4m3fn codes
+    return codes, scales
+
+
+def _nv_check(got, exact, cabs, k, bf16=False):
+    tol = 2.0 * (4 + k / 16) * 2.0 ** -24 * cabs + 3.0 * 2.0 ** -24 * np.abs(exact)
+    if bf16:
+        tol = tol + 2.0 ** -8 * (np.abs(exact) + tol)
+    err = np.abs(got - exact)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, (f"{len(bad)} of {err.size} outside the bound; first {bad[:4].tolist()}, "
+                           f"err {err[tuple(bad[0])]:.3e} tol {tol[tuple(bad[0])]:.3e}")
+
+
+def _nv_gemm(ac, as_, ga, bc, bs, gb, out_dtype=torch.float32):
+    m, n, k = ac.shape[0], bc.shape[0], ac.shape[1] * 2
+    c = torch.full((m, n), float("nan"), dtype=out_dtype, device=DEV)
+    ta = torch.tensor([ga], dtype=torch.float32, device=DEV)
+    tb = torch.tensor([gb], dtype=torch.float32, device=DEV)
+    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B._dt(c), c)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("shape,bf16", [((256, 256, 128), False), ((300, 520, 384), False), ((1, 1, 128), False),
+                                        ((257, 129, 256), False), ((513, 768, 1024), False),
+                                        ((256, 256, 256), True), ((390, 200, 512), True), ((257, 130, 256), True)])
+def test_nvfp4_gemm_random_codes(shape, bf16):
+    m, n, k = shape
+    rng = np.random.default_rng(m * 5 + n * 11 + k)
+    ac, as_ = _nv_operand(rng, m, k)
+    bc, bs = _nv_operand(rng, n, k)
+    ga, gb = np.float32(173.25), np.float32(0.8125)
+    print(f"nvfp4 gemm m={m} n={n} k={k} bf16={bf16}", flush=True)
+    got = _nv_gemm(ac, as_, ga, bc, bs, gb, torch.bfloat16 if bf16 else torch.float32)
+    exact, cabs = oracle.gemm_nvfp4(ac, as_, ga, bc, bs, gb)
+    _nv_check(got, exact, cabs, k, bf16)
+
+
+def test_nvfp4_gemm_wgrad_after_rht_end_to_end():
+    """Wgrad = dY^T X from the column-wise NVFP4 operands after the 128-token RHT
+    (SR for the gradient, RTN for the activation): the product matches the oracle on the
+    library's own codes, and tracks the exact dY^T X, as H H^T = I promises."""
+    tokens, nout, nin = 1024, 256, 384
+    g_bits = si.wgrad_gradient(tokens, nout, seed=4)
+    x_bits = si.activation(tokens, nin, seed=5)
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(DEV)
+    signs = B.fp4q_rht_signs_from_seed(4)
+    qg = B.quantize_nvfp4(to_dev(g_bits), B.COLWISE, rnd=B.SR, sr_seed=40, rht_signs=signs)
+    qx = B.quantize_nvfp4(to_dev(x_bits), B.COLWISE, rnd=B.RTN, rht_signs=signs)
+    w = B.gemm_nvfp4(qg["col_codes"], qg["col_scales"], qg["tensor_scale"],
+                     qx["col_codes"], qx["col_scales"], qx["tensor_scale"]).cpu().numpy().astype(np.float64)
+    h = lambda t: t.cpu().numpy()
+    exact, cabs = oracle.gemm_nvfp4(h(qg["col_codes"]), h(qg["col_scales"]), float(h(qg["tensor_scale"])[0]),
+                                    h(qx["col_codes"]), h(qx["col_scales"]), float(h(qx["tensor_scale"])[0]))
+    _nv_check(w, exact, cabs, tokens)
+    f32 = lambda b: (np.ascontiguousarray(b).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = f32(g_bits).T @ f32(x_bits)
+    rel = np.linalg.norm(w - ref) / np.linalg.norm(ref)
+    assert rel < 0.2, rel
+
+
+def test_nvfp4_gemm_full_size_sampled():
+    m = n = k = 8192
+    rng = np.random.default_rng(9)
+    ac, as_ = _nv_operand(rng, m, k)
+    bc, bs = _nv_operand(rng, n, k)
+    ga, gb = np.float32(50.0), np.float32(3.0)
+    print("nvfp4 gemm full size", flush=True)
+    c = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+    ta = torch.tensor([ga], device=DEV)
+    tb = torch.tensor([gb], device=DEV)
+    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B.BF16, c)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 255, 256, 4095, 8190, 8191])
+    cols = np.array([0, 31, 32, 255, 256, 4096, 8191])
+    exact, cabs = oracle.gemm_nvfp4(ac[rows], as_[rows], ga, bc[cols], bs[cols], gb)
+    got = c[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy()
+    _nv_check(got.astype(np.float64), exact, cabs, k, bf16=True)
