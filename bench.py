@@ -12,7 +12,9 @@ Other workloads (`--config`): weight [8192 x 8192] fp32 NVFP4 16x16 + MXFP4
 ("weight"), the Wgrad pair with the 128x128 RHT ("wgrad"), IF4 + dequantize on
 [32768 x 8192] ("if4"), and the GEMM that consumes MXFP4 operands, Y = X W^T with
 8192 x 8192 x 8192 and bf16 output ("gemm"; measured in FLOP/s against the dense
-FP4 matrix-core peak).  Each prints one JSON line; `--config all` prints one per
+FP4 matrix-core peak), and the NVFP4 weight-gradient GEMM dY^T X on the Wgrad
+workload's RHT-quantized operands ("gemm_nvfp4"; against the dense bf16 peak, the
+MFMA it runs on).  Each prints one JSON line; `--config all` prints one per
 workload.
 
 The roofline object reports the dominant kernel: algorithmic bytes per launch
@@ -43,6 +45,7 @@ PEAK_MFMA_FP4_TFLOPS = 10100.0
 KERNEL_SOURCES = {
     "k_nvfp4_fused": ["fp4q_quant.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
     "k_gemm_mxfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
+    "k_gemm_nvfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
 }
 
 
@@ -393,6 +396,71 @@ class GemmMXFP4(Workload):
                           f"single thread, {dt:.1f} s"}
 
 
+class GemmNVFP4Wgrad(GemmMXFP4):
+    """The weight gradient dY^T X from the Wgrad workload's operands (bf16 [16384 tokens x
+    4096] each; 128-token RHT with seed 4; the gradient with SR, seed 40, the activation
+    with RTN), quantized column-wise to NVFP4 during setup: C [4096 x 4096] over k = 16384
+    tokens, bf16 out, on the bf16 MFMA after an exact decode."""
+    name = "wgrad_gemm_nvfp4_rht_4096x4096x16384_bf16_out"
+    m = n = 4096
+    k = 16384
+    bound, peak, unit = "mfma", PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
+    dtype = "bf16"   # exact bf16 decode of E2M1 x E4M3, bf16 products, fp32 accumulation
+    metric = "NVFP4 GEMM FLOP/s and % of MI355X dense bf16 matrix-core peak"
+
+    def __init__(self):
+        self.flops = 2 * self.m * self.n * self.k
+        self.elements = self.flops
+        self.algo_bytes = (self.m + self.n) * (self.k // 2 + self.k // 16) + 2 * self.m * self.n
+        self.kernel = "k_gemm_nvfp4"
+        self.kernel_bytes = self.algo_bytes
+
+    def setup(self, nbuf):
+        import numpy as np
+        import torch
+        import synth_inputs as si
+        from block_scaled_fp4_05_amd import binding as B
+        self.B = B
+        to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
+        g = to_dev(si.wgrad_gradient(self.k, self.m, seed=4))
+        x = to_dev(si.wgrad_activation(self.k, self.n, seed=4))
+        signs = B.fp4q_rht_signs_from_seed(4)
+        qg = B.quantize_nvfp4(g, B.COLWISE, rnd=B.SR, sr_seed=40, rht_signs=signs)
+        qx = B.quantize_nvfp4(x, B.COLWISE, rnd=B.RTN, rht_signs=signs)
+        torch.cuda.synchronize()
+        del g, x
+        pick = lambda q: (q["col_codes"], q["col_scales"], q["tensor_scale"])
+        self.host = {key: t.cpu().numpy() for key, t in zip(("ac", "as", "ga", "bc", "bs", "gb"), pick(qg) + pick(qx))}
+        nbuf = min(nbuf, 2)
+        ops = (pick(qg), pick(qx))
+        self.ops = [ops] + [(tuple(t.clone() for t in ops[0]), tuple(t.clone() for t in ops[1])) for _ in range(nbuf - 1)]
+        self.y = [torch.empty(self.m, self.n, dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+
+    def step(self, i):
+        B = self.B
+        (ac, as_, ga), (bc, bs, gb) = self.ops[i % len(self.ops)]
+        B.fp4q_gemm_nvfp4(ac, as_, ga, bc, bs, gb, self.m, self.n, self.k, B.BF16, self.y[i % len(self.y)])
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        import oracle
+        h = self.host
+        ga, gb = float(h["ga"][0]), float(h["gb"][0])
+        oracle.lib()
+        t0 = time.perf_counter()
+        oracle.gemm_nvfp4(h["ac"][:1], h["as"][:1], ga, h["bc"][:16], h["bs"][:16], gb)
+        per_out = (time.perf_counter() - t0) / 16
+        nout = int(max(64, min(self.m * 64, budget_s / per_out)))
+        rows, cols = max(1, nout // 64), 64
+        t0 = time.perf_counter()
+        oracle.gemm_nvfp4(np.ascontiguousarray(h["ac"][:rows]), np.ascontiguousarray(h["as"][:rows]), ga,
+                          np.ascontiguousarray(h["bc"][:cols]), np.ascontiguousarray(h["bs"][:cols]), gb)
+        dt = time.perf_counter() - t0
+        return {"value": 2.0 * rows * cols * self.k / dt, "unit": "FLOP/s", "cores": 1, "kind": "oracle",
+                "sample": f"outputs [0..{rows - 1}] x [0..{cols - 1}] of dY^T X (k = {self.k}), exact binary64 "
+                          f"sums, single thread, {dt:.1f} s"}
+
+
 class DeviceCopy(Workload):
     """Calibration, not a hot-path row: a plain device-to-device copy of 64 MiB.  It gives
     the copy rate this machine reaches and the factor between rocprofv3's FETCH_SIZE /
@@ -424,7 +492,7 @@ class DeviceCopy(Workload):
 
 
 WORKLOADS = {"activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT, "if4": IF4RoundTrip,
-             "gemm": GemmMXFP4}
+             "gemm": GemmMXFP4, "gemm_nvfp4": GemmNVFP4Wgrad}
 CALIBRATION = {"copy": DeviceCopy}
 
 
@@ -499,7 +567,7 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
     if mfma:
         flops_s = wl.flops / (ms_per_step * 1e-3)
         line["config"]["whole_step_TFLOPs"] = flops_s / 1e12
-        line["config"]["whole_step_frac_of_fp4_peak"] = flops_s / 1e12 / wl.peak
+        line["config"]["whole_step_frac_of_peak"] = flops_s / 1e12 / wl.peak
         if cpu_budget > 0:
             cb = wl.cpu_baseline(cpu_budget)
             if cb is not None:
