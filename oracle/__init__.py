@@ -76,6 +76,10 @@ def _declare(L: ctypes.CDLL) -> None:
         "ora_dequantize": (None, [_I, _P, _P, _F, _I64, _I64, _P]),
         "ora_gemm_mxfp4": (None, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
         "ora_gemm_nvfp4": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _I64, _P, _P]),
+        "ora_fp6_decode": (_F, [_I, ctypes.c_uint8]),
+        "ora_fp6_rtn": (ctypes.c_uint8, [_I, _F]),
+        "ora_quantize_mxfp6": (None, [_P, _I, _I64, _I64, _I, _P, _P]),
+        "ora_dequantize_mxfp6": (None, [_I, _P, _P, _I64, _I64, _P]),
         "ora_hadamard_entry": (_I, [_I, _I]),
         "ora_rht": (None, [_P, _I, _I64, _I64, _P, _I, _P]),
         "ora_rht_column": (None, [_P, _I, _I64, _I64, _I64, _P, _P]),
@@ -255,6 +259,35 @@ def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, gs: float, rows:
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     y = np.zeros((rows, cols), dtype=np.float32)
     lib().ora_dequantize(fmt, _ptr(codes), _ptr(scales), gs, rows, cols, _ptr(y))
+    return y
+
+
+E2M3, E3M2 = 0, 1
+
+
+def fp6_decode(fmt: int, code: int) -> float:
+    return lib().ora_fp6_decode(fmt, code)
+
+
+def fp6_rtn(fmt: int, v: float) -> int:
+    return lib().ora_fp6_rtn(fmt, v)
+
+
+def quantize_mxfp6(x: np.ndarray, fmt: int):
+    """MX FP6 (fmt E2M3 or E3M2): codes [rows][3 cols / 4] (four per three bytes), E8M0 [rows][cols/32]."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 4 * 3), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    lib().ora_quantize_mxfp6(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequantize_mxfp6(fmt: int, codes: np.ndarray, scales: np.ndarray, rows: int, cols: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    y = np.zeros((rows, cols), dtype=np.float32)
+    lib().ora_dequantize_mxfp6(fmt, _ptr(codes), _ptr(scales), rows, cols, _ptr(y))
     return y
 
 

@@ -490,6 +490,101 @@ void ora_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, float 
 }
 
 /* ------------------------------------------------------------------------- */
+/* MX FP6 [F6 "FP6で隣り合う値の間隔を見てみる", "量子化と6bitの保存"]             */
+/* ------------------------------------------------------------------------- */
+
+/* The two six-bit formats of the OCP MX specification as the page describes them:
+ * sign, then exponent and mantissa bits; fmt 0 = E2M3 (bias 1, largest 7.5), fmt 1 =
+ * E3M2 (bias 3, largest 28, smallest step 0.0625); exponent field 0 holds the
+ * subnormals; no Inf or NaN codes. */
+float ora_fp6_decode(int fmt, uint8_t code)
+{
+    const int ebits = fmt ? 3 : 2, mbits = 5 - ebits, bias = fmt ? 3 : 1;
+    const int s = (code >> 5) & 1, e = (code >> mbits) & ((1 << ebits) - 1), m = code & ((1 << mbits) - 1);
+    double v = (e == 0) ? ldexp((double)m, 1 - bias - mbits)
+                        : ldexp((double)((1 << mbits) + m), e - bias - mbits);
+    return (float)(s ? -v : v);
+}
+
+/* Reading: round to the nearest of the 32 magnitudes, ties to the even code (as for
+ * E2M1), saturating at the largest; the sign bit is copied (so -0 and tiny negative
+ * values give 0x20). */
+uint8_t ora_fp6_rtn(int fmt, float v)
+{
+    const double a = fabs((double)v);
+    const uint8_t sign = signbit(v) ? 0x20 : 0;
+    /* at or beyond the largest magnitude: saturate (the distances below would absorb
+     * the difference between the two largest values for huge inputs) */
+    if (a >= (double)ora_fp6_decode(fmt, 31)) return (uint8_t)(31 | sign);
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 32; ++c) {
+        const double d = fabs(a - (double)ora_fp6_decode(fmt, (uint8_t)c));
+        if (d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return (uint8_t)(best | sign);
+}
+
+/* Four six-bit codes per three bytes [F6 "量子化と6bitの保存"]: code j of a group in
+ * bits 6j .. 6j+5 of the little-endian 24-bit word the three bytes form.  A row of c
+ * elements takes 3c/4 bytes. */
+static void put6(uint8_t* codes, int64_t row_bytes, int64_t r, int64_t c, uint8_t code)
+{
+    uint8_t* g = codes + r * row_bytes + (c / 4) * 3;
+    uint32_t w = (uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16);
+    const int sh = 6 * (int)(c % 4);
+    w = (w & ~(0x3Fu << sh)) | ((uint32_t)(code & 0x3F) << sh);
+    g[0] = (uint8_t)w;
+    g[1] = (uint8_t)(w >> 8);
+    g[2] = (uint8_t)(w >> 16);
+}
+
+static uint8_t get6(const uint8_t* codes, int64_t row_bytes, int64_t r, int64_t c)
+{
+    const uint8_t* g = codes + r * row_bytes + (c / 4) * 3;
+    const uint32_t w = (uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16);
+    return (uint8_t)((w >> (6 * (int)(c % 4))) & 0x3F);
+}
+
+/* MX FP6: blocks of 32 with one E8M0 scale, as MXFP4 with the format's largest value
+ * in place of 6: scale code E8M0_RNE(fl(bamax / max)), elements x * 2^(127 - code)
+ * (one rounding) rounded as ora_fp6_rtn.  codes [rows][3 cols / 4], scales [rows][cols/32]. */
+void ora_quantize_mxfp6(const void* x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
+                        uint8_t* scales)
+{
+    const float maxv = fmt ? 28.0f : 7.5f;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            float bamax = 0.0f;
+            for (int64_t k = 0; k < 32; ++k) {
+                float a = fabsf(load_elem(x, dtype, r * cols + b * 32 + k));
+                if (a > bamax) bamax = a;
+            }
+            const uint8_t e8 = ora_e8m0_encode(bamax / maxv);
+            scales[r * (cols / 32) + b] = e8;
+            for (int64_t k = 0; k < 32; ++k) {
+                const int64_t c = b * 32 + k;
+                const float v = ldexpf(load_elem(x, dtype, r * cols + c), 127 - (int)e8);
+                put6(codes, cols / 4 * 3, r, c, ora_fp6_rtn(fmt, v));
+            }
+        }
+    }
+}
+
+/* x_hat = fp6(code) * 2^(scale - 127), one rounding. */
+void ora_dequantize_mxfp6(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          float* y)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            y[r * cols + c] = ldexpf(ora_fp6_decode(fmt, get6(codes, cols / 4 * 3, r, c)),
+                                     (int)scales[r * (cols / 32) + c / 32] - 127);
+}
+
+/* ------------------------------------------------------------------------- */
 /* FP4 GEMM consumer [NV "NVFP4フロー図"], [GL "FP4による推論と学習"]             */
 /* ------------------------------------------------------------------------- */
 

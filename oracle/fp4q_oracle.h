@@ -48,6 +48,12 @@ void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
 void ora_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float gs_a, const uint8_t* b_codes,
                     const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, double* c,
                     double* cabs);
+float ora_fp6_decode(int fmt, uint8_t code);
+uint8_t ora_fp6_rtn(int fmt, float v);
+void ora_quantize_mxfp6(const void* x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t* codes,
+                        uint8_t* scales);
+void ora_dequantize_mxfp6(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          float* y);
 int ora_hadamard_entry(int i, int t);
 void ora_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
              int inverse, float* y);
