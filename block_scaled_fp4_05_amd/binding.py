@@ -26,7 +26,8 @@ ROWWISE, COLWISE = 1, 2
 AMAX_COMPUTE, AMAX_GIVEN = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_E_NULL", 2: "FP4Q_E_SHAPE", 3: "FP4Q_E_ALIGN", 4: "FP4Q_E_ARG", 5: "FP4Q_E_HIP"}
 
-EXPORTS = ["fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_if4",
+EXPORTS = ["fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_mxfp6",
+           "fp4q_quantize_if4",
            "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax", "fp4q_set_onepass_wait", "fp4q_onepass_fallbacks",
            "fp4q_rht_signs_from_seed",
            "fp4q_status_string", "fp4q_abi_version"]
@@ -54,6 +55,7 @@ def lib() -> ctypes.CDLL:
             "fp4q_quantize_nvfp4": [_P, _I, _I64, _I64, _U, _I, _U64, _P, _U, _P, _P, _P, _P, _P, _P, _P],
             "fp4q_quantize_nvfp4_2d": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P],
             "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P, _P],
+            "fp4q_quantize_mxfp6": [_P, _I, _I64, _I64, _I, _P, _P, _P],
             "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P],
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
             "fp4q_gemm_mxfp4": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P],
@@ -126,6 +128,11 @@ def fp4q_quantize_nvfp4_2d(x, dt, rows, cols, amax_mode, amax, tensor_scale, cod
 def fp4q_quantize_mxfp4(x, dt, rows, cols, rnd, sr_seed, codes, scales, amax=None, stream=None) -> int:
     return _check("fp4q_quantize_mxfp4", lib().fp4q_quantize_mxfp4(
         _p(x), dt, rows, cols, rnd, sr_seed, _p(codes), _p(scales), _p(amax), _s(stream)))
+
+
+def fp4q_quantize_mxfp6(x, dt, rows, cols, fmt, codes, scales, stream=None) -> int:
+    return _check("fp4q_quantize_mxfp6", lib().fp4q_quantize_mxfp6(
+        _p(x), dt, rows, cols, fmt, _p(codes), _p(scales), _s(stream)))
 
 
 def fp4q_quantize_if4(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, scales, stream=None) -> int:
@@ -238,6 +245,19 @@ def quantize_mxfp4(x: torch.Tensor, rnd: int = RTN, sr_seed: int = 0, with_amax:
     if with_amax:
         out["amax"] = torch.empty(1, dtype=torch.float32, device=dev)
     fp4q_quantize_mxfp4(x, _dt(x), rows, cols, rnd, sr_seed, out["codes"], out["scales"], out.get("amax"), stream)
+    return out
+
+
+FP6_E2M3, FP6_E3M2 = 0, 1
+FMT_MXFP6 = {FP6_E2M3: 4, FP6_E3M2: 5}
+
+
+def quantize_mxfp6(x: torch.Tensor, fmt: int = FP6_E2M3, stream=None) -> dict:
+    """MX FP6: codes [rows][3 cols / 4] (four per three bytes), E8M0 scales [rows][cols/32]."""
+    rows, cols = x.shape
+    dev = x.device
+    out = {"codes": _u8(rows, cols // 4 * 3, device=dev), "scales": _u8(rows, cols // 32, device=dev)}
+    fp4q_quantize_mxfp6(x, _dt(x), rows, cols, fmt, out["codes"], out["scales"], stream)
     return out
 
 

@@ -161,6 +161,16 @@ fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
   return after_launch();
 }
 
+fp4q_status fp4q_quantize_mxfp6(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, fp4q_fp6 fmt,
+                                uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (!x || !codes || !scales) return FP4Q_E_NULL;
+  if (!valid_dtype(dt) || (fmt != FP4Q_FP6_E2M3 && fmt != FP4Q_FP6_E3M2)) return FP4Q_E_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0) return FP4Q_E_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FP4Q_E_ALIGN;
+  fp4q::launch_mxfp6(x, dt, rows, cols, fmt == FP4Q_FP6_E3M2 ? 1 : 0, codes, scales, stream);
+  return after_launch();
+}
+
 fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, unsigned amax_mode,
                               float* amax, float* tensor_scale, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream) {
@@ -220,6 +230,13 @@ fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, con
 fp4q_status fp4q_dequantize(fp4q_format fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                             int64_t rows, int64_t cols, fp4q_dtype out_dt, void* y, hipStream_t stream) {
   if (!codes || !scales || !y) return FP4Q_E_NULL;
+  if (fmt == FP4Q_FMT_MXFP6_E2M3 || fmt == FP4Q_FMT_MXFP6_E3M2) {
+    if (!valid_dtype(out_dt)) return FP4Q_E_ARG;
+    if (rows <= 0 || cols <= 0 || cols % 32 != 0) return FP4Q_E_SHAPE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(y)) return FP4Q_E_ALIGN;
+    fp4q::launch_dequant_mxfp6(fmt == FP4Q_FMT_MXFP6_E3M2 ? 1 : 0, codes, scales, rows, cols, out_dt, y, stream);
+    return after_launch();
+  }
   if (fmt != FP4Q_FMT_NVFP4 && fmt != FP4Q_FMT_NVFP4_2D && fmt != FP4Q_FMT_MXFP4 && fmt != FP4Q_FMT_IF4)
     return FP4Q_E_ARG;
   if (!valid_dtype(out_dt)) return FP4Q_E_ARG;

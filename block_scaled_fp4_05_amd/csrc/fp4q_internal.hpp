@@ -67,6 +67,12 @@ void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const u
                           bool sr, uint64_t seed, const AmaxSource& amax, float* tensor_scale,
                           uint8_t* col_codes, uint8_t* col_scales, hipStream_t st);
 
+// MX FP6 (fmt 0 E2M3, 1 E3M2) quantize and dequantize -- fp4q_quant.hip.
+void launch_mxfp6(const void* x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t* codes, uint8_t* scales,
+                  hipStream_t st);
+void launch_dequant_mxfp6(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          int out_dtype, void* y, hipStream_t st);
+
 // MXFP4 GEMM C = A B^T (fp32 accumulate; fp32 or bf16 out) -- fp4q_gemm.hip.  k % 128 == 0.
 bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,

@@ -1469,4 +1469,137 @@ void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const 
 #undef FP4Q_DQ
 }
 
+// ---------------------------------------------------------------------------------------
+// MX FP6 (blog.ast.moe "FP6から考えるLLM量子化", sections "FP6で隣り合う値の間隔を見てみる"
+// and "量子化と6bitの保存"): E2M3 (FMT 0: bias 1, largest 7.5) or E3M2 (FMT 1: bias 3,
+// largest 28), subnormals at exponent 0, no Inf or NaN; 32-element blocks with an E8M0
+// scale as MXFP4; four codes per three bytes, code j of a group in bits 6j .. 6j+5 of the
+// little-endian 24-bit word, so a lane's 16 codes are one 96-bit little-endian word.
+// ---------------------------------------------------------------------------------------
+
+// Round to nearest, ties to the even code, saturating at code 31; the sign bit copied.
+// Normal range: round the fp32 significand to MB bits by an integer add (ties to even)
+// and re-bias the exponent; below the smallest normal 2^(1-BIAS) the step is
+// 2^(1-BIAS-MB), reached by an exact power-of-two scaling and rint.  The two ranges meet:
+// the subnormal result 2^MB is the smallest normal's code.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp6_rtn(float v) {
+  constexpr int MB = FMT ? 2 : 3, BIAS = FMT ? 3 : 1;
+  constexpr float kMinNormal = FMT ? 0.25f : 1.0f;
+  constexpr float kSubScale = (float)(1 << (BIAS - 1 + MB));
+  const uint32_t u = __float_as_uint(v), au = u & 0x7FFFFFFFu;
+  const float a = __uint_as_float(au);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * kSubScale);
+  const uint32_t nrm = ((au + ((1u << (22 - MB)) - 1u) + ((au >> (23 - MB)) & 1u)) >> (23 - MB)) -
+                       ((uint32_t)(127 - BIAS) << MB);
+  const uint32_t code = a < kMinNormal ? sub : nrm;
+  return min(code, 31u) | ((u >> 31) << 5);
+}
+
+template <int FMT>
+__device__ __forceinline__ float fp6_value(uint32_t c) {
+  constexpr int MB = FMT ? 2 : 3, BIAS = FMT ? 3 : 1;
+  const uint32_t e = (c >> MB) & ((1u << (5 - MB)) - 1u), m = c & ((1u << MB) - 1u);
+  const float mag = e ? __uint_as_float(((e + 127u - BIAS) << 23) | (m << (23 - MB)))
+                      : (float)m * (1.0f / (float)(1 << (BIAS - 1 + MB)));
+  return (c & 0x20u) ? -mag : mag;
+}
+
+// 2^(k - 127) for an E8M0 code k: all of 2^-127 .. 2^127 are binary32 values.
+__device__ __forceinline__ float e8m0_value(uint32_t k) { return k ? __uint_as_float(k << 23) : __uint_as_float(0x00400000u); }
+
+// One lane per 16 elements, a lane pair per block (as k_mxfp4).
+template <typename T, int FMT>
+__global__ __launch_bounds__(256) void k_mxfp6(const T* __restrict__ x, int64_t n16, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = g < n16;
+  float a[16];
+  if (ok) {
+    load8(x, g * 16, a);
+    load8(x, g * 16 + 8, a + 8);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a[k] = 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(a[k]));
+  m = lane_xor_max<1>(m);
+  const uint32_t code = e8m0_encode(__fdiv_rn(m, FMT ? 28.0f : 7.5f));
+  const float inv = e8m0_value(254u - code);   // 2^(127 - code), exact
+  uint32_t c[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) c[k] = fp6_rtn<FMT>(a[k] * inv);
+  const uint32_t w0 = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18) | (c[4] << 24) | (c[5] << 30);
+  const uint32_t w1 = (c[5] >> 2) | (c[6] << 4) | (c[7] << 10) | (c[8] << 16) | (c[9] << 22) | (c[10] << 28);
+  const uint32_t w2 = (c[10] >> 4) | (c[11] << 2) | (c[12] << 8) | (c[13] << 14) | (c[14] << 20) | (c[15] << 26);
+  if (ok) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + g * 12);
+    dst[0] = w0;
+    dst[1] = w1;
+    dst[2] = w2;
+    if ((threadIdx.x & 1) == 0) scales[g >> 1] = (uint8_t)code;
+  }
+}
+
+template <int FMT, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_dequant_mxfp6(const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales, int64_t n16,
+                                                       void* __restrict__ y) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n16) return;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + g * 12);
+  const uint64_t lo = (uint64_t)src[0] | ((uint64_t)src[1] << 32);
+  const uint32_t hi = src[2];
+  const float s = e8m0_value(scales[g >> 1]);
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = i < 10 ? (uint32_t)(lo >> (6 * i)) & 63u
+                              : (i == 10 ? (uint32_t)((lo >> 60) | ((uint64_t)hi << 4)) & 63u
+                                         : (hi >> (6 * i - 64)) & 63u);
+    v[i] = fp6_value<FMT>(c) * s;
+  }
+  if constexpr (BF16OUT) {
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u0 = __float_as_uint(v[2 * i]), u1 = __float_as_uint(v[2 * i + 1]);
+      const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16, b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
+      o[i] = b0 | (b1 << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
+    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else {
+    float4* d = reinterpret_cast<float4*>(static_cast<float*>(y) + g * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+}
+
+void launch_mxfp6(const void* x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t* codes, uint8_t* scales,
+                  hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  const int grid = (int)((n16 + 255) / 256);
+  if (dtype == 1) {
+    if (fmt) k_mxfp6<uint16_t, 1><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, codes, scales);
+    else k_mxfp6<uint16_t, 0><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, codes, scales);
+  } else {
+    if (fmt) k_mxfp6<float, 1><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, codes, scales);
+    else k_mxfp6<float, 0><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, codes, scales);
+  }
+}
+
+void launch_dequant_mxfp6(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          int out_dtype, void* y, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  const int grid = (int)((n16 + 255) / 256);
+  auto kern = fmt ? (out_dtype == 1 ? k_dequant_mxfp6<1, true> : k_dequant_mxfp6<1, false>)
+                  : (out_dtype == 1 ? k_dequant_mxfp6<0, true> : k_dequant_mxfp6<0, false>);
+  kern<<<grid, 256, 0, st>>>(codes, scales, n16, y);
+}
+
 }  // namespace fp4q
+

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 4
+#define FP4Q_ABI_VERSION 5
 
 typedef enum {
     FP4Q_OK = 0,
@@ -67,7 +67,11 @@ typedef enum {
 
 typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
 typedef enum { FP4Q_RTN = 0, FP4Q_SR = 1 } fp4q_round;
-typedef enum { FP4Q_FMT_NVFP4 = 0, FP4Q_FMT_NVFP4_2D = 1, FP4Q_FMT_MXFP4 = 2, FP4Q_FMT_IF4 = 3 } fp4q_format;
+typedef enum {
+    FP4Q_FMT_NVFP4 = 0, FP4Q_FMT_NVFP4_2D = 1, FP4Q_FMT_MXFP4 = 2, FP4Q_FMT_IF4 = 3,
+    FP4Q_FMT_MXFP6_E2M3 = 4, FP4Q_FMT_MXFP6_E3M2 = 5
+} fp4q_format;
+typedef enum { FP4Q_FP6_E2M3 = 0, FP4Q_FP6_E3M2 = 1 } fp4q_fp6;
 
 #define FP4Q_ROWWISE 1u
 #define FP4Q_COLWISE 2u
@@ -138,6 +142,21 @@ fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
                                 float* amax, hipStream_t stream);
 
 /*
+ * MX FP6 [F6 "FP6で隣り合う値の間隔を見てみる", "量子化と6bitの保存"]: the OCP MX six-bit
+ * element formats E2M3 (bias 1, largest 7.5) and E3M2 (bias 3, largest 28, smallest
+ * step 0.0625), subnormals at exponent 0, no Inf or NaN; blocks of 32 with an E8M0
+ * scale chosen as for MXFP4 with the format's largest value in place of 6:
+ * E8M0_RNE(fl(bamax / max)).  Elements x * 2^(127 - code) round to the nearest code,
+ * ties to the even code, saturating at the largest; the sign bit is copied.  Four codes
+ * per three bytes: code j of a group of four in bits 6j .. 6j+5 of the little-endian
+ * 24-bit word the three bytes form.  RTN only.
+ *   codes [rows][3*cols/4], E8M0 scales [rows][cols/32].   Shapes: cols % 32 == 0.
+ * fp4q_dequantize with FP4Q_FMT_MXFP6_E2M3 / _E3M2 decodes it (tensor_scale unused).
+ */
+fp4q_status fp4q_quantize_mxfp6(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, fp4q_fp6 fmt,
+                                uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
  * IF4 [IF "2. 提案手法：IF4"]: NVFP4 1x16 row-wise scaling, then per block the
  * FP4 candidate and the INT4 candidate q = clamp(rint(fl(v * fl(7/6))), -7, 7)
  * (restored as fl(q * fl(6/7))) are compared by sum_i fma-accumulated (v_i - r_i)^2,
@@ -203,6 +222,8 @@ fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, con
  *   NVFP4, NVFP4_2D, IF4: x_hat = fl(fl(r * s) / gs), r = the E2M1 value, or for an
  *     IF4 block flagged INT4 r = fl(q * fl(6/7)); gs = *tensor_scale (device float).
  *   MXFP4: x_hat = r * 2^(code-127); tensor_scale may be NULL.
+ *   MXFP6_E2M3 / _E3M2: x_hat = fp6(code) * 2^(scale-127), codes [rows][3*cols/4];
+ *     tensor_scale unused.
  *   out_dt FP4Q_F32 writes float; FP4Q_BF16 writes bf16 = RNE(float result).
  * Shapes as for the matching quantize call.
  */

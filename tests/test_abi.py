@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 4
+    assert B.fp4q_abi_version() == 5
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -117,6 +117,14 @@ def test_other_entry_points_validate():
     assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 5, A2, 0) == 4
     assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, A2, 0) == 3
     assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, A2, 0) == 3
+    # MX FP6
+    assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 48, 0, A, A, 0) == 2
+    assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 64, 2, A, A, 0) == 4
+    assert L.fp4q_quantize_mxfp6(None, B.BF16, 4, 64, 1, A, A, 0) == 1
+    assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 64, 1, MIS, A, 0) == 3
+    assert L.fp4q_dequantize(4, A, A, None, 16, 48, 0, A, 0) == 2
+    assert L.fp4q_dequantize(5, A, MIS, None, 16, 64, 0, A, 0) == 3
+    assert L.fp4q_dequantize(6, A, A, None, 16, 64, 0, A, 0) == 4
     assert L.fp4q_onepass_fallbacks(0, None) == 1
     assert L.fp4q_amax(None, 0, 4, 4, A2, 0) == 1
     assert L.fp4q_amax(A, 0, 0, 4, A2, 0) == 2
