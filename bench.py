@@ -9,8 +9,8 @@ whose total exceeds the 256 MB Infinity Cache, so no step reads another step's
 data from cache.
 
 Other workloads (`--config`): weight [8192 x 8192] fp32 NVFP4 16x16 + MXFP4
-("weight"), the Wgrad pair with the 128x128 RHT ("wgrad"), IF4 + dequantize on
-[32768 x 8192] ("if4"), and the GEMM that consumes MXFP4 operands, Y = X W^T with
+("weight"), MX FP6 E2M3 of the same weight ("mxfp6"), the Wgrad pair with the 128x128
+RHT ("wgrad"), IF4 + dequantize on [32768 x 8192] ("if4"), and the GEMM that consumes MXFP4 operands, Y = X W^T with
 8192 x 8192 x 8192 and bf16 output ("gemm"; measured in FLOP/s against the dense
 FP4 matrix-core peak), and the NVFP4 weight-gradient GEMM dY^T X on the Wgrad
 workload's RHT-quantized operands ("gemm_nvfp4"; against the dense bf16 peak, the
@@ -219,6 +219,55 @@ class WeightNVFP4MX(Workload):
         dt = time.perf_counter() - t0
         return {"value": nrows * self.cols / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
                 "sample": f"NVFP4 16x16 + MXFP4 of rows 0..{nrows - 1}, single thread, {dt:.1f} s"}
+
+
+class WeightMXFP6(Workload):
+    """MX FP6 (E2M3) of the weight workload's fp32 [8192 x 8192] matrix: one read of W,
+    codes packed four per three bytes plus E8M0 scales."""
+    name = "weight_fp32_8192x8192_mxfp6_e2m3"
+    rows = cols = 8192
+
+    def __init__(self):
+        n = self.rows * self.cols
+        self.elements = n
+        self.algo_bytes = 4 * n + n // 4 * 3 + n // 32
+        self.kernel = "k_mxfp6"
+        self.kernel_bytes = self.algo_bytes
+
+    def setup(self, nbuf):
+        import torch
+        import synth_inputs as si
+        from block_scaled_fp4_05_amd import binding as B
+        self.B = B
+        self.host = si.weight(self.rows, self.cols, seed=3)
+        x0 = torch.from_numpy(self.host).to("cuda")
+        nbuf = min(nbuf, 2)
+        self.x = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+        u8 = lambda *sh: torch.empty(*sh, dtype=torch.uint8, device="cuda")
+        self.out = [(u8(self.rows, self.cols // 4 * 3), u8(self.rows, self.cols // 32)) for _ in range(nbuf)]
+
+    def step(self, i):
+        B = self.B
+        c, s = self.out[i % len(self.out)]
+        B.fp4q_quantize_mxfp6(self.x[i % len(self.x)], B.F32, self.rows, self.cols, B.FP6_E2M3, c, s)
+
+    def kernel_launch(self, i):
+        self.step(i)
+
+    def cpu_baseline(self, budget_s):
+        import numpy as np
+        import oracle
+        w = self.host
+        oracle.lib()
+        t0 = time.perf_counter()
+        oracle.quantize_mxfp6(np.ascontiguousarray(w[:4]), oracle.E2M3)
+        per_row = (time.perf_counter() - t0) / 4
+        nrows = int(min(self.rows, max(4, budget_s / per_row)))
+        t0 = time.perf_counter()
+        oracle.quantize_mxfp6(np.ascontiguousarray(w[:nrows]), oracle.E2M3)
+        dt = time.perf_counter() - t0
+        return {"value": nrows * self.cols / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+                "sample": f"MX FP6 E2M3 of rows 0..{nrows - 1}, single thread, {dt:.1f} s"}
 
 
 class WgradRHT(Workload):
@@ -492,7 +541,7 @@ class DeviceCopy(Workload):
 
 
 WORKLOADS = {"activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT, "if4": IF4RoundTrip,
-             "gemm": GemmMXFP4, "gemm_nvfp4": GemmNVFP4Wgrad}
+             "mxfp6": WeightMXFP6, "gemm": GemmMXFP4, "gemm_nvfp4": GemmNVFP4Wgrad}
 CALIBRATION = {"copy": DeviceCopy}
 
 
