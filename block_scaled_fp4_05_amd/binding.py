@@ -58,8 +58,8 @@ def lib() -> ctypes.CDLL:
             "fp4q_quantize_mxfp6": [_P, _I, _I64, _I64, _I, _P, _P, _P],
             "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P],
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
-            "fp4q_gemm_mxfp4": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P],
-            "fp4q_gemm_nvfp4": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P],
+            "fp4q_gemm_mxfp4": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P],
+            "fp4q_gemm_nvfp4": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P],
             "fp4q_dequantize": [_I, _P, _P, _P, _I64, _I64, _I, _P, _P],
             "fp4q_amax": [_P, _I, _I64, _I64, _P, _P],
             "fp4q_set_onepass_wait": [_U],
@@ -145,14 +145,16 @@ def fp4q_rht(x, dt, rows, cols, signs, inverse, y, stream=None) -> int:
     return _check("fp4q_rht", lib().fp4q_rht(_p(x), dt, rows, cols, sp, int(inverse), _p(y), _s(stream)))
 
 
-def fp4q_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m, n, k, out_dt, c, stream=None) -> int:
+def fp4q_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m, n, k, out_dt, c, amax=None, stream=None) -> int:
     return _check("fp4q_gemm_mxfp4", lib().fp4q_gemm_mxfp4(
-        _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), m, n, k, out_dt, _p(c), _s(stream)))
+        _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), m, n, k, out_dt, _p(c), _p(amax), _s(stream)))
 
 
-def fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, out_dt, c, stream=None) -> int:
+def fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, out_dt, c, amax=None,
+                    stream=None) -> int:
     return _check("fp4q_gemm_nvfp4", lib().fp4q_gemm_nvfp4(
-        _p(a_codes), _p(a_scales), _p(a_ts), _p(b_codes), _p(b_scales), _p(b_ts), m, n, k, out_dt, _p(c), _s(stream)))
+        _p(a_codes), _p(a_scales), _p(a_ts), _p(b_codes), _p(b_scales), _p(b_ts), m, n, k, out_dt, _p(c),
+        _p(amax), _s(stream)))
 
 
 def fp4q_dequantize(fmt, codes, scales, tensor_scale, rows, cols, out_dt, y, stream=None) -> int:
@@ -281,19 +283,25 @@ def rht(x: torch.Tensor, signs, inverse: bool = False, stream=None) -> torch.Ten
     return y
 
 
-def gemm_mxfp4(a: dict, b: dict, out_dtype=torch.float32, stream=None) -> torch.Tensor:
-    """C = A B^T for two row-wise MXFP4 operands as quantize_mxfp4 returns them."""
+def gemm_mxfp4(a: dict, b: dict, out_dtype=torch.float32, amax: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """C = A B^T for two row-wise MXFP4 operands as quantize_mxfp4 returns them.
+
+    With ``amax`` (a one-element float32 device tensor) the GEMM also writes max |C| of
+    the stored outputs there."""
     m, n, k = a["codes"].shape[0], b["codes"].shape[0], a["codes"].shape[1] * 2
     c = torch.empty(m, n, dtype=out_dtype, device=a["codes"].device)
-    fp4q_gemm_mxfp4(a["codes"], a["scales"], b["codes"], b["scales"], m, n, k, _dt(c), c, stream)
+    fp4q_gemm_mxfp4(a["codes"], a["scales"], b["codes"], b["scales"], m, n, k, _dt(c), c, amax, stream)
     return c
 
 
-def gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out_dtype=torch.float32, stream=None) -> torch.Tensor:
-    """C = A B^T / (gs_a gs_b) for two row-wise NVFP4 operands (codes, scales, tensor scale)."""
+def gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out_dtype=torch.float32,
+               amax: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C = A B^T / (gs_a gs_b) for two row-wise NVFP4 operands (codes, scales, tensor scale);
+    ``amax`` as for gemm_mxfp4."""
     m, n, k = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
     c = torch.empty(m, n, dtype=out_dtype, device=a_codes.device)
-    fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, _dt(c), c, stream)
+    fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, _dt(c), c, amax, stream)
     return c
 
 

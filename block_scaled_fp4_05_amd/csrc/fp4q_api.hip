@@ -197,32 +197,33 @@ fp4q_status fp4q_rht(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, c
 
 fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                             const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
-                            hipStream_t stream) {
+                            float* amax, hipStream_t stream) {
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4Q_E_NULL;
   if (!valid_dtype(out_dt)) return FP4Q_E_ARG;
   const int64_t lim = (int64_t)1 << 31;
   if (m <= 0 || n <= 0 || k < 128 || k % 128 != 0 || m >= lim || n >= lim || k > ((int64_t)1 << 25))
     return FP4Q_E_SHAPE;
-  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) || !aligned16(c))
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) || !aligned16(c) ||
+      !aligned4(amax))
     return FP4Q_E_ALIGN;
-  if (!fp4q::launch_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m, n, k, out_dt == FP4Q_BF16, c, stream))
+  if (!fp4q::launch_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m, n, k, out_dt == FP4Q_BF16, c, amax, stream))
     return FP4Q_E_SHAPE;
   return after_launch();
 }
 
 fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t m,
-                            int64_t n, int64_t k, fp4q_dtype out_dt, void* c, hipStream_t stream) {
+                            int64_t n, int64_t k, fp4q_dtype out_dt, void* c, float* amax, hipStream_t stream) {
   if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale || !c) return FP4Q_E_NULL;
   if (!valid_dtype(out_dt)) return FP4Q_E_ARG;
   const int64_t lim = (int64_t)1 << 31;
   if (m <= 0 || n <= 0 || k < 128 || k % 128 != 0 || m >= lim || n >= lim || k > ((int64_t)1 << 25))
     return FP4Q_E_SHAPE;
   if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) || !aligned16(c) ||
-      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale))
+      !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned4(amax))
     return FP4Q_E_ALIGN;
   if (!fp4q::launch_gemm_nvfp4(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, m, n, k,
-                               out_dt == FP4Q_BF16, c, stream))
+                               out_dt == FP4Q_BF16, c, amax, stream))
     return FP4Q_E_SHAPE;
   return after_launch();
 }

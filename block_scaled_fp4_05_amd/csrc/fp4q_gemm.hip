@@ -107,6 +107,22 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Output amax: each lane keeps the largest magnitude it stored as fp32 bits (a bf16 h
+// widens exactly to h << 16), which order as unsigned integers as the values do; the wave
+// folds them and one lane posts an atomic max, so a launch makes one atomic per wave.
+// This is the tensor amax that a following amax-scaled quantization of C can be given.
+__device__ __forceinline__ void post_amax(uint32_t m, uint32_t* amax) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0 && m) __hip_atomic_fetch_max(amax, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t w) {
+  return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+
+__global__ void k_gemm_amax_zero(uint32_t* p) { *p = 0u; }
+
 // One 64-element K sub-step of a wave's 128 x 128 block: the 4 A and 4 B fragments.
 struct GemmFrags {
   v8i_t a[4], b[4];
@@ -149,7 +165,8 @@ __device__ __forceinline__ void interleave() {
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
-    const uint8_t* __restrict__ bs, int M, int N, int K, int tiles_m, int tiles_n, void* __restrict__ cout) {
+    const uint8_t* __restrict__ bs, int M, int N, int K, int tiles_m, int tiles_n, void* __restrict__ cout,
+    uint32_t* __restrict__ amax) {
   __shared__ GemmLds lds_;
   GemmStage* st = lds_.st;
   GemmScales* sc = lds_.sc;
@@ -322,19 +339,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     uint16_t* c16 = static_cast<uint16_t*>(cout);
     const bool vec = (N & 7) == 0;
+    uint32_t am = 0;   // largest stored bf16 magnitude
     for (int it = 0; it < 32; ++it) {
       const int row = 4 * it + (lane >> 4), c8 = (lane & 15) * 8;
       if (br + row >= M) continue;
       uint16_t* dst = c16 + (int64_t)(br + row) * N + bc0 + c8;
       const uint16_t* src = e + row * 128 + c8;
       if (vec && bc0 + c8 + 8 <= N) {
-        *reinterpret_cast<u32x4_g*>(dst) = *reinterpret_cast<const u32x4_g*>(src);
+        const u32x4_g v = *reinterpret_cast<const u32x4_g*>(src);
+        *reinterpret_cast<u32x4_g*>(dst) = v;
+        am = max(am, max(max(bf16x2_absmax(v[0]), bf16x2_absmax(v[1])), max(bf16x2_absmax(v[2]), bf16x2_absmax(v[3]))));
       } else {
-        for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) dst[x] = src[x];
+        for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) {
+          dst[x] = src[x];
+          am = max(am, (uint32_t)(src[x] & 0x7FFFu));
+        }
       }
     }
+    if (amax) post_amax(am << 16, amax);
     return;
   }
+  uint32_t am = 0;   // largest stored fp32 magnitude
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -343,10 +368,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fh + (q & 3);
-        if (row < M && col < N) static_cast<float*>(cout)[(int64_t)row * N + col] = acc[i][j][q];
+        if (row < M && col < N) {
+          static_cast<float*>(cout)[(int64_t)row * N + col] = acc[i][j][q];
+          am = max(am, __float_as_uint(acc[i][j][q]) & 0x7FFFFFFFu);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if (amax) post_amax(am, amax);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -410,7 +440,7 @@ template <bool BF16OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ gsa,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ gsb, int M, int N,
-    int K, int tiles_m, int tiles_n, void* __restrict__ cout) {
+    int K, int tiles_m, int tiles_n, void* __restrict__ cout, uint32_t* __restrict__ amax) {
   __shared__ NvStage st[kNvStages];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -524,19 +554,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     uint16_t* c16 = static_cast<uint16_t*>(cout);
     const bool vec = (N & 7) == 0;
+    uint32_t am = 0;   // largest stored bf16 magnitude
     for (int it = 0; it < 32; ++it) {
       const int row = 4 * it + (lane >> 4), c8 = (lane & 15) * 8;
       if (br + row >= M) continue;
       uint16_t* dst = c16 + (int64_t)(br + row) * N + bc0 + c8;
       const uint16_t* src = e + row * 128 + c8;
       if (vec && bc0 + c8 + 8 <= N) {
-        *reinterpret_cast<u32x4_g*>(dst) = *reinterpret_cast<const u32x4_g*>(src);
+        const u32x4_g v = *reinterpret_cast<const u32x4_g*>(src);
+        *reinterpret_cast<u32x4_g*>(dst) = v;
+        am = max(am, max(max(bf16x2_absmax(v[0]), bf16x2_absmax(v[1])), max(bf16x2_absmax(v[2]), bf16x2_absmax(v[3]))));
       } else {
-        for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) dst[x] = src[x];
+        for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) {
+          dst[x] = src[x];
+          am = max(am, (uint32_t)(src[x] & 0x7FFFu));
+        }
       }
     }
+    if (amax) post_amax(am << 16, amax);
     return;
   }
+  uint32_t am = 0;   // largest stored fp32 magnitude
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -545,33 +583,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fh + (q & 3);
-        if (row < M && col < N) static_cast<float*>(cout)[(int64_t)row * N + col] = acc[i][j][q] * inv;
+        if (row < M && col < N) {
+          const float v = acc[i][j][q] * inv;
+          static_cast<float*>(cout)[(int64_t)row * N + col] = v;
+          am = max(am, __float_as_uint(v) & 0x7FFFFFFFu);
+        }
       }
     }
   }
+  if (amax) post_amax(am, amax);
 }
 
 }  // namespace
 
 bool launch_gemm_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs, int64_t m,
-                       int64_t n, int64_t k, bool bf16_out, void* c, hipStream_t st) {
+                       int64_t n, int64_t k, bool bf16_out, void* c, float* amax, hipStream_t st) {
   const int tiles_m = (int)((m + kGemmTile - 1) / kGemmTile), tiles_n = (int)((n + kGemmTile - 1) / kGemmTile);
   const int64_t total = (int64_t)tiles_m * tiles_n;
   if (total > 0x7FFFFFFF) return false;
-  if (bf16_out)
-    k_gemm_mxfp4<true><<<(unsigned)total, 256, 0, st>>>(ac, as, bc, bs, (int)m, (int)n, (int)k, tiles_m, tiles_n, c);
-  else
-    k_gemm_mxfp4<false><<<(unsigned)total, 256, 0, st>>>(ac, as, bc, bs, (int)m, (int)n, (int)k, tiles_m, tiles_n, c);
+  uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
+  if (ab) k_gemm_amax_zero<<<1, 1, 0, st>>>(ab);
+  auto kern = bf16_out ? k_gemm_mxfp4<true> : k_gemm_mxfp4<false>;
+  kern<<<(unsigned)total, 256, 0, st>>>(ac, as, bc, bs, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab);
   return true;
 }
 
 bool launch_gemm_nvfp4(const uint8_t* ac, const uint8_t* as, const float* gsa, const uint8_t* bc, const uint8_t* bs,
-                       const float* gsb, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c, hipStream_t st) {
+                       const float* gsb, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c, float* amax,
+                       hipStream_t st) {
   const int tiles_m = (int)((m + kGemmTile - 1) / kGemmTile), tiles_n = (int)((n + kGemmTile - 1) / kGemmTile);
   const int64_t total = (int64_t)tiles_m * tiles_n;
   if (total > 0x7FFFFFFF) return false;
   auto kern = bf16_out ? k_gemm_nvfp4<true> : k_gemm_nvfp4<false>;
-  kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c);
+  uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
+  if (ab) k_gemm_amax_zero<<<1, 1, 0, st>>>(ab);
+  kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab);
   return true;
 }
 

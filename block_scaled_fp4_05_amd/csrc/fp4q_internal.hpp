@@ -74,12 +74,13 @@ void launch_dequant_mxfp6(int fmt, const uint8_t* codes, const uint8_t* scales, 
                           int out_dtype, void* y, hipStream_t st);
 
 // MXFP4 GEMM C = A B^T (fp32 accumulate; fp32 or bf16 out) -- fp4q_gemm.hip.  k % 128 == 0.
+// Both GEMMs write max |C| over the stored (rounded) outputs to `amax` when it is not null.
 bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,
-                       hipStream_t st);
+                       float* amax, hipStream_t st);
 // NVFP4 1x16 GEMM C = A B^T / (gs_a gs_b) on the bf16 MFMA -- fp4q_gemm.hip.  k % 128 == 0.
 bool launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_ts, int64_t m, int64_t n, int64_t k, bool bf16_out,
-                       void* c, hipStream_t st);
+                       void* c, float* amax, hipStream_t st);
 
 }  // namespace fp4q

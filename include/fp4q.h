@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 5
+#define FP4Q_ABI_VERSION 6
 
 typedef enum {
     FP4Q_OK = 0,
@@ -192,11 +192,17 @@ fp4q_status fp4q_rht(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
  * MFMA with fp32 accumulation; the summation order is the hardware's.
  *   out_dt FP4Q_F32: c is float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
  * Shapes: m >= 1, n >= 1, k >= 128 with k % 128 == 0 and k <= 2^25, m, n < 2^31.
+ *   amax   optional device float (NULL: not computed), 4-byte aligned: receives
+ *          max |c[i][j]| over the m x n outputs as stored (after the bf16 rounding for
+ *          FP4Q_BF16), i.e. the tensor amax that an NVFP4 or IF4 quantization of C
+ *          needs [NV "scaleの導出"], produced by the GEMM's own epilogue so that C is
+ *          not read again for it; pass it on with FP4Q_AMAX_GIVEN.  It is set to 0 on
+ *          the stream before the GEMM starts; a NaN output makes it a NaN.
  */
 fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales,
                             int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
-                            hipStream_t stream);
+                            float* amax, hipStream_t stream);
 
 /*
  * The same product over two row-wise NVFP4 1x16 operands [NV "NVFP4フロー図";
@@ -209,12 +215,12 @@ fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
  * is decoded exactly to bf16 and multiplied on the bf16 MFMA with fp32 accumulation;
  * the sums are multiplied by fl(1 / fl(gs_a gs_b)).
  *   out_dt FP4Q_F32: float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
- * Shapes as fp4q_gemm_mxfp4.  NVFP4 16x16 (2D) scale layouts are not accepted.
+ * Shapes and amax as fp4q_gemm_mxfp4.  NVFP4 16x16 (2D) scale layouts are not accepted.
  */
 fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
                             int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
-                            hipStream_t stream);
+                            float* amax, hipStream_t stream);
 
 /*
  * Dequantize packed codes back to values.  rows x cols is the LOGICAL shape of the

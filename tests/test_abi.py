@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 5
+    assert B.fp4q_abi_version() == 6
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -100,23 +100,26 @@ def test_other_entry_points_validate():
     assert L.fp4q_dequantize(1, A, A, A2, 8, 64, 0, A, 0) == 2
     assert L.fp4q_dequantize(0, A, A, A2, 16, 64, 5, A, 0) == 4
     # GEMM: NULLs, dtype, k % 128, k >= 128, m/n >= 1, alignment of every pointer
-    assert L.fp4q_gemm_mxfp4(None, A, A, A, 64, 64, 128, 0, A2, 0) == 1
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 128, 0, None, 0) == 1
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 128, 2, A2, 0) == 4
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 96, 0, A2, 0) == 2
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 192, 0, A2, 0) == 2
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 0, 64, 128, 0, A2, 0) == 2
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, -1, 128, 0, A2, 0) == 2
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 1 << 31, 64, 128, 0, A2, 0) == 2
-    assert L.fp4q_gemm_mxfp4(A, MIS, A, A, 64, 64, 128, 0, A2, 0) == 3
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 256, 1, MIS, 0) == 3
-    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, (1 << 25) + 128, 0, A2, 0) == 2
+    assert L.fp4q_gemm_mxfp4(None, A, A, A, 64, 64, 128, 0, A2, None, 0) == 1
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 128, 0, None, None, 0) == 1
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 128, 2, A2, None, 0) == 4
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 96, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 192, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 0, 64, 128, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, -1, 128, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 1 << 31, 64, 128, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_mxfp4(A, MIS, A, A, 64, 64, 128, 0, A2, None, 0) == 3
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 256, 1, MIS, None, 0) == 3
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, (1 << 25) + 128, 0, A2, None, 0) == 2
     # NVFP4 GEMM: tensor scales are device floats (4-byte aligned)
-    assert L.fp4q_gemm_nvfp4(A, A, None, A, A, A2, 64, 64, 128, 0, A2, 0) == 1
-    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 192, 0, A2, 0) == 2
-    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 5, A2, 0) == 4
-    assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, A2, 0) == 3
-    assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, A2, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, A, None, A, A, A2, 64, 64, 128, 0, A2, None, 0) == 1
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 192, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 5, A2, None, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, A2, None, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, A2, None, 0) == 3
+    # the optional output amax must be 4-byte aligned
+    assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 128, 0, A2, A2 + 2, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 0, A2, A2 + 1, 0) == 3
     # MX FP6
     assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 48, 0, A, A, 0) == 2
     assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 64, 2, A, A, 0) == 4

@@ -211,3 +211,71 @@ def test_nvfp4_gemm_full_size_sampled():
     exact, cabs = oracle.gemm_nvfp4(ac[rows], as_[rows], ga, bc[cols], bs[cols], gb)
     got = c[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].float().cpu().numpy()
     _nv_check(got.astype(np.float64), exact, cabs, k, bf16=True)
+
+
+# --- output amax from the GEMM epilogue ---------------------------------------------
+
+def _run_with_amax(kind, m, n, k, bf16, rng, amax):
+    dt = torch.bfloat16 if bf16 else torch.float32
+    c = torch.full((m, n), float("nan"), dtype=dt, device=DEV)
+    if kind == "mx":
+        ac, as_ = _operand(rng, m, k)
+        bc, bs = _operand(rng, n, k)
+        args = (_dev(ac), _dev(as_), _dev(bc), _dev(bs), m, n, k, B._dt(c), c)
+        B.fp4q_gemm_mxfp4(*args, amax)
+        exact, cabs = oracle.gemm_mxfp4(ac, as_, bc, bs)
+    else:
+        ac, as_ = _nv_operand(rng, m, k)
+        bc, bs = _nv_operand(rng, n, k)
+        ta = torch.tensor([37.5], device=DEV)
+        tb = torch.tensor([2.25], device=DEV)
+        args = (_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B._dt(c), c)
+        B.fp4q_gemm_nvfp4(*args, amax)
+        exact, cabs = oracle.gemm_nvfp4(ac, as_, np.float32(37.5), bc, bs, np.float32(2.25))
+    torch.cuda.synchronize()
+    # the same call without amax stores the same C
+    c2 = torch.full_like(c, float("nan"))
+    (B.fp4q_gemm_mxfp4 if kind == "mx" else B.fp4q_gemm_nvfp4)(*args[:-1], c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16 if bf16 else torch.int32), c2.view(torch.int16 if bf16 else torch.int32))
+    got = c.float().cpu().numpy().astype(np.float64)
+    (_check if kind == "mx" else _nv_check)(got, exact, cabs, k, bf16)
+    return got
+
+
+@pytest.mark.parametrize("kind", ["mx", "nv"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_gemm_amax_is_max_abs_of_the_stored_output(kind, bf16):
+    """The amax the epilogue posts equals max |C| over exactly the stored m x n outputs
+    (after the bf16 rounding); a second call on the same word, with a smaller product,
+    starts again from zero."""
+    rng = np.random.default_rng(71 + bf16 + 2 * (kind == "nv"))
+    amax = torch.full((1,), 1e30, dtype=torch.float32, device=DEV)
+    for m, n, k in [(300, 520, 384), (257, 130, 256), (1, 1, 128)]:
+        print(f"gemm amax {kind} bf16={bf16} m={m} n={n} k={k}", flush=True)
+        got = _run_with_amax(kind, m, n, k, bf16, rng, amax)
+        assert amax.item() == np.abs(got).max(), (amax.item(), np.abs(got).max())
+
+
+def test_gemm_amax_feeds_the_nvfp4_quantization_of_its_output():
+    """C from the MXFP4 GEMM with its epilogue amax, quantized to NVFP4 with that amax
+    given, is bit-identical to the quantization that computes the amax from C, and to the
+    oracle's quantization of C."""
+    m, n, k = 512, 384, 512
+    x = si.weight(m, k, seed=31, std=1.0)
+    w = si.weight(n, k, seed=32, std=0.05)
+    qa = B.quantize_mxfp4(torch.from_numpy(x).to(DEV))
+    qb = B.quantize_mxfp4(torch.from_numpy(w).to(DEV))
+    amax = torch.empty(1, dtype=torch.float32, device=DEV)
+    print("gemm amax -> nvfp4 quantize", flush=True)
+    c = B.gemm_mxfp4(qa, qb, out_dtype=torch.bfloat16, amax=amax)
+    given = B.quantize_nvfp4(c, B.ROWWISE | B.COLWISE, amax=amax)
+    computed = B.quantize_nvfp4(c, B.ROWWISE | B.COLWISE)
+    torch.cuda.synchronize()
+    assert given["amax"].item() == computed["amax"].item()
+    for key in ("tensor_scale", "row_codes", "row_scales", "col_codes", "col_scales"):
+        assert torch.equal(given[key], computed[key]), key
+    rc, rs, gs = oracle.quantize_nvfp4(c.float().cpu().numpy())
+    assert np.array_equal(given["row_codes"].cpu().numpy(), rc)
+    assert np.array_equal(given["row_scales"].cpu().numpy(), rs)
+    assert given["tensor_scale"].item() == float(gs)
