@@ -279,3 +279,18 @@ def test_gemm_amax_feeds_the_nvfp4_quantization_of_its_output():
     assert np.array_equal(given["row_codes"].cpu().numpy(), rc)
     assert np.array_equal(given["row_scales"].cpu().numpy(), rs)
     assert given["tensor_scale"].item() == float(gs)
+
+
+def test_gemm_amax_full_size_launch():
+    """At 8192^3 with bf16 output (the measured launch), the epilogue amax equals the
+    largest magnitude of the stored product (a property that holds at any size)."""
+    m = n = k = 8192
+    rng = np.random.default_rng(5)
+    ac, as_ = _operand(rng, m, k)
+    bc, bs = _operand(rng, n, k)
+    c = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
+    amax = torch.full((1,), -1.0, device=DEV)
+    print("gemm amax full size", flush=True)
+    B.fp4q_gemm_mxfp4(_dev(ac), _dev(as_), _dev(bc), _dev(bs), m, n, k, B.BF16, c, amax)
+    torch.cuda.synchronize()
+    assert amax.item() == c.float().abs().max().item()
