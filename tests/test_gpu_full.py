@@ -1,0 +1,217 @@
+"""GPU parity at the full sizes of the five workloads, element by element.
+
+Every code, scale and flag byte of every output is compared with the oracle over the
+whole tensor (the oracle runs on row ranges in host threads, see oracle_par.py), the
+amax and tensor scale exactly, and dequantized values at 0 ULP.  The calls are the
+ones the benchmark times, at the same shapes and in the same launch configuration.
+
+The Wgrad operands go through the 128-token random Hadamard transform on MFMA
+(fp32 accumulation), so three things are checked there: the standalone transform
+against the oracle's binary64 transform within 1e-5 of each 128-value column chunk's
+RMS, the fused quantizer against the oracle quantizer fed the library's own transform
+(bit for bit), and the codes of the all-oracle pipeline, which may differ only at
+rounding ties: at a rate of at most 1e-6 and only by one step of the code or scale.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_par as op
+import synth_inputs as si
+from block_scaled_fp4_05_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits32(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def nibbles(codes: np.ndarray) -> np.ndarray:
+    return np.stack([codes & 15, codes >> 4], -1).reshape(codes.shape[0], -1)
+
+
+E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+
+
+# ---------------------------------------------------------------------------------------
+# Tiny reference: the glossary's 4096 values through NVFP4, MXFP4 and IF4 on the GPU
+# ---------------------------------------------------------------------------------------
+
+def test_tiny_reference_formats_and_round_trip_mae():
+    x = si.tiny_reference().reshape(1, 4096)
+    xd = torch.from_numpy(x).to(DEV)
+    xf = x.astype(np.float64)
+
+    nv = B.quantize_nvfp4(xd, B.ROWWISE)
+    c, s, gs = oracle.quantize_nvfp4(x)
+    assert np.array_equal(host(nv["row_codes"]), c) and np.array_equal(host(nv["row_scales"]), s)
+    assert host(nv["tensor_scale"])[0] == gs and host(nv["amax"])[0] == np.float32(oracle.amax(x))
+    y_nv = host(B.dequantize(B.FMT_NVFP4, nv["row_codes"], nv["row_scales"], nv["tensor_scale"], 1, 4096))
+    assert np.array_equal(bits32(y_nv), bits32(oracle.dequantize(oracle.FMT_NVFP4, c, s, gs, 1, 4096)))
+
+    mx = B.quantize_mxfp4(xd)
+    c, s = oracle.quantize_mxfp4(x)
+    assert np.array_equal(host(mx["codes"]), c) and np.array_equal(host(mx["scales"]), s)
+    y_mx = host(B.dequantize(B.FMT_MXFP4, mx["codes"], mx["scales"], None, 1, 4096))
+    assert np.array_equal(bits32(y_mx), bits32(oracle.dequantize(oracle.FMT_MXFP4, c, s, 1.0, 1, 4096)))
+
+    i4 = B.quantize_if4(xd)
+    c, s, gs = oracle.quantize_if4(x)
+    assert np.array_equal(host(i4["codes"]), c) and np.array_equal(host(i4["scales"]), s)
+    y_if = host(B.dequantize(B.FMT_IF4, i4["codes"], i4["scales"], i4["tensor_scale"], 1, 4096))
+    assert np.array_equal(bits32(y_if), bits32(oracle.dequantize(oracle.FMT_IF4, c, s, gs, 1, 4096)))
+
+    mae = [float(np.mean(np.abs(y.astype(np.float64) - xf))) for y in (y_nv, y_mx, y_if)]
+    print(f"tiny reference MAE on the GPU: NVFP4 {mae[0]:.6f}  MXFP4 {mae[1]:.6f}  IF4 {mae[2]:.6f} "
+          f"({int(np.count_nonzero(s >= 0x80))}/256 blocks INT4)")
+    # the oracle's pinned values (4 d.p.), now reached through the library
+    assert [round(m, 4) for m in mae] == [0.0779, 0.1094, 0.0722]
+    assert int(np.count_nonzero(host(i4["scales"]) >= 0x80)) == 153
+
+
+# ---------------------------------------------------------------------------------------
+# Activation: bf16 [8192 x 4096], NVFP4 1x16 row-wise and column-wise, RTN
+# ---------------------------------------------------------------------------------------
+
+def test_activation_full_rowwise_and_colwise():
+    bits = si.activation(8192, 4096, seed=2)
+    xd = dev_bf16(bits)
+    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
+    amax = op.amax(bits)
+    gs = oracle.tensor_scale(amax)
+    assert host(out["amax"])[0] == np.float32(amax)
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    rc, rs = op.quantize_nvfp4(bits, False, gs)
+    assert np.array_equal(host(out["row_codes"]), rc) and np.array_equal(host(out["row_scales"]), rs)
+    cc, cs = op.quantize_nvfp4(bits, True, gs)
+    assert np.array_equal(host(out["col_codes"]), cc) and np.array_equal(host(out["col_scales"]), cs)
+
+
+# ---------------------------------------------------------------------------------------
+# Weight: fp32 [8192 x 8192], NVFP4 16x16 (+ codes of W^T) and MXFP4 (RTN)
+# ---------------------------------------------------------------------------------------
+
+def test_weight_full_2d_transposed_and_mxfp4():
+    w = si.weight(8192, 8192, seed=3)
+    wd = torch.from_numpy(w).to(DEV)
+    # the measured step: MXFP4 reporting the amax, then 16x16 with that amax given
+    mx = B.quantize_mxfp4(wd, with_amax=True)
+    amax = op.amax(w)
+    assert host(mx["amax"])[0] == np.float32(amax)
+    q2 = B.quantize_nvfp4_2d(wd, transposed=True, amax=mx["amax"])
+    gs = oracle.tensor_scale(amax)
+    assert host(q2["tensor_scale"])[0] == np.float32(gs)
+    c, s = op.quantize_nvfp4_2d(w, gs)
+    assert np.array_equal(host(q2["codes"]), c) and np.array_equal(host(q2["scales"]), s)
+    # codes of W^T: the same nibbles transposed (q(W^T) = q(W)^T)
+    ct = host(q2["codes_t"])
+    nt = nibbles(c).T
+    assert np.array_equal(ct, (nt[:, 0::2] | (nt[:, 1::2] << 4)).astype(np.uint8))
+    cm, sm = op.quantize_mxfp4_rtn(w)
+    assert np.array_equal(host(mx["codes"]), cm) and np.array_equal(host(mx["scales"]), sm)
+    # the 16x16 call computing its own amax gives the same bytes
+    q2c = B.quantize_nvfp4_2d(wd)
+    assert torch.equal(q2c["codes"], q2["codes"]) and torch.equal(q2c["scales"], q2["scales"])
+    # 16x16 dequantization of the whole weight at 0 ULP
+    y = host(B.dequantize(B.FMT_NVFP4_2D, q2["codes"], q2["scales"], q2["tensor_scale"], 8192, 8192))
+    assert np.array_equal(bits32(y), bits32(op.dequantize(oracle.FMT_NVFP4_2D, c, s, gs, 8192, 8192)))
+
+
+# ---------------------------------------------------------------------------------------
+# Wgrad: two bf16 [16384 x 4096] operands, RHT along tokens, column-wise NVFP4
+# ---------------------------------------------------------------------------------------
+
+def _rht_within(y: np.ndarray, ref: np.ndarray, tol: float = 1e-5):
+    """Per (128-row chunk, column): max |y - ref| / RMS(ref chunk column); returns the worst."""
+    rows, cols = ref.shape
+    r = ref.reshape(rows // 128, 128, cols).astype(np.float64)
+    d = np.abs(y.reshape(rows // 128, 128, cols).astype(np.float64) - r).max(axis=1)
+    rms = np.sqrt((r ** 2).mean(axis=1))
+    return float(np.max(d / (rms + 1e-30)))
+
+
+@pytest.mark.parametrize("operand,rnd,sr_seed", [("gradient", 1, 40), ("activation", 0, 41)])
+def test_wgrad_full_rht_quantize(operand, rnd, sr_seed):
+    rows, cols = 16384, 4096
+    bits = si.wgrad_gradient(rows, cols, seed=4) if operand == "gradient" else si.wgrad_activation(rows, cols, seed=4)
+    signs = oracle.rht_signs(4)
+    xd = dev_bf16(bits)
+    out = B.quantize_nvfp4(xd, B.COLWISE, rnd=rnd, sr_seed=sr_seed, rht_signs=signs.tolist())
+    yg = host(B.rht(xd, signs.tolist()))
+    codes_g, scales_g = host(out["col_codes"]), host(out["col_scales"])
+    amax_g, gs_g = host(out["amax"])[0], host(out["tensor_scale"])[0]
+    del xd, out
+    torch.cuda.empty_cache()
+
+    # (1) the standalone transform against the binary64 oracle, every column chunk
+    yo = op.rht(bits, signs)
+    worst = _rht_within(yg, yo)
+    print(f"{operand}: worst |gpu - oracle| / chunk RMS = {worst:.3e}")
+    assert worst <= 1e-5
+
+    # (2) the fused kernel's amax and codes = the oracle quantizer on the GPU transform
+    assert amax_g == np.max(np.abs(yg))
+    assert gs_g == np.float32(oracle.tensor_scale(float(amax_g)))
+    c2, s2 = op.quantize_nvfp4(yg, True, float(gs_g), rnd=rnd, seed=sr_seed)
+    assert np.array_equal(codes_g, c2) and np.array_equal(scales_g, s2)
+
+    # (3) the all-oracle pipeline: codes may differ only at rounding ties
+    gs_o = oracle.tensor_scale(float(np.max(np.abs(yo))))
+    c3, s3 = op.quantize_nvfp4(yo, True, gs_o, rnd=rnd, seed=sr_seed)
+    ng, no = nibbles(codes_g), nibbles(c3)
+    mism = ng != no
+    n_mism, n = int(np.count_nonzero(mism)), ng.size
+    n_scale = int(np.count_nonzero(scales_g != s3))
+    print(f"{operand}: gs gpu {gs_g!r} oracle {np.float32(gs_o)!r}; code mismatches {n_mism} of {n} "
+          f"(rate {n_mism / n:.2e}); scale mismatches {n_scale} of {s3.size}")
+    # each mismatch is one step of the E2M1 grid (same sign), and scales one E4M3 step
+    vg, vo = np.abs(E2M1[ng[mism]]), np.abs(E2M1[no[mism]])
+    step = np.maximum(vg, vo)
+    gap = np.abs(vg - vo)
+    assert np.all(gap <= np.where(step > 4, 2.0, np.where(step > 2, 1.0, 0.5)))
+    assert np.all(np.abs(scales_g.astype(int) - s3.astype(int)) <= 1)
+    assert n_mism <= max(1, int(1e-6 * n))
+
+
+# ---------------------------------------------------------------------------------------
+# IF4: bf16 [32768 x 8192], then the dequantization round trip
+# ---------------------------------------------------------------------------------------
+
+def test_if4_full_and_round_trip():
+    rows, cols = 32768, 8192
+    bits = si.if4_mix(rows, cols, seed=5)
+    xd = dev_bf16(bits)
+    out = B.quantize_if4(xd)
+    amax = op.amax(bits)
+    gs = oracle.tensor_scale(amax)
+    assert host(out["amax"])[0] == np.float32(amax)
+    assert host(out["tensor_scale"])[0] == np.float32(gs)
+    c, s = op.quantize_if4(bits, gs)
+    cg, sg = host(out["codes"]), host(out["scales"])
+    assert np.array_equal(sg, s)
+    assert np.array_equal(cg, c)
+    flags = sg >= 0x80
+    rates = [flags[:rows // 2].mean(), flags[rows // 2:3 * rows // 4].mean(), flags[3 * rows // 4:].mean()]
+    print("IF4 INT4 share: N(0,1) %.3f  U(-1,1) %.3f  Laplace %.3f" % tuple(rates))
+    for got, want in zip(rates, (0.63, 0.93, 0.42)):
+        assert abs(got - want) < 0.02
+    del xd
+    y = B.dequantize(B.FMT_IF4, out["codes"], out["scales"], out["tensor_scale"], rows, cols)
+    ref = op.dequantize(oracle.FMT_IF4, c, s, gs, rows, cols)
+    assert np.array_equal(bits32(host(y)), bits32(ref))
+    del y
+    yb = B.dequantize(B.FMT_IF4, out["codes"], out["scales"], out["tensor_scale"], rows, cols,
+                      out_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), si.f32_to_bf16_bits(ref))

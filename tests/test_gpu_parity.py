@@ -102,9 +102,18 @@ def test_nvfp4_stochastic_rounding_matches_philox_oracle(kind):
     # same seed -> same bits; another seed -> different draws
     again = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, rnd=B.SR, sr_seed=seed)
     assert torch.equal(again["row_codes"], out["row_codes"])
+    # another seed: among the elements whose SR code differs from the nearest code
+    # (where the draw decided), about 2/3 change again under an independent draw
+    # (E[1 - f] over f uniform on (0, 1/2), and symmetrically above); at least 40 %
     other = B.quantize_nvfp4(xd, B.ROWWISE, rnd=B.SR, sr_seed=seed + 1)
-    differ = np.count_nonzero(host(other["row_codes"]) != rc)
-    assert differ > rc.size // 10
+    rn, _, _ = oracle.quantize_nvfp4(xh)
+
+    def nib(c):
+        return np.stack([c & 15, c >> 4], -1).reshape(-1)
+    affected = nib(rc) != nib(rn)
+    changed = nib(host(other["row_codes"])) != nib(rc)
+    assert affected.sum() > 1000
+    assert changed[affected].mean() >= 0.40, changed[affected].mean()
 
 
 def test_nvfp4_amax_given():
@@ -139,25 +148,6 @@ def test_nvfp4_degenerate_inputs():
         key = "col" if colwise else "row"
         assert np.array_equal(host(out[key + "_codes"]), c)
         assert np.array_equal(host(out[key + "_scales"]), s)
-
-
-def test_nvfp4_full_activation_config_sampled():
-    """bf16 [8192 x 4096], 1% columns x30, ROW|COL RTN: exact amax/gs, sampled rows and columns."""
-    bits = si.activation(8192, 4096, seed=2)
-    xd = dev_bf16(bits)
-    out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE)
-    amax = oracle.amax(bits)
-    gs = oracle.tensor_scale(amax)
-    assert host(out["amax"])[0] == np.float32(amax)
-    assert host(out["tensor_scale"])[0] == np.float32(gs)
-    rcg, rsg = host(out["row_codes"]), host(out["row_scales"])
-    ccg, csg = host(out["col_codes"]), host(out["col_scales"])
-    for r0 in (0, 127, 4096, 8176):
-        c, s = oracle.quantize_nvfp4_rows(bits, r0, 16, False, gs)
-        assert np.array_equal(rcg[r0:r0 + 16], c) and np.array_equal(rsg[r0:r0 + 16], s)
-    for j0 in (0, 1000, 2047, 4088):
-        c, s = oracle.quantize_nvfp4_rows(bits, j0, 8, True, gs)
-        assert np.array_equal(ccg[j0:j0 + 8], c) and np.array_equal(csg[j0:j0 + 8], s)
 
 
 def _exact_given_amax(xh):
@@ -305,19 +295,6 @@ def test_nvfp4_2d_and_transposed_codes(kind, shape):
     assert np.array_equal(st, s.T)
 
 
-def test_nvfp4_2d_full_weight_config_sampled():
-    w = si.weight(8192, 8192, seed=3)
-    out = B.quantize_nvfp4_2d(dev_f32(w), transposed=True)
-    gs = oracle.tensor_scale(oracle.amax(w))
-    assert host(out["tensor_scale"])[0] == np.float32(gs)
-    cg, sg, ctg = host(out["codes"]), host(out["scales"]), host(out["codes_t"])
-    for r0 in (0, 4096, 8176):
-        c, s, _ = oracle.quantize_nvfp4_2d(np.ascontiguousarray(w[r0:r0 + 16]), gs=gs)
-        assert np.array_equal(cg[r0:r0 + 16], c) and np.array_equal(sg[r0 // 16:r0 // 16 + 1], s)
-        ct, _, _ = oracle.quantize_nvfp4_2d(np.ascontiguousarray(w[:, r0:r0 + 16].T), gs=gs)
-        assert np.array_equal(ctg[r0:r0 + 16], ct)
-
-
 # ---------------------------------------------------------------------------------------
 # MXFP4
 # ---------------------------------------------------------------------------------------
@@ -375,15 +352,6 @@ def test_mxfp4_extreme_blocks():
     assert np.array_equal(host(out["codes"]), c)
 
 
-def test_mxfp4_full_weight_config_sampled():
-    w = si.weight(8192, 8192, seed=3)
-    out = B.quantize_mxfp4(dev_f32(w))
-    cg, sg = host(out["codes"]), host(out["scales"])
-    for r0 in (0, 3000, 8184):
-        c, s = oracle.quantize_mxfp4(np.ascontiguousarray(w[r0:r0 + 8]))
-        assert np.array_equal(cg[r0:r0 + 8], c) and np.array_equal(sg[r0:r0 + 8], s)
-
-
 # ---------------------------------------------------------------------------------------
 # IF4
 # ---------------------------------------------------------------------------------------
@@ -425,24 +393,6 @@ def test_if4_subnormal_scale_blocks():
     codes = s & 0x7F
     assert np.count_nonzero((codes >= 1) & (codes <= 7)) >= 8      # subnormal scales occur
     assert not np.any((codes[:32] >= 1) & (codes[:32] <= 7))       # workgroup 0 has none
-
-
-def test_if4_full_config_sampled():
-    bits = si.if4_mix(32768, 8192, seed=5)
-    out = B.quantize_if4(dev_bf16(bits))
-    amax = oracle.amax(bits)
-    gs = oracle.tensor_scale(amax)
-    assert host(out["tensor_scale"])[0] == np.float32(gs)
-    cg, sg = host(out["codes"]), host(out["scales"])
-    for r0 in (0, 16384, 24576, 32760):
-        c, s, _ = oracle.quantize_if4(np.ascontiguousarray(bits[r0:r0 + 8]), gs=gs)
-        assert np.array_equal(cg[r0:r0 + 8], c) and np.array_equal(sg[r0:r0 + 8], s)
-    # dequantize round trip of the sampled rows at 0 ULP
-    y = B.dequantize(B.FMT_IF4, out["codes"], out["scales"], out["tensor_scale"], 32768, 8192)
-    yh = host(y)
-    for r0 in (0, 24576):
-        ref = oracle.dequantize(oracle.FMT_IF4, cg[r0:r0 + 8], sg[r0:r0 + 8], gs, 8, 8192)
-        assert np.array_equal(f32_bits(yh[r0:r0 + 8]), f32_bits(ref))
 
 
 # ---------------------------------------------------------------------------------------
@@ -568,29 +518,7 @@ def test_rht_fused_two_stage_exact(rnd, shape):
     assert rht_close(y, yo)
     c3, s3, _ = oracle.quantize_nvfp4(yo, colwise=True, rnd=rnd, seed=40)
     mism = np.count_nonzero(host(out["col_codes"]) != c3)
-    assert mism <= max(2, c3.size * 2 * 1e-4)
-
-
-def test_rht_full_wgrad_config_sampled():
-    """Both Wgrad operands at [16384 x 4096]: gradient with SR, activation with RTN."""
-    signs = oracle.rht_signs(4)
-    for kind, rnd, seed in (("grad", 1, 40), ("act", 0, 41)):
-        bits = si.wgrad_gradient(16384, 4096, seed=4) if kind == "grad" else si.wgrad_activation(16384, 4096, seed=4)
-        xd = dev_bf16(bits)
-        out = B.quantize_nvfp4(xd, B.COLWISE, rnd=rnd, sr_seed=seed, rht_signs=signs.tolist())
-        y = B.rht(xd, signs.tolist())
-        amax_g = host(out["amax"])[0]
-        assert amax_g == host(y.abs().max().reshape(1))[0]
-        gs_g = float(host(out["tensor_scale"])[0])
-        ccg, csg = host(out["col_codes"]), host(out["col_scales"])
-        yh = host(y)
-        for j in (0, 777, 4095):
-            ref = oracle.rht_column(bits, j, signs)
-            assert rht_close(yh[:, j:j + 1].copy(), ref.reshape(-1, 1))
-            c2, s2 = oracle.quantize_nvfp4_rows(yh, j, 1, True, gs_g, rnd=rnd, seed=seed)
-            assert np.array_equal(ccg[j:j + 1], c2) and np.array_equal(csg[j:j + 1], s2)
-        del xd, y, out
-        torch.cuda.empty_cache()
+    assert mism <= max(1, int(c3.size * 2 * 1e-6))
 
 
 # ---------------------------------------------------------------------------------------
