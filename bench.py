@@ -1,27 +1,30 @@
 """Benchmark: FP4-quantized elements/s and achieved HBM GB/s on one MI355X.
 
-Default workload (one step = the whole hot path for one batch): NVFP4 1x16
-quantization of a bf16 activation [8192 x 4096] (N(0,1), 1% of the columns x30),
-round-to-nearest, row-wise AND transposed column-wise codes + E4M3 scales + the
-FP32 tensor scale -- tensor amax pass included.  Inputs are synthetic and already
-resident in HBM; consecutive steps rotate over several input/output buffer sets
-whose total exceeds the 256 MB Infinity Cache, so no step reads another step's
-data from cache.
+Headline workload (the default; one step = the whole hot path for one batch): IF4 of a
+bf16 [32768 x 8192] tensor (rows 50 % N(0,1), 25 % U(-1,1), 25 % Laplace(0,1), then
+0.1 % of all elements x50) -- tensor amax, per-16 block FP4-or-INT4 choice flagged in
+the E4M3 scale's sign bit -- then the dequantization round trip back to bf16.  It is the
+largest workload that fits one GPU.  The same run also times the other full-size
+workloads and reports them in the same JSON line (`config.other_workloads`):
+NVFP4 1x16 row-wise + column-wise of a bf16 [8192 x 4096] activation, NVFP4 16x16 and
+MXFP4 of an fp32 [8192 x 8192] weight, and the Wgrad pair (two bf16 [16384 x 4096]
+operands, 128-token random Hadamard transform, column-wise NVFP4, SR on the gradient).
 
-Other workloads (`--config`): weight [8192 x 8192] fp32 NVFP4 16x16 + MXFP4
-("weight"), MX FP6 E2M3 of the same weight ("mxfp6"), the Wgrad pair with the 128x128
-RHT ("wgrad"), IF4 + dequantize on [32768 x 8192] ("if4"), and the GEMM that consumes MXFP4 operands, Y = X W^T with
-8192 x 8192 x 8192 and bf16 output ("gemm"; measured in FLOP/s against the dense
-FP4 matrix-core peak), and the NVFP4 weight-gradient GEMM dY^T X on the Wgrad
-workload's RHT-quantized operands ("gemm_nvfp4"; against the dense bf16 peak, the
-MFMA it runs on).  Each prints one JSON line; `--config all` prints one per
-workload.
+Inputs are synthetic, seeded, and resident in HBM before timing starts.  Consecutive
+steps rotate over input/output sets whose total exceeds the 256 MB Infinity Cache, so
+no step reads an earlier step's data from cache; the single-step distribution is taken
+with a 1 GiB buffer written between steps.  Before anything is timed, the CPU-baseline
+leg runs the oracle on a sample of the headline input and checks the GPU's output for
+that sample byte for byte (the run fails otherwise), once on one thread and once on all
+host cores.
 
-The roofline object reports the dominant kernel: algorithmic bytes per launch
-(compulsory input read + code/scale writes) over that kernel's mean duration,
-timed with HIP events on the stream it runs on.  `traffic` is read from a committed
-counter summary under profiles/ when its recorded source digest matches the
-current kernel sources, else null.
+`roofline` reports the dominant kernel: algorithmic bytes per launch (compulsory input
+read + code/scale writes) over that kernel's mean duration, timed with HIP events on the
+stream it runs on.  `traffic` is read from a committed counter summary under profiles/
+while its recorded source digest matches the kernel's sources, else null.
+
+`--config NAME` runs one workload alone as the line (also `mxfp6`, `gemm`, `gemm_nvfp4`
+and the `copy` calibration); `--gpus N` with N > 1 exits: this library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -29,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -38,12 +42,15 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 PEAK_MFMA_FP4_TFLOPS = 10100.0
-
+METRIC = "FP4-quantized elements/s and achieved HBM GB/s (% of MI355X peak)"
 
 # The sources each profiled kernel is built from; a change to any other file leaves its
 # recorded counters valid.
+QUANT_SOURCES = ["fp4q_quant.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"]
 KERNEL_SOURCES = {
-    "k_nvfp4_fused": ["fp4q_quant.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
+    "k_if4": QUANT_SOURCES, "k_nvfp4_fused": QUANT_SOURCES, "k_nvfp4_2d": QUANT_SOURCES,
+    "k_amax_wide": QUANT_SOURCES, "k_dequant": QUANT_SOURCES,
+    "k_rht_nvfp4_col": ["fp4q_rht.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
     "k_gemm_mxfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
     "k_gemm_nvfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
 }
@@ -72,21 +79,23 @@ def counter_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-# --------------------------------------------------------------------------------------
-# workloads
-# --------------------------------------------------------------------------------------
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
-class Workload:
-    name = ""
-    elements = 0
-    algo_bytes = 0           # compulsory bytes of the whole step
-    kernel = ""              # dominant kernel (symbol substring)
-    kernel_bytes = 0         # algorithmic bytes per launch of the dominant kernel
 
-    def setup(self, nbuf: int): ...
-    def step(self, i: int): ...
-    def kernel_launch(self, i: int): ...
-    def cpu_baseline(self, budget_s: float) -> dict: ...
+def host_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _dev_bf16(bits):
@@ -95,9 +104,164 @@ def _dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
+def _u8(*shape):
+    import torch
+    return torch.empty(*shape, dtype=torch.uint8, device="cuda")
+
+
+def _f1():
+    import torch
+    return torch.zeros(1, dtype=torch.float32, device="cuda")
+
+
+def _timed_oracle(fn, threads: int):
+    """Runs fn() with the split oracle on `threads` host threads; returns (result, seconds)."""
+    import oracle.par as op
+    op.set_threads(threads)
+    try:
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+    finally:
+        op.set_threads(None)
+
+
+def _cpu_line(elements: int, t1: float, tn: float, n: int, sample: str) -> dict:
+    return {"value": elements / tn, "unit": "elements/s", "cores": n, "kind": "oracle", "sample": sample,
+            "single_core_value": elements / t1, "cpu_model": cpu_model(), "parity_checked": True}
+
+
+# --------------------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------------------
+
+class Workload:
+    name = ""
+    dtype = "bf16"
+    elements = 0
+    algo_bytes = 0           # compulsory bytes of the whole step
+    kernel = ""              # dominant kernel (symbol substring)
+    kernel_bytes = 0         # algorithmic bytes per launch of the dominant kernel
+    sets = 2                 # input/output sets the steps rotate over
+
+    def setup(self): ...
+    def step(self, i: int): ...
+    def kernel_launch(self, i: int): ...          # the dominant kernel alone
+    def given_launch(self, i: int): ...           # the call with the tensor amax given
+    def cpu_baseline(self, budget_s: float) -> dict | None: ...
+    def extra(self, stream) -> dict: return {}
+
+
+class IF4RoundTrip(Workload):
+    """IF4 quantize (amax computed) + dequantize back to bf16, bf16 [32768 x 8192]."""
+    name = "if4_roundtrip_bf16_32768x8192"
+    rows, cols = 32768, 8192
+
+    def __init__(self):
+        n = self.rows * self.cols
+        self.elements = n
+        self.quant_bytes = 2 * n + n // 2 + n // 16             # read x, write codes + scales
+        self.deq_bytes = n // 2 + n // 16 + 2 * n                # read codes + scales, write bf16
+        self.algo_bytes = self.quant_bytes + self.deq_bytes
+        self.kernel = "k_if4"
+        self.kernel_bytes = self.quant_bytes
+
+    def setup(self):
+        import torch
+        import synth_inputs as si
+        from block_scaled_fp4_05_amd import binding as B
+        self.B = B
+        self.ws = B.Workspace()
+        self.host = si.if4_mix(self.rows, self.cols, seed=5)
+        x0 = _dev_bf16(self.host)
+        r, c = self.rows, self.cols
+        self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
+        self.out = [dict(amax=_f1(), ts=_f1(), c=_u8(r, c // 2), s=_u8(r, c // 16),
+                         y=torch.empty(r, c, dtype=torch.bfloat16, device="cuda")) for _ in range(self.sets)]
+
+    def _quant(self, i, mode):
+        B, k = self.B, i % self.sets
+        o = self.out[k]
+        B.fp4q_quantize_if4(self.x[k], B.BF16, self.rows, self.cols, mode, o["amax"], o["ts"], o["c"], o["s"],
+                            self.ws)
+
+    def _deq(self, i):
+        B, o = self.B, self.out[i % self.sets]
+        B.fp4q_dequantize(B.FMT_IF4, o["c"], o["s"], o["ts"], self.rows, self.cols, B.BF16, o["y"])
+
+    def step(self, i):
+        self._quant(i, self.B.AMAX_COMPUTE)
+        self._deq(i)
+
+    def kernel_launch(self, i):
+        self._quant(i, self.B.AMAX_GIVEN)
+
+    def given_launch(self, i):
+        self._quant(i, self.B.AMAX_GIVEN)
+
+    def extra(self, stream):
+        import torch
+        B = self.B
+        d = {}
+        d["amax_pass_ms"] = _event_mean(stream, lambda i: B.fp4q_amax(self.x[i % self.sets], B.BF16, self.rows,
+                                                                       self.cols, self.out[i % self.sets]["amax"]))
+        d["amax_pass_GBps"] = 2 * self.elements / (d["amax_pass_ms"] * 1e-3) / 1e9
+        d["quantize_call_ms"] = _event_mean(stream, lambda i: self._quant(i, B.AMAX_COMPUTE))
+        d["quantize_call_GBps"] = self.quant_bytes / (d["quantize_call_ms"] * 1e-3) / 1e9
+        d["dequant_bf16_ms"] = _event_mean(stream, self._deq)
+        d["dequant_bf16_GBps"] = self.deq_bytes / (d["dequant_bf16_ms"] * 1e-3) / 1e9
+        flags = self.out[0]["s"] >= 0x80
+        torch.cuda.synchronize()
+        r = self.rows
+        d["int4_share"] = {"normal": float(flags[:r // 2].float().mean()),
+                           "uniform": float(flags[r // 2:3 * r // 4].float().mean()),
+                           "laplace": float(flags[3 * r // 4:].float().mean())}
+        return d
+
+    def cpu_baseline(self, budget_s):
+        """The oracle on the first rows (IF4 quantize with the whole tensor's scale, then
+        dequantize), checked byte for byte against the GPU's output for those rows."""
+        import numpy as np
+        import oracle
+        import oracle.par as op
+        import torch
+        self.step(0)
+        torch.cuda.synchronize()
+        o = self.out[0]
+        gs = oracle.tensor_scale(op.amax(self.host))
+        if np.float32(gs) != o["ts"].cpu().numpy()[0]:
+            raise AssertionError("bench parity: the tensor scale differs from the oracle's")
+        t0 = time.perf_counter()
+        c, s, _ = oracle.quantize_if4(np.ascontiguousarray(self.host[:64]), gs=gs)
+        oracle.dequantize(oracle.FMT_IF4, c, s, gs, 64, self.cols)
+        per_row = (time.perf_counter() - t0) / 64
+        nrows = int(min(self.rows, max(64, (budget_s / per_row) // 64 * 64)))
+        sample = np.ascontiguousarray(self.host[:nrows])
+
+        def run():
+            cc, ss = op.quantize_if4(sample, gs)
+            yy = op.dequantize(oracle.FMT_IF4, cc, ss, gs, nrows, self.cols)
+            return cc, ss, yy
+        (c1, s1, y1), t1 = _timed_oracle(run, 1)
+        n = host_cores()
+        (cn, sn, yn), tn = _timed_oracle(run, n)
+        yb = o["y"][:nrows].view(torch.int16).cpu().numpy().view(np.uint16)
+        import synth_inputs as si
+        ok = (np.array_equal(o["c"][:nrows].cpu().numpy(), c1) and np.array_equal(o["s"][:nrows].cpu().numpy(), s1)
+              and np.array_equal(yb, si.f32_to_bf16_bits(y1)) and np.array_equal(cn, c1)
+              and np.array_equal(yn.view(np.uint32), y1.view(np.uint32)))
+        if not ok:
+            raise AssertionError("bench parity: the GPU's IF4 codes, scales or round trip differ from the oracle's")
+        return _cpu_line(nrows * self.cols, t1, tn, n,
+                         f"IF4 quantize + dequantize of rows 0..{nrows - 1} ({nrows}x{self.cols} bf16) with the "
+                         f"whole tensor's scale; 1 thread {t1:.1f} s, {n} threads {tn:.1f} s")
+
+
 class ActivationNVFP4(Workload):
+    """NVFP4 1x16 row-wise + column-wise, RTN, amax computed (one pass), bf16 [8192 x 4096]."""
     name = "nvfp4_1x16_rowcol_rtn_bf16_8192x4096"
     rows, cols = 8192, 4096
+    sets = 4
 
     def __init__(self):
         n = self.rows * self.cols
@@ -106,24 +270,23 @@ class ActivationNVFP4(Workload):
         self.kernel = "k_nvfp4_fused"         # the whole step is this one launch
         self.kernel_bytes = self.algo_bytes
 
-    def setup(self, nbuf):
-        import torch
+    def setup(self):
         import synth_inputs as si
         from block_scaled_fp4_05_amd import binding as B
         self.B = B
+        self.ws = B.Workspace()
         self.host = si.activation(self.rows, self.cols, seed=2)
         x0 = _dev_bf16(self.host)
-        self.x = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+        self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
         r, c = self.rows, self.cols
-        u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")
-        self.out = [dict(amax=torch.zeros(1, device="cuda"), ts=torch.zeros(1, device="cuda"),
-                         rc=u8(r, c // 2), rs=u8(r, c // 16), cc=u8(c, r // 2), cs=u8(c, r // 16))
-                    for _ in range(nbuf)]
+        self.out = [dict(amax=_f1(), ts=_f1(), rc=_u8(r, c // 2), rs=_u8(r, c // 16), cc=_u8(c, r // 2),
+                         cs=_u8(c, r // 16)) for _ in range(self.sets)]
 
     def _call(self, i, mode):
-        B, o, x = self.B, self.out[i % len(self.out)], self.x[i % len(self.x)]
-        B.fp4q_quantize_nvfp4(x, B.BF16, self.rows, self.cols, B.ROWWISE | B.COLWISE, B.RTN, 0, None, mode,
-                              o["amax"], o["ts"], o["rc"], o["rs"], o["cc"], o["cs"])
+        B, k = self.B, i % self.sets
+        o = self.out[k]
+        B.fp4q_quantize_nvfp4(self.x[k], B.BF16, self.rows, self.cols, B.ROWWISE | B.COLWISE, B.RTN, 0, None, mode,
+                              o["amax"], o["ts"], o["rc"], o["rs"], o["cc"], o["cs"], self.ws)
 
     def step(self, i):
         self._call(i, self.B.AMAX_COMPUTE)
@@ -132,39 +295,40 @@ class ActivationNVFP4(Workload):
         self._call(i, self.B.AMAX_COMPUTE)
 
     def given_launch(self, i):
-        # the same call with the tensor amax supplied (AMAX_GIVEN): the streaming tile
-        # kernel alone; the amax buffers hold the values a compute-mode call wrote
+        # the streaming tile kernel alone; the amax buffers hold what a compute call wrote
         self._call(i, self.B.AMAX_GIVEN)
 
     def cpu_baseline(self, budget_s):
         import numpy as np
         import oracle
-        bits = self.host
+        import oracle.par as op
+        import torch
+        self.step(0)
+        torch.cuda.synchronize()
+        o = self.out[0]
+        gs = oracle.tensor_scale(op.amax(self.host))
         t0 = time.perf_counter()
-        amax = oracle.amax(bits)
-        gs = oracle.tensor_scale(amax)
-        t_amax = time.perf_counter() - t0
-        # calibrate on 64 rows, then size the sample to the budget
-        t0 = time.perf_counter()
-        oracle.quantize_nvfp4(np.ascontiguousarray(bits[:64]), gs=gs)
-        oracle.quantize_nvfp4(np.ascontiguousarray(bits[:64]), colwise=True, gs=gs)
-        per_row = (time.perf_counter() - t0) / 64
-        nrows = int(min(self.rows, max(64, (budget_s / per_row) // 16 * 16)))
-        sample = np.ascontiguousarray(bits[:nrows])
-        t0 = time.perf_counter()
-        oracle.quantize_nvfp4(sample, gs=gs)
-        oracle.quantize_nvfp4(sample, colwise=True, gs=gs)
-        dt = time.perf_counter() - t0
-        per_elem = dt / (nrows * self.cols) + t_amax / (self.rows * self.cols)
-        return {"value": 1.0 / per_elem, "unit": "elements/s", "cores": 1, "kind": "oracle",
-                "sample": f"tensor amax over all {self.rows}x{self.cols} values, then row-wise and column-wise "
-                          f"NVFP4 of rows 0..{nrows - 1} ({nrows}x{self.cols} bf16), single thread, "
-                          f"{dt + t_amax:.1f} s"}
+        oracle.quantize_nvfp4_rows(self.host, 0, 64, False, gs)
+        oracle.quantize_nvfp4_rows(self.host, 0, 32, True, gs)
+        per = (time.perf_counter() - t0) / (64 * self.cols + 32 * self.rows)
+        nr = int(min(self.rows, max(64, budget_s / 2 / per / self.cols // 64 * 64)))
+        sample = np.ascontiguousarray(self.host[:nr])
+        run = lambda: op.quantize_nvfp4(sample, False, gs)
+        (c1, s1), t1 = _timed_oracle(run, 1)
+        n = host_cores()
+        (cn, sn), tn = _timed_oracle(run, n)
+        if not (np.array_equal(o["rc"][:nr].cpu().numpy(), c1) and np.array_equal(o["rs"][:nr].cpu().numpy(), s1)
+                and np.array_equal(cn, c1)):
+            raise AssertionError("bench parity: NVFP4 row-wise codes differ from the oracle's")
+        return _cpu_line(nr * self.cols, t1, tn, n, f"row-wise NVFP4 of rows 0..{nr - 1}; 1 thread {t1:.1f} s, "
+                                                    f"{n} threads {tn:.1f} s")
 
 
 class WeightNVFP4MX(Workload):
+    """fp32 [8192 x 8192]: MXFP4 (reporting the tensor amax) then NVFP4 16x16 with it."""
     name = "weight_fp32_8192x8192_nvfp4_16x16_and_mxfp4"
     rows = cols = 8192
+    dtype = "f32"
 
     def __init__(self):
         n = self.rows * self.cols
@@ -175,102 +339,48 @@ class WeightNVFP4MX(Workload):
         self.kernel = "k_nvfp4_2d"
         self.kernel_bytes = b2d
 
-    def setup(self, nbuf):
+    def setup(self):
         import torch
         import synth_inputs as si
         from block_scaled_fp4_05_amd import binding as B
         self.B = B
+        self.ws = B.Workspace()
         self.host = si.weight(self.rows, self.cols, seed=3)
         x0 = torch.from_numpy(self.host).to("cuda")
-        nbuf = min(nbuf, 2)                      # 268 MB each: two copies already exceed the cache
-        self.x = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+        self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
         r, c = self.rows, self.cols
-        u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")
-        self.out = [dict(amax=torch.zeros(1, device="cuda"), ts=torch.zeros(1, device="cuda"), c=u8(r, c // 2),
-                         s=u8(r // 16, c // 16), mc=u8(r, c // 2), ms=u8(r, c // 32)) for _ in range(nbuf)]
+        self.out = [dict(amax=_f1(), ts=_f1(), c=_u8(r, c // 2), s=_u8(r // 16, c // 16), mc=_u8(r, c // 2),
+                         ms=_u8(r, c // 32)) for _ in range(self.sets)]
 
     def step(self, i):
         # MXFP4 first: its pass also reports the tensor amax, which the 16x16 call takes
         # as given, so W is read twice rather than three times (amax, 16x16, MXFP4)
-        B, o, x = self.B, self.out[i % len(self.out)], self.x[i % len(self.x)]
-        B.fp4q_quantize_mxfp4(x, B.F32, self.rows, self.cols, B.RTN, 0, o["mc"], o["ms"], o["amax"])
+        B, k = self.B, i % self.sets
+        o, x = self.out[k], self.x[k]
+        B.fp4q_quantize_mxfp4(x, B.F32, self.rows, self.cols, B.RTN, 0, o["mc"], o["ms"], o["amax"], self.ws)
         B.fp4q_quantize_nvfp4_2d(x, B.F32, self.rows, self.cols, B.AMAX_GIVEN, o["amax"], o["ts"], o["c"], o["s"],
-                                 None)
+                                 None, self.ws)
 
     def kernel_launch(self, i):
-        B, o, x = self.B, self.out[i % len(self.out)], self.x[i % len(self.x)]
+        B, k = self.B, i % self.sets
+        o, x = self.out[k], self.x[k]
         B.fp4q_quantize_nvfp4_2d(x, B.F32, self.rows, self.cols, B.AMAX_GIVEN, o["amax"], o["ts"], o["c"], o["s"],
-                                 None)
+                                 None, self.ws)
 
-    def cpu_baseline(self, budget_s):
-        import numpy as np
-        import oracle
-        w = self.host
-        gs = oracle.tensor_scale(oracle.amax(w))
-        t0 = time.perf_counter()
-        oracle.quantize_nvfp4_2d(np.ascontiguousarray(w[:16]), gs=gs)
-        oracle.quantize_mxfp4(np.ascontiguousarray(w[:16]))
-        per_row = (time.perf_counter() - t0) / 16
-        nrows = int(min(self.rows, max(16, (budget_s / per_row) // 16 * 16)))
-        s = np.ascontiguousarray(w[:nrows])
-        t0 = time.perf_counter()
-        oracle.quantize_nvfp4_2d(s, gs=gs)
-        oracle.quantize_mxfp4(s)
-        dt = time.perf_counter() - t0
-        return {"value": nrows * self.cols / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-                "sample": f"NVFP4 16x16 + MXFP4 of rows 0..{nrows - 1}, single thread, {dt:.1f} s"}
+    given_launch = kernel_launch
 
-
-class WeightMXFP6(Workload):
-    """MX FP6 (E2M3) of the weight workload's fp32 [8192 x 8192] matrix: one read of W,
-    codes packed four per three bytes plus E8M0 scales."""
-    name = "weight_fp32_8192x8192_mxfp6_e2m3"
-    rows = cols = 8192
-
-    def __init__(self):
-        n = self.rows * self.cols
-        self.elements = n
-        self.algo_bytes = 4 * n + n // 4 * 3 + n // 32
-        self.kernel = "k_mxfp6"
-        self.kernel_bytes = self.algo_bytes
-
-    def setup(self, nbuf):
-        import torch
-        import synth_inputs as si
-        from block_scaled_fp4_05_amd import binding as B
-        self.B = B
-        self.host = si.weight(self.rows, self.cols, seed=3)
-        x0 = torch.from_numpy(self.host).to("cuda")
-        nbuf = min(nbuf, 2)
-        self.x = [x0] + [x0.clone() for _ in range(nbuf - 1)]
-        u8 = lambda *sh: torch.empty(*sh, dtype=torch.uint8, device="cuda")
-        self.out = [(u8(self.rows, self.cols // 4 * 3), u8(self.rows, self.cols // 32)) for _ in range(nbuf)]
-
-    def step(self, i):
+    def extra(self, stream):
         B = self.B
-        c, s = self.out[i % len(self.out)]
-        B.fp4q_quantize_mxfp6(self.x[i % len(self.x)], B.F32, self.rows, self.cols, B.FP6_E2M3, c, s)
-
-    def kernel_launch(self, i):
-        self.step(i)
-
-    def cpu_baseline(self, budget_s):
-        import numpy as np
-        import oracle
-        w = self.host
-        oracle.lib()
-        t0 = time.perf_counter()
-        oracle.quantize_mxfp6(np.ascontiguousarray(w[:4]), oracle.E2M3)
-        per_row = (time.perf_counter() - t0) / 4
-        nrows = int(min(self.rows, max(4, budget_s / per_row)))
-        t0 = time.perf_counter()
-        oracle.quantize_mxfp6(np.ascontiguousarray(w[:nrows]), oracle.E2M3)
-        dt = time.perf_counter() - t0
-        return {"value": nrows * self.cols / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-                "sample": f"MX FP6 E2M3 of rows 0..{nrows - 1}, single thread, {dt:.1f} s"}
+        ms = _event_mean(stream, lambda i: B.fp4q_quantize_mxfp4(
+            self.x[i % self.sets], B.F32, self.rows, self.cols, B.RTN, 0, self.out[i % self.sets]["mc"],
+            self.out[i % self.sets]["ms"], self.out[i % self.sets]["amax"], self.ws))
+        n = self.elements
+        return {"mxfp4_with_amax_ms": ms, "mxfp4_with_amax_GBps": (4 * n + n // 2 + n // 32) / (ms * 1e-3) / 1e9}
 
 
 class WgradRHT(Workload):
+    """Two bf16 [16384 x 4096] operands: 128-token RHT, column-wise NVFP4 (gradient SR,
+    activation RTN), amax of the transformed tensor computed."""
     name = "wgrad_rht128_nvfp4_col_bf16_2x16384x4096"
     rows, cols = 16384, 4096
 
@@ -282,108 +392,78 @@ class WgradRHT(Workload):
         self.kernel = "k_rht_nvfp4_col"
         self.kernel_bytes = per
 
-    def setup(self, nbuf):
-        import torch
-        import oracle
+    def setup(self):
         import synth_inputs as si
         from block_scaled_fp4_05_amd import binding as B
         self.B = B
-        self.g_host = si.wgrad_gradient(self.rows, self.cols, seed=4)
-        self.x_host = si.wgrad_activation(self.rows, self.cols, seed=4)
+        self.ws = B.Workspace()
+        g0 = _dev_bf16(si.wgrad_gradient(self.rows, self.cols, seed=4))
+        x0 = _dev_bf16(si.wgrad_activation(self.rows, self.cols, seed=4))
         self.signs = B.fp4q_rht_signs_from_seed(4)
-        self.g = [_dev_bf16(self.g_host)]
-        self.xa = [_dev_bf16(self.x_host)]
+        self.g = [g0] + [g0.clone() for _ in range(self.sets - 1)]
+        self.xa = [x0] + [x0.clone() for _ in range(self.sets - 1)]
         r, c = self.rows, self.cols
-        u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")
-        self.out = [dict(amax=torch.zeros(1, device="cuda"), ts=torch.zeros(1, device="cuda"), c=u8(c, r // 2),
-                         s=u8(c, r // 16)) for _ in range(2)]
+        self.out = [[dict(amax=_f1(), ts=_f1(), c=_u8(c, r // 2), s=_u8(c, r // 16)) for _ in range(2)]
+                    for _ in range(self.sets)]
 
     def _q(self, x, o, rnd, seed, mode):
         B = self.B
         B.fp4q_quantize_nvfp4(x, B.BF16, self.rows, self.cols, B.COLWISE, rnd, seed, self.signs, mode, o["amax"],
-                              o["ts"], None, None, o["c"], o["s"])
+                              o["ts"], None, None, o["c"], o["s"], self.ws)
 
     def step(self, i):
-        self._q(self.g[0], self.out[0], self.B.SR, 40, self.B.AMAX_COMPUTE)
-        self._q(self.xa[0], self.out[1], self.B.RTN, 41, self.B.AMAX_COMPUTE)
+        k = i % self.sets
+        self._q(self.g[k], self.out[k][0], self.B.SR, 40, self.B.AMAX_COMPUTE)
+        self._q(self.xa[k], self.out[k][1], self.B.RTN, 41, self.B.AMAX_COMPUTE)
 
     def kernel_launch(self, i):
-        self._q(self.g[0], self.out[0], self.B.SR, 40, self.B.AMAX_GIVEN)
+        k = i % self.sets
+        self._q(self.g[k], self.out[k][0], self.B.SR, 40, self.B.AMAX_GIVEN)
 
-    def cpu_baseline(self, budget_s):
-        import numpy as np
-        import oracle
-        signs = np.array(self.signs, dtype=np.uint32)
-        t0 = time.perf_counter()
-        y = oracle.rht(np.ascontiguousarray(self.g_host[:128]), signs)
-        oracle.quantize_nvfp4(y, colwise=True, rnd=oracle.SR, seed=40)
-        per_chunk = time.perf_counter() - t0
-        nch = int(min(self.rows // 128, max(1, budget_s / per_chunk)))
-        t0 = time.perf_counter()
-        y = oracle.rht(np.ascontiguousarray(self.g_host[:128 * nch]), signs)
-        oracle.quantize_nvfp4(y, colwise=True, rnd=oracle.SR, seed=40)
-        dt = time.perf_counter() - t0
-        return {"value": 128 * nch * self.cols / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-                "sample": f"RHT (binary64) + column-wise NVFP4 SR of the gradient's first {128 * nch} tokens, "
-                          f"single thread, {dt:.1f} s"}
+    given_launch = kernel_launch
+
+    def extra(self, stream):
+        B = self.B
+        rtn = _event_mean(stream, lambda i: self._q(self.xa[i % self.sets], self.out[i % self.sets][1], B.RTN, 41,
+                                                    B.AMAX_GIVEN))
+        flops = 2 * 128 * self.rows * self.cols
+        return {"rtn_quantizer_ms": rtn, "mfma_dense_flop_per_operand": flops}
 
 
-class IF4RoundTrip(Workload):
-    name = "if4_bf16_32768x8192"
-    rows, cols = 32768, 8192
+class WeightMXFP6(Workload):
+    """MX FP6 (E2M3) of the weight workload's fp32 [8192 x 8192] matrix."""
+    name = "weight_fp32_8192x8192_mxfp6_e2m3"
+    rows = cols = 8192
+    dtype = "f32"
 
     def __init__(self):
         n = self.rows * self.cols
         self.elements = n
-        self.algo_bytes = 2 * n + n // 2 + n // 16
-        self.kernel = "k_if4"
+        self.algo_bytes = 4 * n + n // 4 * 3 + n // 32
+        self.kernel = "k_mxfp6"
         self.kernel_bytes = self.algo_bytes
 
-    def setup(self, nbuf):
+    def setup(self):
         import torch
         import synth_inputs as si
         from block_scaled_fp4_05_amd import binding as B
         self.B = B
-        self.host = si.if4_mix(self.rows, self.cols, seed=5)
-        self.x = [_dev_bf16(self.host)]
-        r, c = self.rows, self.cols
-        u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")
-        self.out = [dict(amax=torch.zeros(1, device="cuda"), ts=torch.zeros(1, device="cuda"), c=u8(r, c // 2),
-                         s=u8(r, c // 16))]
-        self.y = torch.empty(r, c, dtype=torch.float32, device="cuda")
+        x0 = torch.from_numpy(si.weight(self.rows, self.cols, seed=3)).to("cuda")
+        self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
+        self.out = [(_u8(self.rows, self.cols // 4 * 3), _u8(self.rows, self.cols // 32)) for _ in range(self.sets)]
 
     def step(self, i):
-        B, o = self.B, self.out[0]
-        B.fp4q_quantize_if4(self.x[0], B.BF16, self.rows, self.cols, B.AMAX_COMPUTE, o["amax"], o["ts"], o["c"], o["s"])
+        B = self.B
+        c, s = self.out[i % self.sets]
+        B.fp4q_quantize_mxfp6(self.x[i % self.sets], B.F32, self.rows, self.cols, B.FP6_E2M3, c, s)
 
-    def kernel_launch(self, i):
-        B, o = self.B, self.out[0]
-        B.fp4q_quantize_if4(self.x[0], B.BF16, self.rows, self.cols, B.AMAX_GIVEN, o["amax"], o["ts"], o["c"], o["s"])
-
-    def dequant(self):
-        B, o = self.B, self.out[0]
-        B.fp4q_dequantize(B.FMT_IF4, o["c"], o["s"], o["ts"], self.rows, self.cols, B.F32, self.y)
-
-    def cpu_baseline(self, budget_s):
-        import numpy as np
-        import oracle
-        gs = oracle.tensor_scale(oracle.amax(self.host))
-        t0 = time.perf_counter()
-        oracle.quantize_if4(np.ascontiguousarray(self.host[:16]), gs=gs)
-        per_row = (time.perf_counter() - t0) / 16
-        nrows = int(min(self.rows, max(16, budget_s / per_row)))
-        t0 = time.perf_counter()
-        oracle.quantize_if4(np.ascontiguousarray(self.host[:nrows]), gs=gs)
-        dt = time.perf_counter() - t0
-        return {"value": nrows * self.cols / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-                "sample": f"IF4 of rows 0..{nrows - 1} ({nrows}x{self.cols}), single thread, {dt:.1f} s"}
+    kernel_launch = step
+    given_launch = step
 
 
 class GemmMXFP4(Workload):
-    """Y = X W^T on MXFP4 operands (the forward GEMM after quantization): X an activation
-    [8192 tokens x 8192] drawn as the activation workload's (N(0,1), 1% of the columns
-    x30, bf16), W the weight workload's [8192 x 8192] N(0, 0.02^2) fp32; both quantized
-    by fp4q_quantize_mxfp4 during setup, Y in bf16."""
+    """Y = X W^T on MXFP4 operands: X an activation [8192 x 8192] (N(0,1), 1 % of the
+    columns x30, bf16), W the weight workload's matrix; Y in bf16."""
     name = "fprop_gemm_mxfp4_8192x8192x8192_bf16_out"
     m = n = k = 8192
     bound, peak, unit = "mfma", PEAK_MFMA_FP4_TFLOPS, "TFLOP/s"
@@ -397,64 +477,35 @@ class GemmMXFP4(Workload):
         self.kernel = "k_gemm_mxfp4"
         self.kernel_bytes = self.algo_bytes
 
-    def setup(self, nbuf):
-        import numpy as np
+    def setup(self):
         import torch
         import synth_inputs as si
         from block_scaled_fp4_05_amd import binding as B
         self.B = B
-        xb = si.activation(self.m, self.k, seed=2)
-        w = si.weight(self.n, self.k, seed=3)
-        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to("cuda")
-        qa = B.quantize_mxfp4(x)
-        qb = B.quantize_mxfp4(torch.from_numpy(w).to("cuda"))
-        torch.cuda.synchronize()
-        self.host = {key: t.cpu().numpy() for key, t in (("ac", qa["codes"]), ("as", qa["scales"]),
-                                                        ("bc", qb["codes"]), ("bs", qb["scales"]))}
-        del x
-        nbuf = min(nbuf, 2)   # 67 MB of operands + 134 MB of output per set: two sets exceed the cache
+        qa = B.quantize_mxfp4(_dev_bf16(si.activation(self.m, self.k, seed=2)))
+        qb = B.quantize_mxfp4(torch.from_numpy(si.weight(self.n, self.k, seed=3)).to("cuda"))
         self.ops = [(qa, qb)] + [({k: v.clone() for k, v in qa.items()}, {k: v.clone() for k, v in qb.items()})
-                                 for _ in range(nbuf - 1)]
-        self.y = [torch.empty(self.m, self.n, dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+                                 for _ in range(self.sets - 1)]
+        self.y = [torch.empty(self.m, self.n, dtype=torch.bfloat16, device="cuda") for _ in range(self.sets)]
 
     def step(self, i):
         B = self.B
-        qa, qb = self.ops[i % len(self.ops)]
+        qa, qb = self.ops[i % self.sets]
         B.fp4q_gemm_mxfp4(qa["codes"], qa["scales"], qb["codes"], qb["scales"], self.m, self.n, self.k, B.BF16,
-                          self.y[i % len(self.y)])
+                          self.y[i % self.sets])
 
-    def kernel_launch(self, i):
-        self.step(i)
-
-    def cpu_baseline(self, budget_s):
-        import numpy as np
-        import oracle
-        h = self.host
-        oracle.lib()                                  # load (and if needed build) before timing
-        t0 = time.perf_counter()
-        oracle.gemm_mxfp4(h["ac"][:1], h["as"][:1], h["bc"][:32], h["bs"][:32])
-        per_out = (time.perf_counter() - t0) / 32
-        nout = int(max(64, min(self.m * 64, budget_s / per_out)))
-        rows, cols = max(1, nout // 64), 64
-        t0 = time.perf_counter()
-        oracle.gemm_mxfp4(np.ascontiguousarray(h["ac"][:rows]), np.ascontiguousarray(h["as"][:rows]),
-                          np.ascontiguousarray(h["bc"][:cols]), np.ascontiguousarray(h["bs"][:cols]))
-        dt = time.perf_counter() - t0
-        return {"value": 2.0 * rows * cols * self.k / dt, "unit": "FLOP/s", "cores": 1, "kind": "oracle",
-                "sample": f"outputs [0..{rows - 1}] x [0..{cols - 1}] of Y (k = {self.k}), exact binary64 sums, "
-                          f"single thread, {dt:.1f} s"}
+    kernel_launch = step
+    given_launch = step
 
 
 class GemmNVFP4Wgrad(GemmMXFP4):
-    """The weight gradient dY^T X from the Wgrad workload's operands (bf16 [16384 tokens x
-    4096] each; 128-token RHT with seed 4; the gradient with SR, seed 40, the activation
-    with RTN), quantized column-wise to NVFP4 during setup: C [4096 x 4096] over k = 16384
+    """dY^T X from the Wgrad workload's RHT-quantized operands: [4096 x 4096] over 16384
     tokens, bf16 out, on the bf16 MFMA after an exact decode."""
     name = "wgrad_gemm_nvfp4_rht_4096x4096x16384_bf16_out"
     m = n = 4096
     k = 16384
     bound, peak, unit = "mfma", PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
-    dtype = "bf16"   # exact bf16 decode of E2M1 x E4M3, bf16 products, fp32 accumulation
+    dtype = "bf16"
     metric = "NVFP4 GEMM FLOP/s and % of MI355X dense bf16 matrix-core peak"
 
     def __init__(self):
@@ -464,212 +515,164 @@ class GemmNVFP4Wgrad(GemmMXFP4):
         self.kernel = "k_gemm_nvfp4"
         self.kernel_bytes = self.algo_bytes
 
-    def setup(self, nbuf):
-        import numpy as np
+    def setup(self):
         import torch
         import synth_inputs as si
         from block_scaled_fp4_05_amd import binding as B
         self.B = B
-        to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
-        g = to_dev(si.wgrad_gradient(self.k, self.m, seed=4))
-        x = to_dev(si.wgrad_activation(self.k, self.n, seed=4))
         signs = B.fp4q_rht_signs_from_seed(4)
-        qg = B.quantize_nvfp4(g, B.COLWISE, rnd=B.SR, sr_seed=40, rht_signs=signs)
-        qx = B.quantize_nvfp4(x, B.COLWISE, rnd=B.RTN, rht_signs=signs)
-        torch.cuda.synchronize()
-        del g, x
+        qg = B.quantize_nvfp4(_dev_bf16(si.wgrad_gradient(self.k, self.m, seed=4)), B.COLWISE, rnd=B.SR, sr_seed=40,
+                              rht_signs=signs)
+        qx = B.quantize_nvfp4(_dev_bf16(si.wgrad_activation(self.k, self.n, seed=4)), B.COLWISE, rht_signs=signs)
         pick = lambda q: (q["col_codes"], q["col_scales"], q["tensor_scale"])
-        self.host = {key: t.cpu().numpy() for key, t in zip(("ac", "as", "ga", "bc", "bs", "gb"), pick(qg) + pick(qx))}
-        nbuf = min(nbuf, 2)
         ops = (pick(qg), pick(qx))
-        self.ops = [ops] + [(tuple(t.clone() for t in ops[0]), tuple(t.clone() for t in ops[1])) for _ in range(nbuf - 1)]
-        self.y = [torch.empty(self.m, self.n, dtype=torch.bfloat16, device="cuda") for _ in range(nbuf)]
+        self.ops = [ops] + [(tuple(t.clone() for t in ops[0]), tuple(t.clone() for t in ops[1]))
+                            for _ in range(self.sets - 1)]
+        self.y = [torch.empty(self.m, self.n, dtype=torch.bfloat16, device="cuda") for _ in range(self.sets)]
 
     def step(self, i):
         B = self.B
-        (ac, as_, ga), (bc, bs, gb) = self.ops[i % len(self.ops)]
-        B.fp4q_gemm_nvfp4(ac, as_, ga, bc, bs, gb, self.m, self.n, self.k, B.BF16, self.y[i % len(self.y)])
+        (ac, as_, ga), (bc, bs, gb) = self.ops[i % self.sets]
+        B.fp4q_gemm_nvfp4(ac, as_, ga, bc, bs, gb, self.m, self.n, self.k, B.BF16, self.y[i % self.sets])
 
-    def cpu_baseline(self, budget_s):
-        import numpy as np
-        import oracle
-        h = self.host
-        ga, gb = float(h["ga"][0]), float(h["gb"][0])
-        oracle.lib()
-        t0 = time.perf_counter()
-        oracle.gemm_nvfp4(h["ac"][:1], h["as"][:1], ga, h["bc"][:16], h["bs"][:16], gb)
-        per_out = (time.perf_counter() - t0) / 16
-        nout = int(max(64, min(self.m * 64, budget_s / per_out)))
-        rows, cols = max(1, nout // 64), 64
-        t0 = time.perf_counter()
-        oracle.gemm_nvfp4(np.ascontiguousarray(h["ac"][:rows]), np.ascontiguousarray(h["as"][:rows]), ga,
-                          np.ascontiguousarray(h["bc"][:cols]), np.ascontiguousarray(h["bs"][:cols]), gb)
-        dt = time.perf_counter() - t0
-        return {"value": 2.0 * rows * cols * self.k / dt, "unit": "FLOP/s", "cores": 1, "kind": "oracle",
-                "sample": f"outputs [0..{rows - 1}] x [0..{cols - 1}] of dY^T X (k = {self.k}), exact binary64 "
-                          f"sums, single thread, {dt:.1f} s"}
+    kernel_launch = step
+    given_launch = step
 
 
 class DeviceCopy(Workload):
-    """Calibration, not a hot-path row: a plain device-to-device copy of 64 MiB.  It gives
-    the copy rate this machine reaches and the factor between rocprofv3's FETCH_SIZE /
-    WRITE_SIZE and bytes actually moved (each is known to be 64 MiB per launch)."""
+    """Calibration, not a hot-path row: a plain device-to-device copy of 64 MiB."""
     name = "device_copy_64MiB"
     nbytes = 64 << 20
+    sets = 4
 
     def __init__(self):
         self.elements = self.nbytes // 2
         self.algo_bytes = 2 * self.nbytes
-        self.kernel = "copyBuffer"
+        self.kernel = "copy"
         self.kernel_bytes = self.algo_bytes
 
-    def setup(self, nbuf):
+    def setup(self):
         import torch
         n = self.nbytes // 2
-        self.src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(nbuf)]
+        self.src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(self.sets)]
         self.dst = [torch.empty_like(t) for t in self.src]
 
     def step(self, i):
-        k = i % len(self.src)
+        k = i % self.sets
         self.dst[k].copy_(self.src[k])
 
-    def kernel_launch(self, i):
-        self.step(i)
-
-    def cpu_baseline(self, budget_s):
-        return None
+    kernel_launch = step
+    given_launch = step
 
 
-WORKLOADS = {"activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT, "if4": IF4RoundTrip,
-             "mxfp6": WeightMXFP6, "gemm": GemmMXFP4, "gemm_nvfp4": GemmNVFP4Wgrad}
-CALIBRATION = {"copy": DeviceCopy}
+HEADLINE = IF4RoundTrip
+OTHERS = [ActivationNVFP4, WeightNVFP4MX, WgradRHT]
+WORKLOADS = {"if4": IF4RoundTrip, "activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT,
+             "mxfp6": WeightMXFP6, "gemm": GemmMXFP4, "gemm_nvfp4": GemmNVFP4Wgrad, "copy": DeviceCopy}
 
 
 # --------------------------------------------------------------------------------------
 
-def run(wl: Workload, steps: int, warmup: int, cpu_budget: float) -> dict:
+def _event_mean(stream, fn, n: int = 20) -> float:
+    """Mean ms of n back-to-back fn(i) between two HIP events on `stream`."""
     import torch
-    wl.setup(nbuf=4)
+    for i in range(2):
+        fn(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def run(wl: Workload, steps: int, warmup: int, cpu_budget: float, flush) -> dict:
+    import torch
+    wl.setup()
+    cb = wl.cpu_baseline(cpu_budget) if cpu_budget > 0 else None    # includes the parity check
+    stream = torch.cuda.current_stream()
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    # whole-step timing
+    # whole-step throughput: K consecutive steps between two synchronizations
     t0 = time.perf_counter()
     for i in range(steps):
         wl.step(warmup + i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / steps
-    # dominant kernel alone: back-to-back launches between two HIP events recorded on
-    # the stream the kernel runs on (torch's current stream, which the binding uses)
-    stream = torch.cuda.current_stream()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    # the dominant kernel alone, back to back, HIP events on the stream it runs on
     nk = max(steps, 20)
-    for i in range(4):
-        wl.kernel_launch(i)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(nk):
-        wl.kernel_launch(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    k_mean = e0.elapsed_time(e1) / nk
+    k_mean = _event_mean(stream, wl.kernel_launch, nk)
     mfma = getattr(wl, "bound", "hbm") == "mfma"
     if mfma:
-        achieved = wl.flops / (k_mean * 1e-3) / 1e12
-        peak, unit = wl.peak, wl.unit
+        achieved, peak, unit = wl.flops / (k_mean * 1e-3) / 1e12, wl.peak, wl.unit
     else:
-        achieved = wl.kernel_bytes / (k_mean * 1e-3) / 1e9
-        peak, unit = PEAK_HBM_GBPS, "GB/s"
-    value = wl.elements / (ms_per_step * 1e-3)
+        achieved, peak, unit = wl.kernel_bytes / (k_mean * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+    step_gbps = wl.algo_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
-        "metric": getattr(wl, "metric", "FP4-quantized elements/s and achieved HBM GB/s (% of MI355X peak)"),
-        "value": value,
+        "metric": getattr(wl, "metric", METRIC),
+        "value": wl.elements / (ms_per_step * 1e-3),
         "unit": "FLOP/s" if mfma else "elements/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": getattr(wl, "dtype", "f32"),
-        "data": "synthetic",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "elements_per_step": wl.elements, "algorithmic_bytes_per_step": wl.algo_bytes,
-                   "whole_step_GBps": wl.algo_bytes / (ms_per_step * 1e-3) / 1e9,
-                   "whole_step_frac_of_hbm_peak": wl.algo_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+                   "whole_step_GBps": step_gbps, "whole_step_frac_of_hbm_peak": step_gbps / PEAK_HBM_GBPS},
         "roofline": {"bound": "mfma" if mfma else "hbm", "kernel": wl.kernel, "achieved": achieved, "peak": peak,
                      "unit": unit, "frac": achieved / peak, "traffic": counter_traffic(wl.kernel),
                      "kernel_ms_mean": k_mean, "kernel_launches_timed": nk,
                      "algorithmic_bytes_per_launch": wl.kernel_bytes},
     }
-    # distribution of single steps: a separate pass, each step between its own events
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # single steps from cold caches: a 1 GiB write between steps, each step between its own events
+    st = []
     for i in range(steps):
-        evs[i][0].record(stream)
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         wl.step(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    st = sorted(a.elapsed_time(b) for a, b in evs)
-    pick = lambda q: st[min(len(st) - 1, int(q * (len(st) - 1) + 0.5))]
-    line["config"]["step_ms_p10"], line["config"]["step_ms_p50"], line["config"]["step_ms_p90"] = (
-        pick(0.1), pick(0.5), pick(0.9))
-    if mfma:
-        flops_s = wl.flops / (ms_per_step * 1e-3)
-        line["config"]["whole_step_TFLOPs"] = flops_s / 1e12
-        line["config"]["whole_step_frac_of_peak"] = flops_s / 1e12 / wl.peak
-        if cpu_budget > 0:
-            cb = wl.cpu_baseline(cpu_budget)
-            if cb is not None:
-                line["cpu_baseline"] = cb
-        return line
-    # the call with the tensor amax given by the caller (no amax pass)
-    given = getattr(wl, "given_launch", wl.kernel_launch)
-    for i in range(4):
-        wl.step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(nk):
-        given(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    g_ms = e0.elapsed_time(e1) / nk
-    line["config"]["amax_given_ms"] = g_ms
-    line["config"]["amax_given_GBps"] = wl.kernel_bytes / (g_ms * 1e-3) / 1e9
-    if isinstance(wl, WgradRHT):
-        flops = 2 * 128 * (wl.rows * wl.cols)            # dense 128x128 contraction over one operand
-        line["roofline"]["mfma_tflops_in_kernel"] = flops / (k_mean * 1e-3) / 1e12
-        line["roofline"]["mfma_frac_of_bf16_peak"] = line["roofline"]["mfma_tflops_in_kernel"] / PEAK_MFMA_BF16_TFLOPS
-    if isinstance(wl, IF4RoundTrip):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        wl.dequant()
-        e0.record(stream)
-        for _ in range(5):
-            wl.dequant()
-        e1.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        dq = e0.elapsed_time(e1) / 5
-        n = wl.rows * wl.cols
-        line["config"]["dequant_ms"] = dq
-        line["config"]["dequant_GBps"] = (n // 2 + n // 16 + 4 * n) / (dq * 1e-3) / 1e9
-    if cpu_budget > 0:
-        cb = wl.cpu_baseline(cpu_budget)
-        if cb is not None:
-            line["cpu_baseline"] = cb
+        st.append(a.elapsed_time(b))
+    st.sort()
+    pick = lambda q: st[min(len(st) - 1, int(q * (len(st) - 1) + 0.5))]
+    line["config"]["cold_step_ms_p10"], line["config"]["cold_step_ms_p50"], line["config"]["cold_step_ms_p90"] = (
+        pick(0.1), pick(0.5), pick(0.9))
+    if not mfma:
+        g_ms = _event_mean(stream, wl.given_launch, nk)
+        line["config"]["amax_given_ms"] = g_ms
+        line["config"]["amax_given_GBps"] = wl.kernel_bytes / (g_ms * 1e-3) / 1e9
+    else:
+        line["config"]["whole_step_TFLOPs"] = wl.flops / (ms_per_step * 1e-3) / 1e12
+    line["config"].update(wl.extra(stream))
+    if cb is not None:
+        line["cpu_baseline"] = cb
     return line
+
+
+def _summary(line: dict) -> dict:
+    """The other workloads' figures, carried inside the headline line."""
+    c, r = line["config"], line["roofline"]
+    keep = {k: v for k, v in c.items() if k not in ("workload",)}
+    return {"workload": c["workload"], "value": line["value"], "unit": line["unit"], "dtype": line["dtype"],
+            "ms_per_step": line["ms_per_step"], **keep,
+            "roofline": {k: r[k] for k in ("bound", "kernel", "achieved", "peak", "unit", "frac", "traffic",
+                                           "kernel_ms_mean")}}
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="activation", choices=list(WORKLOADS) + list(CALIBRATION) + ["all"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline (0: skip)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="headline", choices=["headline"] + list(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of single-thread oracle work for cpu_baseline (0: skip it and its parity check)")
+    ap.add_argument("--no-others", action="store_true", help="headline only (e.g. under a profiler)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; every step is one GPU's share "
-                                   "(see the sharding notes), so --gpus must be 1"}))
+        print(json.dumps({"error": "this library runs on one GPU: every step is one GPU's share of the work "
+                                   "(the multi-GPU sharding is described, not built), so --gpus must be 1"}))
         return 2
     import torch
     if not torch.cuda.is_available():
@@ -677,12 +680,20 @@ def main(argv=None):
         return 1
     from block_scaled_fp4_05_amd import binding as B
     B.lib()
-    names = list(WORKLOADS) if a.config == "all" else [a.config]
-    for n in names:
-        wl = WORKLOADS[n]() if n in WORKLOADS else CALIBRATION[n]()
-        line = run(wl, a.steps, a.warmup, a.cpu_budget)
-        print(json.dumps(line), flush=True)
-        torch.cuda.empty_cache()
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = lambda: scratch.fill_(1)
+    if a.config == "headline":
+        line = run(HEADLINE(), a.steps, a.warmup, a.cpu_budget, flush)
+        if not a.no_others:
+            others = []
+            for cls in OTHERS:
+                torch.cuda.empty_cache()
+                others.append(_summary(run(cls(), a.steps, a.warmup, 0.0, flush)))
+                print(f"# timed {others[-1]['workload']}", file=sys.stderr, flush=True)
+            line["config"]["other_workloads"] = others
+    else:
+        line = run(WORKLOADS[a.config](), a.steps, a.warmup, a.cpu_budget if a.config != "copy" else 0.0, flush)
+    print(json.dumps(line), flush=True)
     return 0
 
 

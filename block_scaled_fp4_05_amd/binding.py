@@ -26,11 +26,10 @@ ROWWISE, COLWISE = 1, 2
 AMAX_COMPUTE, AMAX_GIVEN = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_E_NULL", 2: "FP4Q_E_SHAPE", 3: "FP4Q_E_ALIGN", 4: "FP4Q_E_ARG", 5: "FP4Q_E_HIP"}
 
-EXPORTS = ["fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_mxfp6",
-           "fp4q_quantize_if4",
-           "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax", "fp4q_set_onepass_wait", "fp4q_onepass_fallbacks",
-           "fp4q_rht_signs_from_seed",
-           "fp4q_status_string", "fp4q_abi_version"]
+EXPORTS = ["fp4q_workspace_create", "fp4q_workspace_destroy", "fp4q_workspace_set_wait", "fp4q_workspace_fallbacks",
+           "fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_mxfp6",
+           "fp4q_quantize_if4", "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax",
+           "fp4q_rht_signs_from_seed", "fp4q_status_string", "fp4q_abi_version"]
 
 
 class Fp4qError(RuntimeError):
@@ -52,18 +51,20 @@ def lib() -> ctypes.CDLL:
                                "(there is no CPU fallback)")
         L = ctypes.CDLL(LIB_PATH)
         sig = {
-            "fp4q_quantize_nvfp4": [_P, _I, _I64, _I64, _U, _I, _U64, _P, _U, _P, _P, _P, _P, _P, _P, _P],
-            "fp4q_quantize_nvfp4_2d": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P],
-            "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P, _P],
+            "fp4q_workspace_create": [_P],
+            "fp4q_workspace_destroy": [_P],
+            "fp4q_workspace_set_wait": [_P, _U],
+            "fp4q_workspace_fallbacks": [_P, _P, _P],
+            "fp4q_quantize_nvfp4": [_P, _I, _I64, _I64, _U, _I, _U64, _P, _U, _P, _P, _P, _P, _P, _P, _P, _P],
+            "fp4q_quantize_nvfp4_2d": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P, _P],
+            "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P, _P, _P],
             "fp4q_quantize_mxfp6": [_P, _I, _I64, _I64, _I, _P, _P, _P],
-            "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P],
+            "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P],
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
             "fp4q_gemm_mxfp4": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P],
             "fp4q_gemm_nvfp4": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P],
             "fp4q_dequantize": [_I, _P, _P, _P, _I64, _I64, _I, _P, _P],
             "fp4q_amax": [_P, _I, _I64, _I64, _P, _P],
-            "fp4q_set_onepass_wait": [_U],
-            "fp4q_onepass_fallbacks": [_P, _P],
             "fp4q_rht_signs_from_seed": [_U64, _P],
             "fp4q_status_string": [_I],
             "fp4q_abi_version": [],
@@ -73,7 +74,6 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = _I
         L.fp4q_rht_signs_from_seed.restype = None
-        L.fp4q_set_onepass_wait.restype = None
         L.fp4q_status_string.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -84,6 +84,8 @@ def _p(t) -> int | None:
         return None
     if isinstance(t, int):
         return t
+    if isinstance(t, Workspace):
+        return t.handle
     return t.data_ptr()
 
 
@@ -108,26 +110,71 @@ def _signs_arg(signs):
     return ctypes.addressof(arr), arr
 
 
+# --- workspaces ----------------------------------------------------------------------
+
+class Workspace:
+    """A libfp4q workspace (fp4q_workspace_create on the current device).  close()
+    destroys it; the caller makes sure no enqueued work still uses it."""
+
+    def __init__(self):
+        h = ctypes.c_void_p(0)
+        _check("fp4q_workspace_create", lib().fp4q_workspace_create(ctypes.addressof(h)))
+        self.handle = h.value
+
+    def close(self) -> None:
+        if self.handle:
+            _check("fp4q_workspace_destroy", lib().fp4q_workspace_destroy(self.handle))
+            self.handle = None
+
+
+_ws_cache: dict = {}
+
+
+def stream_workspace(stream=None) -> Workspace:
+    """The helpers' workspace for (current device, stream), created on first use and kept
+    for the life of the process (create one yourself, or pass ws=None, where a call must
+    not allocate, e.g. inside graph capture)."""
+    key = (torch.cuda.current_device(), _s(stream))
+    w = _ws_cache.get(key)
+    if w is None:
+        w = _ws_cache[key] = Workspace()
+    return w
+
+
+def _ws(ws, stream):
+    return stream_workspace(stream) if isinstance(ws, str) and ws == "auto" else ws
+
+
 # --- the C entry points, same names -----------------------------------------------
 
+def fp4q_workspace_set_wait(ws: Workspace, microseconds: int) -> int:
+    return _check("fp4q_workspace_set_wait", lib().fp4q_workspace_set_wait(_p(ws), microseconds))
+
+
+def fp4q_workspace_fallbacks(ws: Workspace, stream=None) -> int:
+    out = ctypes.c_uint32(0)
+    _check("fp4q_workspace_fallbacks", lib().fp4q_workspace_fallbacks(_p(ws), _s(stream), ctypes.addressof(out)))
+    return out.value
+
+
 def fp4q_quantize_nvfp4(x, dt, rows, cols, layouts, rnd, sr_seed, rht_signs, amax_mode, amax, tensor_scale,
-                        row_codes, row_scales, col_codes, col_scales, stream=None) -> int:
+                        row_codes, row_scales, col_codes, col_scales, ws=None, stream=None) -> int:
     sp, _keep = _signs_arg(rht_signs)
     return _check("fp4q_quantize_nvfp4", lib().fp4q_quantize_nvfp4(
         _p(x), dt, rows, cols, layouts, rnd, sr_seed, sp, amax_mode, _p(amax), _p(tensor_scale),
-        _p(row_codes), _p(row_scales), _p(col_codes), _p(col_scales), _s(stream)))
+        _p(row_codes), _p(row_scales), _p(col_codes), _p(col_scales), _p(ws), _s(stream)))
 
 
 def fp4q_quantize_nvfp4_2d(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, scales, codes_t,
-                           stream=None) -> int:
+                           ws=None, stream=None) -> int:
     return _check("fp4q_quantize_nvfp4_2d", lib().fp4q_quantize_nvfp4_2d(
         _p(x), dt, rows, cols, amax_mode, _p(amax), _p(tensor_scale), _p(codes), _p(scales), _p(codes_t),
-        _s(stream)))
+        _p(ws), _s(stream)))
 
 
-def fp4q_quantize_mxfp4(x, dt, rows, cols, rnd, sr_seed, codes, scales, amax=None, stream=None) -> int:
+def fp4q_quantize_mxfp4(x, dt, rows, cols, rnd, sr_seed, codes, scales, amax=None, ws=None, stream=None) -> int:
     return _check("fp4q_quantize_mxfp4", lib().fp4q_quantize_mxfp4(
-        _p(x), dt, rows, cols, rnd, sr_seed, _p(codes), _p(scales), _p(amax), _s(stream)))
+        _p(x), dt, rows, cols, rnd, sr_seed, _p(codes), _p(scales), _p(amax), _p(ws), _s(stream)))
 
 
 def fp4q_quantize_mxfp6(x, dt, rows, cols, fmt, codes, scales, stream=None) -> int:
@@ -135,9 +182,10 @@ def fp4q_quantize_mxfp6(x, dt, rows, cols, fmt, codes, scales, stream=None) -> i
         _p(x), dt, rows, cols, fmt, _p(codes), _p(scales), _s(stream)))
 
 
-def fp4q_quantize_if4(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, scales, stream=None) -> int:
+def fp4q_quantize_if4(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, scales, ws=None,
+                      stream=None) -> int:
     return _check("fp4q_quantize_if4", lib().fp4q_quantize_if4(
-        _p(x), dt, rows, cols, amax_mode, _p(amax), _p(tensor_scale), _p(codes), _p(scales), _s(stream)))
+        _p(x), dt, rows, cols, amax_mode, _p(amax), _p(tensor_scale), _p(codes), _p(scales), _p(ws), _s(stream)))
 
 
 def fp4q_rht(x, dt, rows, cols, signs, inverse, y, stream=None) -> int:
@@ -164,16 +212,6 @@ def fp4q_dequantize(fmt, codes, scales, tensor_scale, rows, cols, out_dt, y, str
 
 def fp4q_amax(x, dt, rows, cols, amax, stream=None) -> int:
     return _check("fp4q_amax", lib().fp4q_amax(_p(x), dt, rows, cols, _p(amax), _s(stream)))
-
-
-def fp4q_set_onepass_wait(microseconds: int) -> None:
-    lib().fp4q_set_onepass_wait(microseconds)
-
-
-def fp4q_onepass_fallbacks(stream=None) -> int:
-    out = ctypes.c_uint32(0)
-    _check("fp4q_onepass_fallbacks", lib().fp4q_onepass_fallbacks(_s(stream), ctypes.addressof(out)))
-    return out.value
 
 
 def fp4q_rht_signs_from_seed(seed: int) -> list[int]:
@@ -205,8 +243,9 @@ def _u8(*shape, device):
 
 
 def quantize_nvfp4(x: torch.Tensor, layouts: int = ROWWISE | COLWISE, rnd: int = RTN, sr_seed: int = 0,
-                   rht_signs=None, amax: torch.Tensor | None = None, stream=None) -> dict:
-    """NVFP4 1x16.  If `amax` is given it is used as the tensor amax (AMAX_GIVEN)."""
+                   rht_signs=None, amax: torch.Tensor | None = None, ws="auto", stream=None) -> dict:
+    """NVFP4 1x16.  If `amax` is given it is used as the tensor amax (AMAX_GIVEN).
+    ws: "auto" (the stream's cached workspace), None (no workspace) or a Workspace."""
     rows, cols = x.shape
     dev = x.device
     out = {"tensor_scale": torch.empty(1, dtype=torch.float32, device=dev)}
@@ -220,12 +259,12 @@ def quantize_nvfp4(x: torch.Tensor, layouts: int = ROWWISE | COLWISE, rnd: int =
         cc, cs = _u8(cols, rows // 2, device=dev), _u8(cols, rows // 16, device=dev)
         out["col_codes"], out["col_scales"] = cc, cs
     fp4q_quantize_nvfp4(x, _dt(x), rows, cols, layouts, rnd, sr_seed, rht_signs, mode, out["amax"],
-                        out["tensor_scale"], rc, rs, cc, cs, stream)
+                        out["tensor_scale"], rc, rs, cc, cs, _ws(ws, stream), stream)
     return out
 
 
 def quantize_nvfp4_2d(x: torch.Tensor, transposed: bool = False, amax: torch.Tensor | None = None,
-                      stream=None) -> dict:
+                      ws="auto", stream=None) -> dict:
     """NVFP4 16x16.  If `amax` is given it is used as the tensor amax (AMAX_GIVEN)."""
     rows, cols = x.shape
     dev = x.device
@@ -235,18 +274,19 @@ def quantize_nvfp4_2d(x: torch.Tensor, transposed: bool = False, amax: torch.Ten
            "codes": _u8(rows, cols // 2, device=dev), "scales": _u8(rows // 16, cols // 16, device=dev),
            "codes_t": _u8(cols, rows // 2, device=dev) if transposed else None}
     fp4q_quantize_nvfp4_2d(x, _dt(x), rows, cols, mode, out["amax"], out["tensor_scale"], out["codes"],
-                           out["scales"], out["codes_t"], stream)
+                           out["scales"], out["codes_t"], _ws(ws, stream), stream)
     return out
 
 
 def quantize_mxfp4(x: torch.Tensor, rnd: int = RTN, sr_seed: int = 0, with_amax: bool = False,
-                   stream=None) -> dict:
+                   ws="auto", stream=None) -> dict:
     rows, cols = x.shape
     dev = x.device
     out = {"codes": _u8(rows, cols // 2, device=dev), "scales": _u8(rows, cols // 32, device=dev)}
     if with_amax:
         out["amax"] = torch.empty(1, dtype=torch.float32, device=dev)
-    fp4q_quantize_mxfp4(x, _dt(x), rows, cols, rnd, sr_seed, out["codes"], out["scales"], out.get("amax"), stream)
+    fp4q_quantize_mxfp4(x, _dt(x), rows, cols, rnd, sr_seed, out["codes"], out["scales"], out.get("amax"),
+                        _ws(ws, stream) if with_amax else None, stream)
     return out
 
 
@@ -263,7 +303,7 @@ def quantize_mxfp6(x: torch.Tensor, fmt: int = FP6_E2M3, stream=None) -> dict:
     return out
 
 
-def quantize_if4(x: torch.Tensor, amax: torch.Tensor | None = None, stream=None) -> dict:
+def quantize_if4(x: torch.Tensor, amax: torch.Tensor | None = None, ws="auto", stream=None) -> dict:
     """IF4.  If `amax` is given it is used as the tensor amax (AMAX_GIVEN)."""
     rows, cols = x.shape
     dev = x.device
@@ -272,7 +312,7 @@ def quantize_if4(x: torch.Tensor, amax: torch.Tensor | None = None, stream=None)
            "tensor_scale": torch.empty(1, dtype=torch.float32, device=dev),
            "codes": _u8(rows, cols // 2, device=dev), "scales": _u8(rows, cols // 16, device=dev)}
     fp4q_quantize_if4(x, _dt(x), rows, cols, mode, out["amax"], out["tensor_scale"], out["codes"],
-                      out["scales"], stream)
+                      out["scales"], _ws(ws, stream), stream)
     return out
 
 

@@ -4,7 +4,18 @@
 #include "../../include/fp4q.h"
 #include "fp4q_internal.hpp"
 
+#include <new>
 #include <stdint.h>
+
+// The caller-owned workspace handle: the device memory and the host's numbering of
+// one-pass launches on it.
+struct fp4q_workspace {
+  int device;
+  fp4q::WorkspaceMem* mem;
+  uint32_t epoch;        // one-pass launches enqueued so far; device slots start at epoch 0
+  uint32_t wait_iters;   // polls of >= 0.1 us before a one-pass wait gives up
+};
+static_assert(sizeof(fp4q::WorkspaceMem) <= FP4Q_WORKSPACE_BYTES, "workspace size in fp4q.h is too small");
 
 namespace {
 
@@ -14,16 +25,31 @@ bool valid_dtype(int d) { return d == FP4Q_F32 || d == FP4Q_BF16; }
 bool valid_round(int r) { return r == FP4Q_RTN || r == FP4Q_SR; }
 
 // Sink of a two-pass call's amax pass and the matching source for its quantizer: the
-// stream's workspace word when it can be had (no zeroing launch), else the caller's float.
-fp4q::AmaxSink amax_sink(float* amax, hipStream_t st, fp4q::AmaxSource* src) {
-  uint64_t* slot = nullptr;
-  uint32_t epoch = 0u;
-  if (fp4q::reserve_amax_slot(st, &slot, &epoch)) {
-    *src = fp4q::AmaxSource{nullptr, slot, amax};
-    return fp4q::AmaxSink{nullptr, slot, epoch};
+// workspace's two-pass state when there is one, else the caller's float (which the
+// amax pass zeroes first).
+fp4q::AmaxSink amax_sink(float* amax, fp4q_workspace* ws, fp4q::AmaxSource* src) {
+  if (ws) {
+    fp4q::TwoPassAmax* tp = &ws->mem->two_pass;
+    *src = fp4q::AmaxSource{nullptr, tp, amax};
+    return fp4q::AmaxSink{nullptr, tp};
   }
   *src = fp4q::AmaxSource{amax, nullptr, nullptr};
-  return fp4q::AmaxSink{amax, nullptr, 0u};
+  return fp4q::AmaxSink{amax, nullptr};
+}
+
+// A workspace must be used on the device it lives on.
+bool ws_ok(const fp4q_workspace* ws) {
+  if (!ws) return true;
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == ws->device;
+}
+
+// Whether work enqueued on `st` is being captured into a graph (then the one-pass
+// kernel, whose launch number is a host value, is not used).
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;   // unknown: take the safe path
+  return cs != hipStreamCaptureStatusNone;
 }
 
 fp4q_status after_launch() {
@@ -67,11 +93,47 @@ const char* fp4q_status_string(fp4q_status s) {
   return "unknown status";
 }
 
-void fp4q_set_onepass_wait(uint32_t microseconds) { fp4q::set_fused_wait_us(microseconds); }
+fp4q_status fp4q_workspace_create(fp4q_workspace** ws) {
+  if (!ws) return FP4Q_E_NULL;
+  *ws = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP4Q_E_HIP;
+  void* mem = nullptr;
+  if (hipMalloc(&mem, FP4Q_WORKSPACE_BYTES) != hipSuccess) return FP4Q_E_HIP;
+  if (hipMemset(mem, 0, FP4Q_WORKSPACE_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(mem);
+    return FP4Q_E_HIP;
+  }
+  fp4q_workspace* w = new (std::nothrow) fp4q_workspace{dev, static_cast<fp4q::WorkspaceMem*>(mem), 0u, 2000u};
+  if (!w) {
+    (void)hipFree(mem);
+    return FP4Q_E_HIP;
+  }
+  *ws = w;
+  return FP4Q_OK;
+}
 
-fp4q_status fp4q_onepass_fallbacks(hipStream_t stream, uint32_t* count) {
-  if (!count) return FP4Q_E_NULL;
-  return fp4q::fused_fallbacks(stream, count) ? FP4Q_OK : FP4Q_E_HIP;
+fp4q_status fp4q_workspace_destroy(fp4q_workspace* ws) {
+  if (!ws) return FP4Q_E_NULL;
+  const hipError_t e = hipFree(ws->mem);
+  delete ws;
+  return e == hipSuccess ? FP4Q_OK : FP4Q_E_HIP;
+}
+
+fp4q_status fp4q_workspace_set_wait(fp4q_workspace* ws, uint32_t microseconds) {
+  if (!ws) return FP4Q_E_NULL;
+  const uint64_t t = (uint64_t)microseconds * 10u;   // one poll round takes at least ~0.1 us
+  ws->wait_iters = t > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)t;
+  return FP4Q_OK;
+}
+
+fp4q_status fp4q_workspace_fallbacks(fp4q_workspace* ws, hipStream_t stream, uint32_t* count) {
+  if (!ws || !count) return FP4Q_E_NULL;
+  if (!ws_ok(ws)) return FP4Q_E_ARG;
+  return hipMemcpyAsync(count, &ws->mem->fused.fallbacks[0], 4, hipMemcpyDeviceToHost, stream) == hipSuccess &&
+                 hipStreamSynchronize(stream) == hipSuccess
+             ? FP4Q_OK
+             : FP4Q_E_HIP;
 }
 
 void fp4q_rht_signs_from_seed(uint64_t seed, uint32_t signs[4]) {
@@ -92,7 +154,7 @@ fp4q_status fp4q_amax(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, 
 fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, unsigned layouts,
                                 fp4q_round rnd, uint64_t sr_seed, const uint32_t* rht_signs, unsigned amax_mode,
                                 float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
-                                uint8_t* col_codes, uint8_t* col_scales, hipStream_t stream) {
+                                uint8_t* col_codes, uint8_t* col_scales, fp4q_workspace* ws, hipStream_t stream) {
   const bool row = (layouts & FP4Q_ROWWISE) != 0, col = (layouts & FP4Q_COLWISE) != 0;
   if (!x || !amax || !tensor_scale) return FP4Q_E_NULL;
   if (row && (!row_codes || !row_scales)) return FP4Q_E_NULL;
@@ -108,13 +170,14 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
   if (!aligned16(x) || !aligned4(amax) || !aligned4(tensor_scale)) return FP4Q_E_ALIGN;
   if (row && (!aligned16(row_codes) || !aligned16(row_scales))) return FP4Q_E_ALIGN;
   if (col && (!aligned16(col_codes) || !aligned16(col_scales))) return FP4Q_E_ALIGN;
+  if (!ws_ok(ws)) return FP4Q_E_ARG;
 
   const bool sr = rnd == FP4Q_SR;
   if (rht_signs) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     fp4q::AmaxSource src{amax, nullptr, nullptr};
     if (amax_mode == FP4Q_AMAX_COMPUTE) {
-      const fp4q::AmaxSink sink = amax_sink(amax, stream, &src);
+      const fp4q::AmaxSink sink = amax_sink(amax, ws, &src);
       fp4q::launch_rht_amax(xb, rows, cols, rht_signs, sink, stream);
     }
     fp4q::launch_rht_nvfp4_col(xb, rows, cols, rht_signs, sr, sr_seed, src, tensor_scale, col_codes, col_scales,
@@ -124,10 +187,22 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
   fp4q::AmaxSource src{amax, nullptr, nullptr};
   if (amax_mode == FP4Q_AMAX_COMPUTE) {
     // one pass when the tensor fits a co-resident grid, else amax first
-    if (fp4q::launch_nvfp4_fused(x, dt, rows, cols, layouts, sr, amax, tensor_scale, row_codes, row_scales,
-                                 col_codes, col_scales, sr_seed, stream))
-      return after_launch();
-    fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, stream, &src), stream);
+    if (ws && !capturing(stream)) {
+      uint32_t epoch = ws->epoch + 1u;
+      if (epoch == 0u) {
+        // after 2^32 launches the numbers repeat: clear the exchange first, so no slot
+        // left by an earlier launch can carry the current number
+        fp4q::launch_clear_fused(&ws->mem->fused, stream);
+        epoch = 1u;
+      }
+      if (fp4q::launch_nvfp4_fused(x, dt, rows, cols, layouts, sr, amax, tensor_scale, row_codes, row_scales,
+                                   col_codes, col_scales, sr_seed, &ws->mem->fused, epoch, ws->wait_iters,
+                                   stream)) {
+        ws->epoch = epoch;
+        return after_launch();
+      }
+    }
+    fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, ws, &src), stream);
   }
   fp4q::launch_nvfp4(x, dt, rows, cols, layouts, sr, src, tensor_scale, row_codes, row_scales, col_codes,
                      col_scales, sr_seed, stream);
@@ -136,28 +211,30 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
 
 fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, unsigned amax_mode,
                                    float* amax, float* tensor_scale, uint8_t* codes, uint8_t* scales,
-                                   uint8_t* codes_t, hipStream_t stream) {
+                                   uint8_t* codes_t, fp4q_workspace* ws, hipStream_t stream) {
   if (!x || !amax || !tensor_scale || !codes || !scales) return FP4Q_E_NULL;
   if (!valid_dtype(dt) || (amax_mode != FP4Q_AMAX_COMPUTE && amax_mode != FP4Q_AMAX_GIVEN)) return FP4Q_E_ARG;
   if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0) return FP4Q_E_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(amax) || !aligned4(tensor_scale) ||
       (codes_t && !aligned16(codes_t)))
     return FP4Q_E_ALIGN;
+  if (!ws_ok(ws)) return FP4Q_E_ARG;
   fp4q::AmaxSource src{amax, nullptr, nullptr};
-  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, stream, &src), stream);
+  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, ws, &src), stream);
   fp4q::launch_nvfp4_2d(x, dt, rows, cols, src, tensor_scale, codes, scales, codes_t, stream);
   return after_launch();
 }
 
 fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, fp4q_round rnd,
                                 uint64_t sr_seed, uint8_t* codes, uint8_t* scales, float* amax,
-                                hipStream_t stream) {
-  if (!x || !codes || !scales) return FP4Q_E_NULL;
+                                fp4q_workspace* ws, hipStream_t stream) {
+  if (!x || !codes || !scales || (amax && !ws)) return FP4Q_E_NULL;
   if (!valid_dtype(dt) || !valid_round(rnd)) return FP4Q_E_ARG;
   if (rows <= 0 || cols <= 0 || cols % 32 != 0) return FP4Q_E_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (amax && !aligned4(amax))) return FP4Q_E_ALIGN;
-  if (!fp4q::launch_mxfp4(x, dt, rows, cols, rnd == FP4Q_SR, codes, scales, sr_seed, amax, stream))
-    return FP4Q_E_HIP;
+  if (!ws_ok(ws)) return FP4Q_E_ARG;
+  fp4q::launch_mxfp4(x, dt, rows, cols, rnd == FP4Q_SR, codes, scales, sr_seed, amax,
+                     ws ? &ws->mem->spread[0][0] : nullptr, stream);
   return after_launch();
 }
 
@@ -173,14 +250,15 @@ fp4q_status fp4q_quantize_mxfp6(const void* x, fp4q_dtype dt, int64_t rows, int6
 
 fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, unsigned amax_mode,
                               float* amax, float* tensor_scale, uint8_t* codes, uint8_t* scales,
-                              hipStream_t stream) {
+                              fp4q_workspace* ws, hipStream_t stream) {
   if (!x || !amax || !tensor_scale || !codes || !scales) return FP4Q_E_NULL;
   if (!valid_dtype(dt) || (amax_mode != FP4Q_AMAX_COMPUTE && amax_mode != FP4Q_AMAX_GIVEN)) return FP4Q_E_ARG;
   if (rows <= 0 || cols <= 0 || cols % 16 != 0) return FP4Q_E_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(amax) || !aligned4(tensor_scale))
     return FP4Q_E_ALIGN;
+  if (!ws_ok(ws)) return FP4Q_E_ARG;
   fp4q::AmaxSource src{amax, nullptr, nullptr};
-  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, stream, &src), stream);
+  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, ws, &src), stream);
   fp4q::launch_if4(x, dt, rows, cols, src, tensor_scale, codes, scales, stream);
   return after_launch();
 }

@@ -281,30 +281,38 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
 }
 
 // Where an amax pass posts its workgroup maxima, and where a quantizer finds the
-// tensor amax.  A pass posts either into a float the caller zeroed (atomic max on
-// its bits) or into a 64-bit word of a per-stream workspace holding
-// (epoch << 32) | bits, where the host numbers the launches on the stream: the
-// first post of a launch replaces whatever an earlier launch left (its epoch is
-// larger), so the word needs no reset between calls.
-// (AmaxSink and AmaxSource are declared with the launchers.)
+// tensor amax: a float the call zeroed first (atomic max on its bits), or the
+// two-pass state of a workspace (TwoPassAmax, with the protocol stated there).  Each
+// workgroup posts once, from one thread.
 __device__ __forceinline__ void post_amax(const AmaxSink& s, float m) {
-  if (s.slot)
-    __hip_atomic_fetch_max(s.slot, ((uint64_t)s.epoch << 32) | __float_as_uint(m), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  else
+  if (s.tp) {
+    const uint32_t e = s.tp->ea;   // no workgroup of an amax pass writes it
+    atomicMax(&s.tp->slot[e & 1u][0], __float_as_uint(m));
+    if (blockIdx.x == 0) {
+      s.tp->eq = e;                   // read by the quantizer that follows
+      s.tp->slot[(e + 1u) & 1u][0] = 0u;   // the next call's slot; nobody reads it now
+    }
+  } else {
     atomic_max_nonneg(s.f, m);
+  }
 }
-__device__ __forceinline__ float read_amax(const AmaxSource& s) {
-  return s.slot ? __uint_as_float((uint32_t)*s.slot) : *s.f;
-}
+
 // The tensor scale from the source; workgroup 0's first thread publishes it (and the
-// amax, when it came from a pass of this call).
+// amax, when it came from a pass of this call) and hands the slot back.
 __device__ __forceinline__ float tensor_scale_publish(const AmaxSource& s, float* tensor_scale) {
-  const float a = read_amax(s);
+  float a;
+  uint32_t e = 0u;
+  if (s.tp) {
+    e = s.tp->eq;   // no workgroup of a quantizer writes it
+    a = __uint_as_float(s.tp->slot[e & 1u][0]);
+  } else {
+    a = *s.f;
+  }
   const float gs = tensor_scale_from_amax(a);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *tensor_scale = gs;
     if (s.out) *s.out = a;
+    if (s.tp) s.tp->ea = e + 1u;   // the next call's amax pass posts into the other slot
   }
   return gs;
 }

@@ -7,50 +7,77 @@
 
 namespace fp4q {
 
-// Where an amax pass posts (a zeroed float, or a per-stream workspace word with an
-// epoch) and where a quantizer reads the tensor amax from (device side in fp4q_dev.hpp).
+constexpr int kFusedMaxWg = 2048;
+constexpr int kAmaxSpread = 128;   // cache lines an amax-reporting pass spreads its posts over
+
+// Device-side state of a two-pass call (an amax pass A, then a quantizer Q) kept in a
+// caller's workspace, so that nothing is numbered on the host and a call captured in
+// a graph stays correct on every replay.  A reads `ea`, posts its workgroup maxima by
+// atomic max into slot[ea & 1], and one of its threads records ea in `eq` and clears
+// the other slot for the next call; Q reads slot[eq & 1] and one of its threads
+// advances ea to eq + 1.  No kernel writes a word that its own workgroups read, and
+// every word is consumed one kernel boundary after it is written.
+struct alignas(128) TwoPassAmax {
+  uint32_t ea;
+  uint32_t pad0[31];
+  uint32_t eq;
+  uint32_t pad1[31];
+  uint32_t slot[2][32];   // float bits (magnitudes), one 128-byte line each
+};
+
+// The one-pass kernel's exchange: per group of workgroups its members' slots and the
+// group maximum, as (epoch << 32) | float bits, plus a count of waits that ran out.
+struct FusedArea {
+  uint64_t local[8][kFusedMaxWg / 8 + 16];
+  uint64_t group[8][16];
+  uint32_t fallbacks[32];
+};
+
+// Device memory of a workspace.  Every word starts at zero.
+struct WorkspaceMem {
+  FusedArea fused;
+  TwoPassAmax two_pass;
+  uint32_t spread[kAmaxSpread][32];   // MXFP4's amax report: zero between calls
+};
+
+// Where an amax pass posts (a float the call zeroed first, or a workspace's two-pass
+// slot) and where a quantizer reads the tensor amax from (device side in fp4q_dev.hpp).
 struct AmaxSink {
   float* f;
-  uint64_t* slot;
-  uint32_t epoch;
+  TwoPassAmax* tp;
 };
 struct AmaxSource {
-  const float* f;         // tensor amax given by the caller, or
-  const uint64_t* slot;   // the word an amax pass of the same stream posted into
-  float* out;             // with `slot`: the caller's amax output, written by one thread
+  const float* f;     // tensor amax given by the caller (or posted into it), or
+  TwoPassAmax* tp;    // the slot an amax pass of the same call posted into
+  float* out;         // with `tp`: the caller's amax output, written by one thread
 };
 
 // amax of x into a zeroed-first float (the standalone entry point) or a sink
 void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t st);
 void launch_amax_to(const void* x, int dtype, int64_t n, const AmaxSink& sink, hipStream_t st);
-// The stream's workspace word for a two-pass call and the call's epoch (false if the
-// workspace cannot be allocated; callers then use the caller's float instead).
-bool reserve_amax_slot(hipStream_t st, uint64_t** slot, uint32_t* epoch);
 
 void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
                   const AmaxSource& amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
                   uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, hipStream_t st);
 
-// NVFP4 with amax computed in the same pass.  Returns false, having enqueued nothing,
-// when the tensor does not fit one co-resident grid.
+// NVFP4 with amax computed in the same pass, through the workspace's exchange area
+// with launch number `epoch`.  Returns false, having enqueued nothing, when the tensor
+// does not fit one co-resident grid.  `wait_iters` bounds each wait (polls of >= 0.1 us).
 bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
                         float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
-                        uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, hipStream_t st);
-// Wait limit of the one-pass kernel's exchange before a workgroup computes a missing
-// maximum itself, and the count of such fallbacks on a stream (synchronizes it).
-void set_fused_wait_us(uint32_t us);
-bool fused_fallbacks(hipStream_t st, uint32_t* count);
-constexpr int kFusedMaxWg = 2048;
-constexpr int kAmaxSpread = 128;   // cache lines an amax-reporting pass spreads its posts over
+                        uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, FusedArea* area, uint32_t epoch,
+                        uint32_t wait_iters, hipStream_t st);
+// Clears a workspace's exchange area on the stream (a fill kernel, no memset node).
+void launch_clear_fused(FusedArea* area, hipStream_t st);
 
 void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                      float* tensor_scale, uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st);
 
-// amax: NULL, or a device float that receives max|x| over the tensor (a second,
-// one-workgroup launch folds the workgroups' spread posts).  False if the per-stream
-// workspace could not be set up (nothing launched then).
-bool launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
-                  uint8_t* scales, uint64_t seed, float* amax, hipStream_t st);
+// amax: NULL, or a device float that receives max|x| over the tensor; the workgroups
+// post into the workspace's spread lines and a second, one-workgroup launch folds them
+// (and clears them for the next call).
+void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
+                  uint8_t* scales, uint64_t seed, float* amax, uint32_t* spread, hipStream_t st);
 
 void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                 float* tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t st);

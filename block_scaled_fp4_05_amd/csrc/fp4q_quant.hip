@@ -14,10 +14,6 @@
 #include "fp4q_dev.hpp"
 #include "fp4q_internal.hpp"
 
-#include <atomic>
-#include <mutex>
-#include <vector>
-
 namespace fp4q {
 
 // ===========================================================================
@@ -124,7 +120,7 @@ static int num_cus();
 template <typename T>
 static void launch_amax_t(const void* x, int64_t n, const AmaxSink& sink, hipStream_t st) {
   const T* xp = static_cast<const T*>(x);
-  if (!sink.slot) k_zero1<<<1, 1, 0, st>>>(sink.f);
+  if (!sink.tp) k_zero1<<<1, 1, 0, st>>>(sink.f);
   if ((int64_t)sizeof(T) * n >= ((int64_t)128 << 20)) {
     const int64_t per16 = 16 / sizeof(T), n16 = n / per16;
     k_amax_wide<T><<<2 * num_cus(), 256, 0, st>>>(static_cast<const u32x4_t*>(x), n16, sink);
@@ -142,7 +138,7 @@ void launch_amax_to(const void* x, int dtype, int64_t n, const AmaxSink& sink, h
 }
 
 void launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t st) {
-  launch_amax_to(x, dtype, n, AmaxSink{amax, nullptr, 0u}, st);
+  launch_amax_to(x, dtype, n, AmaxSink{amax, nullptr}, st);
 }
 
 // ===========================================================================
@@ -639,23 +635,17 @@ void launch_nvfp4(const void* x, int dtype, int64_t rows, int64_t cols, unsigned
 // reads the missing part of x itself (see grid_max).
 // ===========================================================================
 
-// Workspace of the one-pass kernel.  Values that cross workgroups travel in 64-bit
-// slots holding (epoch << 32) | float bits: a reader that sees the current launch's
-// epoch in a slot has the value in the same word, so no fence is needed and nothing
-// is ever reset.  The host numbers launches per stream (epoch 1, 2, ...), so slots
-// left by earlier launches never match.
+// The one-pass kernel's exchange lives in a FusedArea of the caller's workspace.
+// Values that cross workgroups travel in 64-bit slots holding (epoch << 32) | float
+// bits: a reader that sees the current launch's epoch in a slot has the value in the
+// same word, so no fence is needed and nothing is reset between launches.  The host
+// numbers the launches on a workspace (epoch 1, 2, ...), so slots left by earlier
+// launches never match.
 //
 // Workgroups form 8 groups, g = b % 8, and workgroup g leads group g: members post
 // their slots, the leader combines them and posts the group maximum, and every
 // workgroup reads the eight group maxima.  All of it is device-scope traffic, so no
 // step relies on where a workgroup runs.
-struct FusedWs {
-  uint64_t local[8][kFusedMaxWg / 8 + 16];   // per group: members' slots
-  uint64_t group[8][16];                      // per group: its maximum, device scope
-  uint32_t fallbacks[32];                     // waits that ran out and were answered from x
-  uint64_t amax_slot[16];                     // two-pass calls: (epoch << 32) | amax bits, by atomic max
-  uint64_t spread[kAmaxSpread][16];           // MXFP4 amax: (epoch << 32) | magnitude bits, one line each
-};
 
 __device__ __forceinline__ float raw_absmax(const Raw8x8<uint16_t>& raw) {
   // |bf16| orders like its 15 magnitude bits, so a packed 16-bit max does two at once
@@ -752,7 +742,7 @@ __device__ __forceinline__ void read_miss(const GridMaxShared& sh, uint32_t (&w)
 // resident, which the launch size is chosen for, no fallback runs; without it, the
 // grid still finishes with the exact maximum.
 template <typename T>
-__device__ __forceinline__ float all_groups_max(FusedWs* ws, uint32_t epoch, uint32_t wait_iters,
+__device__ __forceinline__ float all_groups_max(FusedArea* ws, uint32_t epoch, uint32_t wait_iters,
                                                 const T* __restrict__ x, int rows, int cols, int tiles_r,
                                                 int tiles_c, GridMaxShared& sh) {
   const int tid = threadIdx.x;
@@ -777,7 +767,7 @@ __device__ __forceinline__ float all_groups_max(FusedWs* ws, uint32_t epoch, uin
 }
 
 template <typename T>
-__device__ __forceinline__ float grid_max(FusedWs* ws, float v, uint32_t epoch, uint32_t wait_iters,
+__device__ __forceinline__ float grid_max(FusedArea* ws, float v, uint32_t epoch, uint32_t wait_iters,
                                           const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c,
                                           GridMaxShared& sh) {
   const int b = blockIdx.x, nwg = gridDim.x, g = b & 7, ng = nwg >> 3;
@@ -844,7 +834,7 @@ __device__ __forceinline__ void fused_phase2(Raw8x8<T> (&raw)[TPW],
 
 template <typename T, int TPW, bool ROW, bool COL, bool SR>
 __global__ __launch_bounds__(256) void k_nvfp4_fused(
-    const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c, FusedWs* __restrict__ ws,
+    const T* __restrict__ x, int rows, int cols, int tiles_r, int tiles_c, FusedArea* __restrict__ ws,
     uint32_t epoch, uint32_t wait_iters,
     float* __restrict__ amax_out, float* __restrict__ tensor_scale,
     uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
@@ -903,62 +893,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_fused(
 
 namespace {
 
-std::atomic<uint32_t> g_wait_iters{2000u};   // polls of >= 256 clocks each: >= 200 us at 2.4 GHz
-
-struct WsEntry {
-  int dev;
-  hipStream_t stream;
-  FusedWs* ws;
-  uint32_t epoch;          // launches enqueued so far; the device words start at epoch 0
-};
-
-struct Launch {
-  FusedWs* ws;
-  uint32_t epoch;
-};
-std::mutex g_ws_mu;
-std::vector<WsEntry> g_ws;
-
-// The stream's workspace on the current device, allocated and zeroed on first use.
-FusedWs* find_ws(hipStream_t st, WsEntry** entry) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  for (WsEntry& e : g_ws)
-    if (e.dev == dev && e.stream == st) {
-      *entry = &e;
-      return e.ws;
-    }
-  FusedWs* ws = nullptr;
-  if (hipMalloc(&ws, sizeof(FusedWs)) != hipSuccess) return nullptr;
-  if (hipMemset(ws, 0, sizeof(FusedWs)) != hipSuccess) {
-    (void)hipFree(ws);
-    return nullptr;
-  }
-  g_ws.push_back(WsEntry{dev, st, ws, 0u});
-  *entry = &g_ws.back();
-  return ws;
-}
-
-// Reserves the next launch on the stream: its workspace and epoch.  An epoch only has
-// to differ from the one a slot held before, so launches may run in any order.
-bool reserve_launch(hipStream_t st, Launch* l) {
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  WsEntry* e = nullptr;
-  if (!find_ws(st, &e)) return false;
-  e->epoch += 1u;
-  if (e->epoch == 0u) {
-    // After 2^32 launches the numbers repeat: clear every word first, so neither a
-    // stale slot nor a larger old epoch can be taken for the current launch's.
-    if (hipMemsetAsync(e->ws, 0, sizeof(FusedWs), st) != hipSuccess) return false;
-    e->epoch = 1u;
-  }
-  *l = Launch{e->ws, e->epoch};
-  return true;
-}
-
 template <typename T, int TPW, bool ROW, bool COL, bool SR>
 bool try_fused_t(const T* x, int rows, int cols, float* amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
-                 uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+                 uint8_t* cs, uint32_t k0, uint32_t k1, FusedArea* area, uint32_t epoch, uint32_t wait_iters,
+                 hipStream_t st) {
   const int tiles_r = (rows + 127) / 128, tiles_c = (cols + 127) / 128, total = tiles_r * tiles_c;
   const int per = (total + 7) / 8;
   const int nwg = 8 * ((per + TPW - 1) / TPW);
@@ -966,31 +904,35 @@ bool try_fused_t(const T* x, int rows, int cols, float* amax, float* ts, uint8_t
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess) return false;
   if (nwg > kFusedMaxWg || nwg > per_cu * num_cus()) return false;
-  Launch l;
-  if (!reserve_launch(st, &l)) return false;
-  kern<<<nwg, 256, 0, st>>>(x, rows, cols, tiles_r, tiles_c, l.ws, l.epoch, g_wait_iters.load(), amax, ts, rc, rs,
-                            cc, cs, k0, k1);
+  kern<<<nwg, 256, 0, st>>>(x, rows, cols, tiles_r, tiles_c, area, epoch, wait_iters, amax, ts, rc, rs, cc, cs, k0,
+                            k1);
   return true;
 }
 
 template <typename T, bool ROW, bool COL, bool SR>
 bool try_fused_rcs(const T* x, int rows, int cols, float* amax, float* ts, uint8_t* rc, uint8_t* rs, uint8_t* cc,
-                   uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+                   uint8_t* cs, uint32_t k0, uint32_t k1, FusedArea* area, uint32_t epoch, uint32_t wait_iters,
+                   hipStream_t st) {
   // fewest tiles per workgroup that still fit one co-resident grid
-  if (try_fused_t<T, 1, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)) return true;
-  if (try_fused_t<T, 2, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)) return true;
+#define FP4Q_TRY(N) try_fused_t<T, N, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, area, epoch, \
+                                                   wait_iters, st)
+  if (FP4Q_TRY(1)) return true;
+  if (FP4Q_TRY(2)) return true;
   if constexpr (sizeof(T) == 2)
-    if (try_fused_t<T, 4, ROW, COL, SR>(x, rows, cols, amax, ts, rc, rs, cc, cs, k0, k1, st)) return true;
+    if (FP4Q_TRY(4)) return true;
+#undef FP4Q_TRY
   return false;
 }
 
 template <typename T>
 bool try_fused_dt(const void* xv, int64_t rows, int64_t cols, unsigned layouts, bool sr, float* amax, float* ts,
-                  uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs, uint32_t k0, uint32_t k1, hipStream_t st) {
+                  uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs, uint32_t k0, uint32_t k1, FusedArea* area,
+                  uint32_t epoch, uint32_t wait_iters, hipStream_t st) {
   const T* x = static_cast<const T*>(xv);
   const bool row = layouts & 1u, col = layouts & 2u;
   const int r = (int)rows, c = (int)cols;
-#define FP4Q_FU(R, C, S) try_fused_rcs<T, R, C, S>(x, r, c, amax, ts, rc, rs, cc, cs, k0, k1, st)
+#define FP4Q_FU(R, C, S) \
+  try_fused_rcs<T, R, C, S>(x, r, c, amax, ts, rc, rs, cc, cs, k0, k1, area, epoch, wait_iters, st)
   if (row && col) return sr ? FP4Q_FU(true, true, true) : FP4Q_FU(true, true, false);
   if (row) return sr ? FP4Q_FU(true, false, true) : FP4Q_FU(true, false, false);
   return sr ? FP4Q_FU(false, true, true) : FP4Q_FU(false, true, false);
@@ -1001,45 +943,25 @@ bool try_fused_dt(const void* xv, int64_t rows, int64_t cols, unsigned layouts, 
 
 bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, unsigned layouts, bool sr,
                         float* amax, float* tensor_scale, uint8_t* rc, uint8_t* rs, uint8_t* cc, uint8_t* cs,
-                        uint64_t seed, hipStream_t st) {
+                        uint64_t seed, FusedArea* area, uint32_t epoch, uint32_t wait_iters, hipStream_t st) {
   if (rows > (1 << 30) || cols > (1 << 30)) return false;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   if (dtype == 1)
-    return try_fused_dt<uint16_t>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
-  return try_fused_dt<float>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, st);
+    return try_fused_dt<uint16_t>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, area, epoch,
+                                  wait_iters, st);
+  return try_fused_dt<float>(x, rows, cols, layouts, sr, amax, tensor_scale, rc, rs, cc, cs, k0, k1, area, epoch,
+                             wait_iters, st);
 }
 
-bool reserve_amax_slot(hipStream_t st, uint64_t** slot, uint32_t* epoch) {
-  Launch l;
-  if (!reserve_launch(st, &l)) return false;
-  *slot = &l.ws->amax_slot[0];
-  *epoch = l.epoch;
-  return true;
+// Zeroes n 32-bit words (a fill kernel rather than a memset, so it is also safe where
+// a caller captures the stream).
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
-bool reserve_amax_spread(hipStream_t st, uint64_t** slots, uint32_t* epoch) {
-  Launch l;
-  if (!reserve_launch(st, &l)) return false;
-  *slots = &l.ws->spread[0][0];
-  *epoch = l.epoch;
-  return true;
-}
-
-void set_fused_wait_us(uint32_t us) {
-  const uint64_t t = (uint64_t)us * 10u;   // one poll round takes at least ~0.1 us
-  g_wait_iters.store(t > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)t);
-}
-
-bool fused_fallbacks(hipStream_t st, uint32_t* count) {
-  FusedWs* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    WsEntry* e = nullptr;
-    ws = find_ws(st, &e);
-  }
-  if (!ws) return false;
-  return hipMemcpyAsync(count, &ws->fallbacks[0], 4, hipMemcpyDeviceToHost, st) == hipSuccess &&
-         hipStreamSynchronize(st) == hipSuccess;
+void launch_clear_fused(FusedArea* area, hipStream_t st) {
+  const int64_t n = (int64_t)(sizeof(FusedArea) / 4);
+  k_fill_zero<<<(int)((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<uint32_t*>(area), n);
 }
 
 // ===========================================================================
@@ -1048,14 +970,14 @@ bool fused_fallbacks(hipStream_t st, uint32_t* count) {
 // ===========================================================================
 
 // AMAX: the workgroup also posts max|x| over its elements (magnitude bits compared as
-// integers, so a NaN wins as it does in the amax pass) into spread slot b % kAmaxSpread,
-// tagged with the launch's epoch; k_spread_max folds the slots afterwards.  Spreading
-// the posts over kAmaxSpread cache lines keeps same-address atomics from queueing.
+// integers, so a NaN wins as it does in the amax pass) by atomic max into spread line
+// b % kAmaxSpread of the workspace, which is zero when the call starts; k_spread_max
+// folds the lines afterwards and clears them again.  Spreading the posts over
+// kAmaxSpread cache lines keeps same-address atomics from queueing.
 template <typename T, bool SR, bool AMAX>
 __global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t n16,
                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                               uint32_t k0, uint32_t k1, uint64_t* __restrict__ spread,
-                                               uint32_t epoch) {
+                                               uint32_t k0, uint32_t k1, uint32_t* __restrict__ spread) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-element group
   const bool ok = g < n16;
   float a[8], b[8];
@@ -1077,9 +999,7 @@ __global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t 
     if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mb;
     __syncthreads();
     if (threadIdx.x == 0)
-      __hip_atomic_fetch_max(&spread[(blockIdx.x % kAmaxSpread) * 16],
-                             ((uint64_t)epoch << 32) | max(max(wm[0], wm[1]), max(wm[2], wm[3])), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+      atomicMax(&spread[(blockIdx.x % kAmaxSpread) * 32], max(max(wm[0], wm[1]), max(wm[2], wm[3])));
   }
   float m = 0.0f;
 #pragma unroll
@@ -1105,33 +1025,27 @@ __global__ __launch_bounds__(256) void k_mxfp4(const T* __restrict__ x, int64_t 
   }
 }
 
-// The tensor amax from the spread slots of launch `epoch` (slots this launch did not
-// reach hold an older epoch and count as 0).
-__global__ __launch_bounds__(256) void k_spread_max(const uint64_t* __restrict__ spread, uint32_t epoch,
-                                                    float* __restrict__ amax) {
+// The tensor amax from the spread lines; then every line is cleared for the next call
+// (one workgroup: all reads are done before the barrier, all clears after it).
+__global__ __launch_bounds__(256) void k_spread_max(uint32_t* __restrict__ spread, float* __restrict__ amax) {
   __shared__ uint32_t wm[4];
   uint32_t mb = 0;
-  for (int i = threadIdx.x; i < kAmaxSpread; i += 256) {
-    const uint64_t w = __hip_atomic_load(&spread[i * 16], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(w >> 32) == epoch) mb = max(mb, (uint32_t)w);
-  }
+  for (int i = threadIdx.x; i < kAmaxSpread; i += 256) mb = max(mb, spread[i * 32]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mb;
   __syncthreads();
+  for (int i = threadIdx.x; i < kAmaxSpread; i += 256) spread[i * 32] = 0u;
   if (threadIdx.x == 0) *amax = __uint_as_float(max(max(wm[0], wm[1]), max(wm[2], wm[3])));
 }
 
-bool launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
-                  uint8_t* scales, uint64_t seed, float* amax, hipStream_t st) {
+void launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr, uint8_t* codes,
+                  uint8_t* scales, uint64_t seed, float* amax, uint32_t* spread, hipStream_t st) {
   const int64_t n16 = rows * cols / 16;
   const int grid = (int)((n16 + 255) / 256);
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  uint64_t* spread = nullptr;
-  uint32_t epoch = 0;
-  if (amax && !reserve_amax_spread(st, &spread, &epoch)) return false;
 #define FP4Q_MX(TY, S, A) \
-  k_mxfp4<TY, S, A><<<grid, 256, 0, st>>>(static_cast<const TY*>(x), n16, codes, scales, k0, k1, spread, epoch)
+  k_mxfp4<TY, S, A><<<grid, 256, 0, st>>>(static_cast<const TY*>(x), n16, codes, scales, k0, k1, spread)
   if (dtype == 1) {
     if (amax) { if (sr) FP4Q_MX(uint16_t, true, true); else FP4Q_MX(uint16_t, false, true); }
     else      { if (sr) FP4Q_MX(uint16_t, true, false); else FP4Q_MX(uint16_t, false, false); }
@@ -1140,8 +1054,7 @@ bool launch_mxfp4(const void* x, int dtype, int64_t rows, int64_t cols, bool sr,
     else      { if (sr) FP4Q_MX(float, true, false); else FP4Q_MX(float, false, false); }
   }
 #undef FP4Q_MX
-  if (amax) k_spread_max<<<1, 256, 0, st>>>(spread, epoch, amax);
-  return true;
+  if (amax) k_spread_max<<<1, 256, 0, st>>>(spread, amax);
 }
 
 // ===========================================================================

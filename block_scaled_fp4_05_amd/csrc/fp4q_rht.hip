@@ -576,7 +576,7 @@ void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint
 
 void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], const AmaxSink& sink,
                      hipStream_t st) {
-  if (!sink.slot) k_zero1_rht<<<1, 1, 0, st>>>(sink.f);
+  if (!sink.tp) k_zero1_rht<<<1, 1, 0, st>>>(sink.f);
   k_rht_amax<<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, pack_signs(signs), sink);
 }
 

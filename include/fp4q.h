@@ -23,19 +23,19 @@
  *  - Tensor, code and scale pointers must be 16-byte aligned, the float[1] amax and
  *    tensor_scale pointers 4-byte aligned (FP4Q_E_ALIGN otherwise).
  *  - Inputs and outputs must not overlap.  The caller allocates every buffer and
- *    keeps it alive until the work on `stream` has completed.  The only memory the
- *    library owns is a small per-(device, stream) workspace (about 35 KB) used by the
- *    calls that compute a tensor amax (the one-pass NVFP4 kernel's exchange, the word
- *    a separate amax pass posts into for the quantizer that follows it, and the lines
- *    an MXFP4 call that reports the amax spreads its posts over), allocated on the
- *    first such call on that stream and kept until the process ends; that first call
- *    is therefore not graph-capturable.
+ *    keeps it alive until the work on `stream` has completed.  No call allocates or
+ *    frees memory, synchronizes, or keeps state between calls, except through an
+ *    fp4q_workspace the caller creates once and passes in (below).
  *  - A call validates its arguments on the host, enqueues its kernels on `stream`
  *    (0 = the null stream) and returns without synchronizing.  On any validation
  *    error nothing is enqueued.  Device faults surface at the caller's next sync.
  *  - Inputs must be finite; codes for non-finite inputs are unspecified.
  *  - All calls are reentrant; calls on different streams may run concurrently
- *    when their output buffers are distinct.
+ *    when their output buffers, and their workspaces, are distinct.
+ *  - The quantize, transform, dequantize and GEMM calls are safe to capture into a
+ *    HIP graph (they enqueue kernels only: no memset, allocation or host
+ *    synchronization); a captured call gives correct results on every replay, also
+ *    when the inputs change between replays.
  *
  * Packed layouts (all byte arrays):
  *  - codes: element 2k of a logical row in bits 0-3 of byte k, element 2k+1 in
@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 6
+#define FP4Q_ABI_VERSION 7
 
 typedef enum {
     FP4Q_OK = 0,
@@ -82,6 +82,49 @@ typedef enum { FP4Q_FP6_E2M3 = 0, FP4Q_FP6_E3M2 = 1 } fp4q_fp6;
 #define FP4Q_AMAX_GIVEN 1u
 
 /*
+ * Workspace: a small piece of device memory (FP4Q_WORKSPACE_BYTES) through which the
+ * workgroups of a call that computes a tensor amax exchange partial maxima
+ * [NV "scaleの導出": the tensor scale needs the maximum of the whole tensor before any
+ * element is encoded].  With a workspace,
+ *   - fp4q_quantize_nvfp4 (AMAX_COMPUTE, no RHT) finds the amax and quantizes in ONE
+ *     read of x when the tensor fits one co-resident grid (about 64 MB of bf16);
+ *   - two-pass calls (an amax pass, then the quantizer) hand the amax over in the
+ *     workspace instead of zeroing the caller's float first (one launch fewer);
+ *   - fp4q_quantize_mxfp4 can report the tensor amax from its own read of x.
+ * Passing NULL instead is always valid: the calls then zero *amax with a one-thread
+ * kernel and post into it (MXFP4's amax report needs a workspace: FP4Q_E_NULL).
+ *
+ * Ownership and rules: fp4q_workspace_create allocates and clears the memory on the
+ * CURRENT device and synchronizes the device before it returns; it is the only call
+ * that allocates.  fp4q_workspace_destroy frees it (the caller first ensures that no
+ * enqueued work still uses it).  A workspace belongs to the device it was created on
+ * (FP4Q_E_ARG on another device) and must not be used by two calls that may run at the
+ * same time (e.g. on two streams without an order between them): its words are the
+ * calls' shared state.  It is not thread-safe.  After a call returns FP4Q_E_HIP its
+ * contents are undefined: destroy and re-create it.  Under stream capture the
+ * one-pass kernel is not used (its launch number lives on the host and would repeat
+ * on every replay); the two-pass protocol keeps all of its state on the device.
+ */
+typedef struct fp4q_workspace fp4q_workspace;
+#define FP4Q_WORKSPACE_BYTES 36864
+
+fp4q_status fp4q_workspace_create(fp4q_workspace** ws);
+fp4q_status fp4q_workspace_destroy(fp4q_workspace* ws);
+
+/* One-pass kernel: a workgroup whose wait for another workgroup's partial maximum
+ * exceeds this limit reads the corresponding part of x itself, so results never depend
+ * on every workgroup being resident.  On an idle GPU the grid is resident and no wait
+ * runs out.  When another kernel occupies the GPU at the same time (e.g. a concurrent
+ * stream), waits can run out and each such call costs about this limit more (still
+ * exact); lower it, or pass AMAX_GIVEN, where that matters.  Default 200 us; 0 makes
+ * every wait give up at once (slow, but exact).  Applies to calls enqueued afterwards. */
+fp4q_status fp4q_workspace_set_wait(fp4q_workspace* ws, uint32_t microseconds);
+
+/* Waits for `stream`, then stores in *count how many waits of one-pass calls on this
+ * workspace ran out and were answered by reading x (0 when the grid was resident). */
+fp4q_status fp4q_workspace_fallbacks(fp4q_workspace* ws, hipStream_t stream, uint32_t* count);
+
+/*
  * NVFP4 with 1x16 blocks [NV "scaleの導出", "Blockwise", "誤差逆伝播と転置"; GL].
  * Tensor scale gs = 2688 / amax (amax = 0 -> 1; overflow -> FLT_MAX), written to
  * *tensor_scale.  Per 16-element block: s = E4M3(fl(fl(bamax * gs) / 6)); each element
@@ -98,6 +141,7 @@ typedef enum { FP4Q_FP6_E2M3 = 0, FP4Q_FP6_E3M2 = 1 } fp4q_fp6;
  *             layouts == FP4Q_COLWISE, rows % 128 == 0 and cols < 2^27.  The amax and
  *             gs are then those of the transformed matrix.
  *   amax, tensor_scale  device float[1] each.
+ *   ws        workspace or NULL (see above).
  * Shapes: ROWWISE needs cols % 16 == 0; COLWISE needs rows % 16 == 0 and cols % 8 == 0.
  * SR uses stream 0 for the row-wise output and stream 1 for the column-wise output;
  * element index idx = row * lcols + col of the logical (output) matrix.  One
@@ -110,7 +154,8 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
                                 unsigned layouts, fp4q_round rnd, uint64_t sr_seed,
                                 const uint32_t* rht_signs, unsigned amax_mode, float* amax,
                                 float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
-                                uint8_t* col_codes, uint8_t* col_scales, hipStream_t stream);
+                                uint8_t* col_codes, uint8_t* col_scales, fp4q_workspace* ws,
+                                hipStream_t stream);
 
 /*
  * NVFP4 with 16x16 blocks for weights [NV "2D scaling"]: one E4M3 scale per 16x16
@@ -118,12 +163,13 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
  *   codes [rows][cols/2], scales [rows/16][cols/16];
  *   codes_t optional (NULL to skip): [cols][rows/2], the same codes in the layout of
  *   W^T, i.e. the codes of q(W^T).
+ *   ws      workspace or NULL.
  * Shapes: rows % 16 == 0, cols % 16 == 0.
  */
 fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
                                    unsigned amax_mode, float* amax, float* tensor_scale,
                                    uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
-                                   hipStream_t stream);
+                                   fp4q_workspace* ws, hipStream_t stream);
 
 /*
  * MXFP4: 32 elements + one E8M0 scale [GL "FP4の仕組み"; F6].  Per block the scale
@@ -134,12 +180,12 @@ fp4q_status fp4q_quantize_nvfp4_2d(const void* x, fp4q_dtype dt, int64_t rows, i
  *   amax  device float[1] or NULL.  Non-NULL also writes max|x| over the tensor, the
  *         value fp4q_amax returns, from the same read of x: a caller that quantizes
  *         one tensor to MXFP4 and to an amax-scaled format passes it on with
- *         FP4Q_AMAX_GIVEN instead of running an amax pass.  Uses the stream's
- *         workspace (see the conventions above); FP4Q_E_HIP if it cannot be allocated.
+ *         FP4Q_AMAX_GIVEN instead of running an amax pass.  Needs a workspace
+ *         (FP4Q_E_NULL if ws is NULL).
  */
 fp4q_status fp4q_quantize_mxfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
                                 fp4q_round rnd, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
-                                float* amax, hipStream_t stream);
+                                float* amax, fp4q_workspace* ws, hipStream_t stream);
 
 /*
  * MX FP6 [F6 "FP6で隣り合う値の間隔を見てみる", "量子化と6bitの保存"]: the OCP MX six-bit
@@ -163,10 +209,12 @@ fp4q_status fp4q_quantize_mxfp6(const void* x, fp4q_dtype dt, int64_t rows, int6
  * i ascending; INT4 is kept only if strictly lower and flagged in bit 7 of the
  * block's E4M3 scale byte.  RTN only.
  *   codes [rows][cols/2], scales [rows][cols/16].   Shapes: cols % 16 == 0.
+ *   ws    workspace or NULL.
  */
 fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
                               unsigned amax_mode, float* amax, float* tensor_scale,
-                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                              uint8_t* codes, uint8_t* scales, fp4q_workspace* ws,
+                              hipStream_t stream);
 
 /*
  * Random Hadamard transform along rows [NV "ランダムアダマール変換"], per chunk of
@@ -244,18 +292,6 @@ fp4q_status fp4q_amax(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, 
 /* The RHT sign mask for a seed: one Philox4x32-10 call with counter {0,0,0,1} and key
  * {lo32(seed), hi32(seed)}; its 128 output bits are the signs (host only). */
 void fp4q_rht_signs_from_seed(uint64_t seed, uint32_t signs[4]);
-
-/* One-pass NVFP4 (AMAX_COMPUTE on a tensor that fits one resident grid): workgroups
- * exchange partial maxima through the per-stream workspace, and a workgroup whose wait
- * for a missing value exceeds this limit reads the corresponding part of x itself, so
- * results never depend on every workgroup being resident.  Default 200 us; 0 makes
- * every wait give up at once (slow, but exact).  Process-wide; applies to calls
- * enqueued afterwards. */
-void fp4q_set_onepass_wait(uint32_t microseconds);
-
-/* Waits for `stream`, then stores in *count how many times one-pass calls on it fell
- * back to reading x for a missing maximum (0 when the grid was resident). */
-fp4q_status fp4q_onepass_fallbacks(hipStream_t stream, uint32_t* count);
 
 const char* fp4q_status_string(fp4q_status status);
 int fp4q_abi_version(void);

@@ -19,7 +19,18 @@ import numpy as np
 import oracle
 
 
+_THREADS = None
+
+
+def set_threads(n: int | None) -> None:
+    """Threads for the split calls (None: the host cores this process may use, at most 16)."""
+    global _THREADS
+    _THREADS = n
+
+
 def workers() -> int:
+    if _THREADS:
+        return _THREADS
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

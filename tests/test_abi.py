@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 6
+    assert B.fp4q_abi_version() == 7
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -51,7 +51,8 @@ def _nv(**kw):
     sp, keep = B._signs_arg(args["rht_signs"])
     return L.fp4q_quantize_nvfp4(args["x"], args["dt"], args["rows"], args["cols"], args["layouts"], args["rnd"],
                                  args["sr_seed"], sp, args["amax_mode"], args["amax"], args["tensor_scale"],
-                                 args["row_codes"], args["row_scales"], args["col_codes"], args["col_scales"], 0)
+                                 args["row_codes"], args["row_scales"], args["col_codes"], args["col_scales"],
+                                 args.get("ws"), 0)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -79,16 +80,15 @@ def test_nvfp4_rowwise_only_accepts_ragged_rows_shape_rules():
 
 def test_other_entry_points_validate():
     L = B.lib()
-    assert L.fp4q_quantize_nvfp4_2d(A, B.F32, 40, 48, 0, A2, A2, A, A, None, 0) == 2
-    assert L.fp4q_quantize_nvfp4_2d(None, B.F32, 32, 48, 0, A2, A2, A, A, None, 0) == 1
-    assert L.fp4q_quantize_nvfp4_2d(A, B.F32, 32, 48, 0, A2, A2, A, A, MIS, 0) == 3
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 48, 0, 0, A, A, None, 0) == 2
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 2, 0, A, A, None, 0) == 4
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, None, A, None, 0) == 1
-    assert L.fp4q_quantize_mxfp4(MIS, B.BF16, 4, 64, 0, 0, A, A, None, 0) == 3
-    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, A, A, A2 + 2, 0) == 3   # misaligned amax
-    assert L.fp4q_quantize_if4(A, B.BF16, 4, 40, 0, A2, A2, A, A, 0) == 2
-    assert L.fp4q_quantize_if4(A, 3, 4, 48, 0, A2, A2, A, A, 0) == 4
+    assert L.fp4q_quantize_nvfp4_2d(A, B.F32, 40, 48, 0, A2, A2, A, A, None, None, 0) == 2
+    assert L.fp4q_quantize_nvfp4_2d(None, B.F32, 32, 48, 0, A2, A2, A, A, None, None, 0) == 1
+    assert L.fp4q_quantize_nvfp4_2d(A, B.F32, 32, 48, 0, A2, A2, A, A, MIS, None, 0) == 3
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 48, 0, 0, A, A, None, None, 0) == 2
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 2, 0, A, A, None, None, 0) == 4
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, None, A, None, None, 0) == 1
+    assert L.fp4q_quantize_mxfp4(MIS, B.BF16, 4, 64, 0, 0, A, A, None, None, 0) == 3
+    assert L.fp4q_quantize_if4(A, B.BF16, 4, 40, 0, A2, A2, A, A, None, 0) == 2
+    assert L.fp4q_quantize_if4(A, 3, 4, 48, 0, A2, A2, A, A, None, 0) == 4
     sig = (ctypes.c_uint32 * 4)(1, 2, 3, 4)
     assert L.fp4q_rht(A, B.BF16, 100, 64, ctypes.addressof(sig), 0, A, 0) == 2
     assert L.fp4q_rht(A, B.BF16, 128, 60, ctypes.addressof(sig), 0, A, 0) == 2
@@ -128,6 +128,12 @@ def test_other_entry_points_validate():
     assert L.fp4q_dequantize(4, A, A, None, 16, 48, 0, A, 0) == 2
     assert L.fp4q_dequantize(5, A, MIS, None, 16, 64, 0, A, 0) == 3
     assert L.fp4q_dequantize(6, A, A, None, 16, 64, 0, A, 0) == 4
-    assert L.fp4q_onepass_fallbacks(0, None) == 1
+    # workspace calls: NULL handle or output
+    assert L.fp4q_workspace_create(None) == 1
+    assert L.fp4q_workspace_destroy(None) == 1
+    assert L.fp4q_workspace_set_wait(None, 5) == 1
+    assert L.fp4q_workspace_fallbacks(None, 0, A2) == 1
+    # MXFP4's amax report needs a workspace
+    assert L.fp4q_quantize_mxfp4(A, B.BF16, 4, 64, 0, 0, A, A, A2, None, 0) == 1
     assert L.fp4q_amax(None, 0, 4, 4, A2, 0) == 1
     assert L.fp4q_amax(A, 0, 0, 4, A2, 0) == 2

@@ -1,7 +1,7 @@
 """GPU parity at the full sizes of the five workloads, element by element.
 
 Every code, scale and flag byte of every output is compared with the oracle over the
-whole tensor (the oracle runs on row ranges in host threads, see oracle_par.py), the
+whole tensor (the oracle runs on row ranges in host threads, oracle/par.py), the
 amax and tensor scale exactly, and dequantized values at 0 ULP.  The calls are the
 ones the benchmark times, at the same shapes and in the same launch configuration.
 
@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-import oracle_par as op
+import oracle.par as op
 import synth_inputs as si
 from block_scaled_fp4_05_amd import binding as B
 

@@ -205,10 +205,13 @@ def test_nvfp4_one_pass_grid_resident_no_fallback(shape):
     rows, cols = shape
     xh, xd = make_input("bf16", rows, cols, seed=31)
     s = torch.cuda.Stream()
+    ws = B.Workspace()
     with torch.cuda.stream(s):
-        before = B.fp4q_onepass_fallbacks(stream=s)
-        out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, stream=s)
-        after = B.fp4q_onepass_fallbacks(stream=s)
+        before = B.fp4q_workspace_fallbacks(ws, stream=s)
+        out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, ws=ws, stream=s)
+        after = B.fp4q_workspace_fallbacks(ws, stream=s)
+    s.synchronize()
+    ws.close()
     assert after == before
     assert host(out["amax"])[0] == np.float32(oracle.amax(xh))
 
@@ -220,14 +223,14 @@ def test_nvfp4_one_pass_forced_fallback_is_exact(shape):
     rows, cols = shape
     xh, xd = make_input("bf16", rows, cols, seed=37)
     s = torch.cuda.Stream()
-    try:
-        B.fp4q_set_onepass_wait(0)
-        with torch.cuda.stream(s):
-            before = B.fp4q_onepass_fallbacks(stream=s)
-            out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, stream=s)
-            after = B.fp4q_onepass_fallbacks(stream=s)
-    finally:
-        B.fp4q_set_onepass_wait(200)
+    ws = B.Workspace()
+    B.fp4q_workspace_set_wait(ws, 0)
+    with torch.cuda.stream(s):
+        before = B.fp4q_workspace_fallbacks(ws, stream=s)
+        out = B.quantize_nvfp4(xd, B.ROWWISE | B.COLWISE, ws=ws, stream=s)
+        after = B.fp4q_workspace_fallbacks(ws, stream=s)
+    s.synchronize()
+    ws.close()
     assert after > before
     rc, rs, gs = oracle.quantize_nvfp4(xh)
     cc, cs, _ = oracle.quantize_nvfp4(xh, colwise=True)

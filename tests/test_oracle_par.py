@@ -2,7 +2,7 @@
 import numpy as np
 
 import oracle
-import oracle_par as op
+import oracle.par as op
 import synth_inputs as si
 
 
