@@ -27,7 +27,7 @@ AMAX_COMPUTE, AMAX_GIVEN = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_E_NULL", 2: "FP4Q_E_SHAPE", 3: "FP4Q_E_ALIGN", 4: "FP4Q_E_ARG", 5: "FP4Q_E_HIP"}
 
 EXPORTS = ["fp4q_workspace_create", "fp4q_workspace_destroy", "fp4q_workspace_set_wait", "fp4q_workspace_fallbacks",
-           "fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_mxfp6",
+           "fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_noalloc", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_mxfp6",
            "fp4q_quantize_if4", "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax",
            "fp4q_rht_signs_from_seed", "fp4q_status_string", "fp4q_abi_version"]
 
@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
             "fp4q_workspace_set_wait": [_P, _U],
             "fp4q_workspace_fallbacks": [_P, _P, _P],
             "fp4q_quantize_nvfp4": [_P, _I, _I64, _I64, _U, _I, _U64, _P, _U, _P, _P, _P, _P, _P, _P, _P, _P],
+            "fp4q_quantize_nvfp4_noalloc": [_P, _I, _I64, _I64, _U, _I, _U64, _P, _U, _P, _P, _P, _P, _P, _P, _P],
             "fp4q_quantize_nvfp4_2d": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P, _P],
             "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P, _P, _P],
             "fp4q_quantize_mxfp6": [_P, _I, _I64, _I64, _I, _P, _P, _P],
@@ -163,6 +164,14 @@ def fp4q_quantize_nvfp4(x, dt, rows, cols, layouts, rnd, sr_seed, rht_signs, ama
     return _check("fp4q_quantize_nvfp4", lib().fp4q_quantize_nvfp4(
         _p(x), dt, rows, cols, layouts, rnd, sr_seed, sp, amax_mode, _p(amax), _p(tensor_scale),
         _p(row_codes), _p(row_scales), _p(col_codes), _p(col_scales), _p(ws), _s(stream)))
+
+
+def fp4q_quantize_nvfp4_noalloc(x, dt, rows, cols, layouts, rnd, sr_seed, rht_signs, amax_mode, amax, tensor_scale,
+                                row_codes, row_scales, col_codes, col_scales, stream=None) -> int:
+    sp, _keep = _signs_arg(rht_signs)
+    return _check("fp4q_quantize_nvfp4_noalloc", lib().fp4q_quantize_nvfp4_noalloc(
+        _p(x), dt, rows, cols, layouts, rnd, sr_seed, sp, amax_mode, _p(amax), _p(tensor_scale),
+        _p(row_codes), _p(row_scales), _p(col_codes), _p(col_scales), _s(stream)))
 
 
 def fp4q_quantize_nvfp4_2d(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, scales, codes_t,

@@ -4,6 +4,7 @@
 #include "../../include/fp4q.h"
 #include "fp4q_internal.hpp"
 
+#include <mutex>
 #include <new>
 #include <stdint.h>
 
@@ -73,6 +74,29 @@ void philox4x32_10_host(const uint32_t ctr[4], const uint32_t key[2], uint32_t o
     k1 += 0xBB67AE85u;
   }
   for (int i = 0; i < 4; ++i) out[i] = c[i];
+}
+
+// Argument checks of fp4q_quantize_nvfp4 (and of its allocation-free form).
+fp4q_status check_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, unsigned layouts, fp4q_round rnd,
+                        const uint32_t* rht_signs, unsigned amax_mode, const float* amax, const float* tensor_scale,
+                        const uint8_t* row_codes, const uint8_t* row_scales, const uint8_t* col_codes,
+                        const uint8_t* col_scales) {
+  const bool row = (layouts & FP4Q_ROWWISE) != 0, col = (layouts & FP4Q_COLWISE) != 0;
+  if (!x || !amax || !tensor_scale) return FP4Q_E_NULL;
+  if (row && (!row_codes || !row_scales)) return FP4Q_E_NULL;
+  if (col && (!col_codes || !col_scales)) return FP4Q_E_NULL;
+  if (!valid_dtype(dt) || !valid_round(rnd) || layouts == 0 || (layouts & ~3u) != 0 ||
+      (amax_mode != FP4Q_AMAX_COMPUTE && amax_mode != FP4Q_AMAX_GIVEN))
+    return FP4Q_E_ARG;
+  if (rht_signs && (layouts != FP4Q_COLWISE || dt != FP4Q_BF16)) return FP4Q_E_ARG;
+  if (rows <= 0 || cols <= 0 || rows > INT32_MAX || cols > INT32_MAX) return FP4Q_E_SHAPE;
+  if (row && cols % 16 != 0) return FP4Q_E_SHAPE;
+  if (col && (rows % 16 != 0 || cols % 8 != 0)) return FP4Q_E_SHAPE;
+  if (rht_signs && (rows % 128 != 0 || cols >= (int64_t(1) << 27))) return FP4Q_E_SHAPE;
+  if (!aligned16(x) || !aligned4(amax) || !aligned4(tensor_scale)) return FP4Q_E_ALIGN;
+  if (row && (!aligned16(row_codes) || !aligned16(row_scales))) return FP4Q_E_ALIGN;
+  if (col && (!aligned16(col_codes) || !aligned16(col_scales))) return FP4Q_E_ALIGN;
+  return FP4Q_OK;
 }
 
 }  // namespace
@@ -155,21 +179,9 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
                                 fp4q_round rnd, uint64_t sr_seed, const uint32_t* rht_signs, unsigned amax_mode,
                                 float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
                                 uint8_t* col_codes, uint8_t* col_scales, fp4q_workspace* ws, hipStream_t stream) {
-  const bool row = (layouts & FP4Q_ROWWISE) != 0, col = (layouts & FP4Q_COLWISE) != 0;
-  if (!x || !amax || !tensor_scale) return FP4Q_E_NULL;
-  if (row && (!row_codes || !row_scales)) return FP4Q_E_NULL;
-  if (col && (!col_codes || !col_scales)) return FP4Q_E_NULL;
-  if (!valid_dtype(dt) || !valid_round(rnd) || layouts == 0 || (layouts & ~3u) != 0 ||
-      (amax_mode != FP4Q_AMAX_COMPUTE && amax_mode != FP4Q_AMAX_GIVEN))
-    return FP4Q_E_ARG;
-  if (rht_signs && (layouts != FP4Q_COLWISE || dt != FP4Q_BF16)) return FP4Q_E_ARG;
-  if (rows <= 0 || cols <= 0) return FP4Q_E_SHAPE;
-  if (row && cols % 16 != 0) return FP4Q_E_SHAPE;
-  if (col && (rows % 16 != 0 || cols % 8 != 0)) return FP4Q_E_SHAPE;
-  if (rht_signs && (rows % 128 != 0 || cols >= (int64_t(1) << 27))) return FP4Q_E_SHAPE;
-  if (!aligned16(x) || !aligned4(amax) || !aligned4(tensor_scale)) return FP4Q_E_ALIGN;
-  if (row && (!aligned16(row_codes) || !aligned16(row_scales))) return FP4Q_E_ALIGN;
-  if (col && (!aligned16(col_codes) || !aligned16(col_scales))) return FP4Q_E_ALIGN;
+  const fp4q_status v = check_nvfp4(x, dt, rows, cols, layouts, rnd, rht_signs, amax_mode, amax, tensor_scale,
+                                    row_codes, row_scales, col_codes, col_scales);
+  if (v != FP4Q_OK) return v;
   if (!ws_ok(ws)) return FP4Q_E_ARG;
 
   const bool sr = rnd == FP4Q_SR;
@@ -328,6 +340,65 @@ fp4q_status fp4q_dequantize(fp4q_format fmt, const uint8_t* codes, const uint8_t
     return FP4Q_E_ALIGN;
   fp4q::launch_dequant(fmt, codes, scales, tensor_scale, rows, cols, out_dt, y, stream);
   return after_launch();
+}
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free NVFP4 entry point.  Its workspace is this file-scope device array (one
+// copy per GPU, alive until the process ends), found once per device by
+// hipGetSymbolAddress; host code uses only that address, never the array's name.
+// ---------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[FP4Q_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+fp4q_workspace g_scratch_ws[kMaxDevices];
+bool g_scratch_ready[kMaxDevices];
+
+// The device's scratch as a workspace, set up on first use with the device current.
+fp4q_workspace* scratch_workspace(hipStream_t stream, fp4q_status* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = FP4Q_E_HIP;
+    return nullptr;
+  }
+  if (!g_scratch_ready[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *err = FP4Q_E_HIP;
+      return nullptr;
+    }
+    g_scratch_ws[dev] = fp4q_workspace{dev, static_cast<fp4q::WorkspaceMem*>(ptr), 0u, 2000u};
+    // every word of a workspace starts at zero: clear it with a fill kernel, ordered
+    // before this call's kernels on the caller's stream
+    fp4q::launch_clear_scratch(ptr, FP4Q_WORKSPACE_BYTES, stream);
+    if (hipGetLastError() != hipSuccess) {
+      *err = FP4Q_E_HIP;
+      return nullptr;
+    }
+    g_scratch_ready[dev] = true;
+  }
+  return &g_scratch_ws[dev];
+}
+
+}  // namespace
+
+fp4q_status fp4q_quantize_nvfp4_noalloc(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, unsigned layouts,
+                                        fp4q_round rnd, uint64_t sr_seed, const uint32_t* rht_signs,
+                                        unsigned amax_mode, float* amax, float* tensor_scale, uint8_t* row_codes,
+                                        uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                                        hipStream_t stream) {
+  // arguments are checked before the scratch is set up, as the workspace form checks them
+  const fp4q_status pre = check_nvfp4(x, dt, rows, cols, layouts, rnd, rht_signs, amax_mode, amax, tensor_scale,
+                                      row_codes, row_scales, col_codes, col_scales);
+  if (pre != FP4Q_OK) return pre;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);   // the launch numbering of the device's scratch
+  fp4q_status err = FP4Q_OK;
+  fp4q_workspace* ws = scratch_workspace(stream, &err);
+  if (!ws) return err;
+  return fp4q_quantize_nvfp4(x, dt, rows, cols, layouts, rnd, sr_seed, rht_signs, amax_mode, amax, tensor_scale,
+                             row_codes, row_scales, col_codes, col_scales, ws, stream);
 }
 
 }  // extern "C"

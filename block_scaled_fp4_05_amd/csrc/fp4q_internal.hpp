@@ -67,8 +67,10 @@ bool launch_nvfp4_fused(const void* x, int dtype, int64_t rows, int64_t cols, un
                         float* amax, float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
                         uint8_t* col_codes, uint8_t* col_scales, uint64_t seed, FusedArea* area, uint32_t epoch,
                         uint32_t wait_iters, hipStream_t st);
-// Clears a workspace's exchange area on the stream (a fill kernel, no memset node).
+// Clears a workspace's exchange area, or any 4-byte aligned range, on the stream (a fill
+// kernel, no memset node).
 void launch_clear_fused(FusedArea* area, hipStream_t st);
+void launch_clear_scratch(void* p, int64_t bytes, hipStream_t st);
 
 void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
                      float* tensor_scale, uint8_t* codes, uint8_t* scales, uint8_t* codes_t, hipStream_t st);

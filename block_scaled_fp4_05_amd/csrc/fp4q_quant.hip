@@ -959,10 +959,12 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, int
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
-void launch_clear_fused(FusedArea* area, hipStream_t st) {
-  const int64_t n = (int64_t)(sizeof(FusedArea) / 4);
-  k_fill_zero<<<(int)((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<uint32_t*>(area), n);
+void launch_clear_scratch(void* p, int64_t bytes, hipStream_t st) {
+  const int64_t n = bytes / 4;
+  k_fill_zero<<<(int)((n + 255) / 256), 256, 0, st>>>(static_cast<uint32_t*>(p), n);
 }
+
+void launch_clear_fused(FusedArea* area, hipStream_t st) { launch_clear_scratch(area, sizeof(FusedArea), st); }
 
 // ===========================================================================
 // MXFP4: flat 1-D kernel, each lane owns half of a 32-element block (16 elements);

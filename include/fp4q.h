@@ -158,6 +158,25 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
                                 hipStream_t stream);
 
 /*
+ * fp4q_quantize_nvfp4 for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments, checks and
+ * results as fp4q_quantize_nvfp4, without a workspace argument.  Its workspace is a
+ * file-scope device array of FP4Q_WORKSPACE_BYTES (36 KiB) inside the library, one copy
+ * per GPU, held from the first call on that GPU until the process ends; the first call
+ * on a GPU looks up the array's address and clears it with a kernel on `stream`.  The
+ * array's size does not depend on the input, so every shape fp4q_quantize_nvfp4 accepts
+ * is accepted.  The call allocates nothing (no hipMalloc, no hipFree).  All calls on one
+ * GPU share the array: calls that may overlap on one GPU (e.g. on two streams without an
+ * order between them) race; order them, or use fp4q_quantize_nvfp4 with one workspace
+ * per stream.  The host part of a call is serialized by a lock.
+ */
+fp4q_status fp4q_quantize_nvfp4_noalloc(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols,
+                                        unsigned layouts, fp4q_round rnd, uint64_t sr_seed,
+                                        const uint32_t* rht_signs, unsigned amax_mode, float* amax,
+                                        float* tensor_scale, uint8_t* row_codes, uint8_t* row_scales,
+                                        uint8_t* col_codes, uint8_t* col_scales, hipStream_t stream);
+
+/*
  * NVFP4 with 16x16 blocks for weights [NV "2D scaling"]: one E4M3 scale per 16x16
  * tile, so quantizing W^T gives exactly the transposed codes and scales.  RTN only.
  *   codes [rows][cols/2], scales [rows/16][cols/16];
