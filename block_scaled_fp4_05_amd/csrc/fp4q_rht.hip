@@ -359,127 +359,153 @@ struct RhtColOp {
   uint32_t k0, k1;
 };
 
-// Transform and quantize one tile (tokens 128*chunk.., columns 64*slab..) whose B
-// operands are in registers.  Lane (n, hk) quantizes columns 64*slab + n (pass 0) and
-// + 32 (pass 1).
-template <bool SR>
-__device__ __forceinline__ void rht_quant_tile(const RhtB& B, int64_t chunk, int64_t slab, const RhtColOp& o,
-                                               const u32x4 (&frag)[8], const u32x4 (&nfrag)[8],
-                                               const RecipTable& rtab) {
+// Output block a (tokens 32a..32a+31 of the chunk) for both column passes p: acc[p] is
+// the 32x32 MFMA block of pass p.  Per output element this is the same chain of eight
+// MFMAs (K-step kk ascending, the same A fragment) as rht_mma_half_b, so all kernels see
+// the same values.
+template <int A>
+__device__ __forceinline__ void rht_mma_block(const RhtB& B, const u32x4 frag[8], const u32x4 nfrag[8],
+                                              f32x16 acc[2]) {
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bool flip = (__builtin_popcount(A & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
+    const bf16x8 fa = __builtin_bit_cast(bf16x8, flip ? nfrag[kk] : frag[kk]);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8, B.b[kk][0]), acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8, B.b[kk][1]), acc[1], 0, 0, 0);
+  }
+}
+
+// Where a lane's outputs of one tile go.  Lane (n, hk) quantizes columns 64*slab + n
+// (pass 0) and + 32 (pass 1).
+struct RhtTileOut {
+  uint8_t* code_base[2];   // this lane's codes of pass p, block a: code_base[p] + 16 a (bytes)
+  uint8_t* scale_dst[2];   // this lane's 4 scale bytes of pass p
+  bool valid[2];
+  uint64_t idx8[2];        // SR: Philox counter of this lane's first 8 tokens of block 0, pass p
+  uint32_t scale_word[2];
+};
+
+__device__ __forceinline__ RhtTileOut rht_tile_out(int64_t chunk, int64_t slab, const RhtColOp& o) {
   const int lane = threadIdx.x & 63, hk = lane >> 5;
   const int64_t half_rows = o.rows >> 1, nb = o.rows >> 4;
   const int64_t tok0 = chunk * 128, col = slab * 64 + (lane & 31);
-  const bool valid[2] = {col < o.cols, col + 32 < o.cols};
-  // this lane's codes of pass p, block a: code_base[p] + 16 a (bytes)
-  uint8_t* const code_base0 = o.ccodes + col * half_rows + (tok0 >> 1) + 8 * hk;
-  uint8_t* const code_base[2] = {code_base0, code_base0 + 32 * half_rows};
+  RhtTileOut t;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int64_t c = col + 32 * p;
+    t.valid[p] = c < o.cols;
+    t.code_base[p] = o.ccodes + c * half_rows + (tok0 >> 1) + 8 * hk;
+    t.scale_dst[p] = o.cscales + c * nb + (tok0 >> 4) + 4 * hk;
+    t.idx8[p] = (uint64_t)(c * o.rows + tok0 + 16 * hk) >> 3;
+    t.scale_word[p] = 0u;
+  }
+  return t;
+}
+
+// Quantizes output block a of both passes from its accumulators.
+template <bool SR>
+__device__ __forceinline__ void rht_quant_block(const f32x16 (&acc)[2], int a, const RhtColOp& o,
+                                                const RecipTable& rtab, RhtTileOut& t) {
   const float gs = o.gs;
-  uint32_t scale_word[2] = {0u, 0u};
-  // RTN: the lane keeps its 8 values of each of the two 16-token blocks of output block
-  // a (tokens 32a + 0..15: A, 16..31: B; registers 0..7 and 8..15) and trades three
-  // words with the lane 32 away instead of regrouping the values: the partial maxima,
-  // the scale codes and the packed codes.  Lane hk then owns block hk's outputs.
-  auto quantize_rtn = [&](f32x16 (&acc)[2][2], int a0) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+  for (int p = 0; p < 2; ++p) {
+    if constexpr (!SR) {
+      // RTN: the lane keeps its 8 values of each of the two 16-token blocks of output
+      // block a (tokens 32a + 0..15: A, 16..31: B; registers 0..7 and 8..15) and trades
+      // three words with the lane 32 away instead of regrouping the values: the partial
+      // maxima, the scale codes and the packed codes.  Lane hk then owns block hk's outputs.
+      float v[16];
+      float mA = 0.0f, mB = 0.0f;
 #pragma unroll
-      for (int ap = 0; ap < 2; ++ap) {
-        const int a = a0 + ap;
-        float t[16];
-        float mA = 0.0f, mB = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          t[k] = (acc[p][ap][k] * kRhtScale) * gs;
-          if (k < 8) mA = __builtin_fmaxf(mA, __builtin_fabsf(t[k]));
-          else mB = __builtin_fmaxf(mB, __builtin_fabsf(t[k]));
-        }
-        // lane hk = 0 receives the partner's A maximum, lane hk = 1 the partner's B one
-        auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mA), __float_as_uint(mB), false, false);
-        const float m = __builtin_fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));
-        const uint32_t sc = nvfp4_scale_code(m);   // scale of block hk
-        auto scs = __builtin_amdgcn_permlane32_swap(sc, sc, false, false);   // every lane: (code A, code B)
-        const RecipPair rpA = rtab.r[scs[0]], rpB = rtab.r[scs[1]];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          t[k] = div2(t[k], rpA);
-          t[8 + k] = div2(t[8 + k], rpB);
-        }
-        // nibbles of A: tokens 4hk + 0..3 then 8 + 4hk + 0..3; likewise for B
-        const uint32_t wA = pack8_rtn(t, 1.0f), wB = pack8_rtn(t + 8, 1.0f);
-        // lane hk = 0 now holds A's words of both halves, lane hk = 1 B's: the own
-        // block's tokens 0..3 / 8..11 in the first word, 4..7 / 12..15 in the second
-        auto wx = __builtin_amdgcn_permlane32_swap(wA, wB, false, false);
-        const uint32_t lo = __builtin_amdgcn_perm(wx[1], wx[0], 0x05040100u);   // tokens 0..7
-        const uint32_t hi = __builtin_amdgcn_perm(wx[1], wx[0], 0x07060302u);   // tokens 8..15
-        if (valid[p]) *reinterpret_cast<uint2*>(code_base[p] + 16 * a) = make_uint2(lo, hi);
-        scale_word[p] |= sc << (8 * a);
+      for (int k = 0; k < 16; ++k) {
+        v[k] = (acc[p][k] * kRhtScale) * gs;
+        if (k < 8) mA = __builtin_fmaxf(mA, __builtin_fabsf(v[k]));
+        else mB = __builtin_fmaxf(mB, __builtin_fabsf(v[k]));
       }
-  };
-  // SR: regroup so that each lane holds 16 consecutive tokens of one block, whose draws
-  // come from two Philox evaluations.
-  auto quantize_sr = [&](f32x16 (&acc)[2][2], int a0) {
+      // lane hk = 0 receives the partner's A maximum, lane hk = 1 the partner's B one
+      auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mA), __float_as_uint(mB), false, false);
+      const float m = __builtin_fmaxf(__uint_as_float(mx[0]), __uint_as_float(mx[1]));
+      const uint32_t sc = nvfp4_scale_code(m);   // scale of block hk
+      auto scs = __builtin_amdgcn_permlane32_swap(sc, sc, false, false);   // every lane: (code A, code B)
+      const RecipPair rpA = rtab.r[scs[0]], rpB = rtab.r[scs[1]];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int ap = 0; ap < 2; ++ap) {
-        const int a = a0 + ap;
-        // regroup: lanes < 32 take rows 0..15 of block a, lanes >= 32 rows 16..31
-        float t[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][j]),
-                                                      __float_as_uint(acc[p][ap][8 + j]), false, false);
-          auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][ap][4 + j]),
-                                                      __float_as_uint(acc[p][ap][12 + j]), false, false);
-          t[j] = __uint_as_float(s02[0]);
-          t[4 + j] = __uint_as_float(s02[1]);
-          t[8 + j] = __uint_as_float(s13[0]);
-          t[12 + j] = __uint_as_float(s13[1]);
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          t[k] = (t[k] * kRhtScale) * gs;
-          m = __builtin_fmaxf(m, __builtin_fabsf(t[k]));
-        }
-        const uint32_t sc = nvfp4_scale_code(m);
-        const RecipPair rp = rtab.r[sc];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) t[k] = div2(t[k], rp);
-        uint32_t w0, w1;
-        if constexpr (SR) {
-          uint32_t r0[8], r1[8];
-          const uint64_t idx8 = (uint64_t)((col + 32 * p) * o.rows + tok0 + 32 * a + 16 * hk) >> 3;
-          sr_draws8(idx8, 1u, o.k0, o.k1, r0);
-          sr_draws8(idx8 + 1, 1u, o.k0, o.k1, r1);
-          w0 = pack8_sr(t, r0, 1.0f);
-          w1 = pack8_sr(t + 8, r1, 1.0f);
-        } else {
-          w0 = pack8_rtn(t, 1.0f);
-          w1 = pack8_rtn(t + 8, 1.0f);
-        }
-        if (valid[p]) *reinterpret_cast<uint2*>(code_base[p] + 16 * a) = make_uint2(w0, w1);
-        scale_word[p] |= sc << (8 * a);
+      for (int k = 0; k < 8; ++k) {
+        v[k] = div2(v[k], rpA);
+        v[8 + k] = div2(v[8 + k], rpB);
       }
-  };
-  f32x16 acc[2][2];
-  rht_mma_half_b<0>(B, frag, nfrag, acc);
-  if constexpr (SR) quantize_sr(acc, 0); else quantize_rtn(acc, 0);
-  rht_mma_half_b<1>(B, frag, nfrag, acc);
-  if constexpr (SR) quantize_sr(acc, 2); else quantize_rtn(acc, 2);
+      // nibbles of A: tokens 4hk + 0..3 then 8 + 4hk + 0..3; likewise for B
+      const uint32_t wA = pack8_rtn(v, 1.0f), wB = pack8_rtn(v + 8, 1.0f);
+      // lane hk = 0 now holds A's words of both halves, lane hk = 1 B's: the own
+      // block's tokens 0..3 / 8..11 in the first word, 4..7 / 12..15 in the second
+      auto wx = __builtin_amdgcn_permlane32_swap(wA, wB, false, false);
+      const uint32_t lo = __builtin_amdgcn_perm(wx[1], wx[0], 0x05040100u);   // tokens 0..7
+      const uint32_t hi = __builtin_amdgcn_perm(wx[1], wx[0], 0x07060302u);   // tokens 8..15
+      if (t.valid[p]) *reinterpret_cast<uint2*>(t.code_base[p] + 16 * a) = make_uint2(lo, hi);
+      t.scale_word[p] |= sc << (8 * a);
+    } else {
+      // SR: regroup so that each lane holds 16 consecutive tokens of one block (lanes < 32
+      // rows 0..15 of block a, lanes >= 32 rows 16..31), whose draws come from two
+      // Philox evaluations.
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][j]), __float_as_uint(acc[p][8 + j]),
+                                                    false, false);
+        auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[p][4 + j]),
+                                                    __float_as_uint(acc[p][12 + j]), false, false);
+        v[j] = __uint_as_float(s02[0]);
+        v[4 + j] = __uint_as_float(s02[1]);
+        v[8 + j] = __uint_as_float(s13[0]);
+        v[12 + j] = __uint_as_float(s13[1]);
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[k] = (v[k] * kRhtScale) * gs;
+        m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+      }
+      const uint32_t sc = nvfp4_scale_code(m);
+      const RecipPair rp = rtab.r[sc];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = div2(v[k], rp);
+      uint32_t r0[8], r1[8];
+      const uint64_t idx8 = t.idx8[p] + (uint64_t)(4 * a);   // 32 tokens per block a = 4 groups of 8
+      sr_draws8(idx8, 1u, o.k0, o.k1, r0);
+      sr_draws8(idx8 + 1, 1u, o.k0, o.k1, r1);
+      const uint32_t w0 = pack8_sr(v, r0, 1.0f), w1 = pack8_sr(v + 8, r1, 1.0f);
+      if (t.valid[p]) *reinterpret_cast<uint2*>(t.code_base[p] + 16 * a) = make_uint2(w0, w1);
+      t.scale_word[p] |= sc << (8 * a);
+    }
+  }
+}
+
+__device__ __forceinline__ void rht_store_scales(const RhtTileOut& t) {
+  const int hk = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     // lane < 32 holds blocks 0,2,4,6 of the chunk and lane >= 32 blocks 1,3,5,7;
     // interleave so each lane stores four consecutive scale bytes.
-    auto sw = __builtin_amdgcn_permlane32_swap(scale_word[p], scale_word[p], false, false);
-    const uint32_t lo = hk ? sw[0] : scale_word[p];   // blocks 0,2,4,6
-    const uint32_t hi = hk ? scale_word[p] : sw[1];   // blocks 1,3,5,7
+    auto sw = __builtin_amdgcn_permlane32_swap(t.scale_word[p], t.scale_word[p], false, false);
+    const uint32_t lo = hk ? sw[0] : t.scale_word[p];   // blocks 0,2,4,6
+    const uint32_t hi = hk ? t.scale_word[p] : sw[1];   // blocks 1,3,5,7
     // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
     const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
     const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
-    if (valid[p])
-      *reinterpret_cast<uint32_t*>(o.cscales + (col + 32 * p) * nb + (tok0 >> 4) + 4 * hk) = hk ? second : first;
+    if (t.valid[p]) *reinterpret_cast<uint32_t*>(t.scale_dst[p]) = hk ? second : first;
   }
+}
+
+// One step of the software pipeline: the MFMAs of the next output block (into `next`)
+// are issued together with the quantization of the current one (from `cur`), so the
+// matrix core and the vector ALUs work at the same time within the wave.
+template <bool SR, int ANEXT>
+__device__ __forceinline__ void rht_pipe_step(const RhtB& B, const u32x4 (&frag)[8], const u32x4 (&nfrag)[8],
+                                              f32x16 (&next)[2], const f32x16 (&cur)[2], int a,
+                                              const RhtColOp& o, const RecipTable& rtab, RhtTileOut& t) {
+  rht_mma_block<ANEXT>(B, frag, nfrag, next);
+  rht_quant_block<SR>(cur, a, o, rtab, t);
 }
 
 template <bool SR>
@@ -495,20 +521,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const RhtColOp op{x, rows, cols, ccodes, cscales, tensor_scale_publish(amax, tensor_scale), k0, k1};
   u32x4 frag[8], nfrag[8];
   make_fragments(sg, true, frag, nfrag);
-  // The next tile streams into the wave's LDS buffer while this one, already read
-  // into registers, is transformed and quantized.
   TileWalk w(rows, cols);
   if (!w.valid()) return;
+  // The wave's tiles form one stream of output blocks (four per tile).  The MFMAs of
+  // block b+1 run while block b is quantized; the next tile streams into the wave's LDS
+  // buffer as soon as the current one has been read into registers.
   rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
-  for (; w.valid(); w.next()) {
-    RhtB B;
-    rht_wait_loads();
-    rht_read_b(st, B);
-    rht_wait_lds();
+  RhtB B;
+  rht_wait_loads();
+  rht_read_b(st, B);
+  rht_wait_lds();
+  {
     TileWalk nw = w;
     nw.next();
-    if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);   // in flight while this tile is worked on
-    rht_quant_tile<SR>(B, w.chunk, w.slab, op, frag, nfrag, rtab);
+    if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
+  }
+  f32x16 acc0[2], acc1[2];
+  rht_mma_block<0>(B, frag, nfrag, acc0);
+  for (;;) {
+    RhtTileOut t = rht_tile_out(w.chunk, w.slab, op);
+    rht_pipe_step<SR, 1>(B, frag, nfrag, acc1, acc0, 0, op, rtab, t);
+    rht_pipe_step<SR, 2>(B, frag, nfrag, acc0, acc1, 1, op, rtab, t);
+    rht_pipe_step<SR, 3>(B, frag, nfrag, acc1, acc0, 2, op, rtab, t);
+    // the last block of this tile overlaps the first MFMAs of the next tile
+    TileWalk nw = w;
+    nw.next();
+    const bool more = nw.valid();
+    if (more) {
+      rht_wait_loads();
+      rht_read_b(st, B);    // the MFMAs above have read the previous B operands
+      rht_wait_lds();
+      TileWalk nnw = nw;
+      nnw.next();
+      if (nnw.valid()) rht_issue(x, cols, nnw.chunk * 128, nnw.slab * 64, st);
+      rht_pipe_step<SR, 0>(B, frag, nfrag, acc0, acc1, 3, op, rtab, t);
+    } else {
+      rht_quant_block<SR>(acc1, 3, op, rtab, t);
+    }
+    rht_store_scales(t);
+    if (!more) break;
+    w = nw;
   }
 }
 
