@@ -1274,9 +1274,11 @@ void launch_nvfp4_2d(const void* x, int dtype, int64_t rows, int64_t cols, const
 // wave span, in four steps of four fp32 outputs or two steps of eight bf16 outputs.
 // ===========================================================================
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+// Two fp32 values -> packed bf16 (first in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 (gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 
 template <int FMT, bool BF16OUT>
@@ -1357,10 +1359,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
     }
     if constexpr (BF16OUT) {
       uint4 o;
-      o.x = f32_to_bf16_rne(out[0]) | (f32_to_bf16_rne(out[1]) << 16);
-      o.y = f32_to_bf16_rne(out[2]) | (f32_to_bf16_rne(out[3]) << 16);
-      o.z = f32_to_bf16_rne(out[4]) | (f32_to_bf16_rne(out[5]) << 16);
-      o.w = f32_to_bf16_rne(out[6]) | (f32_to_bf16_rne(out[7]) << 16);
+      o.x = pack_bf16x2(out[0], out[1]);
+      o.y = pack_bf16x2(out[2], out[3]);
+      o.z = pack_bf16x2(out[4], out[5]);
+      o.w = pack_bf16x2(out[6], out[7]);
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + e) = o;
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(y) + e) = make_float4(out[0], out[1], out[2], out[3]);
@@ -1479,11 +1481,7 @@ __global__ __launch_bounds__(256) void k_dequant_mxfp6(const uint8_t* __restrict
   if constexpr (BF16OUT) {
     uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t u0 = __float_as_uint(v[2 * i]), u1 = __float_as_uint(v[2 * i + 1]);
-      const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16, b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
-      o[i] = b0 | (b1 << 16);
-    }
+    for (int i = 0; i < 8; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
     d[0] = make_uint4(o[0], o[1], o[2], o[3]);
     d[1] = make_uint4(o[4], o[5], o[6], o[7]);
