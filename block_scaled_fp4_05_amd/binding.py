@@ -28,7 +28,7 @@ STATUS = {0: "FP4Q_OK", 1: "FP4Q_E_NULL", 2: "FP4Q_E_SHAPE", 3: "FP4Q_E_ALIGN", 
 
 EXPORTS = ["fp4q_workspace_create", "fp4q_workspace_destroy", "fp4q_workspace_set_wait", "fp4q_workspace_fallbacks",
            "fp4q_quantize_nvfp4", "fp4q_quantize_nvfp4_noalloc", "fp4q_quantize_nvfp4_2d", "fp4q_quantize_mxfp4", "fp4q_quantize_mxfp6",
-           "fp4q_quantize_if4", "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax",
+           "fp4q_quantize_if4", "fp4q_quantize_variant", "fp4q_dequantize_variant", "fp4q_rht", "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4", "fp4q_dequantize", "fp4q_amax",
            "fp4q_rht_signs_from_seed", "fp4q_status_string", "fp4q_abi_version"]
 
 
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "fp4q_quantize_mxfp4": [_P, _I, _I64, _I64, _I, _U64, _P, _P, _P, _P, _P],
             "fp4q_quantize_mxfp6": [_P, _I, _I64, _I64, _I, _P, _P, _P],
             "fp4q_quantize_if4": [_P, _I, _I64, _I64, _U, _P, _P, _P, _P, _P, _P],
+            "fp4q_quantize_variant": [_P, _I, _I64, _I64, _I, _U, _P, _P, _P, _P, _P, _P],
+            "fp4q_dequantize_variant": [_I, _P, _P, _P, _I64, _I64, _I, _P, _P],
             "fp4q_rht": [_P, _I, _I64, _I64, _P, _I, _P, _P],
             "fp4q_gemm_mxfp4": [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P],
             "fp4q_gemm_nvfp4": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P],
@@ -195,6 +197,18 @@ def fp4q_quantize_if4(x, dt, rows, cols, amax_mode, amax, tensor_scale, codes, s
                       stream=None) -> int:
     return _check("fp4q_quantize_if4", lib().fp4q_quantize_if4(
         _p(x), dt, rows, cols, amax_mode, _p(amax), _p(tensor_scale), _p(codes), _p(scales), _p(ws), _s(stream)))
+
+
+def fp4q_quantize_variant(x, dt, rows, cols, var, amax_mode, amax, tensor_scale, codes, scales, ws=None,
+                          stream=None) -> int:
+    return _check("fp4q_quantize_variant", lib().fp4q_quantize_variant(
+        _p(x), dt, rows, cols, var, amax_mode, _p(amax), _p(tensor_scale), _p(codes), _p(scales), _p(ws),
+        _s(stream)))
+
+
+def fp4q_dequantize_variant(var, codes, scales, tensor_scale, rows, cols, out_dt, y, stream=None) -> int:
+    return _check("fp4q_dequantize_variant", lib().fp4q_dequantize_variant(
+        var, _p(codes), _p(scales), _p(tensor_scale), rows, cols, out_dt, _p(y), _s(stream)))
 
 
 def fp4q_rht(x, dt, rows, cols, signs, inverse, y, stream=None) -> int:
@@ -365,3 +379,27 @@ def amax(x: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty(1, dtype=torch.float32, device=x.device)
     fp4q_amax(x, _dt(x), x.shape[0], x.shape[1], out, stream)
     return out
+
+
+VAR_46, VAR_NVINT4, VAR_IF3, VAR_IF4, VAR_IF6 = 0, 1, 2, 3, 4
+VARIANT_BITS = {VAR_46: 4, VAR_NVINT4: 4, VAR_IF3: 3, VAR_IF4: 4, VAR_IF6: 6}
+
+
+def quantize_variant(x: torch.Tensor, var: int, amax: torch.Tensor | None = None, ws="auto", stream=None) -> dict:
+    """Four Over Six, NVINT4, IF3, IF4 or IF6 (codes [rows][cols * bits / 8], scales [rows][cols/16])."""
+    rows, cols = x.shape
+    dev = x.device
+    mode = AMAX_GIVEN if amax is not None else AMAX_COMPUTE
+    out = {"amax": amax if amax is not None else torch.empty(1, dtype=torch.float32, device=dev),
+           "tensor_scale": torch.empty(1, dtype=torch.float32, device=dev),
+           "codes": _u8(rows, cols * VARIANT_BITS[var] // 8, device=dev), "scales": _u8(rows, cols // 16, device=dev)}
+    fp4q_quantize_variant(x, _dt(x), rows, cols, var, mode, out["amax"], out["tensor_scale"], out["codes"],
+                          out["scales"], _ws(ws, stream), stream)
+    return out
+
+
+def dequantize_variant(var: int, codes, scales, tensor_scale, rows: int, cols: int, out_dtype=torch.float32,
+                       stream=None) -> torch.Tensor:
+    y = torch.empty(rows, cols, dtype=out_dtype, device=codes.device)
+    fp4q_dequantize_variant(var, codes, scales, tensor_scale, rows, cols, _dt(y), y, stream)
+    return y

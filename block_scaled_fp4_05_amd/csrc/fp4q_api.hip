@@ -275,6 +275,34 @@ fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_
   return after_launch();
 }
 
+fp4q_status fp4q_quantize_variant(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, fp4q_variant var,
+                                  unsigned amax_mode, float* amax, float* tensor_scale, uint8_t* codes,
+                                  uint8_t* scales, fp4q_workspace* ws, hipStream_t stream) {
+  if (!x || !amax || !tensor_scale || !codes || !scales) return FP4Q_E_NULL;
+  if (!valid_dtype(dt) || (int)var < 0 || (int)var > 4 ||
+      (amax_mode != FP4Q_AMAX_COMPUTE && amax_mode != FP4Q_AMAX_GIVEN))
+    return FP4Q_E_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return FP4Q_E_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned4(amax) || !aligned4(tensor_scale))
+    return FP4Q_E_ALIGN;
+  if (!ws_ok(ws)) return FP4Q_E_ARG;
+  fp4q::AmaxSource src{amax, nullptr, nullptr};
+  if (amax_mode == FP4Q_AMAX_COMPUTE) fp4q::launch_amax_to(x, dt, rows * cols, amax_sink(amax, ws, &src), stream);
+  fp4q::launch_variant((int)var, x, dt, rows, cols, src, tensor_scale, codes, scales, stream);
+  return after_launch();
+}
+
+fp4q_status fp4q_dequantize_variant(fp4q_variant var, const uint8_t* codes, const uint8_t* scales,
+                                    const float* tensor_scale, int64_t rows, int64_t cols, fp4q_dtype out_dt,
+                                    void* y, hipStream_t stream) {
+  if (!codes || !scales || !tensor_scale || !y) return FP4Q_E_NULL;
+  if ((int)var < 0 || (int)var > 4 || !valid_dtype(out_dt)) return FP4Q_E_ARG;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return FP4Q_E_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y) || !aligned4(tensor_scale)) return FP4Q_E_ALIGN;
+  fp4q::launch_dequant_variant((int)var, codes, scales, tensor_scale, rows, cols, out_dt, y, stream);
+  return after_launch();
+}
+
 fp4q_status fp4q_rht(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, const uint32_t* signs, int inverse,
                      float* y, hipStream_t stream) {
   if (!x || !signs || !y) return FP4Q_E_NULL;

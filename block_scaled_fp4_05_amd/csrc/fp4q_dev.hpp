@@ -238,6 +238,40 @@ __device__ __forceinline__ uint32_t pack8_sr(const float v[8], const uint32_t r3
 }
 
 // ---------------------------------------------------------------------------
+// FP6 elements (E2M3: FMT 0, E3M2: FMT 1), OCP MX formats with subnormals at exponent 0.
+// ---------------------------------------------------------------------------
+// Round to nearest, ties to the even code, saturating at code 31; the sign bit copied.
+// Normal range: round the fp32 significand to MB bits by an integer add (ties to even)
+// and re-bias the exponent; below the smallest normal 2^(1-BIAS) the step is
+// 2^(1-BIAS-MB), reached by an exact power-of-two scaling and rint.  The two ranges meet:
+// the subnormal result 2^MB is the smallest normal's code.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp6_rtn(float v) {
+  constexpr int MB = FMT ? 2 : 3, BIAS = FMT ? 3 : 1;
+  constexpr float kMinNormal = FMT ? 0.25f : 1.0f;
+  constexpr float kSubScale = (float)(1 << (BIAS - 1 + MB));
+  const uint32_t u = __float_as_uint(v), au = u & 0x7FFFFFFFu;
+  const float a = __uint_as_float(au);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * kSubScale);
+  const uint32_t nrm = ((au + ((1u << (22 - MB)) - 1u) + ((au >> (23 - MB)) & 1u)) >> (23 - MB)) -
+                       ((uint32_t)(127 - BIAS) << MB);
+  const uint32_t code = a < kMinNormal ? sub : nrm;
+  return min(code, 31u) | ((u >> 31) << 5);
+}
+
+template <int FMT>
+__device__ __forceinline__ float fp6_value(uint32_t c) {
+  constexpr int MB = FMT ? 2 : 3, BIAS = FMT ? 3 : 1;
+  const uint32_t e = (c >> MB) & ((1u << (5 - MB)) - 1u), m = c & ((1u << MB) - 1u);
+  const float mag = e ? __uint_as_float(((e + 127u - BIAS) << 23) | (m << (23 - MB)))
+                      : (float)m * (1.0f / (float)(1 << (BIAS - 1 + MB)));
+  return (c & 0x20u) ? -mag : mag;
+}
+
+// 2^(k - 127) for an E8M0 code k: all of 2^-127 .. 2^127 are binary32 values.
+__device__ __forceinline__ float e8m0_value(uint32_t k) { return k ? __uint_as_float(k << 23) : __uint_as_float(0x00400000u); }
+
+// ---------------------------------------------------------------------------
 // Cross-lane helpers (wave64).
 // ---------------------------------------------------------------------------
 // Maximum with the partner lane (lane ^ 1 or lane ^ 2 within each quad, by DPP) of a
@@ -268,10 +302,12 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Tensor encode scale gs = 2688 / amax (amax = 0 -> 1; overflow -> FLT_MAX),
-// [qiita.com/nishiha/items/b98c2b931d588c4c81d5, "scaleの導出"].
-__device__ __forceinline__ float tensor_scale_from_amax(float amax) {
+// [qiita.com/nishiha/items/b98c2b931d588c4c81d5, "scaleの導出"]: the tensor's largest
+// magnitude maps onto E4M3's 448 times the element format's block maximum (6 for E2M1;
+// other block formats pass 448 * M).
+__device__ __forceinline__ float tensor_scale_from_amax(float amax, float num = 2688.0f) {
   if (!(amax > 0.0f)) return 1.0f;
-  float gs = __fdiv_rn(2688.0f, amax);
+  float gs = __fdiv_rn(num, amax);
   return __builtin_fminf(gs, 3.40282347e38f);
 }
 
@@ -299,7 +335,8 @@ __device__ __forceinline__ void post_amax(const AmaxSink& s, float m) {
 
 // The tensor scale from the source; workgroup 0's first thread publishes it (and the
 // amax, when it came from a pass of this call) and hands the slot back.
-__device__ __forceinline__ float tensor_scale_publish(const AmaxSource& s, float* tensor_scale) {
+__device__ __forceinline__ float tensor_scale_publish(const AmaxSource& s, float* tensor_scale,
+                                                      float num = 2688.0f) {
   float a;
   uint32_t e = 0u;
   if (s.tp) {
@@ -308,7 +345,7 @@ __device__ __forceinline__ float tensor_scale_publish(const AmaxSource& s, float
   } else {
     a = *s.f;
   }
-  const float gs = tensor_scale_from_amax(a);
+  const float gs = tensor_scale_from_amax(a, num);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *tensor_scale = gs;
     if (s.out) *s.out = a;

@@ -96,6 +96,12 @@ void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const u
                           bool sr, uint64_t seed, const AmaxSource& amax, float* tensor_scale,
                           uint8_t* col_codes, uint8_t* col_scales, hipStream_t st);
 
+// Block-format variants (0 Four Over Six, 1 NVINT4, 2 IF3, 3 IF4, 4 IF6) -- fp4q_variant.hip.
+void launch_variant(int var, const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
+                    float* tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t st);
+void launch_dequant_variant(int var, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                            int64_t rows, int64_t cols, int out_dtype, void* y, hipStream_t st);
+
 // MX FP6 (fmt 0 E2M3, 1 E3M2) quantize and dequantize -- fp4q_quant.hip.
 void launch_mxfp6(const void* x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t* codes, uint8_t* scales,
                   hipStream_t st);

@@ -1394,37 +1394,6 @@ void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const 
 // little-endian 24-bit word, so a lane's 16 codes are one 96-bit little-endian word.
 // ---------------------------------------------------------------------------------------
 
-// Round to nearest, ties to the even code, saturating at code 31; the sign bit copied.
-// Normal range: round the fp32 significand to MB bits by an integer add (ties to even)
-// and re-bias the exponent; below the smallest normal 2^(1-BIAS) the step is
-// 2^(1-BIAS-MB), reached by an exact power-of-two scaling and rint.  The two ranges meet:
-// the subnormal result 2^MB is the smallest normal's code.
-template <int FMT>
-__device__ __forceinline__ uint32_t fp6_rtn(float v) {
-  constexpr int MB = FMT ? 2 : 3, BIAS = FMT ? 3 : 1;
-  constexpr float kMinNormal = FMT ? 0.25f : 1.0f;
-  constexpr float kSubScale = (float)(1 << (BIAS - 1 + MB));
-  const uint32_t u = __float_as_uint(v), au = u & 0x7FFFFFFFu;
-  const float a = __uint_as_float(au);
-  const uint32_t sub = (uint32_t)__builtin_rintf(a * kSubScale);
-  const uint32_t nrm = ((au + ((1u << (22 - MB)) - 1u) + ((au >> (23 - MB)) & 1u)) >> (23 - MB)) -
-                       ((uint32_t)(127 - BIAS) << MB);
-  const uint32_t code = a < kMinNormal ? sub : nrm;
-  return min(code, 31u) | ((u >> 31) << 5);
-}
-
-template <int FMT>
-__device__ __forceinline__ float fp6_value(uint32_t c) {
-  constexpr int MB = FMT ? 2 : 3, BIAS = FMT ? 3 : 1;
-  const uint32_t e = (c >> MB) & ((1u << (5 - MB)) - 1u), m = c & ((1u << MB) - 1u);
-  const float mag = e ? __uint_as_float(((e + 127u - BIAS) << 23) | (m << (23 - MB)))
-                      : (float)m * (1.0f / (float)(1 << (BIAS - 1 + MB)));
-  return (c & 0x20u) ? -mag : mag;
-}
-
-// 2^(k - 127) for an E8M0 code k: all of 2^-127 .. 2^127 are binary32 values.
-__device__ __forceinline__ float e8m0_value(uint32_t k) { return k ? __uint_as_float(k << 23) : __uint_as_float(0x00400000u); }
-
 // One lane per 16 elements, a lane pair per block (as k_mxfp4).
 template <typename T, int FMT>
 __global__ __launch_bounds__(256) void k_mxfp6(const T* __restrict__ x, int64_t n16, uint8_t* __restrict__ codes,

@@ -1,0 +1,302 @@
+// fp4q_variant.hip -- block-format variants on NVFP4's two-level scaling, from the
+// explainer of "Adaptive Block-Scaled Data Types" (gist.science/ja/paper/2603.28765):
+//   Four Over Six (section "1. 背景と問題点"): the block maximum maps to 4 instead of 6,
+//     so the E2M1 values +-6 are never produced;
+//   NVINT4 (section "3. 主要な貢献", the INT4 baseline): INT4 elements, block max -> 7;
+//   IF3 and IF6 (section "2. 提案手法：IF4", extensibility): per block the better of an FP
+//     and an INT candidate, as IF4 does at 4 bits -- FP3 E2M0 (0, 1, 2, 4) against INT3,
+//     and FP6 E2M3 (max 7.5) against INT6, the INT candidate scaled by the ratio of the
+//     two formats' maxima and restored with its inverse; the choice is flagged in bit 7
+//     of the block's E4M3 scale byte;
+//   IF4 itself through the same code path (byte-identical to k_if4).
+// Every variant: 16-element row blocks, gs = fl(448 M / amax), s = E4M3(fl(fl(bamax gs) / M)),
+// v = fl(fl(x gs) / s); M is the format's block maximum.
+#include "fp4q_dev.hpp"
+#include "fp4q_internal.hpp"
+
+namespace fp4q {
+
+// Compile-time description of a variant.
+template <int V> struct Var;
+template <> struct Var<0> {   // Four Over Six
+  static constexpr int kBits = 4, kQ = 0;
+  static constexpr bool kFp = true, kInt = false, kDirect = false;
+  static constexpr float kM = 4.0f, kC = 0.0f, kCinv = 0.0f;
+};
+template <> struct Var<1> {   // NVINT4
+  static constexpr int kBits = 4, kQ = 7;
+  static constexpr bool kFp = false, kInt = true, kDirect = true;
+  static constexpr float kM = 7.0f, kC = 1.0f, kCinv = 1.0f;
+};
+template <> struct Var<2> {   // IF3: FP3 E2M0 or INT3
+  static constexpr int kBits = 3, kQ = 3;
+  static constexpr bool kFp = true, kInt = true, kDirect = false;
+  static constexpr float kM = 4.0f, kC = 3.0f / 4.0f, kCinv = 4.0f / 3.0f;
+};
+template <> struct Var<3> {   // IF4: E2M1 or INT4 (the 6/7 rule)
+  static constexpr int kBits = 4, kQ = 7;
+  static constexpr bool kFp = true, kInt = true, kDirect = false;
+  static constexpr float kM = 6.0f, kC = 7.0f / 6.0f, kCinv = 6.0f / 7.0f;
+};
+template <> struct Var<4> {   // IF6: FP6 E2M3 or INT6
+  static constexpr int kBits = 6, kQ = 31;
+  static constexpr bool kFp = true, kInt = true, kDirect = false;
+  static constexpr float kM = 7.5f, kC = 31.0f / 7.5f, kCinv = 7.5f / 31.0f;
+};
+
+// fl(p / M), correctly rounded: M = 4 is an exact scaling, M = 6 the reciprocal pair,
+// otherwise IEEE division (once per block).
+template <int V>
+__device__ __forceinline__ float div_block_max(float p) {
+  if constexpr (Var<V>::kM == 4.0f) return p * 0.25f;
+  else if constexpr (Var<V>::kM == 6.0f) return div2(p, recip6());
+  else return __fdiv_rn(p, Var<V>::kM);
+}
+
+// E4M3 code of y >= 0, saturating at 448 (the convert rounds to nearest even).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  y = __builtin_fminf(y, 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, __float_as_uint(y), false) & 0xFFu;
+}
+
+// FP3 E2M0 code of v: nearest of 0, 1, 2, 4 with ties to the even code (0.5 -> 0,
+// 1.5 -> 2, 3 -> 2), saturating at 4; sign in bit 2.  Returns the code and its value.
+__device__ __forceinline__ uint32_t fp3_rtn(float v, float& r) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.5f) + (uint32_t)(a >= 1.5f) + (uint32_t)(a > 3.0f);
+  const float mag = c ? __uint_as_float((c + 126u) << 23) : 0.0f;   // 2^(c-1)
+  const uint32_t neg = __float_as_uint(v) >> 31;
+  r = neg ? -mag : mag;
+  return c | (neg << 2);
+}
+
+// Sixteen codes of `bits` bits each, code k at bits bits*k of a little-endian word.
+struct Codes16 {
+  uint32_t w[3];
+};
+
+template <int BITS>
+__device__ __forceinline__ void put16(Codes16& o, int k, uint32_t code) {
+  const int b = BITS * k;
+  o.w[b >> 5] |= code << (b & 31);
+  if ((b & 31) + BITS > 32) o.w[(b >> 5) + 1] |= code >> (32 - (b & 31));
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t get16(const Codes16& o, int k) {
+  const int b = BITS * k;
+  uint32_t c = o.w[b >> 5] >> (b & 31);
+  if ((b & 31) + BITS > 32) c |= o.w[(b >> 5) + 1] << (32 - (b & 31));
+  return c & ((1u << BITS) - 1u);
+}
+
+constexpr int kVarBlocks = 4;   // blocks per lane, all loads issued first (as k_if4)
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void k_variant(const T* __restrict__ x, int64_t n16, AmaxSource amax,
+                                                 float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales) {
+  using D = Var<V>;
+  constexpr int BITS = D::kBits;
+  __shared__ RecipTable rtab;
+  fill_recip_table(rtab);
+  __syncthreads();
+  const float gs = tensor_scale_publish(amax, tensor_scale, 448.0f * D::kM);
+  const int64_t g0 = (int64_t)blockIdx.x * (256 * kVarBlocks) + threadIdx.x;
+  float xv[kVarBlocks][16];
+#pragma unroll
+  for (int j = 0; j < kVarBlocks; ++j) {
+    const int64_t g = min(g0 + 256 * j, n16 - 1);   // past the end: reload the last block, not stored
+    load8(x, g * 16, xv[j]);
+    load8(x, g * 16 + 8, xv[j] + 8);
+  }
+#pragma unroll
+  for (int j = 0; j < kVarBlocks; ++j) {
+    const int64_t g = g0 + 256 * j;
+    float v[16];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] = xv[j][k] * gs;
+      m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
+    }
+    const uint32_t sc = e4m3_code(div_block_max<V>(m));
+    const RecipPair rp = rtab.r[sc];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = div2(v[k], rp);
+
+    Codes16 fc{{0u, 0u, 0u}}, ic{{0u, 0u, 0u}};
+    float e_fp = 0.0f, e_int = 0.0f;
+    if constexpr (D::kFp) {
+      float rf[16];
+      if constexpr (BITS == 4) {
+        fc.w[0] = pack8_rtn(v, 1.0f);
+        fc.w[1] = pack8_rtn(v + 8, 1.0f);
+#define FP4Q_DEC(W, Q, O)                                                  \
+  {                                                                        \
+    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(W, 1.0f, Q); \
+    rf[O + 2 * Q] = d[0];                                                  \
+    rf[O + 2 * Q + 1] = d[1];                                              \
+  }
+        FP4Q_DEC(fc.w[0], 0, 0) FP4Q_DEC(fc.w[0], 1, 0) FP4Q_DEC(fc.w[0], 2, 0) FP4Q_DEC(fc.w[0], 3, 0)
+        FP4Q_DEC(fc.w[1], 0, 8) FP4Q_DEC(fc.w[1], 1, 8) FP4Q_DEC(fc.w[1], 2, 8) FP4Q_DEC(fc.w[1], 3, 8)
+#undef FP4Q_DEC
+      } else if constexpr (BITS == 3) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) put16<3>(fc, k, fp3_rtn(v[k], rf[k]));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t c = fp6_rtn<0>(v[k]);
+          rf[k] = fp6_value<0>(c);
+          put16<6>(fc, k, c);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float d = v[k] - rf[k];
+        e_fp = __builtin_fmaf(d, d, e_fp);
+      }
+    }
+    if constexpr (D::kInt) {
+      const float magic = 12582912.0f;   // 1.5 * 2^23: adding it rounds to an integer, ties to even
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        float w = D::kDirect ? v[k] : v[k] * D::kC;
+        w = __builtin_amdgcn_fmed3f(w, -(float)D::kQ, (float)D::kQ);
+        const float y = w + magic;
+        const float qf = y - magic;
+        const float ri = D::kDirect ? qf : qf * D::kCinv;
+        const float d = v[k] - ri;
+        e_int = __builtin_fmaf(d, d, e_int);
+        put16<BITS>(ic, k, __float_as_uint(y) & ((1u << BITS) - 1u));   // two's complement code
+      }
+    }
+    const bool use_int = D::kInt && (!D::kFp || e_int < e_fp);
+    if (g < n16) {
+      const Codes16& c = use_int ? ic : fc;
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(c.w[0], c.w[1]);
+      } else if constexpr (BITS == 3) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(codes + g * 6);   // 2-byte aligned
+        dst[0] = (uint16_t)c.w[0];
+        dst[1] = (uint16_t)(c.w[0] >> 16);
+        dst[2] = (uint16_t)c.w[1];
+      } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(codes + g * 12);
+        dst[0] = c.w[0];
+        dst[1] = c.w[1];
+        dst[2] = c.w[2];
+      }
+      scales[g] = (uint8_t)(sc | (D::kFp && use_int ? 0x80u : 0u));
+    }
+  }
+}
+
+// x_hat = fl(fl(r * s) / gs) with IEEE division; one lane per 16-element block.
+template <int V, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales,
+                                                         const float* __restrict__ tensor_scale, int64_t n16,
+                                                         void* __restrict__ y) {
+  using D = Var<V>;
+  constexpr int BITS = D::kBits;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n16) return;
+  Codes16 c{{0u, 0u, 0u}};
+  if constexpr (BITS == 4) {
+    const uint2 w = *reinterpret_cast<const uint2*>(codes + g * 8);
+    c.w[0] = w.x;
+    c.w[1] = w.y;
+  } else if constexpr (BITS == 3) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(codes + g * 6);
+    c.w[0] = (uint32_t)src[0] | ((uint32_t)src[1] << 16);
+    c.w[1] = src[2];
+  } else {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + g * 12);
+    c.w[0] = src[0];
+    c.w[1] = src[1];
+    c.w[2] = src[2];
+  }
+  const uint32_t sb = scales[g];
+  const float s = e4m3_decode(sb & 0x7Fu);
+  const float gs = *tensor_scale;
+  const bool is_int = !D::kFp || (sb & 0x80u);
+  float out[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t code = get16<BITS>(c, k);
+    float r;
+    if (is_int) {
+      const int q = (int)(code << (32 - BITS)) >> (32 - BITS);
+      r = D::kDirect ? (float)q : (float)q * D::kCinv;
+    } else if constexpr (BITS == 4) {
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
+    } else if constexpr (BITS == 3) {
+      const uint32_t mc = code & 3u;
+      const float mag = mc ? __uint_as_float((mc + 126u) << 23) : 0.0f;
+      r = (code & 4u) ? -mag : mag;
+    } else {
+      r = fp6_value<0>(code);
+    }
+    out[k] = __fdiv_rn(r * s, gs);
+  }
+  if constexpr (BF16OUT) {
+    uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{out[2 * i], out[2 * i + 1]}, bf16x2v));
+    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else {
+    float4* d = reinterpret_cast<float4*>(static_cast<float*>(y) + g * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+  }
+}
+
+template <int V>
+static void launch_variant_v(const void* x, int dtype, int64_t n16, const AmaxSource& amax, float* ts,
+                             uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int grid = (int)((n16 + 256 * kVarBlocks - 1) / (256 * kVarBlocks));
+  if (dtype == 1)
+    k_variant<uint16_t, V><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), n16, amax, ts, codes, scales);
+  else
+    k_variant<float, V><<<grid, 256, 0, st>>>(static_cast<const float*>(x), n16, amax, ts, codes, scales);
+}
+
+void launch_variant(int var, const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax,
+                    float* tensor_scale, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  switch (var) {
+    case 0: launch_variant_v<0>(x, dtype, n16, amax, tensor_scale, codes, scales, st); break;
+    case 1: launch_variant_v<1>(x, dtype, n16, amax, tensor_scale, codes, scales, st); break;
+    case 2: launch_variant_v<2>(x, dtype, n16, amax, tensor_scale, codes, scales, st); break;
+    case 3: launch_variant_v<3>(x, dtype, n16, amax, tensor_scale, codes, scales, st); break;
+    default: launch_variant_v<4>(x, dtype, n16, amax, tensor_scale, codes, scales, st); break;
+  }
+}
+
+template <int V>
+static void launch_dequant_variant_v(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n16,
+                                     int out_dtype, void* y, hipStream_t st) {
+  const int grid = (int)((n16 + 255) / 256);
+  if (out_dtype == 1) k_dequant_variant<V, true><<<grid, 256, 0, st>>>(codes, scales, ts, n16, y);
+  else k_dequant_variant<V, false><<<grid, 256, 0, st>>>(codes, scales, ts, n16, y);
+}
+
+void launch_dequant_variant(int var, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                            int64_t rows, int64_t cols, int out_dtype, void* y, hipStream_t st) {
+  const int64_t n16 = rows * cols / 16;
+  switch (var) {
+    case 0: launch_dequant_variant_v<0>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+    case 1: launch_dequant_variant_v<1>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+    case 2: launch_dequant_variant_v<2>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+    case 3: launch_dequant_variant_v<3>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+    default: launch_dequant_variant_v<4>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+  }
+}
+
+}  // namespace fp4q

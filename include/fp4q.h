@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 7
+#define FP4Q_ABI_VERSION 8
 
 typedef enum {
     FP4Q_OK = 0,
@@ -234,6 +234,44 @@ fp4q_status fp4q_quantize_if4(const void* x, fp4q_dtype dt, int64_t rows, int64_
                               unsigned amax_mode, float* amax, float* tensor_scale,
                               uint8_t* codes, uint8_t* scales, fp4q_workspace* ws,
                               hipStream_t stream);
+
+/*
+ * Block-format variants on NVFP4's two-level scaling, the formats IF4 is compared with
+ * and its extensions [IF "1. 背景と問題点", "2. 提案手法：IF4", "3. 主要な貢献"]:
+ *   FP4Q_VAR_46      Four Over Six: E2M1 with the block maximum mapped to 4 instead of 6
+ *                    (+-6 are never produced); same code and scale layout as NVFP4.
+ *   FP4Q_VAR_NVINT4  INT4 elements q = clamp(rint(v), -7, 7), block maximum 7.
+ *   FP4Q_VAR_IF3     per block FP3 E2M0 (0, 1, 2, 4) or INT3 q = clamp(rint(fl(v * fl(3/4))),
+ *                    -3, 3) restored as fl(q * fl(4/3)); block maximum 4.
+ *   FP4Q_VAR_IF4     IF4 as fp4q_quantize_if4 writes it (the same bytes).
+ *   FP4Q_VAR_IF6     per block FP6 E2M3 (max 7.5) or INT6 with fl(31/7.5), restored with
+ *                    fl(7.5/31); block maximum 7.5.
+ * For each, with M the block maximum: gs = 448 * M / amax (amax = 0 -> 1; overflow ->
+ * FLT_MAX), written to *tensor_scale; per 16-element row block s = E4M3(fl(fl(bamax * gs)
+ * / M)); v = fl(fl(x * gs) / s); the IF variants keep the candidate with the smaller
+ * fma-accumulated squared error (INT only if strictly smaller) and set bit 7 of the scale
+ * byte for INT.  INT codes are two's complement; FP codes sign-magnitude.
+ *   codes  [rows][cols * bits / 8] with bits = 4 (46, NVINT4, IF4), 3 (IF3) or 6 (IF6):
+ *          4-bit codes two per byte (element 2k low nibble); 3-bit codes eight per three
+ *          bytes and 6-bit codes four per three bytes, code j of a group at bits
+ *          bits*j.. of the little-endian 24-bit word.
+ *   scales [rows][cols/16], E4M3 (+ flag).   Shapes: cols % 16 == 0.   RTN only.
+ *   ws     workspace or NULL (as fp4q_quantize_if4).
+ */
+typedef enum {
+    FP4Q_VAR_46 = 0, FP4Q_VAR_NVINT4 = 1, FP4Q_VAR_IF3 = 2, FP4Q_VAR_IF4 = 3, FP4Q_VAR_IF6 = 4
+} fp4q_variant;
+
+fp4q_status fp4q_quantize_variant(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols, fp4q_variant var,
+                                  unsigned amax_mode, float* amax, float* tensor_scale, uint8_t* codes,
+                                  uint8_t* scales, fp4q_workspace* ws, hipStream_t stream);
+
+/* Dequantizes a variant: x_hat = fl(fl(r * s) / gs), r the FP value, or the INT restore
+ * (q for NVINT4, fl(q * cinv) for flagged IF blocks); gs = *tensor_scale (device float).
+ * out_dt FP4Q_F32 or FP4Q_BF16 (RNE of the fp32 result).  Layouts as above. */
+fp4q_status fp4q_dequantize_variant(fp4q_variant var, const uint8_t* codes, const uint8_t* scales,
+                                    const float* tensor_scale, int64_t rows, int64_t cols, fp4q_dtype out_dt,
+                                    void* y, hipStream_t stream);
 
 /*
  * Random Hadamard transform along rows [NV "ランダムアダマール変換"], per chunk of

@@ -89,6 +89,12 @@ def _declare(L: ctypes.CDLL) -> None:
         "ora_e4m3_encode_array": (None, [_P, _I64, _P]),
         "ora_e8m0_encode_array": (None, [_P, _I64, _P]),
         "ora_sr_bits16_array": (None, [_U64, _U32, _P, _I64, _P]),
+        "ora_fp3_decode": (_F, [ctypes.c_uint8]),
+        "ora_fp3_rtn": (ctypes.c_uint8, [_F]),
+        "ora_variant_row_bytes": (_I64, [_I, _I64]),
+        "ora_variant_tensor_scale": (_F, [_I, _F]),
+        "ora_quantize_variant": (None, [_P, _I, _I64, _I64, _I, _F, _P, _P]),
+        "ora_dequantize_variant": (None, [_I, _P, _P, _F, _I64, _I64, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -346,4 +352,42 @@ def plain_block_roundtrip(x: np.ndarray, block: int) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
     y = np.zeros_like(x)
     lib().ora_plain_block_roundtrip(_ptr(x), x.size, block, _ptr(y))
+    return y
+
+
+# --- block-format variants: Four Over Six, NVINT4, IF3, IF4 (generic), IF6 -------------
+
+VAR_46, VAR_NVINT4, VAR_IF3, VAR_IF4, VAR_IF6 = 0, 1, 2, 3, 4
+VARIANT_BITS = {VAR_46: 4, VAR_NVINT4: 4, VAR_IF3: 3, VAR_IF4: 4, VAR_IF6: 6}
+
+
+def fp3_decode(code: int) -> float:
+    return lib().ora_fp3_decode(code)
+
+
+def fp3_rtn(v: float) -> int:
+    return lib().ora_fp3_rtn(v)
+
+
+def variant_tensor_scale(var: int, amax_value: float) -> float:
+    return lib().ora_variant_tensor_scale(var, amax_value)
+
+
+def quantize_variant(x: np.ndarray, var: int, gs: float | None = None):
+    """Returns (codes [rows][cols*bits/8], scales [rows][cols/16], gs)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    if gs is None:
+        gs = variant_tensor_scale(var, amax(x))
+    codes = np.zeros((rows, lib().ora_variant_row_bytes(var, cols)), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    lib().ora_quantize_variant(_ptr(x), _dtype_code(x), rows, cols, var, gs, _ptr(codes), _ptr(scales))
+    return codes, scales, np.float32(gs)
+
+
+def dequantize_variant(var: int, codes: np.ndarray, scales: np.ndarray, gs: float, rows: int, cols: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    y = np.zeros((rows, cols), dtype=np.float32)
+    lib().ora_dequantize_variant(var, _ptr(codes), _ptr(scales), gs, rows, cols, _ptr(y))
     return y

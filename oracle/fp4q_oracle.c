@@ -747,6 +747,211 @@ void ora_plain_block_roundtrip(const float* x, int64_t n, int64_t block, float* 
 }
 
 /* ------------------------------------------------------------------------- */
+/* Block-format variants [IF "1. 背景と問題点", "2. 提案手法：IF4", "3. 主要な貢献"] */
+/* ------------------------------------------------------------------------- */
+
+/* The variants the IF explainer compares IF4 against, and its 3- and 6-bit
+ * extensions, all with NVFP4's two-level scaling on 16-element row blocks: an FP32
+ * tensor encode scale gs = fl(448 * M / amax) and an E4M3 block scale
+ * s = E4M3(fl(fl(bamax * gs) / M)), where M is the block maximum the format maps the
+ * block's largest magnitude to.  Elements are v = fl(fl(x * gs) / s).  Readings (the
+ * page names the formats and their key property, not every constant):
+ *   ORA_VAR_46     Four Over Six: NVFP4 with the block maximum 4 instead of 6 (M = 4);
+ *                  E2M1 elements, so the values +-6 are never produced.
+ *   ORA_VAR_NVINT4 NVFP4 scaling with INT4 elements: M = 7, q = clamp(RNE(v), -7, 7),
+ *                  two's-complement nibbles.
+ *   ORA_VAR_IF3    per block the better of FP3 (E2M0: 0, 1, 2, 4; M = 4) and INT3
+ *                  scaled by the IF4 rule: q = clamp(RNE(fl(v * fl(3/4))), -3, 3),
+ *                  restored as fl(q * fl(4/3)).
+ *   ORA_VAR_IF4    the same generalisation at 4 bits: E2M1 (M = 6) or INT4 with 7/6;
+ *                  it must equal ora_quantize_if4.
+ *   ORA_VAR_IF6    FP6 E2M3 (M = 7.5) or INT6 with fl(31/7.5), restored with fl(7.5/31).
+ * The choice, the error sums and the flag (bit 7 of the scale byte, set = INT) are
+ * IF4's.  Code layouts: 4-bit formats as NVFP4 (two per byte); IF3 packs eight 3-bit
+ * codes into three bytes (code j at bits 3j..3j+2 of the little-endian 24-bit word;
+ * FP3 code = sign bit 2, exponent bits 1..0; INT3 two's complement); IF6 packs four
+ * 6-bit codes into three bytes as MX FP6 does (FP6 E2M3 codes, INT6 two's complement). */
+
+/* FP3 E2M0 (bias 1, exponent field 0 = zero): magnitudes 0, 1, 2, 4. */
+float ora_fp3_decode(uint8_t code)
+{
+    static const float mag[4] = {0.0f, 1.0f, 2.0f, 4.0f};
+    float m = mag[code & 3];
+    return (code & 4) ? -m : m;
+}
+
+/* Nearest FP3 magnitude, ties to the even code, saturating at 4; sign copied. */
+uint8_t ora_fp3_rtn(float v)
+{
+    double a = fabs((double)v);
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c < 4; ++c) {
+        double d = fabs(a - (double)ora_fp3_decode((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    if (a >= 4.0) best = 3;
+    return (uint8_t)(best | (signbit(v) ? 4 : 0));
+}
+
+typedef struct {
+    int bits;        /* code width */
+    float m;         /* block maximum M */
+    int has_fp, has_int;
+    int qmax;        /* INT range +-qmax */
+    int int_direct;  /* 1: INT codes round v itself (NVINT4); 0: fl(v * c), restored fl(q * cinv) */
+    float c, cinv;
+} ora_variant;
+
+static ora_variant variant_of(int var)
+{
+    ora_variant d;
+    memset(&d, 0, sizeof d);
+    switch (var) {
+    case ORA_VAR_46:     d.bits = 4; d.m = 4.0f; d.has_fp = 1; break;
+    case ORA_VAR_NVINT4: d.bits = 4; d.m = 7.0f; d.has_int = 1; d.qmax = 7; d.int_direct = 1; break;
+    case ORA_VAR_IF3:    d.bits = 3; d.m = 4.0f; d.has_fp = d.has_int = 1; d.qmax = 3;
+                         d.c = 3.0f / 4.0f; d.cinv = 4.0f / 3.0f; break;
+    case ORA_VAR_IF4:    d.bits = 4; d.m = 6.0f; d.has_fp = d.has_int = 1; d.qmax = 7;
+                         d.c = 7.0f / 6.0f; d.cinv = 6.0f / 7.0f; break;
+    default:             d.bits = 6; d.m = 7.5f; d.has_fp = d.has_int = 1; d.qmax = 31;
+                         d.c = 31.0f / 7.5f; d.cinv = 7.5f / 31.0f; break;
+    }
+    return d;
+}
+
+static uint8_t fp_rtn_bits(int bits, float v)
+{
+    if (bits == 3) return ora_fp3_rtn(v);
+    if (bits == 4) return ora_e2m1_rtn(v);
+    return ora_fp6_rtn(0, v);
+}
+
+static float fp_decode_bits(int bits, uint8_t code)
+{
+    if (bits == 3) return ora_fp3_decode(code);
+    if (bits == 4) return ora_e2m1_decode(code);
+    return ora_fp6_decode(0, code);
+}
+
+/* Code c of element j of a row, in the row's packed bytes. */
+static void put_code(uint8_t* row, int bits, int64_t j, uint8_t code)
+{
+    if (bits == 4) {
+        uint8_t* p = row + j / 2;
+        *p = (j & 1) ? (uint8_t)((*p & 0x0F) | (code << 4)) : (uint8_t)((*p & 0xF0) | (code & 0x0F));
+        return;
+    }
+    const int per = bits == 3 ? 8 : 4;                    /* codes per three bytes */
+    uint8_t* g = row + (j / per) * 3;
+    uint32_t w = (uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16);
+    const int sh = bits * (int)(j % per);
+    const uint32_t mask = (1u << bits) - 1u;
+    w = (w & ~(mask << sh)) | ((uint32_t)(code & mask) << sh);
+    g[0] = (uint8_t)w;
+    g[1] = (uint8_t)(w >> 8);
+    g[2] = (uint8_t)(w >> 16);
+}
+
+static uint8_t get_code(const uint8_t* row, int bits, int64_t j)
+{
+    if (bits == 4) return (uint8_t)((j & 1) ? row[j / 2] >> 4 : row[j / 2] & 0x0F);
+    const int per = bits == 3 ? 8 : 4;
+    const uint8_t* g = row + (j / per) * 3;
+    const uint32_t w = (uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16);
+    return (uint8_t)((w >> (bits * (int)(j % per))) & ((1u << bits) - 1u));
+}
+
+int64_t ora_variant_row_bytes(int var, int64_t cols)
+{
+    return cols * variant_of(var).bits / 8;
+}
+
+float ora_variant_tensor_scale(int var, float amax)
+{
+    if (!(amax > 0.0f)) return 1.0f;
+    float gs = (448.0f * variant_of(var).m) / amax;
+    if (gs > FLT_MAX) gs = FLT_MAX;
+    return gs;
+}
+
+/* INT restore of a stored INT code. */
+static float int_value(const ora_variant* d, uint8_t code)
+{
+    const int sh = 32 - d->bits;
+    const int q = (int)((uint32_t)code << sh) >> sh;      /* sign-extend the code */
+    return d->int_direct ? (float)q : (float)q * d->cinv;
+}
+
+void ora_quantize_variant(const void* x, int dtype, int64_t rows, int64_t cols, int var, float gs,
+                          uint8_t* codes, uint8_t* scales)
+{
+    const ora_variant d = variant_of(var);
+    const int64_t rb = cols * d.bits / 8;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < cols / 16; ++b) {
+            float xv[16], v[16];
+            float bamax = 0.0f;
+            for (int k = 0; k < 16; ++k) {
+                xv[k] = load_elem(x, dtype, r * cols + b * 16 + k);
+                if (fabsf(xv[k]) > bamax) bamax = fabsf(xv[k]);
+            }
+            const uint8_t sc8 = ora_e4m3_encode((bamax * gs) / d.m);
+            const float s = ora_e4m3_decode(sc8);
+            uint8_t fpc[16], intc[16];
+            float e_fp = 0.0f, e_int = 0.0f;
+            for (int k = 0; k < 16; ++k) {
+                if (s == 0.0f) {                               /* a zero block: signed zeros */
+                    fpc[k] = d.has_fp ? fp_rtn_bits(d.bits, signbit(xv[k]) ? -0.0f : 0.0f) : 0;
+                    intc[k] = 0;
+                    continue;
+                }
+                v[k] = (xv[k] * gs) / s;
+                if (d.has_fp) {
+                    fpc[k] = fp_rtn_bits(d.bits, v[k]);
+                    const float df = v[k] - fp_decode_bits(d.bits, fpc[k]);
+                    e_fp = fmaf(df, df, e_fp);
+                }
+                if (d.has_int) {
+                    float q = rintf(d.int_direct ? v[k] : v[k] * d.c);
+                    if (q > (float)d.qmax) q = (float)d.qmax;
+                    if (q < -(float)d.qmax) q = -(float)d.qmax;
+                    intc[k] = (uint8_t)((int)q & ((1 << d.bits) - 1));
+                    const float di = v[k] - (d.int_direct ? q : q * d.cinv);
+                    e_int = fmaf(di, di, e_int);
+                }
+            }
+            const int use_int = d.has_int && (!d.has_fp || (s != 0.0f && e_int < e_fp));
+            scales[r * (cols / 16) + b] = (uint8_t)(sc8 | (d.has_fp && use_int ? 0x80 : 0));
+            for (int k = 0; k < 16; ++k)
+                put_code(codes + r * rb, d.bits, b * 16 + k, use_int ? intc[k] : fpc[k]);
+        }
+    }
+}
+
+/* x_hat = fl(fl(r * s) / gs): r the FP value, or the INT restore for flagged blocks
+ * (every block for NVINT4). */
+void ora_dequantize_variant(int var, const uint8_t* codes, const uint8_t* scales, float gs, int64_t rows,
+                            int64_t cols, float* y)
+{
+    const ora_variant d = variant_of(var);
+    const int64_t rb = cols * d.bits / 8;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint8_t sc8 = scales[r * (cols / 16) + c / 16];
+            const float s = ora_e4m3_decode((uint8_t)(sc8 & 0x7F));
+            const uint8_t code = get_code(codes + r * rb, d.bits, c);
+            const int is_int = !d.has_fp || (sc8 & 0x80);
+            const float rv = is_int ? int_value(&d, code) : fp_decode_bits(d.bits, code);
+            const float p = rv * s;
+            y[r * cols + c] = p / gs;
+        }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Array forms of the element codecs (plain loops, for the tests' sweeps)      */
 /* ------------------------------------------------------------------------- */
 

@@ -62,6 +62,20 @@ void ora_rht_column(const void* x, int dtype, int64_t rows, int64_t cols, int64_
 
 void ora_plain_block_roundtrip(const float* x, int64_t n, int64_t block, float* y);
 
+#define ORA_VAR_46 0
+#define ORA_VAR_NVINT4 1
+#define ORA_VAR_IF3 2
+#define ORA_VAR_IF4 3
+#define ORA_VAR_IF6 4
+float ora_fp3_decode(uint8_t code);
+uint8_t ora_fp3_rtn(float v);
+int64_t ora_variant_row_bytes(int var, int64_t cols);
+float ora_variant_tensor_scale(int var, float amax);
+void ora_quantize_variant(const void* x, int dtype, int64_t rows, int64_t cols, int var, float gs,
+                          uint8_t* codes, uint8_t* scales);
+void ora_dequantize_variant(int var, const uint8_t* codes, const uint8_t* scales, float gs, int64_t rows,
+                            int64_t cols, float* y);
+
 
 
 void ora_e2m1_rtn_array(const float* v, int64_t n, uint8_t* out);

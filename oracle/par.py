@@ -130,3 +130,26 @@ def rht(x: np.ndarray, signs) -> np.ndarray:
         y[a:b] = oracle.rht(np.ascontiguousarray(x[a:b]), signs)
     _run(one, _ranges(rows, 128, 4 * workers()))
     return y
+
+
+def quantize_variant(x: np.ndarray, var: int, gs: float):
+    """A block-format variant (Four Over Six, NVINT4, IF3, IF4, IF6) of the whole tensor."""
+    rows, cols = x.shape
+    codes = np.empty((rows, cols * oracle.VARIANT_BITS[var] // 8), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+
+    def one(a, b):
+        c, s, _ = oracle.quantize_variant(np.ascontiguousarray(x[a:b]), var, gs=gs)
+        codes[a:b], scales[a:b] = c, s
+    _run(one, _ranges(rows, 1, 4 * workers()))
+    return codes, scales
+
+
+def dequantize_variant(var: int, codes: np.ndarray, scales: np.ndarray, gs: float, rows: int, cols: int):
+    y = np.empty((rows, cols), np.float32)
+
+    def one(a, b):
+        y[a:b] = oracle.dequantize_variant(var, np.ascontiguousarray(codes[a:b]), np.ascontiguousarray(scales[a:b]),
+                                           gs, b - a, cols)
+    _run(one, _ranges(rows, 1, 4 * workers()))
+    return y

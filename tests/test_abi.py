@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 7
+    assert B.fp4q_abi_version() == 8
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -128,6 +128,14 @@ def test_other_entry_points_validate():
     assert L.fp4q_dequantize(4, A, A, None, 16, 48, 0, A, 0) == 2
     assert L.fp4q_dequantize(5, A, MIS, None, 16, 64, 0, A, 0) == 3
     assert L.fp4q_dequantize(6, A, A, None, 16, 64, 0, A, 0) == 4
+    # block-format variants
+    assert L.fp4q_quantize_variant(A, B.BF16, 4, 40, 0, 0, A2, A2, A, A, None, 0) == 2
+    assert L.fp4q_quantize_variant(A, B.BF16, 4, 48, 5, 0, A2, A2, A, A, None, 0) == 4
+    assert L.fp4q_quantize_variant(A, B.BF16, 4, 48, 2, 0, None, A2, A, A, None, 0) == 1
+    assert L.fp4q_quantize_variant(MIS, B.BF16, 4, 48, 4, 0, A2, A2, A, A, None, 0) == 3
+    assert L.fp4q_dequantize_variant(1, A, A, A2, 4, 40, 0, A, 0) == 2
+    assert L.fp4q_dequantize_variant(7, A, A, A2, 4, 48, 0, A, 0) == 4
+    assert L.fp4q_dequantize_variant(2, A, A, None, 4, 48, 0, A, 0) == 1
     # workspace calls: NULL handle or output
     assert L.fp4q_workspace_create(None) == 1
     assert L.fp4q_workspace_destroy(None) == 1
