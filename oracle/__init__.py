@@ -75,7 +75,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "ora_quantize_if4": (None, [_P, _I, _I64, _I64, _F, _P, _P]),
         "ora_dequantize": (None, [_I, _P, _P, _F, _I64, _I64, _P]),
         "ora_gemm_mxfp4": (None, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
-        "ora_gemm_nvfp4": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _I64, _P, _P]),
+        "ora_gemm_nvfp4": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _I64, _I, _P, _P]),
         "ora_fp6_decode": (_F, [_I, ctypes.c_uint8]),
         "ora_fp6_rtn": (ctypes.c_uint8, [_I, _F]),
         "ora_quantize_mxfp6": (None, [_P, _I, _I64, _I64, _I, _P, _P]),
@@ -311,18 +311,21 @@ def gemm_mxfp4(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b
     return c, cabs
 
 
-def gemm_nvfp4(a_codes, a_scales, gs_a, b_codes, b_scales, gs_b):
-    """C = A B^T over two row-wise NVFP4 1x16 operands with tensor scales gs_a, gs_b:
-    (sum of exact products r s r' s') / (gs_a gs_b).  Returns (C, sum |products| / same)."""
+def gemm_nvfp4(a_codes, a_scales, gs_a, b_codes, b_scales, gs_b, tiles: int = 0):
+    """C = A B^T over two row-wise NVFP4 operands with tensor scales gs_a, gs_b:
+    (sum of exact products r s r' s') / (gs_a gs_b).  Returns (C, sum |products| / same).
+    ``tiles`` bit 0 / bit 1 marks A / B as carrying 16x16 scale tiles [rows/16][k/16]."""
     a_codes, a_scales = np.ascontiguousarray(a_codes), np.ascontiguousarray(a_scales)
     b_codes, b_scales = np.ascontiguousarray(b_codes), np.ascontiguousarray(b_scales)
     m, k = a_codes.shape[0], a_codes.shape[1] * 2
     n = b_codes.shape[0]
-    assert b_codes.shape == (n, k // 2) and a_scales.shape == (m, k // 16) and b_scales.shape == (n, k // 16)
+    ra = m // 16 if tiles & 1 else m
+    rb = n // 16 if tiles & 2 else n
+    assert b_codes.shape == (n, k // 2) and a_scales.shape == (ra, k // 16) and b_scales.shape == (rb, k // 16)
     c = np.zeros((m, n), dtype=np.float64)
     cabs = np.zeros((m, n), dtype=np.float64)
     lib().ora_gemm_nvfp4(_ptr(a_codes), _ptr(a_scales), float(gs_a), _ptr(b_codes), _ptr(b_scales), float(gs_b),
-                         m, n, k, _ptr(c), _ptr(cabs))
+                         m, n, k, int(tiles), _ptr(c), _ptr(cabs))
     return c, cabs
 
 

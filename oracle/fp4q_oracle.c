@@ -627,18 +627,22 @@ void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
  * product gs_a * gs_b (exact: two 24-bit significands) rounds once.  cabs is the sum of
  * |products| over the same divisor.  Scale row strides: k/16 bytes. */
 void ora_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float gs_a, const uint8_t* b_codes,
-                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, double* c,
-                    double* cabs)
+                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, int tiles,
+                    double* c, double* cabs)
 {
+    /* tiles bit 0 / bit 1: A / B holds one scale per 16x16 tile [NV "2D scaling"], so
+     * element (i, t) takes the scale of tile (i / 16, t / 16) instead of block (i, t / 16). */
     const double g = (double)gs_a * (double)gs_b;
     for (int64_t i = 0; i < m; ++i) {
+        const int64_t sa = (tiles & 1) ? i / 16 : i;
         for (int64_t j = 0; j < n; ++j) {
+            const int64_t sb = (tiles & 2) ? j / 16 : j;
             double acc = 0.0, mag = 0.0;
             for (int64_t t = 0; t < k; ++t) {
                 double av = (double)ora_e2m1_decode(get_nibble(a_codes, k, i, t)) *
-                            (double)ora_e4m3_decode(a_scales[i * (k / 16) + t / 16]);
+                            (double)ora_e4m3_decode(a_scales[sa * (k / 16) + t / 16]);
                 double bv = (double)ora_e2m1_decode(get_nibble(b_codes, k, j, t)) *
-                            (double)ora_e4m3_decode(b_scales[j * (k / 16) + t / 16]);
+                            (double)ora_e4m3_decode(b_scales[sb * (k / 16) + t / 16]);
                 acc += av * bv;
                 mag += fabs(av * bv);
             }

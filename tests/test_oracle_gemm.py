@@ -150,3 +150,79 @@ def test_nvfp4_gemm_of_quantized_gaussians_tracks_the_float_product():
     ref = x.astype(np.float64) @ w.astype(np.float64).T
     rel = np.linalg.norm(c - ref) / np.linalg.norm(ref)
     assert 0.01 < rel < 0.15      # 16-element blocks with E4M3 scales: tighter than MXFP4
+
+
+# --- NVFP4 16x16 (2D) operands --------------------------------------------------------
+
+def _nv_tiled_operand(rng, rows, k):
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, size=(rows // 16, k // 16), dtype=np.uint8)
+    return codes, scales
+
+
+def test_nvfp4_gemm_with_tiled_operands_brute_force_with_exact_rationals():
+    """A with 16x16 tiles, B with 1x16 blocks and the reverse: element (r, t) of a tiled
+    operand carries the scale of tile (r // 16, t // 16)."""
+    rng = np.random.default_rng(31)
+    m, n, k = 32, 16, 48
+
+    def val(codes, scales, r, t, tiled):
+        byte = int(codes[r, t // 2])
+        nib = (byte >> 4) if (t & 1) else (byte & 15)
+        return _e2m1_exact(nib) * _e4m3_exact(int(scales[r // 16 if tiled else r, t // 16]))
+
+    for tiles in (1, 2, 3):
+        ac, as_ = (_nv_tiled_operand if tiles & 1 else _nv_operand)(rng, m, k)
+        bc, bs = (_nv_tiled_operand if tiles & 2 else _nv_operand)(rng, n, k)
+        gs_a, gs_b = np.float32(3.5), np.float32(0.75)
+        c, _ = oracle.gemm_nvfp4(ac, as_, gs_a, bc, bs, gs_b, tiles=tiles)
+        g = Fraction(float(gs_a)) * Fraction(float(gs_b))
+        for i in (0, 15, 16, 31):
+            for j in (0, 7, 15):
+                exact = sum(val(ac, as_, i, t, tiles & 1) * val(bc, bs, j, t, tiles & 2) for t in range(k)) / g
+                assert abs(Fraction(c[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 52), (tiles, i, j)
+
+
+def test_nvfp4_gemm_tiled_equals_row_blocks_with_replicated_tile_scales():
+    """A tiled operand is the same matrix as a 1x16 operand whose row r holds the scales
+    of tile row r // 16."""
+    rng = np.random.default_rng(32)
+    m, n, k = 48, 32, 128
+    ac, ast = _nv_tiled_operand(rng, m, k)
+    bc, bst = _nv_tiled_operand(rng, n, k)
+    c2, cabs2 = oracle.gemm_nvfp4(ac, ast, 2.0, bc, bst, 5.0, tiles=3)
+    c1, cabs1 = oracle.gemm_nvfp4(ac, np.repeat(ast, 16, axis=0), 2.0, bc, np.repeat(bst, 16, axis=0), 5.0)
+    assert np.array_equal(c2, c1) and np.array_equal(cabs2, cabs1)
+    c3, _ = oracle.gemm_nvfp4(ac, ast, 2.0, bc, np.repeat(bst, 16, axis=0), 5.0, tiles=1)
+    assert np.array_equal(c3, c1)
+
+
+def test_nvfp4_gemm_tiled_equals_matmul_of_the_2d_dequantization():
+    rng = np.random.default_rng(33)
+    m, n, k = 32, 64, 256
+    ac, as_ = _nv_operand(rng, m, k)
+    bc, bs = _nv_tiled_operand(rng, n, k)
+    c, _ = oracle.gemm_nvfp4(ac, as_, 1.0, bc, bs, 1.0, tiles=2)
+    a = oracle.dequantize(0, ac, as_, 1.0, m, k).astype(np.float64)
+    b = oracle.dequantize(1, bc, bs, 1.0, n, k).astype(np.float64)
+    assert np.array_equal(c, a @ b.T)
+
+
+def test_nvfp4_forward_and_dgrad_with_one_2d_weight_quantization():
+    """Y = X W^T uses W quantized in 16x16 tiles; dX = dY W uses W^T, whose 16x16
+    quantization is the transposed tile array, so both products track the float ones."""
+    m, n, k = 64, 96, 512
+    x = si.weight(m, k, seed=41, std=1.0)
+    w = si.weight(n, k, seed=42, std=0.02)
+    dy = si.weight(m, n, seed=43, std=1.0)
+    xc, xs, gx = oracle.quantize_nvfp4(x)
+    wc, ws, gw = oracle.quantize_nvfp4_2d(w)
+    y, _ = oracle.gemm_nvfp4(xc, xs, gx, wc, ws, gw, tiles=2)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert 0.01 < np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.15
+    wtc, wts, gwt = oracle.quantize_nvfp4_2d(np.ascontiguousarray(w.T))
+    assert np.array_equal(wts, ws.T) and gwt == gw
+    dc, ds, gd = oracle.quantize_nvfp4(dy)
+    dx, _ = oracle.gemm_nvfp4(dc, ds, gd, wtc, wts, gwt, tiles=2)
+    ref = dy.astype(np.float64) @ w.astype(np.float64)
+    assert 0.01 < np.linalg.norm(dx - ref) / np.linalg.norm(ref) < 0.15
