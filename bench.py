@@ -533,7 +533,7 @@ class GemmNVFP4Wgrad(GemmMXFP4):
     def step(self, i):
         B = self.B
         (ac, as_, ga), (bc, bs, gb) = self.ops[i % self.sets]
-        B.fp4q_gemm_nvfp4(ac, as_, ga, bc, bs, gb, self.m, self.n, self.k, B.BF16, self.y[i % self.sets])
+        B.fp4q_gemm_nvfp4(ac, as_, ga, bc, bs, gb, self.m, self.n, self.k, 0, B.BF16, self.y[i % self.sets])
 
     kernel_launch = step
     given_launch = step

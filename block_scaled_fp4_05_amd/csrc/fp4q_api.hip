@@ -88,7 +88,7 @@ fp4q_status check_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int64_t cols
   if (!valid_dtype(dt) || !valid_round(rnd) || layouts == 0 || (layouts & ~3u) != 0 ||
       (amax_mode != FP4Q_AMAX_COMPUTE && amax_mode != FP4Q_AMAX_GIVEN))
     return FP4Q_E_ARG;
-  if (rht_signs && (layouts != FP4Q_COLWISE || dt != FP4Q_BF16)) return FP4Q_E_ARG;
+  if (rht_signs && layouts != FP4Q_COLWISE) return FP4Q_E_ARG;
   if (rows <= 0 || cols <= 0 || rows > INT32_MAX || cols > INT32_MAX) return FP4Q_E_SHAPE;
   if (row && cols % 16 != 0) return FP4Q_E_SHAPE;
   if (col && (rows % 16 != 0 || cols % 8 != 0)) return FP4Q_E_SHAPE;
@@ -186,13 +186,13 @@ fp4q_status fp4q_quantize_nvfp4(const void* x, fp4q_dtype dt, int64_t rows, int6
 
   const bool sr = rnd == FP4Q_SR;
   if (rht_signs) {
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const bool f32 = dt == FP4Q_F32;
     fp4q::AmaxSource src{amax, nullptr, nullptr};
     if (amax_mode == FP4Q_AMAX_COMPUTE) {
       const fp4q::AmaxSink sink = amax_sink(amax, ws, &src);
-      fp4q::launch_rht_amax(xb, rows, cols, rht_signs, sink, stream);
+      fp4q::launch_rht_amax(x, f32, rows, cols, rht_signs, sink, stream);
     }
-    fp4q::launch_rht_nvfp4_col(xb, rows, cols, rht_signs, sr, sr_seed, src, tensor_scale, col_codes, col_scales,
+    fp4q::launch_rht_nvfp4_col(x, f32, rows, cols, rht_signs, sr, sr_seed, src, tensor_scale, col_codes, col_scales,
                                stream);
     return after_launch();
   }
@@ -331,17 +331,20 @@ fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, con
 
 fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t m,
-                            int64_t n, int64_t k, fp4q_dtype out_dt, void* c, float* amax, hipStream_t stream) {
+                            int64_t n, int64_t k, unsigned scale_tiles, fp4q_dtype out_dt, void* c, float* amax,
+                            hipStream_t stream) {
   if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale || !c) return FP4Q_E_NULL;
-  if (!valid_dtype(out_dt)) return FP4Q_E_ARG;
+  if (!valid_dtype(out_dt) || (scale_tiles & ~3u) != 0) return FP4Q_E_ARG;
   const int64_t lim = (int64_t)1 << 31;
   if (m <= 0 || n <= 0 || k < 128 || k % 128 != 0 || m >= lim || n >= lim || k > ((int64_t)1 << 25))
+    return FP4Q_E_SHAPE;
+  if (((scale_tiles & FP4Q_TILES_A) && m % 16 != 0) || ((scale_tiles & FP4Q_TILES_B) && n % 16 != 0))
     return FP4Q_E_SHAPE;
   if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) || !aligned16(c) ||
       !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned4(amax))
     return FP4Q_E_ALIGN;
   if (!fp4q::launch_gemm_nvfp4(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, m, n, k,
-                               out_dt == FP4Q_BF16, c, amax, stream))
+                               out_dt == FP4Q_BF16, c, amax, scale_tiles, stream))
     return FP4Q_E_SHAPE;
   return after_launch();
 }

@@ -440,7 +440,7 @@ template <bool BF16OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ gsa,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ gsb, int M, int N,
-    int K, int tiles_m, int tiles_n, void* __restrict__ cout, uint32_t* __restrict__ amax) {
+    int K, int tiles_m, int tiles_n, void* __restrict__ cout, uint32_t* __restrict__ amax, int tile_a, int tile_b) {
   __shared__ NvStage st[kNvStages];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -462,7 +462,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     ob[j] = (uint32_t)((min(n0 + 64 * j + lr, N - 1) - min(n0 + 64 * j, N - 1)) * (int)ldq);
   }
   // Scales: piece g (0..7) of an operand is rows 32 g .. 32 g + 31, two words each;
-  // wave w loads pieces 2w and 2w+1 of A and of B.
+  // wave w loads pieces 2w and 2w+1 of A and of B.  An operand with 16x16 scale tiles
+  // (tile_a / tile_b = 4) reads the scale row of its row's tile, row / 16.
   auto issue = [&](int ks) {
     NvStage& s = st[ks % kNvStages];
     const int kc = min(ks, nk - 1);
@@ -479,8 +480,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int h = 0; h < 2; ++h) {
       const int g = 2 * wave + h, row = 32 * g + (lane >> 1);
       const int64_t so = (int64_t)kc * 8 + 4 * (lane & 1);
-      __builtin_amdgcn_global_load_lds(as + (int64_t)min(m0 + row, M - 1) * lds + so, &s.sa[64 * g], 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(bs + (int64_t)min(n0 + row, N - 1) * lds + so, &s.sb[64 * g], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(as + (int64_t)(min(m0 + row, M - 1) >> tile_a) * lds + so, &s.sa[64 * g], 4,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(bs + (int64_t)(min(n0 + row, N - 1) >> tile_b) * lds + so, &s.sb[64 * g], 4,
+                                       0, 0);
     }
   };
 
@@ -610,14 +613,15 @@ bool launch_gemm_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, 
 
 bool launch_gemm_nvfp4(const uint8_t* ac, const uint8_t* as, const float* gsa, const uint8_t* bc, const uint8_t* bs,
                        const float* gsb, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c, float* amax,
-                       hipStream_t st) {
+                       unsigned tiles2d, hipStream_t st) {
   const int tiles_m = (int)((m + kGemmTile - 1) / kGemmTile), tiles_n = (int)((n + kGemmTile - 1) / kGemmTile);
   const int64_t total = (int64_t)tiles_m * tiles_n;
   if (total > 0x7FFFFFFF) return false;
   auto kern = bf16_out ? k_gemm_nvfp4<true> : k_gemm_nvfp4<false>;
   uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
   if (ab) k_gemm_amax_zero<<<1, 1, 0, st>>>(ab);
-  kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab);
+  kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab,
+                                        (tiles2d & 1u) ? 4 : 0, (tiles2d & 2u) ? 4 : 0);
   return true;
 }
 

@@ -90,9 +90,10 @@ void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const 
 // Random Hadamard transform along rows (chunks of 128) -- fp4q_rht.hip.
 void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4],
                 int inverse, float* y, hipStream_t st);
-void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4],
+// x is bf16 (MFMA contraction) or, with f32, fp32 (VALU butterflies).
+void launch_rht_amax(const void* x, bool f32, int64_t rows, int64_t cols, const uint32_t signs[4],
                      const AmaxSink& sink, hipStream_t st);
-void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4],
+void launch_rht_nvfp4_col(const void* x, bool f32, int64_t rows, int64_t cols, const uint32_t signs[4],
                           bool sr, uint64_t seed, const AmaxSource& amax, float* tensor_scale,
                           uint8_t* col_codes, uint8_t* col_scales, hipStream_t st);
 
@@ -114,8 +115,9 @@ bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const ui
                        const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,
                        float* amax, hipStream_t st);
 // NVFP4 1x16 GEMM C = A B^T / (gs_a gs_b) on the bf16 MFMA -- fp4q_gemm.hip.  k % 128 == 0.
+// tiles2d bit 0 / bit 1: A / B carries 16x16 scale tiles ([rows/16][k/16]) instead of 1x16.
 bool launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_ts, int64_t m, int64_t n, int64_t k, bool bf16_out,
-                       void* c, float* amax, hipStream_t st);
+                       void* c, float* amax, unsigned tiles2d, hipStream_t st);
 
 }  // namespace fp4q

@@ -565,23 +565,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// fp32 input: VALU fast Walsh-Hadamard transform, one lane per (chunk, column),
-// 128 values in registers (7 butterfly stages).  Used for f32 forward/inverse.
+// fp32 input: VALU fast Walsh-Hadamard transform, one lane per (chunk, column) with the
+// column's 128 tokens in registers (7 butterfly stages, 896 adds).  Sylvester H is the
+// 7-fold Kronecker power of [[1, 1], [1, -1]], so stage h (h = 1, 2, ..., 64) pairs
+// tokens i and i + h (i & h == 0) into (a + b, a - b); after the last stage v[i] is
+// sum_t H[i][t] u[t].  Consecutive lanes take consecutive columns, so every token
+// row is one coalesced 256-byte wave load.  The standalone transform, the amax pass
+// and the column-wise quantizer call the same code, so all three see bitwise
+// identical y = fl(v * fl(1/sqrt(128))).  fp32 operands would lose their low 16 bits
+// on the bf16 MFMA path, and fp32 MFMA would run the dense contraction at 1/16 of the
+// bf16 rate, while the transform itself is only 7 adds per element.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_rht_f32(const float* __restrict__ x, int64_t rows, int64_t cols, RhtSigns sg,
-                                                 int inverse, float* __restrict__ y) {
-  const int64_t nchunk = rows / 128;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= nchunk * cols) return;
-  const int64_t chunk = id / cols, j = id - chunk * cols;
-  const int64_t base = chunk * 128 * cols + j;
-  float v[128];
-#pragma unroll
-  for (int t = 0; t < 128; ++t) {
-    float a = x[base + (int64_t)t * cols];
-    if (!inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) a = -a;
-    v[t] = a;
-  }
+__device__ __forceinline__ void fwht128(float (&v)[128]) {
 #pragma unroll
   for (int h = 1; h < 128; h <<= 1)
 #pragma unroll
@@ -591,12 +586,111 @@ __global__ __launch_bounds__(256) void k_rht_f32(const float* __restrict__ x, in
         v[i] = a + b;
         v[i + h] = a - b;
       }
+}
+
+// u[t] = s_t x[128 c + t][j] (forward) or x (inverse) for the column at `base`.
+__device__ __forceinline__ void load_col128(const float* __restrict__ x, int64_t base, int64_t cols,
+                                            const RhtSigns& sg, bool with_signs, float (&v)[128]) {
+#pragma unroll
+  for (int t = 0; t < 128; ++t) {
+    const float a = x[base + (int64_t)t * cols];
+    v[t] = (with_signs && ((sg.w[t >> 5] >> (t & 31)) & 1u)) ? -a : a;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rht_f32(const float* __restrict__ x, int64_t rows, int64_t cols, RhtSigns sg,
+                                                 int inverse, float* __restrict__ y) {
+  const int64_t nchunk = rows / 128;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= nchunk * cols) return;
+  const int64_t chunk = id / cols, j = id - chunk * cols;
+  const int64_t base = chunk * 128 * cols + j;
+  float v[128];
+  load_col128(x, base, cols, sg, !inverse, v);
+  fwht128(v);
 #pragma unroll
   for (int t = 0; t < 128; ++t) {
     float o = v[t] * kRhtScale;
     if (inverse && ((sg.w[t >> 5] >> (t & 31)) & 1u)) o = -o;
     y[base + (int64_t)t * cols] = o;
   }
+}
+
+// Pass 1 for fp32: amax of the forward transform, max |fl(v k)| = fl(max |v| * k).
+__global__ __launch_bounds__(256) void k_rht_amax_f32(const float* __restrict__ x, int64_t rows, int64_t cols,
+                                                      RhtSigns sg, AmaxSink sink) {
+  const int64_t nchunk = rows / 128;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float m = 0.0f;
+  if (id < nchunk * cols) {
+    const int64_t chunk = id / cols, j = id - chunk * cols;
+    float v[128];
+    load_col128(x, chunk * 128 * cols + j, cols, sg, true, v);
+    fwht128(v);
+#pragma unroll
+    for (int t = 0; t < 128; ++t) m = __builtin_fmaxf(m, __builtin_fabsf(v[t]));
+  }
+  __shared__ float wm[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    post_amax(sink, __builtin_fmaxf(__builtin_fmaxf(wm[0], wm[1]), __builtin_fmaxf(wm[2], wm[3])) * kRhtScale);
+}
+
+// Pass 2 for fp32: the lane holds the eight 16-token blocks of its column whole, so each
+// block's maximum, scale and codes stay in the lane; its 64 code bytes and 8 scale bytes
+// are contiguous in the column-wise layout and go out as four 16-byte and one 8-byte store.
+template <bool SR>
+__global__ __launch_bounds__(256) void k_rht_nvfp4_col_f32(const float* __restrict__ x, int64_t rows, int64_t cols,
+                                                           RhtSigns sg, AmaxSource amax,
+                                                           float* __restrict__ tensor_scale,
+                                                           uint8_t* __restrict__ ccodes,
+                                                           uint8_t* __restrict__ cscales, uint32_t k0, uint32_t k1) {
+  __shared__ RecipTable rtab;
+  fill_recip_table(rtab);
+  __syncthreads();
+  const float gs = tensor_scale_publish(amax, tensor_scale);
+  const int64_t nchunk = rows / 128;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= nchunk * cols) return;
+  const int64_t chunk = id / cols, j = id - chunk * cols;
+  float v[128];
+  load_col128(x, chunk * 128 * cols + j, cols, sg, true, v);
+  fwht128(v);
+  uint32_t w[16];
+  uint32_t sc_lo = 0u, sc_hi = 0u;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    float* q = v + 16 * b;
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      q[k] = (q[k] * kRhtScale) * gs;
+      m = __builtin_fmaxf(m, __builtin_fabsf(q[k]));
+    }
+    const uint32_t sc = nvfp4_scale_code(m);
+    const RecipPair rp = rtab.r[sc];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q[k] = div2(q[k], rp);
+    if constexpr (SR) {
+      uint32_t r0[8], r1[8];
+      const uint64_t idx8 = (uint64_t)(j * rows + chunk * 128 + 16 * b) >> 3;
+      sr_draws8(idx8, 1u, k0, k1, r0);
+      sr_draws8(idx8 + 1, 1u, k0, k1, r1);
+      w[2 * b] = pack8_sr(q, r0, 1.0f);
+      w[2 * b + 1] = pack8_sr(q + 8, r1, 1.0f);
+    } else {
+      w[2 * b] = pack8_rtn(q, 1.0f);
+      w[2 * b + 1] = pack8_rtn(q + 8, 1.0f);
+    }
+    if (b < 4) sc_lo |= sc << (8 * b);
+    else sc_hi |= sc << (8 * (b - 4));
+  }
+  uint4* cd = reinterpret_cast<uint4*>(ccodes + j * (rows >> 1) + chunk * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cd[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  *reinterpret_cast<uint2*>(cscales + j * (rows >> 4) + chunk * 8) = make_uint2(sc_lo, sc_hi);
 }
 
 __global__ void k_zero1_rht(float* p) { *p = 0.0f; }
@@ -615,28 +709,46 @@ static int rht_grid(int64_t rows, int64_t cols, int per_simd) {
   return (int)((waves + 3) / 4);
 }
 
+// One lane per (128-row chunk, column).
+static int lane_grid(int64_t rows, int64_t cols) { return (int)((rows / 128 * cols + 255) / 256); }
+
 void launch_rht(const void* x, int dtype, int64_t rows, int64_t cols, const uint32_t signs[4], int inverse, float* y,
                 hipStream_t st) {
   const RhtSigns sg = pack_signs(signs);
   if (dtype == 1) {
     k_rht_bf16<<<rht_grid(rows, cols, 1), 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols, sg, inverse, y);
   } else {
-    const int64_t n = rows / 128 * cols;
-    k_rht_f32<<<(int)((n + 255) / 256), 256, 0, st>>>(static_cast<const float*>(x), rows, cols, sg, inverse, y);
+    k_rht_f32<<<lane_grid(rows, cols), 256, 0, st>>>(static_cast<const float*>(x), rows, cols, sg, inverse, y);
   }
 }
 
-void launch_rht_amax(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], const AmaxSink& sink,
-                     hipStream_t st) {
+void launch_rht_amax(const void* x, bool f32, int64_t rows, int64_t cols, const uint32_t signs[4],
+                     const AmaxSink& sink, hipStream_t st) {
   if (!sink.tp) k_zero1_rht<<<1, 1, 0, st>>>(sink.f);
-  k_rht_amax<<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, pack_signs(signs), sink);
+  if (f32)
+    k_rht_amax_f32<<<lane_grid(rows, cols), 256, 0, st>>>(static_cast<const float*>(x), rows, cols,
+                                                          pack_signs(signs), sink);
+  else
+    k_rht_amax<<<rht_grid(rows, cols, 2), 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols,
+                                                       pack_signs(signs), sink);
 }
 
-void launch_rht_nvfp4_col(const uint16_t* x, int64_t rows, int64_t cols, const uint32_t signs[4], bool sr,
+void launch_rht_nvfp4_col(const void* xv, bool f32, int64_t rows, int64_t cols, const uint32_t signs[4], bool sr,
                           uint64_t seed, const AmaxSource& amax, float* tensor_scale, uint8_t* col_codes,
                           uint8_t* col_scales, hipStream_t st) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const RhtSigns sg = pack_signs(signs);
+  if (f32) {
+    const float* xf = static_cast<const float*>(xv);
+    if (sr)
+      k_rht_nvfp4_col_f32<true><<<lane_grid(rows, cols), 256, 0, st>>>(xf, rows, cols, sg, amax, tensor_scale,
+                                                                       col_codes, col_scales, k0, k1);
+    else
+      k_rht_nvfp4_col_f32<false><<<lane_grid(rows, cols), 256, 0, st>>>(xf, rows, cols, sg, amax, tensor_scale,
+                                                                        col_codes, col_scales, k0, k1);
+    return;
+  }
+  const uint16_t* x = static_cast<const uint16_t*>(xv);
   if (sr)
     k_rht_nvfp4_col<true><<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
                                                                 col_scales, k0, k1);

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 8
+#define FP4Q_ABI_VERSION 9
 
 typedef enum {
     FP4Q_OK = 0,
@@ -139,7 +139,9 @@ fp4q_status fp4q_workspace_fallbacks(fp4q_workspace* ws, hipStream_t stream, uin
  *             Non-NULL applies the 128x128 random Hadamard transform along rows in
  *             chunks of 128 before quantizing [NV "ランダムアダマール変換"]; requires
  *             layouts == FP4Q_COLWISE, rows % 128 == 0 and cols < 2^27.  The amax and
- *             gs are then those of the transformed matrix.
+ *             gs are then those of the transformed matrix, and the quantized values are
+ *             exactly those fp4q_rht returns for the same x and dt: for bf16 the
+ *             contraction runs on MFMA, for fp32 as 7 butterfly stages of fp32 adds.
  *   amax, tensor_scale  device float[1] each.
  *   ws        workspace or NULL (see above).
  * Shapes: ROWWISE needs cols % 16 == 0; COLWISE needs rows % 16 == 0 and cols % 8 == 0.
@@ -278,9 +280,10 @@ fp4q_status fp4q_dequantize_variant(fp4q_variant var, const uint8_t* codes, cons
  * 128 rows, R = S H / sqrt(128) with Sylvester H and S = diag(signs):
  *   inverse == 0:  y = R^T x    (y[128c+i][j] = sum_t H[i][t] s_t x[128c+t][j] / sqrt(128))
  *   inverse != 0:  y = R x      (undoes the forward transform)
- * Contraction on MFMA (bf16 operands, fp32 accumulation); the forward transform is
- * the one fp4q_quantize_nvfp4 applies, bit for bit.  The inverse takes an f32 input
- * rounded to bf16 only if dt == FP4Q_BF16; with dt == FP4Q_F32 it runs on fp32 VALU.
+ * dt == FP4Q_BF16: contraction on MFMA (bf16 operands, fp32 accumulation);
+ * dt == FP4Q_F32: fast Walsh-Hadamard butterflies in fp32 (7 rounded adds per output).
+ * The forward transform is the one fp4q_quantize_nvfp4 applies for the same dt, bit
+ * for bit.
  *   signs  HOST pointer to 4 words.   y  device float [rows][cols].
  * Shapes: rows % 128 == 0, cols % 8 == 0.
  */
@@ -320,11 +323,19 @@ fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
  * is decoded exactly to bf16 and multiplied on the bf16 MFMA with fp32 accumulation;
  * the sums are multiplied by fl(1 / fl(gs_a gs_b)).
  *   out_dt FP4Q_F32: float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
- * Shapes and amax as fp4q_gemm_mxfp4.  NVFP4 16x16 (2D) scale layouts are not accepted.
+ *   scale_tiles  0, or FP4Q_TILES_A / FP4Q_TILES_B (or both): that operand carries NVFP4
+ *          16x16 scales as fp4q_quantize_nvfp4_2d writes them [NV "2D scaling"], one E4M3
+ *          byte per 16x16 tile, [rows/16][k/16] (rows % 16 == 0), e.g. the weight W as B
+ *          in Y = X W^T.  For W^T (the data-gradient product) pass codes_t and the
+ *          transposed tile array: quantizing W^T gives exactly those codes and scales.
+ * Shapes and amax as fp4q_gemm_mxfp4.  IF4 operands are not accepted (an INT4 block's
+ * restore fl(q * fl(6/7)) times its scale is not exact in the bf16 operands).
  */
+#define FP4Q_TILES_A 1u
+#define FP4Q_TILES_B 2u
 fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
-                            int64_t m, int64_t n, int64_t k, fp4q_dtype out_dt, void* c,
+                            int64_t m, int64_t n, int64_t k, unsigned scale_tiles, fp4q_dtype out_dt, void* c,
                             float* amax, hipStream_t stream);
 
 /*

@@ -174,7 +174,19 @@ static void gemms(int64_t m, int64_t n, int64_t k)
     double* cabs = xmalloc((size_t)(m * n) * sizeof(double));
     ora_gemm_mxfp4(ac, as, bc, bs, m, n, k, c, cabs);   /* reads the first k/32 scales per row */
     ora_gemm_mxfp4(ac, as, bc, bs, m, n, k, c, NULL);
-    ora_gemm_nvfp4(ac, as, 0.75f, bc, bs, 3.0f, m, n, k, c, cabs);
+    ora_gemm_nvfp4(ac, as, 0.75f, bc, bs, 3.0f, m, n, k, 0, c, cabs);
+    if (m % 16 == 0 && n % 16 == 0) {
+        /* 16x16 tiles: exact-size tile arrays, so a read past [rows/16][k/16] is caught */
+        uint8_t* ta = xmalloc((size_t)(m / 16 * (k / 16)));
+        uint8_t* tb = xmalloc((size_t)(n / 16 * (k / 16)));
+        memcpy(ta, as, (size_t)(m / 16 * (k / 16)));
+        memcpy(tb, bs, (size_t)(n / 16 * (k / 16)));
+        ora_gemm_nvfp4(ac, ta, 0.75f, bc, tb, 3.0f, m, n, k, 3, c, cabs);
+        ora_gemm_nvfp4(ac, ta, 0.75f, bc, bs, 3.0f, m, n, k, 1, c, cabs);
+        ora_gemm_nvfp4(ac, as, 0.75f, bc, tb, 3.0f, m, n, k, 2, c, NULL);
+        free(ta);
+        free(tb);
+    }
     free(ac);
     free(bc);
     free(as);
@@ -265,6 +277,7 @@ int main(void)
     }
     gemms(3, 5, 128);
     gemms(1, 1, 256);
+    gemms(32, 48, 128);
 
     if (failures) {
         fprintf(stderr, "%d failures\n", failures);

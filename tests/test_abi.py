@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 8
+    assert B.fp4q_abi_version() == 9
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -60,7 +60,7 @@ def _nv(**kw):
     (dict(row_codes=None), 1), (dict(col_scales=None), 1),
     (dict(dt=7), 4), (dict(rnd=3), 4), (dict(layouts=0), 4), (dict(layouts=4), 4), (dict(amax_mode=5), 4),
     (dict(rht_signs=[1, 2, 3, 4]), 4),                               # RHT needs COLWISE only
-    (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, dt=B.F32), 4),  # RHT needs bf16
+    (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, dt=B.F32), 2),  # fp32 accepted; rows % 128 fails
     (dict(rows=0), 2), (dict(cols=-16), 2), (dict(cols=40), 2), (dict(rows=40), 2),
     (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, rows=64), 2),   # rows % 128
     (dict(rht_signs=[1, 2, 3, 4], layouts=B.COLWISE, rows=128, cols=1 << 27), 2),   # RHT: cols < 2^27
@@ -112,14 +112,18 @@ def test_other_entry_points_validate():
     assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 256, 1, MIS, None, 0) == 3
     assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, (1 << 25) + 128, 0, A2, None, 0) == 2
     # NVFP4 GEMM: tensor scales are device floats (4-byte aligned)
-    assert L.fp4q_gemm_nvfp4(A, A, None, A, A, A2, 64, 64, 128, 0, A2, None, 0) == 1
-    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 192, 0, A2, None, 0) == 2
-    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 5, A2, None, 0) == 4
-    assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, A2, None, 0) == 3
-    assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, A2, None, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, A, None, A, A, A2, 64, 64, 128, 0, 0, A2, None, 0) == 1
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 192, 0, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 0, 5, A2, None, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, 0, A2, None, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, 0, A2, None, 0) == 3
+    # 16x16 scale tiles: flag bits 0-1 only, and the tiled operand's rows a multiple of 16
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 4, 0, A2, None, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 40, 64, 128, 1, 0, A2, None, 0) == 2
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 40, 128, 2, 0, A2, None, 0) == 2
     # the optional output amax must be 4-byte aligned
     assert L.fp4q_gemm_mxfp4(A, A, A, A, 64, 64, 128, 0, A2, A2 + 2, 0) == 3
-    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 0, A2, A2 + 1, 0) == 3
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 0, 0, A2, A2 + 1, 0) == 3
     # MX FP6
     assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 48, 0, A, A, 0) == 2
     assert L.fp4q_quantize_mxfp6(A, B.BF16, 4, 64, 2, A, A, 0) == 4

@@ -29,6 +29,10 @@ def dev_bf16(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
+def dev_f32(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     return t.cpu().numpy()
@@ -142,12 +146,18 @@ def _rht_within(y: np.ndarray, ref: np.ndarray, tol: float = 1e-5):
     return float(np.max(d / (rms + 1e-30)))
 
 
-@pytest.mark.parametrize("operand,rnd,sr_seed", [("gradient", 1, 40), ("activation", 0, 41)])
+@pytest.mark.parametrize("operand,rnd,sr_seed", [("gradient", 1, 40), ("activation", 0, 41), ("gradient_f32", 1, 42)])
 def test_wgrad_full_rht_quantize(operand, rnd, sr_seed):
     rows, cols = 16384, 4096
-    bits = si.wgrad_gradient(rows, cols, seed=4) if operand == "gradient" else si.wgrad_activation(rows, cols, seed=4)
     signs = oracle.rht_signs(4)
-    xd = dev_bf16(bits)
+    if operand == "gradient_f32":
+        # an fp32 gradient: all 24 significand bits carry through the VALU transform
+        bits = si.weight(rows, cols, seed=4, std=1e-3)
+        xd = dev_f32(bits)
+    else:
+        bits = (si.wgrad_gradient(rows, cols, seed=4) if operand == "gradient"
+                else si.wgrad_activation(rows, cols, seed=4))
+        xd = dev_bf16(bits)
     out = B.quantize_nvfp4(xd, B.COLWISE, rnd=rnd, sr_seed=sr_seed, rht_signs=signs.tolist())
     yg = host(B.rht(xd, signs.tolist()))
     codes_g, scales_g = host(out["col_codes"]), host(out["col_scales"])

@@ -146,12 +146,12 @@ def _nv_check(got, exact, cabs, k, bf16=False):
                            f"err {err[tuple(bad[0])]:.3e} tol {tol[tuple(bad[0])]:.3e}")
 
 
-def _nv_gemm(ac, as_, ga, bc, bs, gb, out_dtype=torch.float32):
+def _nv_gemm(ac, as_, ga, bc, bs, gb, out_dtype=torch.float32, tiles=0):
     m, n, k = ac.shape[0], bc.shape[0], ac.shape[1] * 2
     c = torch.full((m, n), float("nan"), dtype=out_dtype, device=DEV)
     ta = torch.tensor([ga], dtype=torch.float32, device=DEV)
     tb = torch.tensor([gb], dtype=torch.float32, device=DEV)
-    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B._dt(c), c)
+    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, tiles, B._dt(c), c)
     torch.cuda.synchronize()
     return c.float().cpu().numpy().astype(np.float64)
 
@@ -194,6 +194,54 @@ def test_nvfp4_gemm_wgrad_after_rht_end_to_end():
     assert rel < 0.2, rel
 
 
+@pytest.mark.parametrize("shape,tiles,bf16", [((256, 256, 128), 2, False), ((304, 528, 384), 1, False),
+                                              ((256, 256, 256), 3, True), ((272, 160, 512), 2, True),
+                                              ((16, 16, 128), 3, False), ((257, 144, 256), 2, False)])
+def test_nvfp4_gemm_with_16x16_scale_tiles(shape, tiles, bf16):
+    """Operands carrying one E4M3 scale per 16x16 tile, [rows/16][k/16]: the kernel reads
+    tile row r // 16 for row r, across ragged M/N edges and several K tiles."""
+    m, n, k = shape
+    rng = np.random.default_rng(m * 3 + n * 7 + k + tiles)
+    ac, as_ = _nv_operand(rng, m, k)
+    bc, bs = _nv_operand(rng, n, k)
+    if tiles & 1:
+        as_ = as_[: m // 16].copy()
+    if tiles & 2:
+        bs = bs[: n // 16].copy()
+    ga, gb = np.float32(3.0), np.float32(0.375)
+    print(f"nvfp4 gemm tiles={tiles} m={m} n={n} k={k} bf16={bf16}", flush=True)
+    got = _nv_gemm(ac, as_, ga, bc, bs, gb, torch.bfloat16 if bf16 else torch.float32, tiles)
+    exact, cabs = oracle.gemm_nvfp4(ac, as_, ga, bc, bs, gb, tiles=tiles)
+    _nv_check(got, exact, cabs, k, bf16)
+
+
+def test_nvfp4_forward_and_dgrad_with_2d_weight_end_to_end():
+    """Y = X W^T with W quantized in 16x16 tiles by the library, and dX = dY W with the
+    library's 16x16 quantization of W^T: both products match the oracle on the library's
+    own operands, and W^T's tiles are the transposed tile array of W."""
+    m, n, k = 256, 384, 512
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(DEV)
+    x_bits = si.activation(m, k, seed=51)
+    w = torch.from_numpy(si.weight(n, k, seed=52, std=0.02)).to(DEV)
+    dy_bits = si.activation(m, n, seed=53)
+    qx = B.quantize_nvfp4(to_dev(x_bits), B.ROWWISE)
+    qw = B.quantize_nvfp4_2d(w, transposed=True)
+    qwt = B.quantize_nvfp4_2d(w.t().contiguous())
+    qd = B.quantize_nvfp4(to_dev(dy_bits), B.ROWWISE)
+    h = lambda t: t.cpu().numpy()
+    # one quantization of W serves both products: W^T's codes and tiles are W's transposed
+    assert np.array_equal(h(qwt["scales"]), h(qw["scales"]).T)
+    assert np.array_equal(h(qwt["codes"]), h(qw["codes_t"]))
+    y = B.gemm_nvfp4(qx["row_codes"], qx["row_scales"], qx["tensor_scale"], qw["codes"], qw["scales"],
+                     qw["tensor_scale"], scale_tiles=B.TILES_B)
+    dx = B.gemm_nvfp4(qd["row_codes"], qd["row_scales"], qd["tensor_scale"], qwt["codes"], qwt["scales"],
+                      qwt["tensor_scale"], scale_tiles=B.TILES_B)
+    for got, (a, b) in ((y, (qx, qw)), (dx, (qd, qwt))):
+        exact, cabs = oracle.gemm_nvfp4(h(a["row_codes"]), h(a["row_scales"]), float(h(a["tensor_scale"])[0]),
+                                        h(b["codes"]), h(b["scales"]), float(h(b["tensor_scale"])[0]), tiles=2)
+        _nv_check(got.cpu().numpy().astype(np.float64), exact, cabs, a["row_codes"].shape[1] * 2)
+
+
 def test_nvfp4_gemm_full_size_sampled():
     m = n = k = 8192
     rng = np.random.default_rng(9)
@@ -204,7 +252,7 @@ def test_nvfp4_gemm_full_size_sampled():
     c = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
     ta = torch.tensor([ga], device=DEV)
     tb = torch.tensor([gb], device=DEV)
-    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B.BF16, c)
+    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, 0, B.BF16, c)
     torch.cuda.synchronize()
     rows = np.array([0, 1, 127, 128, 255, 256, 4095, 8190, 8191])
     cols = np.array([0, 31, 32, 255, 256, 4096, 8191])
@@ -229,7 +277,7 @@ def _run_with_amax(kind, m, n, k, bf16, rng, amax):
         bc, bs = _nv_operand(rng, n, k)
         ta = torch.tensor([37.5], device=DEV)
         tb = torch.tensor([2.25], device=DEV)
-        args = (_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B._dt(c), c)
+        args = (_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, 0, B._dt(c), c)
         B.fp4q_gemm_nvfp4(*args, amax)
         exact, cabs = oracle.gemm_nvfp4(ac, as_, np.float32(37.5), bc, bs, np.float32(2.25))
     torch.cuda.synchronize()

@@ -497,17 +497,23 @@ def test_rht_standalone_within_tolerance(kind):
     assert rht_close(yf, ref)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(512, 256), (256, 200), (128, 72)])
 @pytest.mark.parametrize("rnd", [0, 1])
-def test_rht_fused_two_stage_exact(rnd, shape):
+def test_rht_fused_two_stage_exact(rnd, shape, dtype):
     """The fused RHT + column-wise NVFP4 equals the oracle quantizer fed with the
-    library's own transform output, bit for bit; against the all-oracle pipeline the
-    codes may differ only at rounding ties.  Widths that are not a multiple of 64
-    leave a partial last column slab."""
+    library's own transform output (of the same dtype), bit for bit; against the
+    all-oracle pipeline the codes may differ only at rounding ties.  Widths that are
+    not a multiple of 64 leave a partial last column slab (bf16) or a partial last
+    workgroup (fp32)."""
     rows, cols = shape
-    bits = si.wgrad_gradient(rows, cols, seed=3)
+    if dtype == "bf16":
+        bits = si.wgrad_gradient(rows, cols, seed=3)
+        xd = dev_bf16(bits)
+    else:
+        bits = si.weight(rows, cols, seed=3, std=1e-3)
+        xd = dev_f32(bits)
     signs = oracle.rht_signs(4)
-    xd = dev_bf16(bits)
     out = B.quantize_nvfp4(xd, B.COLWISE, rnd=rnd, sr_seed=40, rht_signs=signs.tolist())
     y = host(B.rht(xd, signs.tolist()))
     amax_g, gs_g = host(out["amax"])[0], host(out["tensor_scale"])[0]
