@@ -573,10 +573,11 @@ WORKLOADS = {"if4": IF4RoundTrip, "activation": ActivationNVFP4, "weight": Weigh
 
 # --------------------------------------------------------------------------------------
 
-def _event_mean(stream, fn, n: int = 20) -> float:
-    """Mean ms of n back-to-back fn(i) between two HIP events on `stream`."""
+def _event_mean(stream, fn, n: int = 100, warm: int = 50) -> float:
+    """Mean ms of n back-to-back fn(i) between two HIP events on `stream`, after `warm`
+    untimed launches that bring the clocks to the level a stream of such launches runs at."""
     import torch
-    for i in range(2):
+    for i in range(warm):
         fn(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -602,7 +603,7 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float, flush) -> dict
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
     # the dominant kernel alone, back to back, HIP events on the stream it runs on
-    nk = max(steps, 20)
+    nk = max(steps, 100)
     k_mean = _event_mean(stream, wl.kernel_launch, nk)
     mfma = getattr(wl, "bound", "hbm") == "mfma"
     if mfma:

@@ -1075,17 +1075,34 @@ __device__ __forceinline__ void decode8_fp4(uint32_t w, float scale, float r[8])
 // INT4 candidate for 8 scaled values under the 6/7 rule: q = clamp(rint(v*fl(7/6)), -7, 7)
 // via the 1.5*2^23 rounding constant (its low nibble is q in two's complement), restored
 // as fl(q*fl(6/7)); accumulates both squared-error sums in element order.
-__device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[8], float& e_fp, float& e_int) {
-  const float c76 = 7.0f / 6.0f, c67 = 6.0f / 7.0f, magic = 12582912.0f;
+// The clamp only matters in blocks whose E4M3 scale is subnormal: with a normal scale s
+// (code >= 8) the scale is at least 15/16 of fl(bamax*gs)/6, so |v| <= 6.4 (one ulp
+// more at most) and |fl(v*fl(7/6))| <= 7.47, which rounds to at most 7 anyway.
+// The restore fl(q*fl(6/7)) comes from a 16-entry LDS table indexed by q + 8, whose
+// byte address is one shift-and-add of y's bits (y = 1.5*2^23 + q as an integer).
+struct If4RestoreTable {
+  float r[16];   // r[i] = fl((i - 8) * fl(6/7))
+};
+constexpr uint32_t kIf4MagicBits = 0x4B400000u;   // bits of 1.5*2^23
+
+__device__ __forceinline__ void fill_if4_restore(If4RestoreTable& t) {
+  if (threadIdx.x < 16) t.r[threadIdx.x] = (float)((int)threadIdx.x - 8) * (6.0f / 7.0f);
+}
+
+template <bool CLAMP>
+__device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[8], const If4RestoreTable& rt,
+                                               float& e_fp, float& e_int) {
+  const float c76 = 7.0f / 6.0f, magic = 12582912.0f;
+  // &rt.r[q + 8] = rt.r + (bits(y) - kIf4MagicBits + 8), all in 32-bit LDS addresses
+  const float* base = rt.r + 8 - kIf4MagicBits;
   uint32_t yb[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     float wv = v[k] * c76;
-    wv = __builtin_amdgcn_fmed3f(wv, -7.0f, 7.0f);
+    if constexpr (CLAMP) wv = __builtin_amdgcn_fmed3f(wv, -7.0f, 7.0f);
     const float y = wv + magic;
-    const float qf = y - magic;
-    const float ri = qf * c67;
     yb[k] = __float_as_uint(y);
+    const float ri = base[yb[k]];
     const float dfp = v[k] - rf[k];
     const float dint = v[k] - ri;
     e_fp = __builtin_fmaf(dfp, dfp, e_fp);
@@ -1104,52 +1121,91 @@ __device__ __forceinline__ uint32_t if4_block8(const float v[8], const float rf[
 // scale, reciprocal table) is shared by the four.
 constexpr int kIf4Blocks = 4;
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n16, AmaxSource amax,
-                                             float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
-                                             uint8_t* __restrict__ scales) {
-  __shared__ RecipTable rtab;
-  fill_recip_table(rtab);
-  __syncthreads();
-  const float gs = tensor_scale_publish(amax, tensor_scale);
+// One 16-element block held as two halves a, b of scaled values x*gs: scale, both
+// candidates, choice.  Writes the 8 code bytes and the flagged scale byte.
+template <bool CLAMP>
+__device__ __forceinline__ void if4_encode(float (&a)[8], float (&b)[8], uint32_t sc, const RecipPair rp,
+                                           const If4RestoreTable& rt, uint2& codes, uint32_t& scale) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = div2(a[k], rp);
+    b[k] = div2(b[k], rp);
+  }
+  const uint32_t fa = pack8_rtn(a, 1.0f), fb = pack8_rtn(b, 1.0f);
+  float ra[8], rb[8];
+  decode8_fp4(fa, 1.0f, ra);
+  decode8_fp4(fb, 1.0f, rb);
+  float e_fp = 0.0f, e_int = 0.0f;
+  const uint32_t ia = if4_block8<CLAMP>(a, ra, rt, e_fp, e_int);
+  const uint32_t ib = if4_block8<CLAMP>(b, rb, rt, e_fp, e_int);
+  const bool use_int = e_int < e_fp;
+  codes = use_int ? make_uint2(ia, ib) : make_uint2(fa, fb);
+  scale = sc | (use_int ? 0x80u : 0u);
+}
+
+// max |v| over 16 values, as a tree of three-input maxima.
+__device__ __forceinline__ float absmax16(const float (&a)[8], const float (&b)[8]) {
+  auto m3 = [](float x, float y, float z) {
+    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x), __builtin_fabsf(y)), __builtin_fabsf(z));
+  };
+  const float p0 = m3(a[0], a[1], a[2]), p1 = m3(a[3], a[4], a[5]), p2 = m3(a[6], a[7], b[0]);
+  const float p3 = m3(b[1], b[2], b[3]), p4 = m3(b[4], b[5], b[6]);
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(p0, p1), p2),
+                         __builtin_fmaxf(__builtin_fmaxf(p3, p4), __builtin_fabsf(b[7])));
+}
+
+// The blocks of one lane.  CHECK: the workgroup's last chunk may run past n16 (loads
+// are clamped to the last block and stores skipped); otherwise every block exists.
+template <typename T, bool CHECK>
+__device__ __forceinline__ void if4_lane(const T* __restrict__ x, int64_t n16, float gs, const RecipTable& rtab,
+                                         const If4RestoreTable& rt, uint8_t* __restrict__ codes,
+                                         uint8_t* __restrict__ scales) {
   const int64_t g0 = (int64_t)blockIdx.x * (256 * kIf4Blocks) + threadIdx.x;
   float a[kIf4Blocks][8], b[kIf4Blocks][8];
 #pragma unroll
   for (int j = 0; j < kIf4Blocks; ++j) {
-    const int64_t g = min(g0 + 256 * j, n16 - 1);   // past the end: reload the last block, not stored
+    const int64_t g = CHECK ? min(g0 + 256 * j, n16 - 1) : g0 + 256 * j;
     load8(x, g * 16, a[j]);
     load8(x, g * 16 + 8, b[j]);
   }
 #pragma unroll
   for (int j = 0; j < kIf4Blocks; ++j) {
-    const int64_t g = g0 + 256 * j;
-    float m = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       a[j][k] = a[j][k] * gs;
       b[j][k] = b[j][k] * gs;
-      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[j][k]), __builtin_fabsf(b[j][k])));
     }
-    const uint32_t sc = nvfp4_scale_code(m);
+    const uint32_t sc = nvfp4_scale_code(absmax16(a[j], b[j]));
     const RecipPair rp = rtab.r[sc];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      a[j][k] = div2(a[j][k], rp);
-      b[j][k] = div2(b[j][k], rp);
-    }
-    const uint32_t fa = pack8_rtn(a[j], 1.0f), fb = pack8_rtn(b[j], 1.0f);
-    float ra[8], rb[8];
-    decode8_fp4(fa, 1.0f, ra);
-    decode8_fp4(fb, 1.0f, rb);
-    float e_fp = 0.0f, e_int = 0.0f;
-    const uint32_t ia = if4_block8(a[j], ra, e_fp, e_int);
-    const uint32_t ib = if4_block8(b[j], rb, e_fp, e_int);
-    const bool use_int = e_int < e_fp;
-    if (g < n16) {
-      *reinterpret_cast<uint2*>(codes + g * 8) = use_int ? make_uint2(ia, ib) : make_uint2(fa, fb);
-      scales[g] = (uint8_t)(sc | (use_int ? 0x80u : 0u));
+    uint2 cw;
+    uint32_t sw;
+    // the clamp only for waves holding a block with a subnormal scale (uniform branch)
+    if (__builtin_amdgcn_ballot_w64(sc < 8u) != 0)
+      if4_encode<true>(a[j], b[j], sc, rp, rt, cw, sw);
+    else
+      if4_encode<false>(a[j], b[j], sc, rp, rt, cw, sw);
+    const int64_t g = g0 + 256 * j;
+    if (!CHECK || g < n16) {
+      *reinterpret_cast<uint2*>(codes + g * 8) = cw;
+      scales[g] = (uint8_t)sw;
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_if4(const T* __restrict__ x, int64_t n16, AmaxSource amax,
+                                             float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  __shared__ RecipTable rtab;
+  __shared__ If4RestoreTable rt;
+  fill_recip_table(rtab);
+  fill_if4_restore(rt);
+  __syncthreads();
+  const float gs = tensor_scale_publish(amax, tensor_scale);
+  if ((int64_t)(blockIdx.x + 1) * (256 * kIf4Blocks) <= n16)
+    if4_lane<T, false>(x, n16, gs, rtab, rt, codes, scales);
+  else
+    if4_lane<T, true>(x, n16, gs, rtab, rt, codes, scales);
 }
 
 void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const AmaxSource& amax, float* tensor_scale,
