@@ -35,8 +35,10 @@ struct RhtSigns { uint32_t w[4]; };
 __device__ __forceinline__ uint32_t parity(uint32_t v) { return __builtin_popcount(v) & 1u; }
 
 // A-operand fragments: lane (il = lane & 31, hk = lane >> 5), K-step kk holds
-// K[32a + il][16kk + 8hk + e] without the H_4 factor, e = 0..7.
-__device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_signs, u32x4 frag[8], u32x4 nfrag[8]) {
+// K[32a + il][16kk + 8hk + e] without the H_4 factor, e = 0..7.  Where H_4 is -1 the
+// MFMA takes the fragment with its eight sign bits flipped (four XORs), made at the
+// point of use rather than kept in registers.
+__device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_signs, u32x4 frag[8]) {
   const uint32_t lane = threadIdx.x & 63, il = lane & 31, hk = lane >> 5;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -54,8 +56,14 @@ __device__ __forceinline__ void make_fragments(const RhtSigns& sg, bool with_sig
       d[q] = half[0] | (half[1] << 16);
     }
     frag[kk] = u32x4{d[0], d[1], d[2], d[3]};
-    nfrag[kk] = frag[kk] ^ 0x80008000u;
   }
+}
+
+// The A operand of K-step kk for output block a: frag[kk] times H_4[a][kk/2] (a and kk
+// are constants after unrolling, so the choice costs nothing).
+__device__ __forceinline__ bf16x8 a_operand(const u32x4 frag[8], int a, int kk) {
+  const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;
+  return __builtin_bit_cast(bf16x8, flip ? (frag[kk] ^ 0x80008000u) : frag[kk]);
 }
 
 // The 64 words one lane reads for a tile: tokens tok0 + 16kk + 8hk + r (r = 0..7) of
@@ -154,8 +162,7 @@ __device__ __forceinline__ void rht_read_b(const RhtStage& st, RhtB& B) {
 // pair.  Working in halves keeps 64 accumulators live instead of 128, which lets two
 // waves share a SIMD.
 template <int H>
-__device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag[8], const u32x4 nfrag[8],
-                                             f32x16 acc[2][2]) {
+__device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag[8], f32x16 acc[2][2]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -172,8 +179,7 @@ __device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap) {
       const int a = 2 * H + ap;
-      const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
-      const bf16x8 fa = __builtin_bit_cast(bf16x8, flip ? nfrag[kk] : frag[kk]);
+      const bf16x8 fa = a_operand(frag, a, kk);
       acc[0][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][ap], 0, 0, 0);
       acc[1][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][ap], 0, 0, 0);
     }
@@ -183,8 +189,7 @@ __device__ __forceinline__ void rht_mma_half(const RhtRaw& raw, const u32x4 frag
 // The same contraction from ready B operands (column slot n of pass p is tile column
 // 32p + n); per output element the MFMA sums are the same as above.
 template <int H>
-__device__ __forceinline__ void rht_mma_half_b(const RhtB& B, const u32x4 frag[8], const u32x4 nfrag[8],
-                                               f32x16 acc[2][2]) {
+__device__ __forceinline__ void rht_mma_half_b(const RhtB& B, const u32x4 frag[8], f32x16 acc[2][2]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -195,8 +200,7 @@ __device__ __forceinline__ void rht_mma_half_b(const RhtB& B, const u32x4 frag[8
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap) {
       const int a = 2 * H + ap;
-      const bool flip = (__builtin_popcount(a & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
-      const bf16x8 fa = __builtin_bit_cast(bf16x8, flip ? nfrag[kk] : frag[kk]);
+      const bf16x8 fa = a_operand(frag, a, kk);
       acc[0][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v0, acc[0][ap], 0, 0, 0);
       acc[1][ap] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, v1, acc[1][ap], 0, 0, 0);
     }
@@ -265,8 +269,8 @@ struct TileWalk {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                   RhtSigns sg, int inverse, float* __restrict__ y) {
-  u32x4 frag[8], nfrag[8];
-  make_fragments(sg, !inverse, frag, nfrag);
+  u32x4 frag[8];
+  make_fragments(sg, !inverse, frag);
   const TileIter it(rows, cols);
   const int lane = threadIdx.x & 63;
   for (int64_t tile = wave_id(); tile < it.ntiles; tile += wave_count()) {
@@ -288,9 +292,9 @@ __global__ __launch_bounds__(256) void k_rht_bf16(const uint16_t* __restrict__ x
         }
     };
     f32x16 acc[2][2];
-    rht_mma_half<0>(raw, frag, nfrag, acc);
+    rht_mma_half<0>(raw, frag, acc);
     emit(acc, 0);
-    rht_mma_half<1>(raw, frag, nfrag, acc);
+    rht_mma_half<1>(raw, frag, acc);
     emit(acc, 2);
   }
 }
@@ -302,8 +306,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                   RhtSigns sg, AmaxSink sink) {
   __shared__ RhtStage stage[4];
   RhtStage& st = stage[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
-  u32x4 frag[8], nfrag[8];
-  make_fragments(sg, true, frag, nfrag);
+  u32x4 frag[8];
+  make_fragments(sg, true, frag);
   const int lane = threadIdx.x & 63;
   float m = 0.0f;
   TileWalk w(rows, cols);
@@ -327,9 +331,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int r = 0; r < 16; ++r) t[p] = __builtin_fmaxf(t[p], __builtin_fabsf(acc[p][a][r]));
     };
     f32x16 acc[2][2];
-    rht_mma_half_b<0>(B, frag, nfrag, acc);
+    rht_mma_half_b<0>(B, frag, acc);
     fold(acc);
-    rht_mma_half_b<1>(B, frag, nfrag, acc);
+    rht_mma_half_b<1>(B, frag, acc);
     fold(acc);
     if (col < cols) m = __builtin_fmaxf(m, t[0]);
     if (col + 32 < cols) m = __builtin_fmaxf(m, t[1]);
@@ -364,41 +368,73 @@ struct RhtColOp {
 // MFMAs (K-step kk ascending, the same A fragment) as rht_mma_half_b, so all kernels see
 // the same values.
 template <int A>
-__device__ __forceinline__ void rht_mma_block(const RhtB& B, const u32x4 frag[8], const u32x4 nfrag[8],
+__device__ __forceinline__ void rht_mma_block(const RhtB& B, const u32x4 frag[8],
                                               f32x16 acc[2]) {
   acc[0] = f32x16{};
   acc[1] = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    const bool flip = (__builtin_popcount(A & (kk >> 1)) & 1) != 0;   // H_4[a][kk/2]
-    const bf16x8 fa = __builtin_bit_cast(bf16x8, flip ? nfrag[kk] : frag[kk]);
+    const bf16x8 fa = a_operand(frag, A, kk);
     acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8, B.b[kk][0]), acc[0], 0, 0, 0);
     acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8, B.b[kk][1]), acc[1], 0, 0, 0);
   }
 }
 
 // Where a lane's outputs of one tile go.  Lane (n, hk) quantizes columns 64*slab + n
-// (pass 0) and + 32 (pass 1).
+// (pass 0) and + 32 (pass 1).  Output block a of a column is 16 code bytes at 16 a of
+// the column's 64-byte span in the tile, lane hk encoding bytes 8 hk..8 hk + 7; after
+// blocks a and a + 1 the lane pair trades one half each, so lane 0 stores block a and
+// lane 1 block a + 1 as whole 16-byte pieces.
+// Addresses and counters are a wave-uniform part (scalar registers) plus one 32-bit
+// lane part shared by both passes, which keeps the quantizer's vector registers free.
 struct RhtTileOut {
-  uint8_t* code_base[2];   // this lane's codes of pass p, block a: code_base[p] + 16 a (bytes)
-  uint8_t* scale_dst[2];   // this lane's 4 scale bytes of pass p
+  uint8_t* code_u[2];      // column 64 slab + 32 p, first token of the chunk
+  uint8_t* scale_u[2];
+  uint64_t idx8_u[2];      // SR: Philox counter of that column's first 8 tokens of the chunk
+  uint32_t code_l, scale_l, idx8_l;   // lane (n, hk): column n's offset (scales, SR: plus its half)
   bool valid[2];
-  uint64_t idx8[2];        // SR: Philox counter of this lane's first 8 tokens of block 0, pass p
   uint32_t scale_word[2];
+  uint2 prev[2];           // this lane's 8 code bytes of the last even block, pass p
 };
 
+// Codes of block a (8 bytes of this lane, pass p).  PAIR: held for an even a, stored
+// with the held half for an odd a; otherwise stored as they are (the SR pass, whose
+// registers are all taken by the draws, keeps the 8-byte stores).
+template <bool PAIR>
+__device__ __forceinline__ void rht_put_codes(RhtTileOut& t, int a, int p, uint2 w) {
+  const uint32_t hk = (threadIdx.x & 63) >> 5;
+  if constexpr (!PAIR) {
+    if (t.valid[p]) *reinterpret_cast<uint2*>(t.code_u[p] + t.code_l + 8 * hk + 16 * a) = w;
+    return;
+  }
+  if ((a & 1) == 0) {
+    t.prev[p] = w;
+    return;
+  }
+  // lanes >= 32 take lane hk = 0's half of block a; lanes < 32 hk = 1's half of block a - 1
+  auto sx = __builtin_amdgcn_permlane32_swap(t.prev[p].x, w.x, false, false);
+  auto sy = __builtin_amdgcn_permlane32_swap(t.prev[p].y, w.y, false, false);
+  if (t.valid[p])
+    *reinterpret_cast<uint4*>(t.code_u[p] + t.code_l + 16 * hk + 16 * (a - 1)) = make_uint4(sx[0], sy[0], sx[1],
+                                                                                           sy[1]);
+}
+
 __device__ __forceinline__ RhtTileOut rht_tile_out(int64_t chunk, int64_t slab, const RhtColOp& o) {
-  const int lane = threadIdx.x & 63, hk = lane >> 5;
+  const uint32_t lane = threadIdx.x & 63, hk = lane >> 5, n = lane & 31;
   const int64_t half_rows = o.rows >> 1, nb = o.rows >> 4;
-  const int64_t tok0 = chunk * 128, col = slab * 64 + (lane & 31);
+  const int64_t tok0 = chunk * 128;
   RhtTileOut t;
+  // the lane parts stay below 2^32: 32 columns of a tensor with rows < 2^31
+  t.code_l = n * (uint32_t)half_rows;
+  t.scale_l = n * (uint32_t)nb + 4u * hk;
+  t.idx8_l = n * (uint32_t)(o.rows >> 3) + 2u * hk;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int64_t c = col + 32 * p;
-    t.valid[p] = c < o.cols;
-    t.code_base[p] = o.ccodes + c * half_rows + (tok0 >> 1) + 8 * hk;
-    t.scale_dst[p] = o.cscales + c * nb + (tok0 >> 4) + 4 * hk;
-    t.idx8[p] = (uint64_t)(c * o.rows + tok0 + 16 * hk) >> 3;
+    const int64_t c0 = slab * 64 + 32 * p;   // the column of lane n = 0
+    t.valid[p] = c0 + n < o.cols;
+    t.code_u[p] = o.ccodes + c0 * half_rows + (tok0 >> 1);
+    t.scale_u[p] = o.cscales + c0 * nb + (tok0 >> 4);
+    t.idx8_u[p] = (uint64_t)(c0 * o.rows + tok0) >> 3;
     t.scale_word[p] = 0u;
   }
   return t;
@@ -442,7 +478,7 @@ __device__ __forceinline__ void rht_quant_block(const f32x16 (&acc)[2], int a, c
       auto wx = __builtin_amdgcn_permlane32_swap(wA, wB, false, false);
       const uint32_t lo = __builtin_amdgcn_perm(wx[1], wx[0], 0x05040100u);   // tokens 0..7
       const uint32_t hi = __builtin_amdgcn_perm(wx[1], wx[0], 0x07060302u);   // tokens 8..15
-      if (t.valid[p]) *reinterpret_cast<uint2*>(t.code_base[p] + 16 * a) = make_uint2(lo, hi);
+      rht_put_codes<true>(t, a, p, make_uint2(lo, hi));
       t.scale_word[p] |= sc << (8 * a);
     } else {
       // SR: regroup so that each lane holds 16 consecutive tokens of one block (lanes < 32
@@ -471,11 +507,11 @@ __device__ __forceinline__ void rht_quant_block(const f32x16 (&acc)[2], int a, c
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = div2(v[k], rp);
       uint32_t r0[8], r1[8];
-      const uint64_t idx8 = t.idx8[p] + (uint64_t)(4 * a);   // 32 tokens per block a = 4 groups of 8
+      const uint64_t idx8 = t.idx8_u[p] + t.idx8_l + (uint64_t)(4 * a);   // 32 tokens per block a = 4 groups of 8
       sr_draws8(idx8, 1u, o.k0, o.k1, r0);
       sr_draws8(idx8 + 1, 1u, o.k0, o.k1, r1);
       const uint32_t w0 = pack8_sr(v, r0, 1.0f), w1 = pack8_sr(v + 8, r1, 1.0f);
-      if (t.valid[p]) *reinterpret_cast<uint2*>(t.code_base[p] + 16 * a) = make_uint2(w0, w1);
+      rht_put_codes<false>(t, a, p, make_uint2(w0, w1));
       t.scale_word[p] |= sc << (8 * a);
     }
   }
@@ -493,7 +529,7 @@ __device__ __forceinline__ void rht_store_scales(const RhtTileOut& t) {
     // bytes of lo: b0 b2 b4 b6, of hi: b1 b3 b5 b7
     const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // b0 b1 b2 b3
     const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // b4 b5 b6 b7
-    if (t.valid[p]) *reinterpret_cast<uint32_t*>(t.scale_dst[p]) = hk ? second : first;
+    if (t.valid[p]) *reinterpret_cast<uint32_t*>(t.scale_u[p] + t.scale_l) = hk ? second : first;
   }
 }
 
@@ -501,10 +537,10 @@ __device__ __forceinline__ void rht_store_scales(const RhtTileOut& t) {
 // are issued together with the quantization of the current one (from `cur`), so the
 // matrix core and the vector ALUs work at the same time within the wave.
 template <bool SR, int ANEXT>
-__device__ __forceinline__ void rht_pipe_step(const RhtB& B, const u32x4 (&frag)[8], const u32x4 (&nfrag)[8],
+__device__ __forceinline__ void rht_pipe_step(const RhtB& B, const u32x4 (&frag)[8],
                                               f32x16 (&next)[2], const f32x16 (&cur)[2], int a,
                                               const RhtColOp& o, const RecipTable& rtab, RhtTileOut& t) {
-  rht_mma_block<ANEXT>(B, frag, nfrag, next);
+  rht_mma_block<ANEXT>(B, frag, next);
   rht_quant_block<SR>(cur, a, o, rtab, t);
 }
 
@@ -519,8 +555,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   fill_recip_table(rtab);
   __syncthreads();
   const RhtColOp op{x, rows, cols, ccodes, cscales, tensor_scale_publish(amax, tensor_scale), k0, k1};
-  u32x4 frag[8], nfrag[8];
-  make_fragments(sg, true, frag, nfrag);
+  u32x4 frag[8];
+  make_fragments(sg, true, frag);
   TileWalk w(rows, cols);
   if (!w.valid()) return;
   // The wave's tiles form one stream of output blocks (four per tile).  The MFMAs of
@@ -537,12 +573,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
   }
   f32x16 acc0[2], acc1[2];
-  rht_mma_block<0>(B, frag, nfrag, acc0);
+  rht_mma_block<0>(B, frag, acc0);
   for (;;) {
     RhtTileOut t = rht_tile_out(w.chunk, w.slab, op);
-    rht_pipe_step<SR, 1>(B, frag, nfrag, acc1, acc0, 0, op, rtab, t);
-    rht_pipe_step<SR, 2>(B, frag, nfrag, acc0, acc1, 1, op, rtab, t);
-    rht_pipe_step<SR, 3>(B, frag, nfrag, acc1, acc0, 2, op, rtab, t);
+    rht_pipe_step<SR, 1>(B, frag, acc1, acc0, 0, op, rtab, t);
+    rht_pipe_step<SR, 2>(B, frag, acc0, acc1, 1, op, rtab, t);
+    rht_pipe_step<SR, 3>(B, frag, acc1, acc0, 2, op, rtab, t);
     // the last block of this tile overlaps the first MFMAs of the next tile
     TileWalk nw = w;
     nw.next();
@@ -554,7 +590,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       TileWalk nnw = nw;
       nnw.next();
       if (nnw.valid()) rht_issue(x, cols, nnw.chunk * 128, nnw.slab * 64, st);
-      rht_pipe_step<SR, 0>(B, frag, nfrag, acc0, acc1, 3, op, rtab, t);
+      rht_pipe_step<SR, 0>(B, frag, acc0, acc1, 3, op, rtab, t);
     } else {
       rht_quant_block<SR>(acc1, 3, op, rtab, t);
     }
@@ -749,12 +785,8 @@ void launch_rht_nvfp4_col(const void* xv, bool f32, int64_t rows, int64_t cols, 
     return;
   }
   const uint16_t* x = static_cast<const uint16_t*>(xv);
-  if (sr)
-    k_rht_nvfp4_col<true><<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
-                                                                col_scales, k0, k1);
-  else
-    k_rht_nvfp4_col<false><<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes,
-                                                                 col_scales, k0, k1);
+  auto kern = sr ? k_rht_nvfp4_col<true> : k_rht_nvfp4_col<false>;
+  kern<<<rht_grid(rows, cols, 2), 256, 0, st>>>(x, rows, cols, sg, amax, tensor_scale, col_codes, col_scales, k0, k1);
 }
 
 }  // namespace fp4q
