@@ -51,6 +51,10 @@ KERNEL_SOURCES = {
     "k_if4": QUANT_SOURCES, "k_nvfp4_fused": QUANT_SOURCES, "k_nvfp4_2d": QUANT_SOURCES,
     "k_amax_wide": QUANT_SOURCES, "k_dequant": QUANT_SOURCES,
     "k_rht_nvfp4_col": ["fp4q_rht.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
+    "k_rht_amax": ["fp4q_rht.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
+    "k_variant": ["fp4q_variant.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
+    "k_dequant_variant": ["fp4q_variant.hip", "fp4q_dev.hpp", "fp4q_internal.hpp"],
+    "k_mxfp4": QUANT_SOURCES, "k_mxfp6": QUANT_SOURCES,
     "k_gemm_mxfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
     "k_gemm_nvfp4": ["fp4q_gemm.hip", "fp4q_internal.hpp"],
 }
@@ -539,6 +543,71 @@ class GemmNVFP4Wgrad(GemmMXFP4):
     given_launch = step
 
 
+class BlockVariants(Workload):
+    """The block formats compared with IF4 on the IF4 workload's bf16 [32768 x 8192]
+    tensor: Four Over Six, NVINT4, IF3 and IF6 (NVFP4 two-level scaling, 16-element
+    blocks), each quantized with the tensor amax given and dequantized back to bf16."""
+    name = "block_variants_46_nvint4_if3_if6_bf16_32768x8192"
+    rows, cols = 32768, 8192
+
+    def __init__(self):
+        from block_scaled_fp4_05_amd import binding as B
+        n = self.rows * self.cols
+        self.vars = [(B.VAR_46, "four_over_six"), (B.VAR_NVINT4, "nvint4"), (B.VAR_IF3, "if3"), (B.VAR_IF6, "if6")]
+        self.bits = {v: B.VARIANT_BITS[v] for v, _ in self.vars}
+        self.qbytes = {v: 2 * n + n * self.bits[v] // 8 + n // 16 for v, _ in self.vars}
+        self.dbytes = {v: n * self.bits[v] // 8 + n // 16 + 2 * n for v, _ in self.vars}
+        self.elements = n * len(self.vars)
+        self.algo_bytes = sum(self.qbytes.values()) + sum(self.dbytes.values())
+        self.kernel = "k_variant"             # the IF6 quantizer, the heaviest of the four
+        self.kernel_bytes = self.qbytes[B.VAR_IF6]
+
+    def setup(self):
+        import torch
+        import synth_inputs as si
+        from block_scaled_fp4_05_amd import binding as B
+        self.B = B
+        self.ws = B.Workspace()
+        x0 = _dev_bf16(si.if4_mix(self.rows, self.cols, seed=5))
+        r, c = self.rows, self.cols
+        self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
+        self.amax = [_f1() for _ in range(self.sets)]
+        for k in range(self.sets):
+            B.fp4q_amax(self.x[k], B.BF16, r, c, self.amax[k])
+        self.out = [{v: dict(ts=_f1(), c=_u8(r, c * self.bits[v] // 8), s=_u8(r, c // 16),
+                             y=torch.empty(r, c, dtype=torch.bfloat16, device="cuda")) for v, _ in self.vars}
+                    for _ in range(self.sets)]
+
+    def _quant(self, i, v):
+        B, k = self.B, i % self.sets
+        o = self.out[k][v]
+        B.fp4q_quantize_variant(self.x[k], B.BF16, self.rows, self.cols, v, B.AMAX_GIVEN, self.amax[k], o["ts"],
+                                o["c"], o["s"], self.ws)
+
+    def _deq(self, i, v):
+        B, o = self.B, self.out[i % self.sets][v]
+        B.fp4q_dequantize_variant(v, o["c"], o["s"], o["ts"], self.rows, self.cols, B.BF16, o["y"])
+
+    def step(self, i):
+        for v, _ in self.vars:
+            self._quant(i, v)
+            self._deq(i, v)
+
+    def kernel_launch(self, i):
+        self._quant(i, self.B.VAR_IF6)
+
+    given_launch = kernel_launch
+
+    def extra(self, stream):
+        d = {}
+        for v, nm in self.vars:
+            q = _event_mean(stream, lambda i, v=v: self._quant(i, v))
+            dq = _event_mean(stream, lambda i, v=v: self._deq(i, v))
+            d[nm] = {"bits": self.bits[v], "quantize_ms": q, "quantize_GBps": self.qbytes[v] / (q * 1e-3) / 1e9,
+                     "dequant_bf16_ms": dq, "dequant_GBps": self.dbytes[v] / (dq * 1e-3) / 1e9}
+        return d
+
+
 class DeviceCopy(Workload):
     """Calibration, not a hot-path row: a plain device-to-device copy of 64 MiB."""
     name = "device_copy_64MiB"
@@ -566,8 +635,9 @@ class DeviceCopy(Workload):
 
 
 HEADLINE = IF4RoundTrip
-OTHERS = [ActivationNVFP4, WeightNVFP4MX, WgradRHT]
+OTHERS = [ActivationNVFP4, WeightNVFP4MX, WgradRHT, BlockVariants]
 WORKLOADS = {"if4": IF4RoundTrip, "activation": ActivationNVFP4, "weight": WeightNVFP4MX, "wgrad": WgradRHT,
+             "variants": BlockVariants,
              "mxfp6": WeightMXFP6, "gemm": GemmMXFP4, "gemm_nvfp4": GemmNVFP4Wgrad, "copy": DeviceCopy}
 
 
