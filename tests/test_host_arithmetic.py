@@ -6,8 +6,8 @@ and form the pair from the hardware reciprocal estimate plus one Newton step.
 host_checks/division_check.c verifies both exhaustively over every dividend
 significand and every E4M3 divisor (CPU only, libm fmaf).  Dequantization divides
 by the FP32 tensor scale with a corrected reciprocal; host_checks/
-dequant_division_check.c verifies it for every dividend the decoder can form
-against every divisor significand."""
+dequant_division_check.c verifies it for every dividend the decoders of all block
+formats (NVFP4, IF4, the variants) can form against every divisor significand."""
 import os
 import subprocess
 
