@@ -92,89 +92,119 @@ __device__ __forceinline__ uint32_t get16(const Codes16& o, int k) {
 
 constexpr int kVarBlocks = 4;   // blocks per lane, all loads issued first (as k_if4)
 
-template <typename T, int V>
-__global__ __launch_bounds__(256) void k_variant(const T* __restrict__ x, int64_t n16, AmaxSource amax,
-                                                 float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales) {
+// Restore values of an INT candidate, fl((i - 2^(BITS-1)) * cinv) for i = 0 .. 2^BITS - 1,
+// read at the address one shift-and-add makes of the rounded value's bits (as k_if4).
+struct VarRestore {
+  float r[64];
+};
+constexpr uint32_t kMagicBits = 0x4B400000u;   // bits of 1.5 * 2^23
+
+// Whether the INT candidate needs its clamp with a normal block scale: the scale is at
+// least 15/16 of fl(bamax gs)/M, so |v| <= M * 16/15 (one ulp more at most) and the
+// clamp can only act if fl(v * c) may reach kQ + 1/2.
+template <int V>
+constexpr bool clamp_always() {
+  using D = Var<V>;
+  return D::kInt && (D::kM * 16.0f / 15.0f * (D::kDirect ? 1.0f : D::kC) * 1.0001f >= (float)D::kQ + 0.5f);
+}
+
+// One block: v holds x * gs on entry.  Writes the packed codes and the flagged scale.
+template <int V, bool CLAMP>
+__device__ __forceinline__ void variant_block(float (&v)[16], uint32_t sc, const RecipPair rp, const VarRestore& rt,
+                                              Codes16& out, uint32_t& scale_byte) {
   using D = Var<V>;
   constexpr int BITS = D::kBits;
-  __shared__ RecipTable rtab;
-  fill_recip_table(rtab);
-  __syncthreads();
-  const float gs = tensor_scale_publish(amax, tensor_scale, 448.0f * D::kM);
-  const int64_t g0 = (int64_t)blockIdx.x * (256 * kVarBlocks) + threadIdx.x;
-  float xv[kVarBlocks][16];
 #pragma unroll
-  for (int j = 0; j < kVarBlocks; ++j) {
-    const int64_t g = min(g0 + 256 * j, n16 - 1);   // past the end: reload the last block, not stored
-    load8(x, g * 16, xv[j]);
-    load8(x, g * 16 + 8, xv[j] + 8);
-  }
-#pragma unroll
-  for (int j = 0; j < kVarBlocks; ++j) {
-    const int64_t g = g0 + 256 * j;
-    float v[16];
-    float m = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      v[k] = xv[j][k] * gs;
-      m = __builtin_fmaxf(m, __builtin_fabsf(v[k]));
-    }
-    const uint32_t sc = e4m3_code(div_block_max<V>(m));
-    const RecipPair rp = rtab.r[sc];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = div2(v[k], rp);
+  for (int k = 0; k < 16; ++k) v[k] = div2(v[k], rp);
 
-    Codes16 fc{{0u, 0u, 0u}}, ic{{0u, 0u, 0u}};
-    float e_fp = 0.0f, e_int = 0.0f;
-    if constexpr (D::kFp) {
-      float rf[16];
-      if constexpr (BITS == 4) {
-        fc.w[0] = pack8_rtn(v, 1.0f);
-        fc.w[1] = pack8_rtn(v + 8, 1.0f);
+  Codes16 fc{{0u, 0u, 0u}}, ic{{0u, 0u, 0u}};
+  float e_fp = 0.0f, e_int = 0.0f;
+  if constexpr (D::kFp) {
+    float rf[16];
+    if constexpr (BITS == 4) {
+      fc.w[0] = pack8_rtn(v, 1.0f);
+      fc.w[1] = pack8_rtn(v + 8, 1.0f);
 #define FP4Q_DEC(W, Q, O)                                                  \
   {                                                                        \
     const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(W, 1.0f, Q); \
     rf[O + 2 * Q] = d[0];                                                  \
     rf[O + 2 * Q + 1] = d[1];                                              \
   }
-        FP4Q_DEC(fc.w[0], 0, 0) FP4Q_DEC(fc.w[0], 1, 0) FP4Q_DEC(fc.w[0], 2, 0) FP4Q_DEC(fc.w[0], 3, 0)
-        FP4Q_DEC(fc.w[1], 0, 8) FP4Q_DEC(fc.w[1], 1, 8) FP4Q_DEC(fc.w[1], 2, 8) FP4Q_DEC(fc.w[1], 3, 8)
+      FP4Q_DEC(fc.w[0], 0, 0) FP4Q_DEC(fc.w[0], 1, 0) FP4Q_DEC(fc.w[0], 2, 0) FP4Q_DEC(fc.w[0], 3, 0)
+      FP4Q_DEC(fc.w[1], 0, 8) FP4Q_DEC(fc.w[1], 1, 8) FP4Q_DEC(fc.w[1], 2, 8) FP4Q_DEC(fc.w[1], 3, 8)
 #undef FP4Q_DEC
-      } else if constexpr (BITS == 3) {
+    } else if constexpr (BITS == 3) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) put16<3>(fc, k, fp3_rtn(v[k], rf[k]));
-      } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const uint32_t c = fp6_rtn<0>(v[k]);
-          rf[k] = fp6_value<0>(c);
-          put16<6>(fc, k, c);
-        }
-      }
+      for (int k = 0; k < 16; ++k) put16<3>(fc, k, fp3_rtn(v[k], rf[k]));
+    } else {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float d = v[k] - rf[k];
-        e_fp = __builtin_fmaf(d, d, e_fp);
+        const uint32_t c = fp6_rtn<0>(v[k]);
+        rf[k] = fp6_value<0>(c);
+        put16<6>(fc, k, c);
       }
     }
-    if constexpr (D::kInt) {
-      const float magic = 12582912.0f;   // 1.5 * 2^23: adding it rounds to an integer, ties to even
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        float w = D::kDirect ? v[k] : v[k] * D::kC;
-        w = __builtin_amdgcn_fmed3f(w, -(float)D::kQ, (float)D::kQ);
-        const float y = w + magic;
-        const float qf = y - magic;
-        const float ri = D::kDirect ? qf : qf * D::kCinv;
-        const float d = v[k] - ri;
-        e_int = __builtin_fmaf(d, d, e_int);
-        put16<BITS>(ic, k, __float_as_uint(y) & ((1u << BITS) - 1u));   // two's complement code
-      }
+    for (int k = 0; k < 16; ++k) {
+      const float d = v[k] - rf[k];
+      e_fp = __builtin_fmaf(d, d, e_fp);
     }
-    const bool use_int = D::kInt && (!D::kFp || e_int < e_fp);
-    if (g < n16) {
-      const Codes16& c = use_int ? ic : fc;
+  }
+  if constexpr (D::kInt) {
+    const float magic = 12582912.0f;   // 1.5 * 2^23: adding it rounds to an integer, ties to even
+    // &rt.r[q + 2^(BITS-1)] = rt.r + (bits(y) - kMagicBits + 2^(BITS-1)), in 32-bit LDS addresses
+    const float* base = rt.r + (1u << (BITS - 1)) - kMagicBits;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float w = D::kDirect ? v[k] : v[k] * D::kC;
+      if constexpr (CLAMP) w = __builtin_amdgcn_fmed3f(w, -(float)D::kQ, (float)D::kQ);
+      const float y = w + magic;
+      const float ri = D::kDirect ? y - magic : base[__float_as_uint(y)];
+      const float d = v[k] - ri;
+      e_int = __builtin_fmaf(d, d, e_int);
+      put16<BITS>(ic, k, __float_as_uint(y) & ((1u << BITS) - 1u));   // two's complement code
+    }
+  }
+  const bool use_int = D::kInt && (!D::kFp || e_int < e_fp);
+  out = use_int ? ic : fc;
+  scale_byte = sc | (D::kFp && use_int ? 0x80u : 0u);
+}
+
+template <typename T, int V, bool CHECK>
+__device__ __forceinline__ void variant_lane(const T* __restrict__ x, int64_t n16, float gs, const RecipTable& rtab,
+                                             const VarRestore& rt, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  using D = Var<V>;
+  constexpr int BITS = D::kBits;
+  const int64_t g0 = (int64_t)blockIdx.x * (256 * kVarBlocks) + threadIdx.x;
+  float xv[kVarBlocks][16];
+#pragma unroll
+  for (int j = 0; j < kVarBlocks; ++j) {
+    const int64_t g = CHECK ? min(g0 + 256 * j, n16 - 1) : g0 + 256 * j;   // past the end: reload, not stored
+    load8(x, g * 16, xv[j]);
+    load8(x, g * 16 + 8, xv[j] + 8);
+  }
+#pragma unroll
+  for (int j = 0; j < kVarBlocks; ++j) {
+    const int64_t g = g0 + 256 * j;
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      xv[j][k] = xv[j][k] * gs;
+      m = __builtin_fmaxf(m, __builtin_fabsf(xv[j][k]));
+    }
+    const uint32_t sc = e4m3_code(div_block_max<V>(m));
+    const RecipPair rp = rtab.r[sc];
+    Codes16 c;
+    uint32_t sb;
+    if constexpr (clamp_always<V>() || !D::kInt) {
+      variant_block<V, D::kInt>(xv[j], sc, rp, rt, c, sb);
+    } else {
+      // the clamp only for waves holding a block whose scale is subnormal (uniform branch)
+      if (__builtin_amdgcn_ballot_w64(sc < 8u) != 0) variant_block<V, true>(xv[j], sc, rp, rt, c, sb);
+      else variant_block<V, false>(xv[j], sc, rp, rt, c, sb);
+    }
+    if (!CHECK || g < n16) {
       if constexpr (BITS == 4) {
         *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(c.w[0], c.w[1]);
       } else if constexpr (BITS == 3) {
@@ -188,12 +218,33 @@ __global__ __launch_bounds__(256) void k_variant(const T* __restrict__ x, int64_
         dst[1] = c.w[1];
         dst[2] = c.w[2];
       }
-      scales[g] = (uint8_t)(sc | (D::kFp && use_int ? 0x80u : 0u));
+      scales[g] = (uint8_t)sb;
     }
   }
 }
 
-// x_hat = fl(fl(r * s) / gs) with IEEE division; one lane per 16-element block.
+template <typename T, int V>
+__global__ __launch_bounds__(256) void k_variant(const T* __restrict__ x, int64_t n16, AmaxSource amax,
+                                                 float* __restrict__ tensor_scale, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales) {
+  using D = Var<V>;
+  __shared__ RecipTable rtab;
+  __shared__ VarRestore rt;
+  fill_recip_table(rtab);
+  if (threadIdx.x < (1u << D::kBits))
+    rt.r[threadIdx.x] = (float)((int)threadIdx.x - (1 << (D::kBits - 1))) * D::kCinv;
+  __syncthreads();
+  const float gs = tensor_scale_publish(amax, tensor_scale, 448.0f * D::kM);
+  if ((int64_t)(blockIdx.x + 1) * (256 * kVarBlocks) <= n16)
+    variant_lane<T, V, false>(x, n16, gs, rtab, rt, codes, scales);
+  else
+    variant_lane<T, V, true>(x, n16, gs, rtab, rt, codes, scales);
+}
+
+// x_hat = fl(fl(r * s) / gs); one lane per 16-element block.  The division is the
+// corrected reciprocal of k_dequant: correctly rounded for every dividend any of these
+// formats forms (checked exhaustively on the host) while s/gs lies in [2^-98, 2^96]; IEEE
+// division otherwise.  INT restores come from the same table as the quantizer's.
 template <int V, bool BF16OUT>
 __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
@@ -201,6 +252,11 @@ __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restri
                                                          void* __restrict__ y) {
   using D = Var<V>;
   constexpr int BITS = D::kBits;
+  __shared__ VarRestore rt;
+  if (threadIdx.x < (1u << BITS))
+    rt.r[threadIdx.x ^ (1u << (BITS - 1))] =   // indexed by the two's complement code
+        (float)((int)threadIdx.x - (1 << (BITS - 1))) * (D::kDirect ? 1.0f : D::kCinv);
+  __syncthreads();
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= n16) return;
   Codes16 c{{0u, 0u, 0u}};
@@ -220,26 +276,31 @@ __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restri
   }
   const uint32_t sb = scales[g];
   const float s = e4m3_decode(sb & 0x7Fu);
-  const float gs = *tensor_scale;
+  const float gs = *tensor_scale, rgs = __fdiv_rn(1.0f, gs);
   const bool is_int = !D::kFp || (sb & 0x80u);
-  float out[16];
+  float rv[16], out[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const uint32_t code = get16<BITS>(c, k);
-    float r;
     if (is_int) {
-      const int q = (int)(code << (32 - BITS)) >> (32 - BITS);
-      r = D::kDirect ? (float)q : (float)q * D::kCinv;
+      rv[k] = rt.r[code];
     } else if constexpr (BITS == 4) {
-      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
+      rv[k] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
     } else if constexpr (BITS == 3) {
       const uint32_t mc = code & 3u;
       const float mag = mc ? __uint_as_float((mc + 126u) << 23) : 0.0f;
-      r = (code & 4u) ? -mag : mag;
+      rv[k] = (code & 4u) ? -mag : mag;
     } else {
-      r = fp6_value<0>(code);
+      rv[k] = fp6_value<0>(code);
     }
-    out[k] = __fdiv_rn(r * s, gs);
+  }
+  const float ratio = s * rgs;
+  if (ratio >= 0x1p-98f && ratio <= 0x1p+96f) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) out[k] = div_rs(rv[k] * s, gs, rgs);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) out[k] = __fdiv_rn(rv[k] * s, gs);
   }
   if constexpr (BF16OUT) {
     uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
