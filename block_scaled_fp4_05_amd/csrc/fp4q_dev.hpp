@@ -268,6 +268,40 @@ __device__ __forceinline__ float fp6_value(uint32_t c) {
   return (c & 0x20u) ? -mag : mag;
 }
 
+// The same rounding by gfx950's FP6 converts (v_cvt_scalef32_2xpk16_{fp6,bf6}_f32 with
+// scale 1: nearest-even, saturating at the largest magnitude, sign copied, -0 and tiny
+// negatives to the negative zero code), checked against the oracle's rounding on every
+// grid point, midpoint and its neighbours, signed zeros, huge values and 13 000 random
+// values in an in-bounds probe.  The instruction takes two 16-element vectors and writes
+// 32 six-bit codes, code j at bits 6j of six words, code 2i from element i of the first
+// vector and 2i + 1 from element i of the second; so the elements of two groups g and h
+// (16 each) are handed over as (g0, g2, .., g14, h0, .., h14) and (g1, .., g15, h1, ..,
+// h15), and g's codes land in words 0..2, h's in words 3..5.  The decode writes element j
+// from code j.
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef float f32x32v __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6v __attribute__((ext_vector_type(6)));
+
+template <int FMT>
+__device__ __forceinline__ u32x6v fp6_encode32(const float g[16], const float h[16]) {
+  f32x16v a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = g[2 * i];
+    b[i] = g[2 * i + 1];
+    a[8 + i] = h[2 * i];
+    b[8 + i] = h[2 * i + 1];
+  }
+  if constexpr (FMT == 0) return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+  else return __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, 1.0f);
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x32v fp6_decode32(u32x6v w) {
+  if constexpr (FMT == 0) return __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(w, 1.0f);
+  else return __builtin_amdgcn_cvt_scalef32_pk32_f32_bf6(w, 1.0f);
+}
+
 // 2^(k - 127) for an E8M0 code k: all of 2^-127 .. 2^127 are binary32 values.
 __device__ __forceinline__ float e8m0_value(uint32_t k) { return k ? __uint_as_float(k << 23) : __uint_as_float(0x00400000u); }
 

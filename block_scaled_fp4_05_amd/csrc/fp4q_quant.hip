@@ -1470,12 +1470,11 @@ __global__ __launch_bounds__(256) void k_mxfp6(const T* __restrict__ x, int64_t 
   m = lane_xor_max<1>(m);
   const uint32_t code = e8m0_encode(__fdiv_rn(m, FMT ? 28.0f : 7.5f));
   const float inv = e8m0_value(254u - code);   // 2^(127 - code), exact
-  uint32_t c[16];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) c[k] = fp6_rtn<FMT>(a[k] * inv);
-  const uint32_t w0 = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18) | (c[4] << 24) | (c[5] << 30);
-  const uint32_t w1 = (c[5] >> 2) | (c[6] << 4) | (c[7] << 10) | (c[8] << 16) | (c[9] << 22) | (c[10] << 28);
-  const uint32_t w2 = (c[10] >> 4) | (c[11] << 2) | (c[12] << 8) | (c[13] << 14) | (c[14] << 20) | (c[15] << 26);
+  for (int k = 0; k < 16; ++k) a[k] *= inv;
+  // one convert for the lane's 16 elements (given twice; the second copy is not used)
+  const u32x6v cw = fp6_encode32<FMT>(a, a);
+  const uint32_t w0 = cw[0], w1 = cw[1], w2 = cw[2];
   if (ok) {
     uint32_t* dst = reinterpret_cast<uint32_t*>(codes + g * 12);
     dst[0] = w0;
@@ -1492,17 +1491,18 @@ __global__ __launch_bounds__(256) void k_dequant_mxfp6(const uint8_t* __restrict
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= n16) return;
   const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + g * 12);
-  const uint64_t lo = (uint64_t)src[0] | ((uint64_t)src[1] << 32);
-  const uint32_t hi = src[2];
   const float s = e8m0_value(scales[g >> 1]);
+  u32x6v cw;
+  cw[0] = src[0];
+  cw[1] = src[1];
+  cw[2] = src[2];
+  cw[3] = cw[0];
+  cw[4] = cw[1];
+  cw[5] = cw[2];
+  const f32x32v r = fp6_decode32<FMT>(cw);   // elements 16..31 repeat 0..15
   float v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t c = i < 10 ? (uint32_t)(lo >> (6 * i)) & 63u
-                              : (i == 10 ? (uint32_t)((lo >> 60) | ((uint64_t)hi << 4)) & 63u
-                                         : (hi >> (6 * i - 64)) & 63u);
-    v[i] = fp6_value<FMT>(c) * s;
-  }
+  for (int i = 0; i < 16; ++i) v[i] = r[i] * s;
   if constexpr (BF16OUT) {
     uint32_t o[8];
 #pragma unroll

@@ -137,12 +137,14 @@ __device__ __forceinline__ void variant_block(float (&v)[16], uint32_t sc, const
 #pragma unroll
       for (int k = 0; k < 16; ++k) put16<3>(fc, k, fp3_rtn(v[k], rf[k]));
     } else {
+      // FP6 E2M3 by the hardware convert and its decode (the block given twice)
+      const u32x6v cw = fp6_encode32<0>(v, v);
+      fc.w[0] = cw[0];
+      fc.w[1] = cw[1];
+      fc.w[2] = cw[2];
+      const f32x32v d = fp6_decode32<0>(cw);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t c = fp6_rtn<0>(v[k]);
-        rf[k] = fp6_value<0>(c);
-        put16<6>(fc, k, c);
-      }
+      for (int k = 0; k < 16; ++k) rf[k] = d[k];
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -279,6 +281,14 @@ __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restri
   const float gs = *tensor_scale, rgs = __fdiv_rn(1.0f, gs);
   const bool is_int = !D::kFp || (sb & 0x80u);
   float rv[16], out[16];
+  f32x32v d6;
+  if constexpr (BITS == 6) {
+    u32x6v cw;
+    cw[0] = cw[3] = c.w[0];
+    cw[1] = cw[4] = c.w[1];
+    cw[2] = cw[5] = c.w[2];
+    d6 = fp6_decode32<0>(cw);   // FP6 E2M3 values of the block's codes (elements 16..31 repeat them)
+  }
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const uint32_t code = get16<BITS>(c, k);
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restri
       const float mag = mc ? __uint_as_float((mc + 126u) << 23) : 0.0f;
       rv[k] = (code & 4u) ? -mag : mag;
     } else {
-      rv[k] = fp6_value<0>(code);
+      rv[k] = d6[k];
     }
   }
   const float ratio = s * rgs;
