@@ -1376,10 +1376,11 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
     const int64_t e = e0 + (int64_t)j * 64 * EPL;
     if (e >= n) break;
     float rv[EPL], out[EPL];
-    if (FMT == 3 && (sc[j] & 0x80u)) {
-      const float c67 = 6.0f / 7.0f;
+    if (FMT == 4 || (FMT == 3 && (sc[j] & 0x80u))) {
+      // INT4 restore: fl(q * fl(6/7)) for IF4's flagged blocks, q itself for NVINT4 (FMT 4)
+      const float c = FMT == 4 ? 1.0f : 6.0f / 7.0f;
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) rv[k] = (float)((int)(((cw[j] >> (4 * k)) & 0xFu) ^ 8u) - 8) * c67;
+      for (int k = 0; k < EPL; ++k) rv[k] = (float)((int)(((cw[j] >> (4 * k)) & 0xFu) ^ 8u) - 8) * c;
     } else {
       f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j], 1.0f, 0);
       rv[0] = d[0]; rv[1] = d[1];
@@ -1437,7 +1438,8 @@ void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const 
     case 0: FP4Q_DQ(0); break;
     case 1: FP4Q_DQ(1); break;
     case 2: FP4Q_DQ(2); break;
-    default: FP4Q_DQ(3); break;
+    case 3: FP4Q_DQ(3); break;
+    default: FP4Q_DQ(4); break;   // NVINT4 (the block-format variant), not a public format code
   }
 #undef FP4Q_DQ
 }

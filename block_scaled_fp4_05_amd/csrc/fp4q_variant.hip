@@ -243,10 +243,14 @@ __global__ __launch_bounds__(256) void k_variant(const T* __restrict__ x, int64_
     variant_lane<T, V, true>(x, n16, gs, rtab, rt, codes, scales);
 }
 
-// x_hat = fl(fl(r * s) / gs); one lane per 16-element block.  The division is the
-// corrected reciprocal of k_dequant: correctly rounded for every dividend any of these
-// formats forms (checked exhaustively on the host) while s/gs lies in [2^-98, 2^96]; IEEE
-// division otherwise.  INT restores come from the same table as the quantizer's.
+// x_hat = fl(fl(r * s) / gs) for the 3- and 6-bit formats (the 4-bit ones go through
+// k_dequant).  As in k_dequant a lane takes 8 consecutive elements (half a block) per step
+// and the lanes of a wave consecutive spans, so every store instruction writes one
+// contiguous 1 KiB (bf16) or 2 KiB (fp32); the lane reads its block's packed codes and
+// scale byte (the partner lane reads the same).  The division is the corrected
+// reciprocal of k_dequant: correctly rounded for every dividend any of these formats
+// forms (checked exhaustively on the host) while s/gs lies in [2^-98, 2^96]; IEEE
+// division otherwise.  INT restores come from a table as in the quantizer.
 template <int V, bool BF16OUT>
 __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
@@ -254,77 +258,85 @@ __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restri
                                                          void* __restrict__ y) {
   using D = Var<V>;
   constexpr int BITS = D::kBits;
+  constexpr int STEPS = 4;   // 4 steps of 8 elements: 32 per lane, 2048 per wave
   __shared__ VarRestore rt;
   if (threadIdx.x < (1u << BITS))
     rt.r[threadIdx.x ^ (1u << (BITS - 1))] =   // indexed by the two's complement code
         (float)((int)threadIdx.x - (1 << (BITS - 1))) * (D::kDirect ? 1.0f : D::kCinv);
   __syncthreads();
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= n16) return;
-  Codes16 c{{0u, 0u, 0u}};
-  if constexpr (BITS == 4) {
-    const uint2 w = *reinterpret_cast<const uint2*>(codes + g * 8);
-    c.w[0] = w.x;
-    c.w[1] = w.y;
-  } else if constexpr (BITS == 3) {
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(codes + g * 6);
-    c.w[0] = (uint32_t)src[0] | ((uint32_t)src[1] << 16);
-    c.w[1] = src[2];
-  } else {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + g * 12);
-    c.w[0] = src[0];
-    c.w[1] = src[1];
-    c.w[2] = src[2];
-  }
-  const uint32_t sb = scales[g];
-  const float s = e4m3_decode(sb & 0x7Fu);
+  const int64_t n = n16 * 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t e0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 * 8 * STEPS) + lane * 8;
   const float gs = *tensor_scale, rgs = __fdiv_rn(1.0f, gs);
-  const bool is_int = !D::kFp || (sb & 0x80u);
-  float rv[16], out[16];
-  f32x32v d6;
-  if constexpr (BITS == 6) {
-    u32x6v cw;
-    cw[0] = cw[3] = c.w[0];
-    cw[1] = cw[4] = c.w[1];
-    cw[2] = cw[5] = c.w[2];
-    d6 = fp6_decode32<0>(cw);   // FP6 E2M3 values of the block's codes (elements 16..31 repeat them)
-  }
+  // loads first (clamped addresses), so all of them are in flight together
+  Codes16 c[STEPS];
+  uint32_t sb[STEPS];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const uint32_t code = get16<BITS>(c, k);
-    if (is_int) {
-      rv[k] = rt.r[code];
-    } else if constexpr (BITS == 4) {
-      rv[k] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
-    } else if constexpr (BITS == 3) {
-      const uint32_t mc = code & 3u;
-      const float mag = mc ? __uint_as_float((mc + 126u) << 23) : 0.0f;
-      rv[k] = (code & 4u) ? -mag : mag;
+  for (int j = 0; j < STEPS; ++j) {
+    const int64_t g = min(e0 + (int64_t)j * 512, n - 8) >> 4;
+    c[j].w[0] = c[j].w[1] = c[j].w[2] = 0u;
+    if constexpr (BITS == 3) {
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(codes + g * 6);
+      c[j].w[0] = (uint32_t)src[0] | ((uint32_t)src[1] << 16);
+      c[j].w[1] = src[2];
     } else {
-      rv[k] = d6[k];
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + g * 12);
+      c[j].w[0] = src[0];
+      c[j].w[1] = src[1];
+      c[j].w[2] = src[2];
     }
+    sb[j] = scales[g];
   }
-  const float ratio = s * rgs;
-  if (ratio >= 0x1p-98f && ratio <= 0x1p+96f) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) out[k] = div_rs(rv[k] * s, gs, rgs);
-  } else {
+  for (int j = 0; j < STEPS; ++j) {
+    const int64_t e = e0 + (int64_t)j * 512;
+    if (e >= n) break;
+    const int half = (int)((e >> 3) & 1);
+    const float s = e4m3_decode(sb[j] & 0x7Fu);
+    const bool is_int = !D::kFp || (sb[j] & 0x80u);
+    float rv[8], out[8];
+    f32x32v d6;
+    if constexpr (BITS == 6) {
+      u32x6v cw;
+      cw[0] = cw[3] = c[j].w[0];
+      cw[1] = cw[4] = c[j].w[1];
+      cw[2] = cw[5] = c[j].w[2];
+      d6 = fp6_decode32<0>(cw);   // FP6 E2M3 values of the block's codes (16..31 repeat them)
+    }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) out[k] = __fdiv_rn(rv[k] * s, gs);
-  }
-  if constexpr (BF16OUT) {
-    uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + g * 16);
-    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-    uint32_t o[8];
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t code0 = get16<BITS>(c[j], k), code1 = get16<BITS>(c[j], 8 + k);
+      const uint32_t code = half ? code1 : code0;
+      if (is_int) {
+        rv[k] = rt.r[code];
+      } else if constexpr (BITS == 3) {
+        const uint32_t mc = code & 3u;
+        const float mag = mc ? __uint_as_float((mc + 126u) << 23) : 0.0f;
+        rv[k] = (code & 4u) ? -mag : mag;
+      } else {
+        rv[k] = half ? d6[8 + k] : d6[k];
+      }
+    }
+    const float ratio = s * rgs;
+    if (ratio >= 0x1p-98f && ratio <= 0x1p+96f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{out[2 * i], out[2 * i + 1]}, bf16x2v));
-    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  } else {
-    float4* d = reinterpret_cast<float4*>(static_cast<float*>(y) + g * 16);
+      for (int k = 0; k < 8; ++k) out[k] = div_rs(rv[k] * s, gs, rgs);
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+      for (int k = 0; k < 8; ++k) out[k] = __fdiv_rn(rv[k] * s, gs);
+    }
+    if constexpr (BF16OUT) {
+      typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{out[2 * i], out[2 * i + 1]}, bf16x2v));
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + e) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+      float4* d = reinterpret_cast<float4*>(static_cast<float*>(y) + e);
+      d[0] = make_float4(out[0], out[1], out[2], out[3]);
+      d[1] = make_float4(out[4], out[5], out[6], out[7]);
+    }
   }
 }
 
@@ -353,7 +365,7 @@ void launch_variant(int var, const void* x, int dtype, int64_t rows, int64_t col
 template <int V>
 static void launch_dequant_variant_v(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t n16,
                                      int out_dtype, void* y, hipStream_t st) {
-  const int grid = (int)((n16 + 255) / 256);
+  const int grid = (int)((n16 * 16 + 8191) / 8192);   // 2048 elements per wave, 4 waves
   if (out_dtype == 1) k_dequant_variant<V, true><<<grid, 256, 0, st>>>(codes, scales, ts, n16, y);
   else k_dequant_variant<V, false><<<grid, 256, 0, st>>>(codes, scales, ts, n16, y);
 }
@@ -362,10 +374,12 @@ void launch_dequant_variant(int var, const uint8_t* codes, const uint8_t* scales
                             int64_t rows, int64_t cols, int out_dtype, void* y, hipStream_t st) {
   const int64_t n16 = rows * cols / 16;
   switch (var) {
-    case 0: launch_dequant_variant_v<0>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
-    case 1: launch_dequant_variant_v<1>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+    // the 4-bit formats decode as NVFP4 (Four Over Six: E2M1 on E4M3 scales) and as IF4's
+    // INT4 blocks without the 6/7 factor (NVINT4), in k_dequant's store-coalesced layout
+    case 0: launch_dequant(0, codes, scales, tensor_scale, rows, cols, out_dtype, y, st); break;
+    case 1: launch_dequant(4, codes, scales, tensor_scale, rows, cols, out_dtype, y, st); break;
     case 2: launch_dequant_variant_v<2>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
-    case 3: launch_dequant_variant_v<3>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
+    case 3: launch_dequant(3, codes, scales, tensor_scale, rows, cols, out_dtype, y, st); break;   // IF4
     default: launch_dequant_variant_v<4>(codes, scales, tensor_scale, n16, out_dtype, y, st); break;
   }
 }
