@@ -162,7 +162,7 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <bool BF16OUT>
+template <bool BF16OUT, bool AMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mxfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
     const uint8_t* __restrict__ bs, int M, int N, int K, int tiles_m, int tiles_n, void* __restrict__ cout,
@@ -348,15 +348,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (vec && bc0 + c8 + 8 <= N) {
         const u32x4_g v = *reinterpret_cast<const u32x4_g*>(src);
         *reinterpret_cast<u32x4_g*>(dst) = v;
-        am = max(am, max(max(bf16x2_absmax(v[0]), bf16x2_absmax(v[1])), max(bf16x2_absmax(v[2]), bf16x2_absmax(v[3]))));
+        if constexpr (AMAX)
+          am = max(am, max(max(bf16x2_absmax(v[0]), bf16x2_absmax(v[1])), max(bf16x2_absmax(v[2]), bf16x2_absmax(v[3]))));
       } else {
         for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) {
           dst[x] = src[x];
-          am = max(am, (uint32_t)(src[x] & 0x7FFFu));
+          if constexpr (AMAX) am = max(am, (uint32_t)(src[x] & 0x7FFFu));
         }
       }
     }
-    if (amax) post_amax(am << 16, amax);
+    if constexpr (AMAX) post_amax(am << 16, amax);
     return;
   }
   uint32_t am = 0;   // largest stored fp32 magnitude
@@ -370,13 +371,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int row = m0 + wm * 128 + 32 * i + 8 * (q >> 2) + 4 * fh + (q & 3);
         if (row < M && col < N) {
           static_cast<float*>(cout)[(int64_t)row * N + col] = acc[i][j][q];
-          am = max(am, __float_as_uint(acc[i][j][q]) & 0x7FFFFFFFu);
+          if constexpr (AMAX) am = max(am, __float_as_uint(acc[i][j][q]) & 0x7FFFFFFFu);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (amax) post_amax(am, amax);
+  if constexpr (AMAX) post_amax(am, amax);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -436,7 +437,7 @@ __device__ __forceinline__ float e4m3_byte(uint32_t w, int byte) {
 // gives lane half 0 the row's code word q (elements 8q..8q+7, block q/2) and half 1 the
 // word 8 + q (block 4 + q/2): a lane reads 32 contiguous bytes of codes and one scale
 // word (blocks 4 fh .. 4 fh + 3) per row and step.
-template <bool BF16OUT>
+template <bool BF16OUT, bool AMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ gsa,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ gsb, int M, int N,
@@ -566,15 +567,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (vec && bc0 + c8 + 8 <= N) {
         const u32x4_g v = *reinterpret_cast<const u32x4_g*>(src);
         *reinterpret_cast<u32x4_g*>(dst) = v;
-        am = max(am, max(max(bf16x2_absmax(v[0]), bf16x2_absmax(v[1])), max(bf16x2_absmax(v[2]), bf16x2_absmax(v[3]))));
+        if constexpr (AMAX)
+          am = max(am, max(max(bf16x2_absmax(v[0]), bf16x2_absmax(v[1])), max(bf16x2_absmax(v[2]), bf16x2_absmax(v[3]))));
       } else {
         for (int x = 0; x < 8 && bc0 + c8 + x < N; ++x) {
           dst[x] = src[x];
-          am = max(am, (uint32_t)(src[x] & 0x7FFFu));
+          if constexpr (AMAX) am = max(am, (uint32_t)(src[x] & 0x7FFFu));
         }
       }
     }
-    if (amax) post_amax(am << 16, amax);
+    if constexpr (AMAX) post_amax(am << 16, amax);
     return;
   }
   uint32_t am = 0;   // largest stored fp32 magnitude
@@ -589,12 +591,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (row < M && col < N) {
           const float v = acc[i][j][q] * inv;
           static_cast<float*>(cout)[(int64_t)row * N + col] = v;
-          am = max(am, __float_as_uint(v) & 0x7FFFFFFFu);
+          if constexpr (AMAX) am = max(am, __float_as_uint(v) & 0x7FFFFFFFu);
         }
       }
     }
   }
-  if (amax) post_amax(am, amax);
+  if constexpr (AMAX) post_amax(am, amax);
 }
 
 }  // namespace
@@ -606,7 +608,9 @@ bool launch_gemm_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, 
   if (total > 0x7FFFFFFF) return false;
   uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
   if (ab) k_gemm_amax_zero<<<1, 1, 0, st>>>(ab);
-  auto kern = bf16_out ? k_gemm_mxfp4<true> : k_gemm_mxfp4<false>;
+  // the amax fold only in the instances that report it: the others compile as without it
+  auto kern = bf16_out ? (ab ? k_gemm_mxfp4<true, true> : k_gemm_mxfp4<true, false>)
+                       : (ab ? k_gemm_mxfp4<false, true> : k_gemm_mxfp4<false, false>);
   kern<<<(unsigned)total, 256, 0, st>>>(ac, as, bc, bs, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab);
   return true;
 }
@@ -617,9 +621,10 @@ bool launch_gemm_nvfp4(const uint8_t* ac, const uint8_t* as, const float* gsa, c
   const int tiles_m = (int)((m + kGemmTile - 1) / kGemmTile), tiles_n = (int)((n + kGemmTile - 1) / kGemmTile);
   const int64_t total = (int64_t)tiles_m * tiles_n;
   if (total > 0x7FFFFFFF) return false;
-  auto kern = bf16_out ? k_gemm_nvfp4<true> : k_gemm_nvfp4<false>;
   uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
   if (ab) k_gemm_amax_zero<<<1, 1, 0, st>>>(ab);
+  auto kern = bf16_out ? (ab ? k_gemm_nvfp4<true, true> : k_gemm_nvfp4<true, false>)
+                       : (ab ? k_gemm_nvfp4<false, true> : k_gemm_nvfp4<false, false>);
   kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab,
                                         (tiles2d & 1u) ? 4 : 0, (tiles2d & 2u) ? 4 : 0);
   return true;
