@@ -363,23 +363,6 @@ struct RhtColOp {
   uint32_t k0, k1;
 };
 
-// Output block a (tokens 32a..32a+31 of the chunk) for both column passes p: acc[p] is
-// the 32x32 MFMA block of pass p.  Per output element this is the same chain of eight
-// MFMAs (K-step kk ascending, the same A fragment) as rht_mma_half_b, so all kernels see
-// the same values.
-template <int A>
-__device__ __forceinline__ void rht_mma_block(const RhtB& B, const u32x4 frag[8],
-                                              f32x16 acc[2]) {
-  acc[0] = f32x16{};
-  acc[1] = f32x16{};
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const bf16x8 fa = a_operand(frag, A, kk);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8, B.b[kk][0]), acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8, B.b[kk][1]), acc[1], 0, 0, 0);
-  }
-}
-
 // Where a lane's outputs of one tile go.  Lane (n, hk) quantizes columns 64*slab + n
 // (pass 0) and + 32 (pass 1).  Output block a of a column is 16 code bytes at 16 a of
 // the column's 64-byte span in the tile, lane hk encoding bytes 8 hk..8 hk + 7; after
@@ -533,17 +516,6 @@ __device__ __forceinline__ void rht_store_scales(const RhtTileOut& t) {
   }
 }
 
-// One step of the software pipeline: the MFMAs of the next output block (into `next`)
-// are issued together with the quantization of the current one (from `cur`), so the
-// matrix core and the vector ALUs work at the same time within the wave.
-template <bool SR, int ANEXT>
-__device__ __forceinline__ void rht_pipe_step(const RhtB& B, const u32x4 (&frag)[8],
-                                              f32x16 (&next)[2], const f32x16 (&cur)[2], int a,
-                                              const RhtColOp& o, const RecipTable& rtab, RhtTileOut& t) {
-  rht_mma_block<ANEXT>(B, frag, next);
-  rht_quant_block<SR>(cur, a, o, rtab, t);
-}
-
 template <bool SR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_rht_nvfp4_col(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                        RhtSigns sg, AmaxSource amax,
@@ -559,44 +531,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   make_fragments(sg, true, frag);
   TileWalk w(rows, cols);
   if (!w.valid()) return;
-  // The wave's tiles form one stream of output blocks (four per tile).  The MFMAs of
-  // block b+1 run while block b is quantized; the next tile streams into the wave's LDS
-  // buffer as soon as the current one has been read into registers.
-  rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
+  // Per tile: wait for its loads, read its B operands, start the next tile's loads into
+  // the same buffer, then two halves of MFMAs (output blocks 2H, 2H + 1 of both column
+  // passes), each followed by the quantization of its two blocks.  The quantization
+  // waits for its half's MFMAs; the wave's SIMD partner keeps the vector ALUs busy
+  // meanwhile (the two waves' VALU and MFMA work overlap).
   RhtB B;
-  rht_wait_loads();
-  rht_read_b(st, B);
-  rht_wait_lds();
-  {
-    TileWalk nw = w;
-    nw.next();
-    if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
-  }
-  f32x16 acc0[2], acc1[2];
-  rht_mma_block<0>(B, frag, acc0);
-  for (;;) {
+  rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
+  for (; w.valid(); w.next()) {
+    rht_wait_loads();
+    rht_read_b(st, B);
+    rht_wait_lds();
+    {
+      TileWalk nw = w;
+      nw.next();
+      if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
+    }
     RhtTileOut t = rht_tile_out(w.chunk, w.slab, op);
-    rht_pipe_step<SR, 1>(B, frag, acc1, acc0, 0, op, rtab, t);
-    rht_pipe_step<SR, 2>(B, frag, acc0, acc1, 1, op, rtab, t);
-    rht_pipe_step<SR, 3>(B, frag, acc1, acc0, 2, op, rtab, t);
-    // the last block of this tile overlaps the first MFMAs of the next tile
-    TileWalk nw = w;
-    nw.next();
-    const bool more = nw.valid();
-    if (more) {
-      rht_wait_loads();
-      rht_read_b(st, B);    // the MFMAs above have read the previous B operands
-      rht_wait_lds();
-      TileWalk nnw = nw;
-      nnw.next();
-      if (nnw.valid()) rht_issue(x, cols, nnw.chunk * 128, nnw.slab * 64, st);
-      rht_pipe_step<SR, 0>(B, frag, acc0, acc1, 3, op, rtab, t);
-    } else {
-      rht_quant_block<SR>(acc1, 3, op, rtab, t);
+    f32x16 acc[2][2];
+    rht_mma_half_b<0>(B, frag, acc);
+    {
+      const f32x16 b0[2] = {acc[0][0], acc[1][0]};
+      rht_quant_block<SR>(b0, 0, op, rtab, t);
+      const f32x16 b1[2] = {acc[0][1], acc[1][1]};
+      rht_quant_block<SR>(b1, 1, op, rtab, t);
+    }
+    rht_mma_half_b<1>(B, frag, acc);
+    {
+      const f32x16 b2[2] = {acc[0][0], acc[1][0]};
+      rht_quant_block<SR>(b2, 2, op, rtab, t);
+      const f32x16 b3[2] = {acc[0][1], acc[1][1]};
+      rht_quant_block<SR>(b3, 3, op, rtab, t);
     }
     rht_store_scales(t);
-    if (!more) break;
-    w = nw;
   }
 }
 
