@@ -311,21 +311,22 @@ def gemm_mxfp4(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b
     return c, cabs
 
 
-def gemm_nvfp4(a_codes, a_scales, gs_a, b_codes, b_scales, gs_b, tiles: int = 0):
-    """C = A B^T over two row-wise NVFP4 operands with tensor scales gs_a, gs_b:
+def gemm_nvfp4(a_codes, a_scales, gs_a, b_codes, b_scales, gs_b, flags: int = 0):
+    """C = A B^T over two row-wise NVFP4 (or IF4) operands with tensor scales gs_a, gs_b:
     (sum of exact products r s r' s') / (gs_a gs_b).  Returns (C, sum |products| / same).
-    ``tiles`` bit 0 / bit 1 marks A / B as carrying 16x16 scale tiles [rows/16][k/16]."""
+    ``flags`` bit 0 / bit 1 marks A / B as carrying 16x16 scale tiles [rows/16][k/16];
+    bit 2 / bit 3 marks A / B as IF4, whose INT4 blocks restore as fl(q fl(6/7)) s."""
     a_codes, a_scales = np.ascontiguousarray(a_codes), np.ascontiguousarray(a_scales)
     b_codes, b_scales = np.ascontiguousarray(b_codes), np.ascontiguousarray(b_scales)
     m, k = a_codes.shape[0], a_codes.shape[1] * 2
     n = b_codes.shape[0]
-    ra = m // 16 if tiles & 1 else m
-    rb = n // 16 if tiles & 2 else n
+    ra = m // 16 if flags & 1 else m
+    rb = n // 16 if flags & 2 else n
     assert b_codes.shape == (n, k // 2) and a_scales.shape == (ra, k // 16) and b_scales.shape == (rb, k // 16)
     c = np.zeros((m, n), dtype=np.float64)
     cabs = np.zeros((m, n), dtype=np.float64)
     lib().ora_gemm_nvfp4(_ptr(a_codes), _ptr(a_scales), float(gs_a), _ptr(b_codes), _ptr(b_scales), float(gs_b),
-                         m, n, k, int(tiles), _ptr(c), _ptr(cabs))
+                         m, n, k, int(flags), _ptr(c), _ptr(cabs))
     return c, cabs
 
 

@@ -626,23 +626,34 @@ void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
  * quantization produces) the binary64 sum are exact; the one division by the binary64
  * product gs_a * gs_b (exact: two 24-bit significands) rounds once.  cabs is the sum of
  * |products| over the same divisor.  Scale row strides: k/16 bytes. */
+/* One element of a GEMM operand, r * s in binary64 (exact): an E2M1 value times its
+ * block's E4M3 scale or, in an IF4 operand's INT4 block (scale bit 7 set
+ * [IF "2. 提案手法：IF4"]), the 6/7-rule restore fl(q * fl(6/7)) times the scale. */
+static double gemm_elem(const uint8_t* codes, uint8_t scale, int if4, int64_t k, int64_t row, int64_t t)
+{
+    const uint8_t nib = get_nibble(codes, k, row, t);
+    if (if4 && (scale & 0x80))
+        return (double)ora_int4_decode(nib) * (double)ora_e4m3_decode((uint8_t)(scale & 0x7F));
+    return (double)ora_e2m1_decode(nib) * (double)ora_e4m3_decode(scale);
+}
+
 void ora_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float gs_a, const uint8_t* b_codes,
-                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, int tiles,
+                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, int flags,
                     double* c, double* cabs)
 {
-    /* tiles bit 0 / bit 1: A / B holds one scale per 16x16 tile [NV "2D scaling"], so
-     * element (i, t) takes the scale of tile (i / 16, t / 16) instead of block (i, t / 16). */
+    /* flags bit 0 / bit 1: A / B holds one scale per 16x16 tile [NV "2D scaling"], so
+     * element (i, t) takes the scale of tile (i / 16, t / 16) instead of block (i, t / 16);
+     * bit 2 / bit 3: A / B is IF4 (1x16 blocks whose flagged scales mark INT4 blocks). */
     const double g = (double)gs_a * (double)gs_b;
+    const int if4_a = (flags >> 2) & 1, if4_b = (flags >> 3) & 1;
     for (int64_t i = 0; i < m; ++i) {
-        const int64_t sa = (tiles & 1) ? i / 16 : i;
+        const int64_t sa = (flags & 1) ? i / 16 : i;
         for (int64_t j = 0; j < n; ++j) {
-            const int64_t sb = (tiles & 2) ? j / 16 : j;
+            const int64_t sb = (flags & 2) ? j / 16 : j;
             double acc = 0.0, mag = 0.0;
             for (int64_t t = 0; t < k; ++t) {
-                double av = (double)ora_e2m1_decode(get_nibble(a_codes, k, i, t)) *
-                            (double)ora_e4m3_decode(a_scales[sa * (k / 16) + t / 16]);
-                double bv = (double)ora_e2m1_decode(get_nibble(b_codes, k, j, t)) *
-                            (double)ora_e4m3_decode(b_scales[sb * (k / 16) + t / 16]);
+                double av = gemm_elem(a_codes, a_scales[sa * (k / 16) + t / 16], if4_a, k, i, t);
+                double bv = gemm_elem(b_codes, b_scales[sb * (k / 16) + t / 16], if4_b, k, j, t);
                 acc += av * bv;
                 mag += fabs(av * bv);
             }

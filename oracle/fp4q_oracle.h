@@ -45,8 +45,9 @@ void ora_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, float 
 
 void ora_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                     const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, double* c, double* cabs);
+/* flags: bit 0 / 1 A / B has 16x16 scale tiles; bit 2 / 3 A / B is IF4. */
 void ora_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, float gs_a, const uint8_t* b_codes,
-                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, int tiles,
+                    const uint8_t* b_scales, float gs_b, int64_t m, int64_t n, int64_t k, int flags,
                     double* c, double* cabs);
 float ora_fp6_decode(int fmt, uint8_t code);
 uint8_t ora_fp6_rtn(int fmt, float v);

@@ -175,6 +175,8 @@ static void gemms(int64_t m, int64_t n, int64_t k)
     ora_gemm_mxfp4(ac, as, bc, bs, m, n, k, c, cabs);   /* reads the first k/32 scales per row */
     ora_gemm_mxfp4(ac, as, bc, bs, m, n, k, c, NULL);
     ora_gemm_nvfp4(ac, as, 0.75f, bc, bs, 3.0f, m, n, k, 0, c, cabs);
+    ora_gemm_nvfp4(ac, as, 0.75f, bc, bs, 3.0f, m, n, k, 12, c, cabs);   /* IF4 x IF4: flagged scales */
+    ora_gemm_nvfp4(ac, as, 0.75f, bc, bs, 3.0f, m, n, k, 4, c, NULL);
     if (m % 16 == 0 && n % 16 == 0) {
         /* 16x16 tiles: exact-size tile arrays, so a read past [rows/16][k/16] is caught */
         uint8_t* ta = xmalloc((size_t)(m / 16 * (k / 16)));

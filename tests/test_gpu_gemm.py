@@ -211,7 +211,7 @@ def test_nvfp4_gemm_with_16x16_scale_tiles(shape, tiles, bf16):
     ga, gb = np.float32(3.0), np.float32(0.375)
     print(f"nvfp4 gemm tiles={tiles} m={m} n={n} k={k} bf16={bf16}", flush=True)
     got = _nv_gemm(ac, as_, ga, bc, bs, gb, torch.bfloat16 if bf16 else torch.float32, tiles)
-    exact, cabs = oracle.gemm_nvfp4(ac, as_, ga, bc, bs, gb, tiles=tiles)
+    exact, cabs = oracle.gemm_nvfp4(ac, as_, ga, bc, bs, gb, flags=tiles)
     _nv_check(got, exact, cabs, k, bf16)
 
 
@@ -238,7 +238,7 @@ def test_nvfp4_forward_and_dgrad_with_2d_weight_end_to_end():
                       qwt["tensor_scale"], scale_tiles=B.TILES_B)
     for got, (a, b) in ((y, (qx, qw)), (dx, (qd, qwt))):
         exact, cabs = oracle.gemm_nvfp4(h(a["row_codes"]), h(a["row_scales"]), float(h(a["tensor_scale"])[0]),
-                                        h(b["codes"]), h(b["scales"]), float(h(b["tensor_scale"])[0]), tiles=2)
+                                        h(b["codes"]), h(b["scales"]), float(h(b["tensor_scale"])[0]), flags=2)
         _nv_check(got.cpu().numpy().astype(np.float64), exact, cabs, a["row_codes"].shape[1] * 2)
 
 

@@ -175,7 +175,7 @@ def test_nvfp4_gemm_with_tiled_operands_brute_force_with_exact_rationals():
         ac, as_ = (_nv_tiled_operand if tiles & 1 else _nv_operand)(rng, m, k)
         bc, bs = (_nv_tiled_operand if tiles & 2 else _nv_operand)(rng, n, k)
         gs_a, gs_b = np.float32(3.5), np.float32(0.75)
-        c, _ = oracle.gemm_nvfp4(ac, as_, gs_a, bc, bs, gs_b, tiles=tiles)
+        c, _ = oracle.gemm_nvfp4(ac, as_, gs_a, bc, bs, gs_b, flags=tiles)
         g = Fraction(float(gs_a)) * Fraction(float(gs_b))
         for i in (0, 15, 16, 31):
             for j in (0, 7, 15):
@@ -190,10 +190,10 @@ def test_nvfp4_gemm_tiled_equals_row_blocks_with_replicated_tile_scales():
     m, n, k = 48, 32, 128
     ac, ast = _nv_tiled_operand(rng, m, k)
     bc, bst = _nv_tiled_operand(rng, n, k)
-    c2, cabs2 = oracle.gemm_nvfp4(ac, ast, 2.0, bc, bst, 5.0, tiles=3)
+    c2, cabs2 = oracle.gemm_nvfp4(ac, ast, 2.0, bc, bst, 5.0, flags=3)
     c1, cabs1 = oracle.gemm_nvfp4(ac, np.repeat(ast, 16, axis=0), 2.0, bc, np.repeat(bst, 16, axis=0), 5.0)
     assert np.array_equal(c2, c1) and np.array_equal(cabs2, cabs1)
-    c3, _ = oracle.gemm_nvfp4(ac, ast, 2.0, bc, np.repeat(bst, 16, axis=0), 5.0, tiles=1)
+    c3, _ = oracle.gemm_nvfp4(ac, ast, 2.0, bc, np.repeat(bst, 16, axis=0), 5.0, flags=1)
     assert np.array_equal(c3, c1)
 
 
@@ -202,7 +202,7 @@ def test_nvfp4_gemm_tiled_equals_matmul_of_the_2d_dequantization():
     m, n, k = 32, 64, 256
     ac, as_ = _nv_operand(rng, m, k)
     bc, bs = _nv_tiled_operand(rng, n, k)
-    c, _ = oracle.gemm_nvfp4(ac, as_, 1.0, bc, bs, 1.0, tiles=2)
+    c, _ = oracle.gemm_nvfp4(ac, as_, 1.0, bc, bs, 1.0, flags=2)
     a = oracle.dequantize(0, ac, as_, 1.0, m, k).astype(np.float64)
     b = oracle.dequantize(1, bc, bs, 1.0, n, k).astype(np.float64)
     assert np.array_equal(c, a @ b.T)
@@ -217,12 +217,95 @@ def test_nvfp4_forward_and_dgrad_with_one_2d_weight_quantization():
     dy = si.weight(m, n, seed=43, std=1.0)
     xc, xs, gx = oracle.quantize_nvfp4(x)
     wc, ws, gw = oracle.quantize_nvfp4_2d(w)
-    y, _ = oracle.gemm_nvfp4(xc, xs, gx, wc, ws, gw, tiles=2)
+    y, _ = oracle.gemm_nvfp4(xc, xs, gx, wc, ws, gw, flags=2)
     ref = x.astype(np.float64) @ w.astype(np.float64).T
     assert 0.01 < np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.15
     wtc, wts, gwt = oracle.quantize_nvfp4_2d(np.ascontiguousarray(w.T))
     assert np.array_equal(wts, ws.T) and gwt == gw
     dc, ds, gd = oracle.quantize_nvfp4(dy)
-    dx, _ = oracle.gemm_nvfp4(dc, ds, gd, wtc, wts, gwt, tiles=2)
+    dx, _ = oracle.gemm_nvfp4(dc, ds, gd, wtc, wts, gwt, flags=2)
     ref = dy.astype(np.float64) @ w.astype(np.float64)
     assert 0.01 < np.linalg.norm(dx - ref) / np.linalg.norm(ref) < 0.15
+
+
+# --- IF4 operands -------------------------------------------------------------------
+
+def _if4_operand(rng, rows, k, int_share=0.5):
+    """Random codes and E4M3 scales with the INT4 flag (bit 7) on about int_share of the blocks."""
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, size=(rows, k // 16), dtype=np.uint8)
+    flags = (rng.random(size=scales.shape) < int_share).astype(np.uint8) << 7
+    return codes, scales | flags
+
+
+def _if4_exact(codes, scales, r, t):
+    """Element (r, t) of an IF4 operand as an exact rational, computed apart from the C:
+    an INT4 block restores q as the float32 product fl(q * fl(6/7)) (numpy's float32
+    multiply), scaled by the E4M3 value of the scale byte without its flag bit."""
+    byte = int(codes[r, t // 2])
+    nib = (byte >> 4) if (t & 1) else (byte & 15)
+    sc = int(scales[r, t // 16])
+    if sc & 0x80:
+        q = nib - 16 if nib >= 8 else nib
+        u = np.float32(q) * np.float32(6.0 / 7.0)
+        return Fraction(float(u)) * _e4m3_exact(sc & 0x7F)
+    return _e2m1_exact(nib) * _e4m3_exact(sc)
+
+
+def test_if4_gemm_brute_force_with_exact_rationals():
+    """IF4 x NVFP4, NVFP4 x IF4 and IF4 x IF4 (flags 4, 8, 12): every product is exact in
+    binary64 (at most 24 + 4 bits times 6 or 28 bits), but with INT4 restores the running
+    sum no longer fits 53 bits, so C is the exact rational sum within the summation bound
+    (k + 1) 2^-53 sum |products| (k additions and the division by gs_a gs_b); negative
+    INT4 codes (nibbles 8..15) and both block kinds occur in every row."""
+    rng = np.random.default_rng(61)
+    m, n, k = 3, 4, 96
+    for flags in (4, 8, 12):
+        ac, as_ = (_if4_operand if flags & 4 else _nv_operand)(rng, m, k)
+        bc, bs = (_if4_operand if flags & 8 else _nv_operand)(rng, n, k)
+        gs_a, gs_b = np.float32(11.5), np.float32(0.3125)
+        c, cabs = oracle.gemm_nvfp4(ac, as_, gs_a, bc, bs, gs_b, flags=flags)
+        va = (lambda r, t: _if4_exact(ac, as_, r, t)) if flags & 4 else \
+            (lambda r, t: _e2m1_exact(((int(ac[r, t // 2]) >> 4) if t & 1 else int(ac[r, t // 2]) & 15)) *
+             _e4m3_exact(int(as_[r, t // 16])))
+        vb = (lambda r, t: _if4_exact(bc, bs, r, t)) if flags & 8 else \
+            (lambda r, t: _e2m1_exact(((int(bc[r, t // 2]) >> 4) if t & 1 else int(bc[r, t // 2]) & 15)) *
+             _e4m3_exact(int(bs[r, t // 16])))
+        g = Fraction(float(gs_a)) * Fraction(float(gs_b))
+        for i in range(m):
+            for j in range(n):
+                exact = sum(va(i, t) * vb(j, t) for t in range(k)) / g
+                mag = sum(abs(va(i, t) * vb(j, t)) for t in range(k)) / g
+                bound = (k + 1) * mag * Fraction(1, 2 ** 53)
+                assert abs(Fraction(c[i, j]) - exact) <= bound, (flags, i, j)
+                assert abs(Fraction(cabs[i, j]) - mag) <= bound
+
+
+def test_if4_gemm_without_int4_blocks_is_the_nvfp4_product():
+    rng = np.random.default_rng(62)
+    m, n, k = 17, 21, 256
+    ac, as_ = _if4_operand(rng, m, k, int_share=0.0)
+    bc, bs = _if4_operand(rng, n, k, int_share=0.0)
+    ref, ref_abs = oracle.gemm_nvfp4(ac, as_, 3.0, bc, bs, 7.0)
+    for flags in (4, 8, 12):
+        c, cabs = oracle.gemm_nvfp4(ac, as_, 3.0, bc, bs, 7.0, flags=flags)
+        assert np.array_equal(c, ref) and np.array_equal(cabs, ref_abs)
+
+
+def test_if4_gemm_of_quantized_gaussians_tracks_the_float_product():
+    """Y = X W^T on the oracle's IF4 quantization of both operands tracks the float
+    product at least as closely as NVFP4 does (IF4 picks the smaller block error)."""
+    m, n, k = 40, 48, 1024
+    x = si.weight(m, k, seed=63, std=1.0)
+    w = si.weight(n, k, seed=64, std=0.02)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    xc, xs, gx = oracle.quantize_if4(x)
+    wc, ws, gw = oracle.quantize_if4(w)
+    assert (xs & 0x80).any() and (ws & 0x80).any()
+    c, _ = oracle.gemm_nvfp4(xc, xs, gx, wc, ws, gw, flags=12)
+    rel_if4 = np.linalg.norm(c - ref) / np.linalg.norm(ref)
+    nc, ns, gn = oracle.quantize_nvfp4(x)
+    vc, vs, gv = oracle.quantize_nvfp4(w)
+    c_nv, _ = oracle.gemm_nvfp4(nc, ns, gn, vc, vs, gv)
+    rel_nv = np.linalg.norm(c_nv - ref) / np.linalg.norm(ref)
+    assert 0.005 < rel_if4 < 0.15 and rel_if4 <= rel_nv * 1.02, (rel_if4, rel_nv)
