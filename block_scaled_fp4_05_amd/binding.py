@@ -221,13 +221,13 @@ def fp4q_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, m, n, k, out_dt, c, am
         _p(a_codes), _p(a_scales), _p(b_codes), _p(b_scales), m, n, k, out_dt, _p(c), _p(amax), _s(stream)))
 
 
-TILES_A, TILES_B = 1, 2
+TILES_A, TILES_B, IF4_A, IF4_B = 1, 2, 4, 8
 
 
-def fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, scale_tiles, out_dt, c, amax=None,
+def fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, operand_flags, out_dt, c, amax=None,
                     stream=None) -> int:
     return _check("fp4q_gemm_nvfp4", lib().fp4q_gemm_nvfp4(
-        _p(a_codes), _p(a_scales), _p(a_ts), _p(b_codes), _p(b_scales), _p(b_ts), m, n, k, scale_tiles, out_dt,
+        _p(a_codes), _p(a_scales), _p(a_ts), _p(b_codes), _p(b_scales), _p(b_ts), m, n, k, operand_flags, out_dt,
         _p(c), _p(amax), _s(stream)))
 
 
@@ -362,13 +362,13 @@ def gemm_mxfp4(a: dict, b: dict, out_dtype=torch.float32, amax: torch.Tensor | N
 
 
 def gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, out_dtype=torch.float32,
-               amax: torch.Tensor | None = None, scale_tiles: int = 0, stream=None) -> torch.Tensor:
-    """C = A B^T / (gs_a gs_b) for two row-wise NVFP4 operands (codes, scales, tensor scale);
-    ``scale_tiles`` marks operands with 16x16 scale tiles (TILES_A, TILES_B); ``amax`` as for
-    gemm_mxfp4."""
+               amax: torch.Tensor | None = None, operand_flags: int = 0, stream=None) -> torch.Tensor:
+    """C = A B^T / (gs_a gs_b) for two row-wise NVFP4 or IF4 operands (codes, scales, tensor
+    scale); ``operand_flags`` marks operands with 16x16 scale tiles (TILES_A, TILES_B) and IF4
+    operands (IF4_A, IF4_B); ``amax`` as for gemm_mxfp4."""
     m, n, k = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
     c = torch.empty(m, n, dtype=out_dtype, device=a_codes.device)
-    fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, scale_tiles, _dt(c), c, amax, stream)
+    fp4q_gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, m, n, k, operand_flags, _dt(c), c, amax, stream)
     return c
 
 

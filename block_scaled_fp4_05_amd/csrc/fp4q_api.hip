@@ -331,10 +331,14 @@ fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, con
 
 fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale, int64_t m,
-                            int64_t n, int64_t k, unsigned scale_tiles, fp4q_dtype out_dt, void* c, float* amax,
+                            int64_t n, int64_t k, unsigned operand_flags, fp4q_dtype out_dt, void* c, float* amax,
                             hipStream_t stream) {
   if (!a_codes || !a_scales || !a_tensor_scale || !b_codes || !b_scales || !b_tensor_scale || !c) return FP4Q_E_NULL;
-  if (!valid_dtype(out_dt) || (scale_tiles & ~3u) != 0) return FP4Q_E_ARG;
+  const unsigned scale_tiles = operand_flags & 3u;
+  if (!valid_dtype(out_dt) || (operand_flags & ~15u) != 0 ||
+      ((operand_flags & FP4Q_TILES_A) && (operand_flags & FP4Q_IF4_A)) ||
+      ((operand_flags & FP4Q_TILES_B) && (operand_flags & FP4Q_IF4_B)))
+    return FP4Q_E_ARG;
   const int64_t lim = (int64_t)1 << 31;
   if (m <= 0 || n <= 0 || k < 128 || k % 128 != 0 || m >= lim || n >= lim || k > ((int64_t)1 << 25))
     return FP4Q_E_SHAPE;
@@ -344,7 +348,7 @@ fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, con
       !aligned4(a_tensor_scale) || !aligned4(b_tensor_scale) || !aligned4(amax))
     return FP4Q_E_ALIGN;
   if (!fp4q::launch_gemm_nvfp4(a_codes, a_scales, a_tensor_scale, b_codes, b_scales, b_tensor_scale, m, n, k,
-                               out_dt == FP4Q_BF16, c, amax, scale_tiles, stream))
+                               out_dt == FP4Q_BF16, c, amax, operand_flags, stream))
     return FP4Q_E_SHAPE;
   return after_launch();
 }

@@ -431,13 +431,49 @@ __device__ __forceinline__ float e4m3_byte(uint32_t w, int byte) {
   }
 }
 
+// IF4 operands [IF "2. 提案手法：IF4"]: a block whose scale byte has bit 7 set holds
+// two's-complement INT4 codes q, restored as fl(q fl(6/7)), times the E4M3 scale of the
+// byte's low seven bits.  Such an element e = fl(fl(q fl(6/7)) s) has up to 24
+// significant bits, more than bf16 holds, so the MFMA takes it in two parts, hi = bf16(e)
+// and lo = bf16(e - hi) (e - hi is exact in fp32), and the kernel issues a second MFMA
+// with the lo parts: hi + lo is within (2^-16 + 2^-24) |e| of the restore times s (two
+// bf16 roundings of at most 2^-8 each, after e's fp32 rounding), and every product of
+// parts is exact in fp32.  E2M1 blocks of an IF4 operand decode exactly as above with
+// lo = 0.  With both operands IF4 the lo x lo products (at most about 2^-16 of the
+// product) are left out.
+constexpr float kSixSevenths = 6.0f / 7.0f;   // fl(6/7)
+
+template <bool LO>
+__device__ __forceinline__ bf16x8_t if4_decode(uint32_t w, uint32_t sb) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)(sb & 0x7Fu), 0);
+  if (!(sb & 0x80u)) {
+    if constexpr (LO) return __builtin_bit_cast(bf16x8_t, u32x4_g{0u, 0u, 0u, 0u});
+    else return nv_decode(w, s);
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int q = (int)(w << (28 - 8 * k - 4 * e)) >> 28;   // element 2k + e, sign-extended
+      const float v = ((float)q * kSixSevenths) * s;
+      const uint32_t hb = bf16_rne(v);
+      h[e] = LO ? (uint32_t)bf16_rne(v - __uint_as_float(hb << 16)) : hb;
+    }
+    o[k] = h[0] | (h[1] << 16);
+  }
+  return __builtin_bit_cast(bf16x8_t, u32x4_g{o[0], o[1], o[2], o[3]});
+}
+
 // C = (A B^T) / (gs_a gs_b).  v_mfma_f32_32x32x16_bf16 takes, per lane, eight
 // consecutive K elements of row l % 32 in its half l / 32 of the instruction's 16; K
 // order inside a step is free as long as A and B agree, so MFMA q (0..7) of a step
 // gives lane half 0 the row's code word q (elements 8q..8q+7, block q/2) and half 1 the
 // word 8 + q (block 4 + q/2): a lane reads 32 contiguous bytes of codes and one scale
 // word (blocks 4 fh .. 4 fh + 3) per row and step.
-template <bool BF16OUT, bool AMAX>
+// IF4 bit 0 / bit 1: A / B is an IF4 operand.
+template <bool BF16OUT, bool AMAX, int IF4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_nvfp4(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ gsa,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ gsb, int M, int N,
@@ -530,13 +566,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       bf16x8_t fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fa[i] = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
-        fb[i] = nv_decode(rb[i][q >> 2][q & 3], e4m3_byte(wb[i], q >> 1));
+        if constexpr (IF4 & 1) fa[i] = if4_decode<false>(ra[i][q >> 2][q & 3], (wa[i] >> (8 * (q >> 1))) & 0xFFu);
+        else fa[i] = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
+        if constexpr (IF4 & 2) fb[i] = if4_decode<false>(rb[i][q >> 2][q & 3], (wb[i] >> (8 * (q >> 1))) & 0xFFu);
+        else fb[i] = nv_decode(rb[i][q >> 2][q & 3], e4m3_byte(wb[i], q >> 1));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      if constexpr (IF4 & 2) {   // hi(A) x lo(B)
+        bf16x8_t fl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fl[j] = if4_decode<true>(rb[j][q >> 2][q & 3], (wb[j] >> (8 * (q >> 1))) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fl[j], acc[i][j], 0, 0, 0);
+      }
+      if constexpr (IF4 & 1) {   // lo(A) x hi(B)
+        bf16x8_t fl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fl[i] = if4_decode<true>(ra[i][q >> 2][q & 3], (wa[i] >> (8 * (q >> 1))) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], fb[j], acc[i][j], 0, 0, 0);
+      }
     }
   }
   wait_vm<0>();   // the loads issued past k land before anything reuses LDS
@@ -615,18 +673,27 @@ bool launch_gemm_mxfp4(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, 
   return true;
 }
 
+template <bool BF16OUT, bool AMAX>
+static auto nvfp4_kernel(unsigned if4) {
+  return if4 == 0 ? k_gemm_nvfp4<BF16OUT, AMAX, 0>
+       : if4 == 1 ? k_gemm_nvfp4<BF16OUT, AMAX, 1>
+       : if4 == 2 ? k_gemm_nvfp4<BF16OUT, AMAX, 2>
+                  : k_gemm_nvfp4<BF16OUT, AMAX, 3>;
+}
+
 bool launch_gemm_nvfp4(const uint8_t* ac, const uint8_t* as, const float* gsa, const uint8_t* bc, const uint8_t* bs,
                        const float* gsb, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c, float* amax,
-                       unsigned tiles2d, hipStream_t st) {
+                       unsigned flags, hipStream_t st) {
   const int tiles_m = (int)((m + kGemmTile - 1) / kGemmTile), tiles_n = (int)((n + kGemmTile - 1) / kGemmTile);
   const int64_t total = (int64_t)tiles_m * tiles_n;
   if (total > 0x7FFFFFFF) return false;
   uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
   if (ab) k_gemm_amax_zero<<<1, 1, 0, st>>>(ab);
-  auto kern = bf16_out ? (ab ? k_gemm_nvfp4<true, true> : k_gemm_nvfp4<true, false>)
-                       : (ab ? k_gemm_nvfp4<false, true> : k_gemm_nvfp4<false, false>);
+  const unsigned if4 = (flags >> 2) & 3u;
+  auto kern = bf16_out ? (ab ? nvfp4_kernel<true, true>(if4) : nvfp4_kernel<true, false>(if4))
+                       : (ab ? nvfp4_kernel<false, true>(if4) : nvfp4_kernel<false, false>(if4));
   kern<<<(unsigned)total, 256, 0, st>>>(ac, as, gsa, bc, bs, gsb, (int)m, (int)n, (int)k, tiles_m, tiles_n, c, ab,
-                                        (tiles2d & 1u) ? 4 : 0, (tiles2d & 2u) ? 4 : 0);
+                                        (flags & 1u) ? 4 : 0, (flags & 2u) ? 4 : 0);
   return true;
 }
 

@@ -115,9 +115,10 @@ bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const ui
                        const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,
                        float* amax, hipStream_t st);
 // NVFP4 1x16 GEMM C = A B^T / (gs_a gs_b) on the bf16 MFMA -- fp4q_gemm.hip.  k % 128 == 0.
-// tiles2d bit 0 / bit 1: A / B carries 16x16 scale tiles ([rows/16][k/16]) instead of 1x16.
+// flags bit 0 / bit 1: A / B carries 16x16 scale tiles ([rows/16][k/16]) instead of 1x16;
+// bit 2 / bit 3: A / B is IF4 (scale bit 7 marks INT4 blocks).
 bool launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,
                        const uint8_t* b_scales, const float* b_ts, int64_t m, int64_t n, int64_t k, bool bf16_out,
-                       void* c, float* amax, unsigned tiles2d, hipStream_t st);
+                       void* c, float* amax, unsigned flags, hipStream_t st);
 
 }  // namespace fp4q

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 9
+#define FP4Q_ABI_VERSION 10
 
 typedef enum {
     FP4Q_OK = 0,
@@ -323,19 +323,32 @@ fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
  * is decoded exactly to bf16 and multiplied on the bf16 MFMA with fp32 accumulation;
  * the sums are multiplied by fl(1 / fl(gs_a gs_b)).
  *   out_dt FP4Q_F32: float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
- *   scale_tiles  0, or FP4Q_TILES_A / FP4Q_TILES_B (or both): that operand carries NVFP4
- *          16x16 scales as fp4q_quantize_nvfp4_2d writes them [NV "2D scaling"], one E4M3
- *          byte per 16x16 tile, [rows/16][k/16] (rows % 16 == 0), e.g. the weight W as B
- *          in Y = X W^T.  For W^T (the data-gradient product) pass codes_t and the
+ *   operand_flags  0 or an OR of:
+ *     FP4Q_TILES_A / FP4Q_TILES_B: that operand carries NVFP4 16x16 scales as
+ *          fp4q_quantize_nvfp4_2d writes them [NV "2D scaling"], one E4M3 byte per
+ *          16x16 tile, [rows/16][k/16] (rows % 16 == 0), e.g. the weight W as B in
+ *          Y = X W^T.  For W^T (the data-gradient product) pass codes_t and the
  *          transposed tile array: quantizing W^T gives exactly those codes and scales.
- * Shapes and amax as fp4q_gemm_mxfp4.  IF4 operands are not accepted (an INT4 block's
- * restore fl(q * fl(6/7)) times its scale is not exact in the bf16 operands).
+ *     FP4Q_IF4_A / FP4Q_IF4_B: that operand is IF4 as fp4q_quantize_if4 writes it
+ *          [IF "2. 提案手法：IF4"]: a scale byte with bit 7 set marks an INT4 block whose
+ *          element is fl(q * fl(6/7)) * s (q the two's-complement nibble, s the E4M3 value
+ *          of the low seven bits).  Such an element e has up to 24 significant bits; the
+ *          MFMA takes it as hi + lo, hi = bf16(e) and lo = bf16(e - hi), with a second
+ *          MFMA for the lo parts (twice the MFMA work for one IF4 operand, three times for
+ *          two): hi + lo is within (2^-16 + 2^-24) |e| of the exact element (bf16
+ *          rounding twice, after the fp32 rounding of e), so one IF4 operand puts each
+ *          product within that of the exact one; with both IF4 the lo x lo product (at
+ *          most about 2^-16 of the product) is left out, about 3 * 2^-16 in all.
+ *     TILES and IF4 on the same operand: FP4Q_E_ARG (IF4 blocks are 1x16).
+ * Shapes and amax as fp4q_gemm_mxfp4.
  */
 #define FP4Q_TILES_A 1u
 #define FP4Q_TILES_B 2u
+#define FP4Q_IF4_A 4u
+#define FP4Q_IF4_B 8u
 fp4q_status fp4q_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tensor_scale,
-                            int64_t m, int64_t n, int64_t k, unsigned scale_tiles, fp4q_dtype out_dt, void* c,
+                            int64_t m, int64_t n, int64_t k, unsigned operand_flags, fp4q_dtype out_dt, void* c,
                             float* amax, hipStream_t stream);
 
 /*

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_entry_point():
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert B.fp4q_abi_version() == 9
+    assert B.fp4q_abi_version() == 10
     assert B.fp4q_status_string(0) == "ok"
     assert "NULL" in B.fp4q_status_string(1)
 
@@ -117,8 +117,12 @@ def test_other_entry_points_validate():
     assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 0, 5, A2, None, 0) == 4
     assert L.fp4q_gemm_nvfp4(A, A, A2 + 2, A, A, A2, 64, 64, 128, 0, 0, A2, None, 0) == 3
     assert L.fp4q_gemm_nvfp4(A, MIS, A2, A, A, A2, 64, 64, 128, 0, 0, A2, None, 0) == 3
-    # 16x16 scale tiles: flag bits 0-1 only, and the tiled operand's rows a multiple of 16
-    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 4, 0, A2, None, 0) == 4
+    # operand flags: bits 0-3 only; an operand cannot be both 16x16-tiled and IF4; a
+    # tiled operand's rows are a multiple of 16
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 16, 0, A2, None, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 1 | 4, 0, A2, None, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 128, 2 | 8, 0, A2, None, 0) == 4
+    assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 64, 192, 4, 0, A2, None, 0) == 2
     assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 40, 64, 128, 1, 0, A2, None, 0) == 2
     assert L.fp4q_gemm_nvfp4(A, A, A2, A, A, A2, 64, 40, 128, 2, 0, A2, None, 0) == 2
     # the optional output amax must be 4-byte aligned

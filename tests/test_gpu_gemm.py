@@ -146,12 +146,12 @@ def _nv_check(got, exact, cabs, k, bf16=False):
                            f"err {err[tuple(bad[0])]:.3e} tol {tol[tuple(bad[0])]:.3e}")
 
 
-def _nv_gemm(ac, as_, ga, bc, bs, gb, out_dtype=torch.float32, tiles=0):
+def _nv_gemm(ac, as_, ga, bc, bs, gb, out_dtype=torch.float32, flags=0):
     m, n, k = ac.shape[0], bc.shape[0], ac.shape[1] * 2
     c = torch.full((m, n), float("nan"), dtype=out_dtype, device=DEV)
     ta = torch.tensor([ga], dtype=torch.float32, device=DEV)
     tb = torch.tensor([gb], dtype=torch.float32, device=DEV)
-    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, tiles, B._dt(c), c)
+    B.fp4q_gemm_nvfp4(_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, flags, B._dt(c), c)
     torch.cuda.synchronize()
     return c.float().cpu().numpy().astype(np.float64)
 
@@ -233,9 +233,9 @@ def test_nvfp4_forward_and_dgrad_with_2d_weight_end_to_end():
     assert np.array_equal(h(qwt["scales"]), h(qw["scales"]).T)
     assert np.array_equal(h(qwt["codes"]), h(qw["codes_t"]))
     y = B.gemm_nvfp4(qx["row_codes"], qx["row_scales"], qx["tensor_scale"], qw["codes"], qw["scales"],
-                     qw["tensor_scale"], scale_tiles=B.TILES_B)
+                     qw["tensor_scale"], operand_flags=B.TILES_B)
     dx = B.gemm_nvfp4(qd["row_codes"], qd["row_scales"], qd["tensor_scale"], qwt["codes"], qwt["scales"],
-                      qwt["tensor_scale"], scale_tiles=B.TILES_B)
+                      qwt["tensor_scale"], operand_flags=B.TILES_B)
     for got, (a, b) in ((y, (qx, qw)), (dx, (qd, qwt))):
         exact, cabs = oracle.gemm_nvfp4(h(a["row_codes"]), h(a["row_scales"]), float(h(a["tensor_scale"])[0]),
                                         h(b["codes"]), h(b["scales"]), float(h(b["tensor_scale"])[0]), flags=2)
@@ -342,3 +342,81 @@ def test_gemm_amax_full_size_launch():
     B.fp4q_gemm_mxfp4(_dev(ac), _dev(as_), _dev(bc), _dev(bs), m, n, k, B.BF16, c, amax)
     torch.cuda.synchronize()
     assert amax.item() == c.float().abs().max().item()
+
+
+# --- IF4 operands -------------------------------------------------------------------
+# An IF4 operand's INT4 element e = fl(fl(q fl(6/7)) s) reaches the bf16 MFMA as
+# hi + lo (hi = bf16(e), lo = bf16(e - hi)): two bf16 roundings of at most 2^-8 each
+# after e's fp32 rounding put hi + lo within d = 2^-16 + 2^-23 of the exact element
+# (2^-23 also covering the product of the small terms).  One IF4 operand: each product
+# term within d |a b|.  Both: (1 + d)^2 - 1 plus the omitted lo x lo (at most about
+# 2^-16 |a b|), below 3 d.  Each K block then takes 1 + (IF4 operands) MFMAs, which
+# lengthens the fp32 accumulation chain by that factor.
+
+def _if4_operand(rng, rows, k, int_share=0.5):
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, size=(rows, k // 16), dtype=np.uint8)
+    flags = (rng.random(size=scales.shape) < int_share).astype(np.uint8) << 7
+    return codes, scales | flags
+
+
+def _if4_check(got, exact, cabs, k, nif4, bf16=False):
+    d = 2.0 ** -16 + 2.0 ** -23
+    split = d if nif4 == 1 else 3.0 * d
+    tol = (2.0 * (4 + (1 + nif4) * k / 16) * 2.0 ** -24 + split) * cabs + 3.0 * 2.0 ** -24 * np.abs(exact)
+    if bf16:
+        tol = tol + 2.0 ** -8 * (np.abs(exact) + tol)
+    err = np.abs(got - exact)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, (f"{len(bad)} of {err.size} outside the bound; first {bad[:4].tolist()}, "
+                           f"err {err[tuple(bad[0])]:.3e} tol {tol[tuple(bad[0])]:.3e}")
+
+
+@pytest.mark.parametrize("shape,flags,bf16", [((256, 256, 128), 4, False), ((300, 520, 384), 8, False),
+                                              ((257, 129, 256), 12, False), ((1, 1, 128), 12, False),
+                                              ((390, 200, 512), 4, True), ((513, 768, 1024), 12, True),
+                                              ((64, 2048, 2048), 8, True)])
+def test_if4_gemm_random_codes(shape, flags, bf16):
+    """IF4 x NVFP4, NVFP4 x IF4 and IF4 x IF4 on random codes with about half the blocks
+    flagged INT4, across ragged M/N edges and several K steps."""
+    m, n, k = shape
+    rng = np.random.default_rng(m * 13 + n * 5 + k + flags)
+    ac, as_ = (_if4_operand if flags & 4 else _nv_operand)(rng, m, k)
+    bc, bs = (_if4_operand if flags & 8 else _nv_operand)(rng, n, k)
+    ga, gb = np.float32(41.75), np.float32(0.6875)
+    print(f"if4 gemm flags={flags} m={m} n={n} k={k} bf16={bf16}", flush=True)
+    got = _nv_gemm(ac, as_, ga, bc, bs, gb, torch.bfloat16 if bf16 else torch.float32, flags)
+    exact, cabs = oracle.gemm_nvfp4(ac, as_, ga, bc, bs, gb, flags=flags)
+    _if4_check(got, exact, cabs, k, bin(flags >> 2).count("1"), bf16)
+
+
+def test_if4_gemm_without_int4_blocks_is_the_nvfp4_product():
+    """With no block flagged the IF4 path stores bit-identical outputs to the NVFP4 path."""
+    m, n, k = 320, 288, 512
+    rng = np.random.default_rng(77)
+    ac, as_ = _if4_operand(rng, m, k, int_share=0.0)
+    bc, bs = _if4_operand(rng, n, k, int_share=0.0)
+    ref = _nv_gemm(ac, as_, 5.0, bc, bs, 0.5)
+    for flags in (4, 8, 12):
+        assert np.array_equal(_nv_gemm(ac, as_, 5.0, bc, bs, 0.5, flags=flags), ref), flags
+
+
+def test_if4_gemm_of_quantizer_outputs_end_to_end():
+    """Y = X W^T from fp4q_quantize_if4 of a bf16 activation and an fp32 weight: the product
+    matches the oracle on the library's own codes and tracks the float product."""
+    m, n, k = 256, 320, 1024
+    x_bits = si.activation(m, k, seed=81)
+    w = si.weight(n, k, seed=82, std=0.02)
+    to_dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(DEV)
+    qx = B.quantize_if4(to_dev(x_bits))
+    qw = B.quantize_if4(torch.from_numpy(w).to(DEV))
+    h = lambda t: t.cpu().numpy()
+    assert (h(qx["scales"]) & 0x80).any() and (h(qw["scales"]) & 0x80).any()
+    y = B.gemm_nvfp4(qx["codes"], qx["scales"], qx["tensor_scale"], qw["codes"], qw["scales"], qw["tensor_scale"],
+                     operand_flags=B.IF4_A | B.IF4_B).cpu().numpy().astype(np.float64)
+    exact, cabs = oracle.gemm_nvfp4(h(qx["codes"]), h(qx["scales"]), float(h(qx["tensor_scale"])[0]),
+                                    h(qw["codes"]), h(qw["scales"]), float(h(qw["tensor_scale"])[0]), flags=12)
+    _if4_check(y, exact, cabs, k, 2)
+    f32 = lambda b: (np.ascontiguousarray(b).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = f32(x_bits) @ w.astype(np.float64).T
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.15
