@@ -443,27 +443,31 @@ __device__ __forceinline__ float e4m3_byte(uint32_t w, int byte) {
 // product) are left out.
 constexpr float kSixSevenths = 6.0f / 7.0f;   // fl(6/7)
 
-template <bool LO>
-__device__ __forceinline__ bf16x8_t if4_decode(uint32_t w, uint32_t sb) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16, rounded to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t{a, b}), bf16x2_t));
+}
+
+// Eight elements of an IF4 operand (code word w, scale byte sb) as hi and lo bf16 parts.
+__device__ __forceinline__ void if4_decode(uint32_t w, uint32_t sb, bf16x8_t& hi, bf16x8_t& lo) {
   const float s = __builtin_amdgcn_cvt_f32_fp8((int)(sb & 0x7Fu), 0);
   if (!(sb & 0x80u)) {
-    if constexpr (LO) return __builtin_bit_cast(bf16x8_t, u32x4_g{0u, 0u, 0u, 0u});
-    else return nv_decode(w, s);
+    hi = nv_decode(w, s);
+    lo = __builtin_bit_cast(bf16x8_t, u32x4_g{0u, 0u, 0u, 0u});
+    return;
   }
-  uint32_t o[4];
+  uint32_t h[4], l[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint32_t h[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int q = (int)(w << (28 - 8 * k - 4 * e)) >> 28;   // element 2k + e, sign-extended
-      const float v = ((float)q * kSixSevenths) * s;
-      const uint32_t hb = bf16_rne(v);
-      h[e] = LO ? (uint32_t)bf16_rne(v - __uint_as_float(hb << 16)) : hb;
-    }
-    o[k] = h[0] | (h[1] << 16);
+    const int q0 = (int)(w << (28 - 8 * k)) >> 28, q1 = (int)(w << (24 - 8 * k)) >> 28;   // elements 2k, 2k+1
+    const float v0 = ((float)q0 * kSixSevenths) * s, v1 = ((float)q1 * kSixSevenths) * s;
+    h[k] = pk_bf16(v0, v1);
+    l[k] = pk_bf16(v0 - __uint_as_float(h[k] << 16), v1 - __uint_as_float(h[k] & 0xFFFF0000u));
   }
-  return __builtin_bit_cast(bf16x8_t, u32x4_g{o[0], o[1], o[2], o[3]});
+  hi = __builtin_bit_cast(bf16x8_t, u32x4_g{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8_t, u32x4_g{l[0], l[1], l[2], l[3]});
 }
 
 // C = (A B^T) / (gs_a gs_b).  v_mfma_f32_32x32x16_bf16 takes, per lane, eight
@@ -563,37 +567,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      bf16x8_t fa[4], fb[4];
+      if constexpr (IF4 == 0) {
+        bf16x8_t fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (IF4 & 1) fa[i] = if4_decode<false>(ra[i][q >> 2][q & 3], (wa[i] >> (8 * (q >> 1))) & 0xFFu);
-        else fa[i] = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
-        if constexpr (IF4 & 2) fb[i] = if4_decode<false>(rb[i][q >> 2][q & 3], (wb[i] >> (8 * (q >> 1))) & 0xFFu);
-        else fb[i] = nv_decode(rb[i][q >> 2][q & 3], e4m3_byte(wb[i], q >> 1));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      if constexpr (IF4 & 2) {   // hi(A) x lo(B)
-        bf16x8_t fl[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fl[j] = if4_decode<true>(rb[j][q >> 2][q & 3], (wb[j] >> (8 * (q >> 1))) & 0xFFu);
+        for (int i = 0; i < 4; ++i) {
+          fa[i] = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
+          fb[i] = nv_decode(rb[i][q >> 2][q & 3], e4m3_byte(wb[i], q >> 1));
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fl[j], acc[i][j], 0, 0, 0);
-      }
-      if constexpr (IF4 & 1) {   // lo(A) x hi(B)
-        bf16x8_t fl[4];
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      } else {
+        // B's four fragments (and their lo parts) first, then A one fragment at a time, so
+        // that only one A lo part is live: hi x hi, hi(A) x lo(B), lo(A) x hi(B).
+        bf16x8_t fb[4], fbl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fl[i] = if4_decode<true>(ra[i][q >> 2][q & 3], (wa[i] >> (8 * (q >> 1))) & 0xFFu);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (IF4 & 2) if4_decode(rb[j][q >> 2][q & 3], (wb[j] >> (8 * (q >> 1))) & 0xFFu, fb[j], fbl[j]);
+          else fb[j] = nv_decode(rb[j][q >> 2][q & 3], e4m3_byte(wb[j], q >> 1));
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          bf16x8_t fa, fal;
+          if constexpr (IF4 & 1) if4_decode(ra[i][q >> 2][q & 3], (wa[i] >> (8 * (q >> 1))) & 0xFFu, fa, fal);
+          else fa = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+          if constexpr (IF4 & 2) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fbl[j], acc[i][j], 0, 0, 0);
+          }
+          if constexpr (IF4 & 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fal, fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
       }
     }
   }
