@@ -375,14 +375,20 @@ def _if4_check(got, exact, cabs, k, nif4, bf16=False):
 @pytest.mark.parametrize("shape,flags,bf16", [((256, 256, 128), 4, False), ((300, 520, 384), 8, False),
                                               ((257, 129, 256), 12, False), ((1, 1, 128), 12, False),
                                               ((390, 200, 512), 4, True), ((513, 768, 1024), 12, True),
-                                              ((64, 2048, 2048), 8, True)])
+                                              ((64, 2048, 2048), 8, True), ((272, 160, 512), 1 | 8, False),
+                                              ((256, 304, 384), 4 | 2, True)])
 def test_if4_gemm_random_codes(shape, flags, bf16):
     """IF4 x NVFP4, NVFP4 x IF4 and IF4 x IF4 on random codes with about half the blocks
-    flagged INT4, across ragged M/N edges and several K steps."""
+    flagged INT4, across ragged M/N edges and several K steps; also an IF4 operand against
+    a 16x16-tiled NVFP4 one (flags 9 and 6)."""
     m, n, k = shape
     rng = np.random.default_rng(m * 13 + n * 5 + k + flags)
     ac, as_ = (_if4_operand if flags & 4 else _nv_operand)(rng, m, k)
     bc, bs = (_if4_operand if flags & 8 else _nv_operand)(rng, n, k)
+    if flags & 1:
+        as_ = as_[: m // 16].copy()
+    if flags & 2:
+        bs = bs[: n // 16].copy()
     ga, gb = np.float32(41.75), np.float32(0.6875)
     print(f"if4 gemm flags={flags} m={m} n={n} k={k} bf16={bf16}", flush=True)
     got = _nv_gemm(ac, as_, ga, bc, bs, gb, torch.bfloat16 if bf16 else torch.float32, flags)
