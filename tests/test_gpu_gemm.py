@@ -426,3 +426,27 @@ def test_if4_gemm_of_quantizer_outputs_end_to_end():
     f32 = lambda b: (np.ascontiguousarray(b).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     ref = f32(x_bits) @ w.astype(np.float64).T
     assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.15
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_if4_gemm_amax_is_max_abs_of_the_stored_output(bf16):
+    """The epilogue amax with IF4 operands (their own kernel instances): it equals max |C|
+    over the stored outputs, and C is the same with and without it."""
+    m, n, k = 288, 352, 640
+    rng = np.random.default_rng(91 + bf16)
+    ac, as_ = _if4_operand(rng, m, k)
+    bc, bs = _if4_operand(rng, n, k)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    ta = torch.tensor([7.5], device=DEV)
+    tb = torch.tensor([0.25], device=DEV)
+    amax = torch.full((1,), float("nan"), device=DEV)
+    c = torch.full((m, n), float("nan"), dtype=dt, device=DEV)
+    c2 = torch.full_like(c, float("nan"))
+    args = (_dev(ac), _dev(as_), ta, _dev(bc), _dev(bs), tb, m, n, k, B.IF4_A | B.IF4_B, B._dt(c))
+    B.fp4q_gemm_nvfp4(*args, c, amax)
+    B.fp4q_gemm_nvfp4(*args, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16 if bf16 else torch.int32), c2.view(torch.int16 if bf16 else torch.int32))
+    assert amax.item() == c.float().abs().max().item()
+    exact, cabs = oracle.gemm_nvfp4(ac, as_, np.float32(7.5), bc, bs, np.float32(0.25), flags=12)
+    _if4_check(c.float().cpu().numpy().astype(np.float64), exact, cabs, k, 2, bf16)
