@@ -542,6 +542,25 @@ class GemmNVFP4Wgrad(GemmMXFP4):
     kernel_launch = step
     given_launch = step
 
+    def extra(self, stream):
+        """The same product with IF4 operands (fp4q_quantize_if4 of dY^T and X^T, no RHT):
+        one IF4 operand (A) and both, against the NVFP4 product above."""
+        import torch
+        import synth_inputs as si
+        B = self.B
+        t = lambda b: _dev_bf16(b).t().contiguous()
+        qa = B.quantize_if4(t(si.wgrad_gradient(self.k, self.m, seed=4)))
+        qb = B.quantize_if4(t(si.wgrad_activation(self.k, self.n, seed=4)))
+        (nc, ns, ng), _ = self.ops[0]
+        y = self.y[0]
+        one = lambda i: B.fp4q_gemm_nvfp4(qa["codes"], qa["scales"], qa["tensor_scale"], nc, ns, ng, self.m, self.n,
+                                          self.k, B.IF4_A, B.BF16, y)
+        both = lambda i: B.fp4q_gemm_nvfp4(qa["codes"], qa["scales"], qa["tensor_scale"], qb["codes"], qb["scales"],
+                                           qb["tensor_scale"], self.m, self.n, self.k, B.IF4_A | B.IF4_B, B.BF16, y)
+        share = float(((qa["scales"] & 0x80) != 0).float().mean().item())
+        return {"if4_a_ms": _event_mean(stream, one, n=20, warm=10),
+                "if4_both_ms": _event_mean(stream, both, n=20, warm=10), "if4_int4_block_share_a": share}
+
 
 class BlockVariants(Workload):
     """The block formats compared with IF4 on the IF4 workload's bf16 [32768 x 8192]
