@@ -430,8 +430,15 @@ class WgradRHT(Workload):
         B = self.B
         rtn = _event_mean(stream, lambda i: self._q(self.xa[i % self.sets], self.out[i % self.sets][1], B.RTN, 41,
                                                     B.AMAX_GIVEN))
+        sr = _event_mean(stream, self.kernel_launch, n=50, warm=20)
         flops = 2 * 128 * self.rows * self.cols
-        return {"rtn_quantizer_ms": rtn, "mfma_dense_flop_per_operand": flops}
+        # the transform as a dense contraction on the bf16 MFMA, against its dense peak; the
+        # algorithmic minimum, a fast Walsh-Hadamard transform, is 7 adds per element
+        util = lambda ms: flops / (ms * 1e-3) / 1e12
+        return {"rtn_quantizer_ms": rtn, "mfma_dense_flop_per_operand": flops,
+                "mfma_TFLOPs_sr": util(sr), "mfma_frac_of_bf16_peak_sr": util(sr) / PEAK_MFMA_BF16_TFLOPS,
+                "mfma_TFLOPs_rtn": util(rtn), "mfma_frac_of_bf16_peak_rtn": util(rtn) / PEAK_MFMA_BF16_TFLOPS,
+                "fwht_adds_per_element": 7}
 
 
 class WeightMXFP6(Workload):
@@ -677,7 +684,20 @@ def _event_mean(stream, fn, n: int = 100, warm: int = 50) -> float:
     return e0.elapsed_time(e1) / n
 
 
-def run(wl: Workload, steps: int, warmup: int, cpu_budget: float, flush) -> dict:
+def copy_reference(stream) -> float:
+    """GB/s (bytes read + written) of a plain device copy of 512 MiB, beyond the 256 MB
+    Infinity Cache: the bandwidth a streaming kernel can reach on this machine, beside the
+    8 TB/s of the specification."""
+    import torch
+    n = 1 << 29
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    ms = _event_mean(stream, lambda i: dst.copy_(src), n=20, warm=5)
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def run(wl: Workload, steps: int, warmup: int, cpu_budget: float, flush, copy_gbps: float | None = None) -> dict:
     import torch
     wl.setup()
     cb = wl.cpu_baseline(cpu_budget) if cpu_budget > 0 else None    # includes the parity check
@@ -735,6 +755,10 @@ def run(wl: Workload, steps: int, warmup: int, cpu_budget: float, flush) -> dict
     else:
         line["config"]["whole_step_TFLOPs"] = wl.flops / (ms_per_step * 1e-3) / 1e12
     line["config"].update(wl.extra(stream))
+    if copy_gbps and not mfma:
+        line["config"]["copy_reference_GBps"] = copy_gbps
+        line["config"]["whole_step_frac_of_copy"] = step_gbps / copy_gbps
+        line["roofline"]["frac_of_copy"] = achieved / copy_gbps
     if cb is not None:
         line["cpu_baseline"] = cb
     return line
@@ -746,8 +770,8 @@ def _summary(line: dict) -> dict:
     keep = {k: v for k, v in c.items() if k not in ("workload",)}
     return {"workload": c["workload"], "value": line["value"], "unit": line["unit"], "dtype": line["dtype"],
             "ms_per_step": line["ms_per_step"], **keep,
-            "roofline": {k: r[k] for k in ("bound", "kernel", "achieved", "peak", "unit", "frac", "traffic",
-                                           "kernel_ms_mean")}}
+            "roofline": {k: r[k] for k in ("bound", "kernel", "achieved", "peak", "unit", "frac", "frac_of_copy",
+                                           "traffic", "kernel_ms_mean") if k in r}}
 
 
 def main(argv=None):
@@ -772,17 +796,19 @@ def main(argv=None):
     B.lib()
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     flush = lambda: scratch.fill_(1)
+    copy_gbps = copy_reference(torch.cuda.current_stream())
     if a.config == "headline":
-        line = run(HEADLINE(), a.steps, a.warmup, a.cpu_budget, flush)
+        line = run(HEADLINE(), a.steps, a.warmup, a.cpu_budget, flush, copy_gbps)
         if not a.no_others:
             others = []
             for cls in OTHERS:
                 torch.cuda.empty_cache()
-                others.append(_summary(run(cls(), a.steps, a.warmup, 0.0, flush)))
+                others.append(_summary(run(cls(), a.steps, a.warmup, 0.0, flush, copy_gbps)))
                 print(f"# timed {others[-1]['workload']}", file=sys.stderr, flush=True)
             line["config"]["other_workloads"] = others
     else:
-        line = run(WORKLOADS[a.config](), a.steps, a.warmup, a.cpu_budget if a.config != "copy" else 0.0, flush)
+        line = run(WORKLOADS[a.config](), a.steps, a.warmup, a.cpu_budget if a.config != "copy" else 0.0, flush,
+                   copy_gbps)
     print(json.dumps(line), flush=True)
     return 0
 
