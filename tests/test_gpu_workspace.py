@@ -106,6 +106,50 @@ def test_graph_capture_first_call_on_a_fresh_stream_replays_correctly():
     ws.close()
 
 
+def test_graph_capture_of_rht_2d_variant_dequant_and_gemm_calls_replays_correctly():
+    """The other two-pass calls and the GEMM epilogue amax under capture: the RHT
+    column-wise quantizer with SR, NVFP4 16x16, the IF6 variant with its dequantization,
+    and an MXFP4 GEMM reporting max |C|.  Each replay, on a new input, stores what the same
+    calls made eagerly on that input store (each eager path is checked against the oracle
+    elsewhere)."""
+    rows, cols = 512, 768
+    ws = B.Workspace()
+    signs = B.fp4q_rht_signs_from_seed(11)
+    x = torch.empty(rows, cols, dtype=torch.bfloat16, device=DEV)
+    inputs = [si.activation(rows, cols, seed=s) for s in (61, 62, 63)]
+    inputs = [si.f32_to_bf16_bits(si.bf16_bits_to_f32(b) * np.float32(3.0 ** -i)) for i, b in enumerate(inputs)]
+    x.copy_(dev_bf16(inputs[0]))
+    torch.cuda.synchronize()
+
+    def calls():
+        r = B.quantize_nvfp4(x, B.COLWISE, rnd=B.SR, sr_seed=7, rht_signs=signs, ws=ws)
+        t = B.quantize_nvfp4_2d(x, ws=ws)
+        v = B.quantize_variant(x, B.VAR_IF6, ws=ws)
+        y = B.dequantize_variant(B.VAR_IF6, v["codes"], v["scales"], v["tensor_scale"], rows, cols, torch.bfloat16)
+        m = B.quantize_mxfp4(x, ws=ws)
+        amax = torch.empty(1, dtype=torch.float32, device=DEV)
+        c = B.gemm_mxfp4(m, m, torch.bfloat16, amax=amax)
+        return {"rc": r["col_codes"], "rs": r["col_scales"], "rts": r["tensor_scale"], "tc": t["codes"],
+                "tsc": t["scales"], "vc": v["codes"], "vs": v["scales"], "y": y, "c": c, "camax": amax}
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = calls()
+    for i, bits in enumerate(inputs):
+        x.copy_(dev_bf16(bits))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = calls()
+        torch.cuda.synchronize()
+        for k in cap:
+            assert torch.equal(cap[k], eager[k]), (i, k)
+        assert cap["camax"].item() == cap["c"].float().abs().max().item(), i
+    del g
+    torch.cuda.synchronize()
+    ws.close()
+
+
 @pytest.mark.parametrize("shape", [(256, 512), (4000, 2608)])
 def test_no_workspace_equals_workspace(shape):
     rows, cols = shape
