@@ -511,13 +511,13 @@ class GemmMXFP4(Workload):
 
 class GemmNVFP4Wgrad(GemmMXFP4):
     """dY^T X from the Wgrad workload's RHT-quantized operands: [4096 x 4096] over 16384
-    tokens, bf16 out, on the bf16 MFMA after an exact decode."""
+    tokens, bf16 out, on the f16 MFMA after an exact decode (dense peak 2.5 PFLOP/s, as bf16)."""
     name = "wgrad_gemm_nvfp4_rht_4096x4096x16384_bf16_out"
     m = n = 4096
     k = 16384
     bound, peak, unit = "mfma", PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
     dtype = "bf16"
-    metric = "NVFP4 GEMM FLOP/s and % of MI355X dense bf16 matrix-core peak"
+    metric = "NVFP4 GEMM FLOP/s and % of MI355X dense f16/bf16 matrix-core peak"
 
     def __init__(self):
         self.flops = 2 * self.m * self.n * self.k

@@ -383,11 +383,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------------------
 // NVFP4 1x16 operands: the scaled MFMA takes only power-of-two (E8M0) block scales, and an
 // E4M3 scale has a 3-bit significand, so each element is decoded to r * s (at most six
-// significant bits: exact in bf16) and multiplied on the bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16); the tensor scales are applied once to the fp32 sums.
+// significant bits: exact in f16 and in bf16) and multiplied on a 16-bit MFMA with fp32
+// accumulation, f16 (v_mfma_f32_32x32x16_f16) for NVFP4 operands and bf16 where an IF4
+// operand takes part; the tensor scales are applied once to the fp32 sums.
 // The scaled FP4 convert applies only the exponent of its scale operand (checked on the
 // box with non-power-of-two scales), so the decode converts with scale 1 and multiplies
-// by s in fp32.
+// by s afterwards.
 // ---------------------------------------------------------------------------------------
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -420,6 +421,23 @@ __device__ __forceinline__ bf16x8_t nv_decode(uint32_t w, float s) {
   const uint32_t o2 = nv_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), s);
   const uint32_t o3 = nv_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), s);
   return __builtin_bit_cast(bf16x8_t, u32x4_g{o0, o1, o2, o3});
+}
+
+// The same decode to f16 for the f16 MFMA: r * s lies between 2^-10 and 2688 in magnitude
+// (E2M1 magnitudes 0.5..6 times E4M3 scales 2^-9..448) with at most six significant bits,
+// so it is exact in f16's normal range and the packed f16 multiply never rounds; the convert
+// gives r itself (scale 1) and s is an exact f16 too.  Half the instructions of the bf16
+// decode: one convert and one packed multiply per two elements.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x8_t nv_decode_h(uint32_t w, _Float16 s) {
+  const f16x2_t ss = {s, s};
+  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  return f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ float e4m3_byte(uint32_t w, int byte) {
@@ -470,7 +488,7 @@ __device__ __forceinline__ void if4_decode(uint32_t w, uint32_t sb, bf16x8_t& hi
   lo = __builtin_bit_cast(bf16x8_t, u32x4_g{l[0], l[1], l[2], l[3]});
 }
 
-// C = (A B^T) / (gs_a gs_b).  v_mfma_f32_32x32x16_bf16 takes, per lane, eight
+// C = (A B^T) / (gs_a gs_b).  v_mfma_f32_32x32x16_f16 / _bf16 take, per lane, eight
 // consecutive K elements of row l % 32 in its half l / 32 of the instruction's 16; K
 // order inside a step is free as long as A and B agree, so MFMA q (0..7) of a step
 // gives lane half 0 the row's code word q (elements 8q..8q+7, block q/2) and half 1 the
@@ -568,17 +586,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if constexpr (IF4 == 0) {
-        bf16x8_t fa[4], fb[4];
+        f16x8_t fa[4], fb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[i] = nv_decode(ra[i][q >> 2][q & 3], e4m3_byte(wa[i], q >> 1));
-          fb[i] = nv_decode(rb[i][q >> 2][q & 3], e4m3_byte(wb[i], q >> 1));
+          fa[i] = nv_decode_h(ra[i][q >> 2][q & 3], (_Float16)e4m3_byte(wa[i], q >> 1));
+          fb[i] = nv_decode_h(rb[i][q >> 2][q & 3], (_Float16)e4m3_byte(wb[i], q >> 1));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       } else {
         // B's four fragments (and their lo parts) first, then A one fragment at a time, so
         // that only one A lo part is live: hi x hi, hi(A) x lo(B), lo(A) x hi(B).

@@ -114,7 +114,7 @@ void launch_dequant_mxfp6(int fmt, const uint8_t* codes, const uint8_t* scales, 
 bool launch_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, bool bf16_out, void* c,
                        float* amax, hipStream_t st);
-// NVFP4 1x16 GEMM C = A B^T / (gs_a gs_b) on the bf16 MFMA -- fp4q_gemm.hip.  k % 128 == 0.
+// NVFP4 1x16 GEMM C = A B^T / (gs_a gs_b) on the f16 / bf16 MFMA -- fp4q_gemm.hip.  k % 128 == 0.
 // flags bit 0 / bit 1: A / B carries 16x16 scale tiles ([rows/16][k/16]) instead of 1x16;
 // bit 2 / bit 3: A / B is IF4 (scale bit 7 marks INT4 blocks).
 bool launch_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts, const uint8_t* b_codes,

@@ -320,8 +320,9 @@ fp4q_status fp4q_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
  * (row-wise, or the column-wise output of the transposed operand, e.g. the Wgrad pair
  * after the RHT), and gs_a = *a_tensor_scale, gs_b = *b_tensor_scale (device floats,
  * the encode scales the quantizer stored).  Each r * s (at most six significant bits)
- * is decoded exactly to bf16 and multiplied on the bf16 MFMA with fp32 accumulation;
- * the sums are multiplied by fl(1 / fl(gs_a gs_b)).
+ * is decoded exactly to f16 (bf16 where an IF4 operand takes part, see below) and
+ * multiplied on the 16-bit MFMA with fp32 accumulation; the sums are multiplied by
+ * fl(1 / fl(gs_a gs_b)).
  *   out_dt FP4Q_F32: float [m][n];  FP4Q_BF16: bf16 [m][n] = RNE(fp32 result).
  *   operand_flags  0 or an OR of:
  *     FP4Q_TILES_A / FP4Q_TILES_B: that operand carries NVFP4 16x16 scales as

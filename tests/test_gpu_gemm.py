@@ -124,7 +124,7 @@ def test_gemm_full_size_sampled():
 
 
 # ---------------------------------------------------------------------------------------
-# NVFP4 operands (bf16 MFMA after an exact decode).  Each product of two decoded values
+# NVFP4 operands (f16 MFMA after an exact decode; bf16 with IF4 operands).  Each product of two decoded values
 # r s has at most twelve significant bits, exact in fp32; an instruction sums 16, so the
 # summation depth is at most 4 + k/16.  The tensor scales add three roundings
 # (fl(gs_a gs_b), its reciprocal, the product): 3 u |C|.
