@@ -583,14 +583,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       wa[i] = s.sa[srA + 64 * i];
       wb[i] = s.sb[srB + 64 * i];
     }
+    // the scale bytes as f16 pairs, two per convert (E4M3 values are exact in f16)
+    f16x2_t sha[4][2], shb[4][2];
+    if constexpr (IF4 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sha[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa[i], 1.0f, false);
+        sha[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa[i], 1.0f, true);
+        shb[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb[i], 1.0f, false);
+        shb[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb[i], 1.0f, true);
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if constexpr (IF4 == 0) {
         f16x8_t fa[4], fb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[i] = nv_decode_h(ra[i][q >> 2][q & 3], (_Float16)e4m3_byte(wa[i], q >> 1));
-          fb[i] = nv_decode_h(rb[i][q >> 2][q & 3], (_Float16)e4m3_byte(wb[i], q >> 1));
+          fa[i] = nv_decode_h(ra[i][q >> 2][q & 3], sha[i][q >> 2][(q >> 1) & 1]);
+          fb[i] = nv_decode_h(rb[i][q >> 2][q & 3], shb[i][q >> 2][(q >> 1) & 1]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
