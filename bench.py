@@ -516,7 +516,7 @@ class GemmNVFP4Wgrad(GemmMXFP4):
     m = n = 4096
     k = 16384
     bound, peak, unit = "mfma", PEAK_MFMA_BF16_TFLOPS, "TFLOP/s"
-    dtype = "bf16"
+    dtype = "f16"   # exact f16 decodes of r * s, fp32 accumulation
     metric = "NVFP4 GEMM FLOP/s and % of MI355X dense f16/bf16 matrix-core peak"
 
     def __init__(self):
