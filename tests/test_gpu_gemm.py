@@ -171,6 +171,28 @@ def test_nvfp4_gemm_random_codes(shape, bf16):
     _nv_check(got, exact, cabs, k, bf16)
 
 
+def test_nvfp4_gemm_decode_range_edges():
+    """The largest and smallest decoded magnitudes, 6 * 448 = 2688 and 0.5 * 2^-9 = 2^-10
+    (E4M3 codes 126 and 1), in every combination and both signs: the decode keeps them
+    exact, so each output is an exact sum that the oracle reproduces."""
+    m, n, k = 256, 256, 256
+    rng = np.random.default_rng(77)
+    big, small = 0x7, 0x1                                   # E2M1 codes of 6 and 0.5
+    def operand(rows):
+        nib = np.where(rng.random((rows, k)) < 0.5, big, small).astype(np.uint8)
+        nib |= (rng.random((rows, k)) < 0.5).astype(np.uint8) << 3          # sign bit
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        scales = np.where(rng.random((rows, k // 16)) < 0.5, 126, 1).astype(np.uint8)
+        return codes, scales
+    ac, as_ = operand(m)
+    bc, bs = operand(n)
+    ga, gb = np.float32(1.0), np.float32(1.0)
+    print(f"nvfp4 gemm decode range edges m={m} n={n} k={k}", flush=True)
+    got = _nv_gemm(ac, as_, ga, bc, bs, gb)
+    exact, cabs = oracle.gemm_nvfp4(ac, as_, ga, bc, bs, gb)
+    _nv_check(got, exact, cabs, k)
+
+
 def test_nvfp4_gemm_wgrad_after_rht_end_to_end():
     """Wgrad = dY^T X from the column-wise NVFP4 operands after the 128-token RHT
     (SR for the gradient, RTN for the activation): the product matches the oracle on the
