@@ -1219,24 +1219,40 @@ void launch_if4(const void* x, int dtype, int64_t rows, int64_t cols, const Amax
 }
 
 // ===========================================================================
-// NVFP4 16x16 (2D).  Sixteen lanes own one 16x16 tile, one tile row each; a wave
-// holds four horizontally adjacent tiles.  The tile maximum is a 16-lane DPP
-// reduction.  The optional transposed codes go through LDS.
+// NVFP4 16x16 (2D).  Sixteen lanes own one 16x16 tile, four columns of four rows
+// each; a wave holds four horizontally adjacent tiles.  The tile maximum is a
+// 16-lane reduction.  The optional transposed codes go through LDS.
 // ===========================================================================
 
-__device__ __forceinline__ float max16_lanes(float v) {
+// Maximum over the 16 lanes of one 16x16 tile in the layout of k_nvfp4_2d: lanes
+// l ^ 1, l ^ 2 (DPP within the quad), l ^ 16 and l ^ 32 (lane-row swaps).
+__device__ __forceinline__ float max_tile_lanes(float v) {
   v = lane_xor_max<1>(v);
   v = lane_xor_max<2>(v);
-  // rotate within rows of 16 lanes by 4 and 8 (v >= 0: integer max on the bits)
-  uint32_t u = __float_as_uint(v);
-  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x124, 0xF, 0xF, false));
-  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, false));
-  return __uint_as_float(u);
+  const uint32_t u = __float_as_uint(v);
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);   // (own, l ^ 16) in some order
+  const float m16 = __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  const uint32_t w = __float_as_uint(m16);
+  auto s32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);   // (own, l ^ 32) in some order
+  return __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 
-// A workgroup takes k2dSteps consecutive runs of 16 tiles (each wave four
-// horizontally adjacent tiles per run); all of a lane's row loads are issued before
-// any tile is encoded.
+__device__ __forceinline__ void load4(const float* __restrict__ p, float* o) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float* o) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+}
+
+// A wave holds four horizontally adjacent 16x16 tiles per run.  Lane l = 16q + 4t + u
+// takes columns 4u..4u+3 of tile t in rows q, q+4, q+8 and q+12, so each of its four
+// row loads is one instruction over four whole 64-column row pieces (one contiguous
+// 256-byte span per row in a 16-aligned run of tiles).  A workgroup takes k2dSteps
+// consecutive runs of 16 tiles; all of a lane's row loads are issued before any tile
+// is encoded.  Each lane stores the 2 code bytes of its four columns per row: one
+// store instruction writes four rows' 32 contiguous bytes per tile run of a wave.
 constexpr int k2dSteps = 4;
 
 template <typename T, bool TRANS>
@@ -1251,8 +1267,8 @@ __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64
   const float gs = tensor_scale_publish(amax, tensor_scale);
   const int64_t tiles_c = cols >> 4, tiles = (rows >> 4) * tiles_c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tin = lane >> 4, i = lane & 15;                 // tile within wave, row within tile
-  float a[k2dSteps][8], b[k2dSteps][8];
+  const int q = lane >> 4, tin = (lane >> 2) & 3, u = lane & 3;
+  float v[k2dSteps][16];   // v[j][4k + e]: row q + 4k, column 4u + e of the lane's tile
   int64_t br[k2dSteps], bc[k2dSteps];
   bool ok[k2dSteps];
 #pragma unroll
@@ -1262,42 +1278,43 @@ __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64
     const int64_t t = ok[j] ? tile : tiles - 1;            // past the end: reload the last tile
     br[j] = t / tiles_c;
     bc[j] = t - br[j] * tiles_c;
-    const int64_t r = br[j] * 16 + i, c0 = bc[j] * 16;
-    load8(x, r * cols + c0, a[j]);
-    load8(x, r * cols + c0 + 8, b[j]);
+    const T* px = x + (br[j] * 16 + q) * cols + bc[j] * 16 + 4 * u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load4(px + 4 * k * cols, &v[j][4 * k]);
   }
 #pragma unroll
   for (int j = 0; j < k2dSteps; ++j) {
     float m = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      a[j][k] = a[j][k] * gs;
-      b[j][k] = b[j][k] * gs;
-      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(a[j][k]), __builtin_fabsf(b[j][k])));
+    for (int k = 0; k < 16; ++k) {
+      v[j][k] = v[j][k] * gs;
+      m = __builtin_fmaxf(m, __builtin_fabsf(v[j][k]));
     }
-    m = max16_lanes(m);
+    m = max_tile_lanes(m);
     const uint32_t sc = nvfp4_scale_code(m);
     const RecipPair rp = rtab.r[sc];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      a[j][k] = div2(a[j][k], rp);
-      b[j][k] = div2(b[j][k], rp);
-    }
-    const uint32_t w0 = pack8_rtn(a[j], 1.0f), w1 = pack8_rtn(b[j], 1.0f);
-    const int64_t r = br[j] * 16 + i, c0 = bc[j] * 16;
+    for (int k = 0; k < 16; ++k) v[j][k] = div2(v[j][k], rp);
+    // w0: rows q (bits 0..15) and q + 4 (16..31); w1: rows q + 8 and q + 12
+    const uint32_t w0 = pack8_rtn(&v[j][0], 1.0f), w1 = pack8_rtn(&v[j][8], 1.0f);
+    const uint16_t piece[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
     if (ok[j]) {
-      *reinterpret_cast<uint2*>(codes + r * (cols >> 1) + (c0 >> 1)) = make_uint2(w0, w1);
-      if (i == 0) scales[br[j] * tiles_c + bc[j]] = (uint8_t)sc;
+      uint8_t* dst = codes + (br[j] * 16 + q) * (cols >> 1) + bc[j] * 8 + 2 * u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) *reinterpret_cast<uint16_t*>(dst + 4 * k * (cols >> 1)) = piece[k];
+      if ((lane & 0x33) == 0) scales[br[j] * tiles_c + bc[j]] = (uint8_t)sc;   // q == 0, u == 0
     }
     if constexpr (TRANS) {
-      lds[j][wave * 4 + tin][i][0] = w0;
-      lds[j][wave * 4 + tin][i][1] = w1;
+      uint16_t* l16 = reinterpret_cast<uint16_t*>(&lds[j][wave * 4 + tin][0][0]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l16[(q + 4 * k) * 4 + u] = piece[k];
     }
   }
   if constexpr (TRANS) {
     __syncthreads();
-    // lane i now gathers column i of its tile: nibble i of every row
-    const int tb = wave * 4 + tin, word = i >> 3, sh = (i & 7) * 4;
+    // lane l now gathers column i = l & 15 of tile l >> 4 of its wave: nibble i of every row
+    const int tt = lane >> 4, i = lane & 15;
+    const int tb = wave * 4 + tt, word = i >> 3, sh = (i & 7) * 4;
 #pragma unroll
     for (int j = 0; j < k2dSteps; ++j) {
       uint32_t o0 = 0, o1 = 0;
@@ -1306,8 +1323,11 @@ __global__ __launch_bounds__(256) void k_nvfp4_2d(const T* __restrict__ x, int64
         o0 |= ((lds[j][tb][rr][word] >> sh) & 0xFu) << (4 * rr);
         o1 |= ((lds[j][tb][rr + 8][word] >> sh) & 0xFu) << (4 * rr);
       }
-      const int64_t c0 = bc[j] * 16;
-      if (ok[j]) *reinterpret_cast<uint2*>(codes_t + (c0 + i) * (rows >> 1) + (br[j] * 16 >> 1)) = make_uint2(o0, o1);
+      const int64_t tile = ((int64_t)blockIdx.x * k2dSteps + j) * 16 + tb;
+      if (tile < tiles) {
+        const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
+        *reinterpret_cast<uint2*>(codes_t + (tc * 16 + i) * (rows >> 1) + (tr * 16 >> 1)) = make_uint2(o0, o1);
+      }
     }
   }
 }
