@@ -104,7 +104,12 @@ __device__ __forceinline__ uint32_t rht_swz(uint32_t r) { return ((r & 1u) * 3u)
 // The address of load i is the uniform row base of tokens tok0 + 8i (scalar registers)
 // plus this lane's byte offset, which fits 32 bits because cols < 2^27 (checked by the
 // caller); with the buffer picked by a uniform wave index, the per-load address and
-// LDS base steps run on the scalar unit.
+// LDS base steps run on the scalar unit.  NT marks the loads non-temporal: the
+// quantizer's read is the operand's last, and with it the amax pass of the next
+// operand runs 26 instead of 30 us on bf16 16384 x 4096 (the quantizer itself is as
+// fast either way); the amax pass keeps normal loads, which leave the operand in the
+// Infinity Cache for the quantizer after it.
+template <bool NT>
 __device__ __forceinline__ void rht_issue(const uint16_t* __restrict__ x, int64_t cols, int64_t tok0, int64_t col0,
                                           RhtStage& st) {
   const uint32_t lane = threadIdx.x & 63;
@@ -113,7 +118,7 @@ __device__ __forceinline__ void rht_issue(const uint16_t* __restrict__ x, int64_
   const char* rows0 = reinterpret_cast<const char*>(x + tok0 * cols);
 #pragma unroll
   for (int i = 0; i < 16; ++i)
-    __builtin_amdgcn_global_load_lds(rows0 + (int64_t)(16 * i) * cols + off, &st.w[i * 256], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rows0 + (int64_t)(16 * i) * cols + off, &st.w[i * 256], 16, 0, NT ? 2 : 0);   // aux bit 1: nt
 }
 
 // The direct loads are invisible to the compiler's wait counting: wait for every
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lane = threadIdx.x & 63;
   float m = 0.0f;
   TileWalk w(rows, cols);
-  if (w.valid()) rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
+  if (w.valid()) rht_issue<false>(x, cols, w.chunk * 128, w.slab * 64, st);
   for (; w.valid(); w.next()) {
     const int64_t col = w.slab * 64 + (lane & 31);   // column of pass 0; pass 1 is col + 32
     RhtB B;
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rht_wait_lds();
     TileWalk nw = w;
     nw.next();
-    if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
+    if (nw.valid()) rht_issue<false>(x, cols, nw.chunk * 128, nw.slab * 64, st);
     float t[2] = {0.0f, 0.0f};
     auto fold = [&](const f32x16 (&acc)[2][2]) {
 #pragma unroll
@@ -537,7 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // waits for its half's MFMAs; the wave's SIMD partner keeps the vector ALUs busy
   // meanwhile (the two waves' VALU and MFMA work overlap).
   RhtB B;
-  rht_issue(x, cols, w.chunk * 128, w.slab * 64, st);
+  rht_issue<true>(x, cols, w.chunk * 128, w.slab * 64, st);
   for (; w.valid(); w.next()) {
     rht_wait_loads();
     rht_read_b(st, B);
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     {
       TileWalk nw = w;
       nw.next();
-      if (nw.valid()) rht_issue(x, cols, nw.chunk * 128, nw.slab * 64, st);
+      if (nw.valid()) rht_issue<true>(x, cols, nw.chunk * 128, nw.slab * 64, st);
     }
     RhtTileOut t = rht_tile_out(w.chunk, w.slab, op);
     f32x16 acc[2][2];
