@@ -43,6 +43,21 @@ __device__ __forceinline__ void load8(const float* __restrict__ p, int64_t i, fl
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// Four consecutive elements, loaded non-temporally.  For kernels whose input is read
+// once and whose load instructions each cover whole cache lines (k_nvfp4_2d,
+// k_mxfp4): on fp32 8192 x 8192 the 16x16 quantizer runs 50.5 against 55.2 us with
+// them.  Kernels whose instructions read parts of lines that later instructions
+// complete are slower with non-temporal loads, since the parts no longer meet in L2.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void load4(const float* __restrict__ p, float* o) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float* o) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+}
+
 // ---------------------------------------------------------------------------
 // Division by a block scale in two operations, correctly rounded.
 //
