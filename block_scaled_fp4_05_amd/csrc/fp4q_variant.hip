@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256) void k_dequant_variant(const uint8_t* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{out[2 * i], out[2 * i + 1]}, bf16x2v));
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + e) = make_uint4(o[0], o[1], o[2], o[3]);
+      // a wave's store covers 1 KiB of whole lines, written once: non-temporal
+      __builtin_nontemporal_store(u32x4_t{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(y) + e));
     } else {
       float4* d = reinterpret_cast<float4*>(static_cast<float*>(y) + e);
       d[0] = make_float4(out[0], out[1], out[2], out[3]);
