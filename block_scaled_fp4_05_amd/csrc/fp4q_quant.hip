@@ -984,10 +984,20 @@ void launch_clear_fused(FusedArea* area, hipStream_t st) { launch_clear_scratch(
 // folds the lines afterwards and clears them again.  Spreading the posts over
 // kAmaxSpread cache lines keeps same-address atomics from queueing.  The post comes
 // after the codes are stored.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));  // the other quad of 8
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, false));  // the other half of 16
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);                  // the other row of 32
+  u = max(s16[0], s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);                  // the other half of 64
+  return max(s32[0], s32[1]);
+}
+
 __device__ __forceinline__ void mx_post_amax(uint32_t mb, uint32_t* __restrict__ spread) {
   __shared__ uint32_t wm[4];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+  mb = wave_max_u32(mb);
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mb;
   __syncthreads();
   if (threadIdx.x == 0)
