@@ -777,8 +777,12 @@ def _summary(line: dict) -> dict:
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 50 warm-up steps: after the host-side set-up the GPU's clocks need a few
+    # milliseconds of load to settle, and the VALU-bound kernels run up to 8 % slower
+    # until they have (IF4 round trip: 328 us per step over 20 steps after 5, 303 us over
+    # 100 after 50, 305 us over 200 after 200); the cold single steps are reported apart
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="headline", choices=["headline"] + list(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of single-thread oracle work for cpu_baseline (0: skip it and its parity check)")
