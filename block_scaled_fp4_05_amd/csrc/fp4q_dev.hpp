@@ -58,6 +58,60 @@ __device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float* o) 
   o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
 }
 
+// Sixteen consecutive elements per lane, where the 64 lanes of a wave take 64
+// consecutive 16-element groups, read with whole cache lines per load instruction.
+// stage_issue16 copies the wave's span (4 KB of fp32, 2 KB of bf16, starting at
+// element e_wave) to the wave's LDS buffer `buf` by non-temporal direct loads
+// (`global_load_lds_dwordx4`, no VGPR holds the data), each instruction covering 1 KB.
+// Within an instruction lane j fetches the 16-byte chunk that reading lane j % G needs
+// as its chunk j / G (G = 16 for fp32, 32 for bf16), so the chunks land transposed and
+// the 16-byte LDS reads of 16 consecutive reading lanes fall on distinct banks.  Chunks
+// at or past element n are fetched from the tensor's last chunk instead; only lanes
+// whose groups lie past the end read them.  After stage_wait (every direct load of the
+// wave done), stage_read16 gives each lane its 16 elements.  All lanes of the wave take
+// part; each buffer is filled once.
+__device__ __forceinline__ void lds_load16_nt(const void* g, uint32_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 2);   // aux bit 1: nt
+}
+
+template <typename T>
+__device__ __forceinline__ void stage_issue16(const T* __restrict__ x, int64_t n, int64_t e_wave, uint32_t* buf) {
+  constexpr int CH = 16 / (int)sizeof(T);          // elements per chunk: 4 (fp32) or 8 (bf16)
+  constexpr int SPANS = (int)sizeof(T);            // 1 KB load instructions per wave
+  constexpr int G = 64 / SPANS;                    // reading lanes per instruction
+  const int lane = threadIdx.x & 63;
+  const int c = lane / G, m = lane % G;            // fetch chunk c of reading lane m
+#pragma unroll
+  for (int sp = 0; sp < SPANS; ++sp) {
+    int64_t e = e_wave + (int64_t)CH * (sp * 64 + (16 / CH) * m + c);
+    e = e < n ? e : n - CH;
+    lds_load16_nt(x + e, buf + sp * 256);
+  }
+}
+
+__device__ __forceinline__ void stage_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <typename T>
+__device__ __forceinline__ void stage_read16(const uint32_t* buf, float out[16]) {
+  constexpr int CH = 16 / (int)sizeof(T);
+  constexpr int G = 64 / (int)sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int sp = lane / G, m = lane % G;
+#pragma unroll
+  for (int cc = 0; cc < 16 / CH; ++cc) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(buf + sp * 256 + 4 * (G * cc + m));
+    if constexpr (sizeof(T) == 4) {
+      out[4 * cc + 0] = __uint_as_float(w.x); out[4 * cc + 1] = __uint_as_float(w.y);
+      out[4 * cc + 2] = __uint_as_float(w.z); out[4 * cc + 3] = __uint_as_float(w.w);
+    } else {
+      out[8 * cc + 0] = bf16_lo(w.x); out[8 * cc + 1] = bf16_hi(w.x);
+      out[8 * cc + 2] = bf16_lo(w.y); out[8 * cc + 3] = bf16_hi(w.y);
+      out[8 * cc + 4] = bf16_lo(w.z); out[8 * cc + 5] = bf16_hi(w.z);
+      out[8 * cc + 6] = bf16_lo(w.w); out[8 * cc + 7] = bf16_hi(w.w);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Division by a block scale in two operations, correctly rounded.
 //

@@ -1523,13 +1523,15 @@ void launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const 
 template <typename T, int FMT>
 __global__ __launch_bounds__(256) void k_mxfp6(const T* __restrict__ x, int64_t n16, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales) {
+  __shared__ uint32_t stg[4][sizeof(T) * 256];   // each wave's span: 4 KB (fp32) or 2 KB (bf16)
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = g < n16;
   float a[16];
-  if (ok) {
-    load8(x, g * 16, a);
-    load8(x, g * 16 + 8, a + 8);
-  } else {
+  uint32_t* buf = stg[threadIdx.x >> 6];
+  stage_issue16(x, n16 * 16, ((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63u)) * 16, buf);
+  stage_wait();
+  stage_read16<T>(buf, a);
+  if (!ok) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) a[k] = 0.0f;
   }
